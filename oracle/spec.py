@@ -1,0 +1,208 @@
+"""Self-speculative decoding round on the float64 decoder (oracle).
+
+TEST INFRASTRUCTURE: see ``oracle/__init__.py``.
+
+Round structure (self-speculative decoding page, m.lqnn.cn/news/278124):
+* State: committed tokens; KV valid for positions 0..P-1; the last committed
+  token ("pending") sits at position P without KV.  Invariant P ==
+  len(tokens) - 1 (the page's §3.3 assert, restated for this convention).
+* Draft (§2.1, §4.2): k serial steps of layers 0..L-1 at position P+s,
+  writing KV at slot P+s, then final norm + LM head (§3.1: the norm must not be
+  skipped), then argmax or a sample from q = softmax(z/T).  Reading: a
+  finishing first-L pass over the last draft token gives verify its k+1 rows,
+  so verify only runs layers L..N-1 (KV reuse, §2.1 and §2.3).
+* Verify (§4.3): layers L..N-1 over rows [x, d_1..d_k] at P..P+k, then the
+  head: k+1 distributions; row i judges d_{i+1}, row k is the bonus.
+* Accept: greedy = longest prefix where the draft token equals the target's
+  argmax, then the target's argmax at the first mismatch ("DSpark" page §2.1;
+  greedy is its own branch, self-speculative page §2.4); stochastic = the
+  page's accept_or_reject (§4.3) with min(1, p/q), residual max(0, p-q),
+  fall back to p when the residual sums to <= 0, bonus from p_k.
+* Rollback (§3.3, §4.3): keep x, d_1..d_a, so P <- P + a + 1.  The page's
+  "seq_len + i" would drop d_a's KV under its own convention; this is the
+  reading listed in the design doc.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .decoder import Row, softmax
+
+FLAG_BAND = 1e-3  # |p/q - u| below this marks an acceptance decision as a near-tie
+SLOT_ACCEPT = 16  # uniform slots: 0..k-1 draft samples, 16.. accept tests, 32 residual/bonus
+SLOT_RESAMPLE = 32
+N_UNIFORMS = 48
+
+
+@dataclass
+class SeqState:
+    sid: int
+    tokens: list
+    P: int
+    pending: int
+    rounds: list = field(default_factory=list)  # accepted count per round
+
+    def check(self):
+        assert self.P == len(self.tokens) - 1, (self.P, len(self.tokens))
+        assert self.tokens[-1] == self.pending
+
+
+def argmax(z):
+    """Index of the largest value; ties go to the lowest index."""
+    return int(np.argmax(z))
+
+
+def probs(z, T):
+    """softmax(z / T) in float64."""
+    return softmax(np.asarray(z, dtype=np.float64) / T)
+
+
+def sample_index(w, u):
+    """Inverse-CDF draw from non-negative weights w with a uniform u in [0, 1).
+
+    S = sum(w) and the running sums C_j are taken in float64 in id order; the
+    draw is the smallest j with u*S < C_j, else the largest j with w_j > 0.
+    A zero-weight id is never returned.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    C = np.cumsum(w)
+    S = C[-1]
+    j = int(np.searchsorted(C, u * S, side="right"))
+    if j >= len(w):
+        j = int(np.nonzero(w > 0)[0][-1])
+    return j
+
+
+def chain_rows(sid, P, n, first=0):
+    """Rows first..first+n-1 of a chain at P: position = slot = P+i; row i sees
+    slots 0..P+i (committed context plus itself and earlier rows)."""
+    return [Row(sid, P + i, P + i, np.arange(P + i + 1)) for i in range(first, first + n)]
+
+
+def prefill(dec, cache, sid, prompt, mode="greedy", T=1.0, u=None):
+    """Run the prompt through all layers; the first generated token is the
+    argmax (or a sample with uniform slot 32) of the last row's logits."""
+    n = len(prompt)
+    rows = [Row(sid, i, i, np.arange(i + 1)) for i in range(n)]
+    h = dec.forward_layers(cache, rows, dec.embed(prompt), 0, dec.cfg.n_layers)
+    z = dec.head(h[-1:])[0]
+    y = argmax(z) if mode == "greedy" else sample_index(probs(z, T), u[SLOT_RESAMPLE])
+    st = SeqState(sid, list(int(t) for t in prompt) + [y], n, y)
+    st.check()
+    return st, z
+
+
+def draft_chain(dec, cache, st, k, mode="greedy", T=1.0, u=None, exit_layer=None):
+    """k draft steps plus the finishing pass.
+
+    Returns (tokens [x, d_1..d_k], draft logits [k][V], hidden_L [k+1][d]).
+    """
+    L = dec.cfg.exit_layer if exit_layer is None else exit_layer
+    toks, zs, hs = [st.pending], [], []
+    for s in range(k + 1):
+        row = chain_rows(st.sid, st.P, 1, first=s)
+        h = dec.forward_layers(cache, row, dec.embed([toks[s]]), 0, L)
+        hs.append(h[0])
+        if s < k:
+            z = dec.head(h)[0]
+            zs.append(z)
+            toks.append(argmax(z) if mode == "greedy" else sample_index(probs(z, T), u[s]))
+    zs = np.array(zs) if zs else np.zeros((0, dec.cfg.vocab))
+    return toks, zs, np.array(hs)
+
+
+def verify_rows(dec, cache, rows, h_or_tokens, start):
+    """Layers start..N-1 over the rows, then final norm + head.  With start ==
+    0 the rows' inputs are token ids (plain full-depth forward)."""
+    h = dec.embed(h_or_tokens) if start == 0 else np.asarray(h_or_tokens, dtype=np.float64)
+    h = dec.forward_layers(cache, rows, h, start, dec.cfg.n_layers)
+    return dec.head(h)
+
+
+def verify_chain(dec, cache, st, toks, hidden_L, exit_layer=None):
+    L = dec.cfg.exit_layer if exit_layer is None else exit_layer
+    rows = chain_rows(st.sid, st.P, len(toks))
+    return verify_rows(dec, cache, rows, toks if L == 0 else hidden_L, L)
+
+
+def accept_greedy_chain(toks, logits):
+    """a = longest prefix of drafts matching the target argmax; y = argmax of row a."""
+    k = len(toks) - 1
+    a = 0
+    while a < k and toks[a + 1] == argmax(logits[a]):
+        a += 1
+    return a, argmax(logits[a])
+
+
+def accept_stochastic_chain(toks, p_rows, q_rows, u):
+    """The page's accept_or_reject, left to right with shared uniforms.
+
+    p_rows[i], q_rows[i]: target and draft distributions at row i (the
+    distribution that judges toks[i+1]); p_rows has k+1 rows.  Uses uniform
+    slots 16+i for the tests and slot 32 for the residual or bonus draw.
+    Returns (a, y, flags) with flags = rows whose |p/q - u| < 1e-3.
+    """
+    k = len(toks) - 1
+    flags = []
+    for i in range(k):
+        tok = toks[i + 1]
+        p, q = p_rows[i], q_rows[i]
+        ratio = p[tok] / q[tok] if q[tok] > 0 else 0.0
+        ui = u[SLOT_ACCEPT + i]
+        if abs(ratio - ui) < FLAG_BAND:
+            flags.append(i)
+        if ui < min(1.0, ratio):
+            continue
+        w = np.maximum(p - q, 0.0)
+        if w.sum() <= 0:
+            w = p
+        return i, sample_index(w, u[SLOT_RESAMPLE]), flags
+    return k, sample_index(p_rows[k], u[SLOT_RESAMPLE]), flags
+
+
+def commit_chain(cache, st, toks, a, y):
+    """Keep x, d_1..d_a and append y: P <- P + a + 1; later slots are garbage."""
+    st.tokens += [int(t) for t in toks[1:a + 1]] + [int(y)]
+    st.P += a + 1
+    st.pending = int(y)
+    st.rounds.append(a)
+    cache.poison(st.sid, st.P)  # a stale read of a rolled-back slot turns into NaN
+    st.check()
+
+
+def spec_round(dec, cache, st, k, mode="greedy", T=1.0, u=None, exit_layer=None):
+    """One round: draft, verify, accept, commit.  Returns (a, y, logits, flags)."""
+    L = dec.cfg.exit_layer if exit_layer is None else exit_layer
+    toks, zd, hL = draft_chain(dec, cache, st, k, mode, T, u, L)
+    zt = verify_chain(dec, cache, st, toks, hL, L)
+    if mode == "greedy":
+        a, y = accept_greedy_chain(toks, zt)
+        flags = []
+    else:
+        p_rows = [probs(z, T) for z in zt]
+        q_rows = [probs(z, T) for z in zd]
+        a, y, flags = accept_stochastic_chain(toks, p_rows, q_rows, u)
+    commit_chain(cache, st, toks, a, y)
+    return a, y, zt, flags
+
+
+def ar_step(dec, cache, st):
+    """Plain greedy autoregressive step: the pending token through all layers."""
+    z = verify_rows(dec, cache, chain_rows(st.sid, st.P, 1), [st.pending], 0)[0]
+    y = argmax(z)
+    commit_chain(cache, st, [st.pending], 0, y)
+    return y, z
+
+
+def generate_ar(dec, cache, sid, prompt, n_new):
+    st, _ = prefill(dec, cache, sid, prompt)
+    while len(st.tokens) - len(prompt) < n_new:
+        ar_step(dec, cache, st)
+    return st.tokens[len(prompt):len(prompt) + n_new], st
+
+
+def generate_spec(dec, cache, sid, prompt, n_new, k, exit_layer=None):
+    st, _ = prefill(dec, cache, sid, prompt)
+    while len(st.tokens) - len(prompt) < n_new:
+        spec_round(dec, cache, st, k, exit_layer=exit_layer)
+    return st.tokens[len(prompt):len(prompt) + n_new], st
