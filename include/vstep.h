@@ -1,0 +1,210 @@
+/*
+ * vstep.h: C ABI of the speculative-decoding verify-step library (gfx950).
+ *
+ * The library runs one self-speculative decoding round on one GPU:
+ *   draft   first L layers + final norm + LM head, k serial steps, writing
+ *           the first-L KV that verify reuses;
+ *   verify  layers L..N-1 over k+1 chain rows or the rows of a draft tree,
+ *           with a per-row ancestor mask, then the head;
+ *   accept  greedy longest matching prefix / path, or stochastic
+ *           min(1, p/q) with residual resampling from normalize(max(0, p-q));
+ *   commit  roll the KV state back to the accepted prefix (or compact the
+ *           accepted tree path).
+ * Sources: self-speculative decoding page (m.lqnn.cn/news/278124) §2.1
+ * (layer-skip draft, KV reuse, k+1 positions), §2.4 (acceptance rule), §3.3
+ * (shared cache, rollback), §4.1-§4.3 (forward_layers interface, draft,
+ * verify, accept_or_reject); "DSpark" page (0539edu.com/news/4524681) §2.1
+ * (greedy block verification); "FlashSpec" page (lnrk.cn/news/47842) §2.2
+ * and §3.2 (tree batch in level order, parent mask, per-node positions).
+ *
+ * Conventions
+ * - Every device buffer is allocated by the caller and passed as a raw
+ *   pointer; the library never allocates device memory and never
+ *   synchronises, except where a call says so.  `stream` is a hipStream_t.
+ * - Token ids int32; uniforms fp64 in [0,1); logits and hidden states fp32,
+ *   row-major; weights and the KV cache bf16.
+ * - Sequence state lives on the device: P (KV length = position of the
+ *   pending token), the pending token (last committed token, no KV yet) and
+ *   the committed count.  Invariant after every commit: P == committed - 1.
+ * - Rows of one pass are grouped by sequence.  Row r of sequence s has an
+ *   in-round index idx (0 = first row of s in the pass), writes its KV at
+ *   slot P_s + idx, sits at position P_s + depth, and attends to all slots
+ *   < P_s plus the in-round slots P_s + j whose bit j is set in its mask.
+ *   A NULL depth/mask array means a chain: depth = idx, mask = bits 0..idx.
+ * - Errors: every call validates its arguments on the host before anything
+ *   is enqueued and returns a negative vs_status without touching device
+ *   state; vs_last_error() describes the last failure of the calling thread.
+ *   Faults of earlier asynchronous work surface as VS_E_DEVICE.
+ */
+#ifndef VSTEP_H
+#define VSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vs_status;
+#define VS_OK 0
+#define VS_E_INVAL (-1)  /* bad argument (NULL pointer, out-of-range id, bad mode) */
+#define VS_E_SHAPE (-2)  /* shape not supported (alignment, row counts, head sizes) */
+#define VS_E_NOKV (-3)   /* KV pool or sequence capacity exhausted */
+#define VS_E_STATE (-4)  /* call order violated (sequence not open, no prefill) */
+#define VS_E_DEVICE (-5) /* a HIP runtime call failed */
+
+#define VS_GREEDY 0
+#define VS_SAMPLE 1
+
+#define VS_MAX_ROWS 64     /* rows per sequence per pass (uint64 masks) */
+#define VS_MAX_SEQS 64     /* sequences per pass */
+#define VS_MAX_K 16        /* chain draft length */
+#define VS_N_UNIFORMS 48   /* per sequence per round: 0..k-1 draft, 16.. accept, 32 residual/bonus */
+#define VS_RESULT_INTS 24  /* per sequence: a, y, flags, n_path, path[20] */
+
+/* Weight tensors, canonical bf16 row-major layout:
+ *  EMBED [V][d]; ATTN_NORM [d]; WQ [H*hd][d]; WK [Hkv*hd][d]; WV [Hkv*hd][d];
+ *  WO [d][H*hd]; FFN_NORM [d]; W_GATE [F][d]; W_UP [F][d]; W_DOWN [d][F];
+ *  FINAL_NORM [d]; HEAD [V][d]. */
+enum vs_tensor {
+  VS_T_EMBED = 0, VS_T_ATTN_NORM, VS_T_WQ, VS_T_WK, VS_T_WV, VS_T_WO, VS_T_FFN_NORM,
+  VS_T_W_GATE, VS_T_W_UP, VS_T_W_DOWN, VS_T_FINAL_NORM, VS_T_HEAD, VS_T_COUNT
+};
+
+/* Llama-style pre-norm decoder: RMSNorm(eps), rotate-half RoPE(theta) on q
+ * and k, softmax attention scaled by 1/sqrt(head_dim) with grouped KV heads,
+ * SwiGLU FFN, untied embedding and head.  exit_layer = L, the draft depth. */
+typedef struct vs_model_cfg {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, exit_layer;
+  float rms_eps, rope_theta;
+} vs_model_cfg;
+
+typedef struct vs_model vs_model;
+typedef struct vs_kv vs_kv;
+
+/* One pass's rows: n_seq sequences (ids seq[i], host), n_rows[i] rows each
+ * (host, 1..64), optional device arrays depth[M] / mask[M] (M = sum n_rows). */
+typedef struct vs_batch {
+  int32_t n_seq;
+  const int32_t* seq;
+  const int32_t* n_rows;
+  const int32_t* d_depth;
+  const uint64_t* d_mask;
+} vs_batch;
+
+const char* vs_last_error(void);
+
+/* ---- sizing (host only, no GPU needed) ---- */
+/* Bytes of the packed weight buffer. 0 if the shape is unsupported. */
+size_t vs_weight_bytes(const vs_model_cfg* cfg);
+/* Bytes of the model workspace for passes of up to max_rows rows in total,
+ * max_seqs sequences and contexts up to max_ctx tokens. */
+size_t vs_workspace_bytes(const vs_model_cfg* cfg, int32_t max_rows, int32_t max_seqs, int32_t max_ctx);
+/* Bytes of a KV pool of n_blocks blocks of 16 tokens (all layers, K and V)
+ * plus the per-sequence state for max_seqs sequences of up to
+ * max_blocks_per_seq blocks. */
+size_t vs_kv_bytes(const vs_model_cfg* cfg, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq);
+
+/* ---- model ---- */
+/* Create a model over caller-owned device buffers: d_weights
+ * (vs_weight_bytes) receives packed weights through vs_model_set_tensor;
+ * d_workspace (vs_workspace_bytes with the same limits) holds activations.
+ * Zeroes the workspace counters on `stream`. */
+vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_workspace, int32_t max_rows,
+                          int32_t max_seqs, int32_t max_ctx, void* stream, vs_model** out);
+/* Pack one canonical bf16 tensor (device pointer, read during the call's
+ * kernels only) into the weight buffer.  layer is ignored for EMBED,
+ * FINAL_NORM and HEAD. */
+vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const void* d_src, void* stream);
+void vs_model_destroy(vs_model* m);
+
+/* ---- KV cache ---- */
+vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq,
+                       void* stream, vs_kv** out);
+void vs_kv_destroy(vs_kv* kv);
+/* Open a sequence able to hold max_len KV slots (prompt + generated tokens
+ * + in-round scratch); reserves its blocks from the pool up front. */
+vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id);
+vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
+/* Device pointers of the per-sequence state arrays [max_seqs]:
+ * P (KV length), pending token, committed count (read-only for callers). */
+vs_status vs_kv_state(vs_kv* kv, int32_t** d_P, int32_t** d_pending, int32_t** d_committed);
+/* Device pointers of layer `layer`'s K and V pools [n_blocks][Hkv][16][hd]
+ * and the block table [max_seqs][max_blocks_per_seq] (int32). */
+vs_status vs_kv_layer(vs_kv* kv, int32_t layer, void** d_k, void** d_v, int32_t** d_block_table);
+/* Host-side upper bound of P for a sequence (exact after vs_kv_sync). */
+vs_status vs_kv_sync(vs_kv* kv, void* stream); /* blocks: reads P back */
+
+/* ---- the round ---- */
+/* Prompt of n tokens (device) through all layers in passes of <= 64 rows;
+ * sets P = n and pending = argmax (greedy) or a draw with d_u[32] (sample,
+ * softmax at temperature temp) of the last row.  d_logits_last [V] optional. */
+vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t mode,
+                     float temp, const double* d_u, float* d_logits_last, void* stream);
+
+/* The pages' forward_layers(start, end): layers [start, end) over the rows.
+ * Input: token ids (start == 0) or hidden rows [M][d] (start > 0).  Writes
+ * each layer's K/V at the rows' slots.  d_hidden_out [M][d] optional. */
+vs_status vs_forward_layers(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start, int32_t end,
+                            const int32_t* d_tokens, const float* d_hidden_in, float* d_hidden_out, void* stream);
+/* Final RMSNorm + LM head of hidden rows [M][d] -> logits [M][V]. */
+vs_status vs_head(vs_model* m, int32_t M, const float* d_hidden, float* d_logits, void* stream);
+
+/* Chain draft of k[i] tokens for each sequence (host array, 0..16): k[i]
+ * serial steps of layers 0..L-1 + final norm + head, then a finishing
+ * first-L pass over the last draft token.  Greedy takes the argmax; sample
+ * draws from softmax(z/temp) with uniform slot s of d_u[i][48].
+ * Outputs, in verify-row order (sequence i owns rows R_i..R_i+k[i]):
+ *   d_tokens [M]: x, d_1..d_k;  d_hidden_L [M][d]: layer-L input of each row;
+ *   d_draft_logits [M][V] (optional; row R_i+s holds the logits that drew
+ *   d_{s+1}, the last row of each sequence is left untouched). */
+vs_status vs_draft(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
+                   float temp, const double* d_u, int32_t* d_tokens, float* d_hidden_L, float* d_draft_logits,
+                   void* stream);
+
+/* Verify: layers start_layer..N-1 over the batch rows (input hidden_L rows,
+ * or token ids when start_layer == 0), then the head -> d_logits [M][V]. */
+vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_layer, const int32_t* d_tokens,
+                    const float* d_hidden_in, float* d_logits, void* stream);
+
+/* Accept.  Greedy (any mask shape): walk from row 0 of each sequence to the
+ * child whose token equals the argmax of the current row (lowest id on
+ * ties); a = path length, y = argmax at the last node.  Sample (chain only):
+ * for i < k test u[16+i] < min(1, p_i(d)/q_i(d)) with p = softmax(z/temp) of
+ * d_logits row i and q of d_draft_logits row i, both in fp64; on the first
+ * reject draw y from normalize(max(0, p-q)) (p if that sums to <= 0) with
+ * u[32]; if all pass draw y from p_k.
+ * d_result [n_seq][24]: a, y, flags (bit0 near-tie), n_path, path rows. */
+vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
+                    const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                    void* stream);
+
+/* Commit: P += a + 1, pending = y, committed += a + 1.  For masks that are not
+ * chains, first copies the K/V (all layers) of the accepted path rows
+ * P + path[i] to slots P + 1 + i. */
+vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_result, void* stream);
+
+/* One chain round: vs_draft + vs_verify(exit_layer) + vs_accept + vs_commit
+ * with the model's own scratch for tokens, hidden rows and logits.
+ * d_result as for vs_accept; d_tokens [M] receives the round's row tokens. */
+vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
+                  float temp, const double* d_u, int32_t* d_tokens, int32_t* d_result, void* stream);
+
+/* Per-kernel-family timing, measured with HIP events around every launch on
+ * the launching stream while enabled (adds event records between kernels).
+ * vs_stats_read synchronises. */
+typedef struct vs_kernel_stat {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+  double bytes; /* algorithmic HBM bytes of all timed launches */
+} vs_kernel_stat;
+vs_status vs_stats_enable(vs_model* m, int32_t on);
+vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* n_out);
+vs_status vs_stats_reset(vs_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

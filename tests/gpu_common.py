@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU tests: engines with synthetic weights, device
+arrays, and reading the paged KV cache back in slot order."""
+import numpy as np
+import torch
+
+import synth
+from synth import gpu_weights
+from synth.model_weights import SynthWeights
+from oracle.decoder import Decoder
+from verification_verify_step_amd import binding as B
+from verification_verify_step_amd.runtime import Engine
+
+LOGIT_TOL = 2e-2  # max-abs logit agreement, bf16 weights/KV with fp32 accumulation
+NEAR_TIE = 4e-2   # a greedy choice whose top-1 - top-2 gap is below this may legitimately differ
+
+
+def engine(cfg, eps=None, force_host=False, **kw):
+    e = Engine(cfg, **kw)
+    gpu_weights.load(e, cfg, eps=eps, force_host=force_host)
+    return e
+
+
+def oracle_decoder(cfg, eps=None):
+    w = SynthWeights(cfg, precision="bf16")
+    if eps is not None:
+        w = gpu_weights.ScaledWeights(w, cfg, eps)
+    return Decoder(cfg, w)
+
+
+def i32(a):
+    return torch.tensor(np.asarray(a, dtype=np.int32), device="cuda")
+
+
+def f64(a):
+    return torch.tensor(np.asarray(a, dtype=np.float64), device="cuda")
+
+
+def prompt(cfg, n, req=0):
+    return synth.tokens(synth.SEED_PROMPTS, synth.stream_prompt(req), cfg.vocab, n)
+
+
+def uniforms(req, rnd):
+    return synth.uniforms(synth.SEED_UNIFORMS, synth.stream_uniform(req, rnd), B.VS_N_UNIFORMS)
+
+
+def kv_slots(e, seq, layer, slots):
+    """K, V of the given slots as float64 arrays [Hkv][n][hd]."""
+    K, V, bt = e.kv_layer(layer)
+    slots = np.asarray(slots)
+    blocks = bt[seq].cpu().numpy()[slots // 16]
+    idx_b = torch.from_numpy(blocks.astype(np.int64)).cuda()
+    idx_o = torch.from_numpy((slots % 16).astype(np.int64)).cuda()
+    k = K[idx_b, :, idx_o, :].permute(1, 0, 2).double().cpu().numpy()
+    v = V[idx_b, :, idx_o, :].permute(1, 0, 2).double().cpu().numpy()
+    return k, v
+
+
+def result_rows(res, n_seq):
+    r = res[:n_seq].cpu().numpy()
+    return [(int(x[0]), int(x[1]), int(x[2]), [int(p) for p in x[4:4 + x[3]]]) for x in r]
+
+
+def near_tie(z):
+    s = np.sort(np.asarray(z, dtype=np.float64))
+    return s[-1] - s[-2] < NEAR_TIE

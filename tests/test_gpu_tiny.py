@@ -1,0 +1,255 @@
+"""GPU parity on the tiny decoder (2 layers, d 256, 4x64 heads, FFN 1024,
+V 2048, draft = layer 0 + head, chain k = 4, greedy, 32 new tokens) against
+the CPU oracle, through the C ABI.  Floating point within LOGIT_TOL; integer
+outputs (tokens off near-ties, accepted lengths, paths, state) bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import spec, tree
+from oracle.decoder import KVCache
+from synth.workloads import TINY
+from tests import gpu_common as G
+from verification_verify_step_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+CFG = TINY
+
+
+@pytest.fixture(scope="module")
+def eng():
+    return G.engine(CFG, force_host=True, max_rows=64, max_seqs=8, max_ctx=512)
+
+
+@pytest.fixture(scope="module")
+def dec():
+    return G.oracle_decoder(CFG)
+
+
+def _prefill(e, toks, mode=B.VS_GREEDY, u=None, T=1.0):
+    seq = e.open(480)
+    t = G.i32(toks)
+    z = torch.empty(CFG.vocab, dtype=torch.float32, device="cuda")
+    du = G.f64(u) if u is not None else None
+    B.vs_prefill(e.model, e.kv, seq, t.data_ptr(), len(toks), mode, T, du.data_ptr() if du is not None else None,
+                 z.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    return seq, z.cpu().numpy().astype(np.float64)
+
+
+def test_device_generator_matches_host():
+    n = 1 << 20
+    d = torch.empty(n, dtype=torch.int16, device="cuda")
+    s = synth.stream_weight(synth.T_W_UP, 5)
+    synth.dev_normal_bf16(synth.SEED_WEIGHTS, s, n, d.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    host = synth.normal_bf16_bits(synth.SEED_WEIGHTS, s, n)
+    assert np.array_equal(d.cpu().numpy().view(np.uint16), host)
+
+
+def test_prefill_logits_and_kv(eng, dec):
+    p = G.prompt(CFG, 64, req=0)
+    seq, z = _prefill(eng, p)
+    cache = KVCache(CFG, 512)
+    st, zo = spec.prefill(dec, cache, 0, p)
+    assert np.abs(z - zo).max() <= G.LOGIT_TOL, np.abs(z - zo).max()
+    P, pending, committed = eng.state()
+    assert P[seq] == 64 and committed[seq] == 65
+    if not G.near_tie(zo):
+        assert pending[seq] == st.pending
+    for l in range(CFG.n_layers):
+        k, v = G.kv_slots(eng, seq, l, np.arange(64))
+        Ko, Vo = cache.get(0, l)
+        assert np.abs(k - Ko[:, :64]).max() <= 0.05 * max(1.0, np.abs(Ko[:, :64]).max())
+        assert np.abs(v - Vo[:, :64]).max() <= 0.05 * max(1.0, np.abs(Vo[:, :64]).max())
+        # stored values are bf16 and mostly identical to the oracle's bf16 rounding
+        assert np.mean(k == Ko[:, :64]) > 0.9
+
+
+@pytest.mark.parametrize("eps", [None, 0.0, 0.5])
+def test_spec_equals_ar_and_oracle(eng, eps):
+    """GPU speculative tokens == GPU greedy AR tokens == oracle greedy tokens
+    (the last up to the first near-tie of the oracle)."""
+    e = eng if eps is None else G.engine(CFG, eps=eps, force_host=True, max_rows=64, max_seqs=4, max_ctx=512)
+    dec = G.oracle_decoder(CFG, eps=eps)
+    p = G.prompt(CFG, 64, req=1)
+    n_new, k = 32, 4
+    # speculative on the GPU
+    sA, _ = _prefill(e, p)
+    toks = torch.empty(64, dtype=torch.int32, device="cuda")
+    res = torch.zeros((8, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    P0 = e.state()[0][sA]
+    out_spec = [e.state()[1][sA]]
+    accepted = []
+    while len(out_spec) < n_new:
+        B.vs_step(e.model, e.kv, [sA], [k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), res.data_ptr(), e.stream)
+        a, y, _, path = G.result_rows(res, 1)[0]
+        t = toks[:k + 1].cpu().tolist()
+        out_spec += t[1:a + 1] + [y]
+        accepted.append(a)
+        P, pending, committed = e.state()
+        assert P[sA] == committed[sA] - 1 and pending[sA] == y
+        e.sync()
+    assert e.state()[0][sA] == P0 + len(out_spec) - 1
+    # greedy AR on the GPU: the pending token through all layers, one row
+    sB, _ = _prefill(e, p)
+    pend_ptr = B.vs_kv_state(e.kv)[1] + 4 * sB
+    z = torch.empty((1, CFG.vocab), dtype=torch.float32, device="cuda")
+    batch = B.make_batch([sB], [1])
+    out_ar = [e.state()[1][sB]]
+    while len(out_ar) < n_new:
+        B.vs_verify(e.model, e.kv, batch, 0, pend_ptr, None, z.data_ptr(), e.stream)
+        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, pend_ptr, z.data_ptr(), None, None, res.data_ptr(), e.stream)
+        B.vs_commit(e.model, e.kv, batch, res.data_ptr(), e.stream)
+        out_ar.append(G.result_rows(res, 1)[0][1])
+    assert out_spec[:n_new] == out_ar[:n_new]
+    if eps == 0.0:
+        assert all(a == k for a in accepted[:-1])
+    # the oracle's greedy tokens, compared up to its first near-tie
+    cache = KVCache(CFG, 512)
+    st, z0 = spec.prefill(dec, cache, 0, p)
+    ref, zs = [st.pending], [z0]
+    while len(ref) < n_new:
+        y, zz = spec.ar_step(dec, cache, st)
+        ref.append(y)
+        zs.append(zz)
+    for i in range(n_new):
+        if G.near_tie(zs[i]):
+            break
+        assert out_ar[i] == ref[i], (i, out_ar[:i + 1], ref[:i + 1])
+    seqs_close = [sA, sB]
+    for s in seqs_close:
+        B.vs_seq_close(e.kv, s)
+
+
+def test_draft_verify_parity(eng, dec):
+    p = G.prompt(CFG, 48, req=2)
+    seq, _ = _prefill(eng, p)
+    cache = KVCache(CFG, 512)
+    st, _ = spec.prefill(dec, cache, 0, p)
+    k = 4
+    toks = torch.empty(k + 1, dtype=torch.int32, device="cuda")
+    hL = torch.empty((k + 1, CFG.d_model), dtype=torch.float32, device="cuda")
+    dl = torch.empty((k + 1, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_draft(eng.model, eng.kv, [seq], [k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), hL.data_ptr(), dl.data_ptr(),
+               eng.stream)
+    ot, oz, oh = spec.draft_chain(dec, cache, st, k)
+    gt = toks.cpu().tolist()
+    assert gt[0] == ot[0]
+    gz = dl[:k].cpu().numpy().astype(np.float64)
+    for s in range(k):
+        if gt[:s + 1] != ot[:s + 1]:
+            break
+        assert np.abs(gz[s] - oz[s]).max() <= G.LOGIT_TOL
+        if not G.near_tie(oz[s]):
+            assert gt[s + 1] == ot[s + 1]
+    if gt == ot:
+        gh = hL.cpu().numpy().astype(np.float64)
+        assert np.abs(gh - oh).max() <= 1e-2 * max(1.0, np.abs(oh).max())
+        # verify over the GPU's own hidden rows vs the oracle's verify
+        z = torch.empty((k + 1, CFG.vocab), dtype=torch.float32, device="cuda")
+        B.vs_verify(eng.model, eng.kv, B.make_batch([seq], [k + 1]), CFG.exit_layer, toks.data_ptr(), hL.data_ptr(),
+                    z.data_ptr(), eng.stream)
+        zo = spec.verify_chain(dec, cache, st, ot, oh)
+        assert np.abs(z.cpu().numpy() - zo).max() <= G.LOGIT_TOL
+    B.vs_seq_close(eng.kv, seq)
+
+
+def test_chain_masks_equal_implicit_chain(eng):
+    p = G.prompt(CFG, 40, req=3)
+    seq, _ = _prefill(eng, p)
+    k = 5
+    toks = G.i32(G.prompt(CFG, k + 1, req=9))
+    z1 = torch.empty((k + 1, CFG.vocab), dtype=torch.float32, device="cuda")
+    z2 = torch.empty_like(z1)
+    B.vs_verify(eng.model, eng.kv, B.make_batch([seq], [k + 1]), 0, toks.data_ptr(), None, z1.data_ptr(), eng.stream)
+    depth = G.i32(np.arange(k + 1))
+    mask = torch.tensor([(1 << (i + 1)) - 1 for i in range(k + 1)], dtype=torch.int64, device="cuda")
+    B.vs_verify(eng.model, eng.kv, B.make_batch([seq], [k + 1], depth.data_ptr(), mask.data_ptr()), 0,
+                toks.data_ptr(), None, z2.data_ptr(), eng.stream)
+    assert torch.equal(z1, z2)
+    B.vs_seq_close(eng.kv, seq)
+
+
+def test_tree_verify_accept_commit(eng, dec):
+    """64 tree rows with ancestor masks and per-node positions: logits vs the
+    oracle, the greedy walk bit-exact on the GPU's own logits, and the
+    compaction of the accepted path's KV."""
+    p = G.prompt(CFG, 40, req=4)
+    seq, _ = _prefill(eng, p)
+    cache = KVCache(CFG, 512)
+    st, _ = spec.prefill(dec, cache, 0, p)
+    nodes, order, toks, _ = tree.draft_tree(dec, cache, st)
+    rows = tree.tree_rows(nodes, order, 0, st.P)
+    zo = spec.verify_rows(dec, cache, rows, toks, 0)
+    depth = G.i32([nodes[n].depth for n in order])
+    mask = torch.tensor(np.array(tree.masks_of_rows(nodes, order), dtype=np.uint64).view(np.int64), device="cuda")
+    batch = B.make_batch([seq], [64], depth.data_ptr(), mask.data_ptr())
+    dt = G.i32(toks)
+    z = torch.empty((64, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_verify(eng.model, eng.kv, batch, 0, dt.data_ptr(), None, z.data_ptr(), eng.stream)
+    zg = z.cpu().numpy().astype(np.float64)
+    assert np.abs(zg - zo).max() <= G.LOGIT_TOL
+    # greedy walk on identical logits
+    res = torch.zeros((8, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    B.vs_accept(eng.model, batch, B.VS_GREEDY, 1.0, dt.data_ptr(), z.data_ptr(), None, None, res.data_ptr(),
+                eng.stream)
+    a, y, _, path = G.result_rows(res, 1)[0]
+    oa, opath, oy = tree.accept_greedy_tree(toks, tree.parents_of_rows(nodes, order), z.cpu().numpy())
+    assert (a, path, y) == (oa, opath, oy)
+    # compaction: force a 3-node path and check every layer's KV moved
+    P0 = eng.state()[0][seq]
+    parents = tree.parents_of_rows(nodes, order)
+    leaf = max(r for r in range(64) if nodes[order[r]].depth == 3)
+    forced = [leaf]
+    while parents[forced[-1]] > 0:
+        forced.append(parents[forced[-1]])
+    forced = forced[::-1]
+    before = [G.kv_slots(eng, seq, l, [P0 + r for r in forced]) for l in range(CFG.n_layers)]
+    r = torch.zeros((8, B.VS_RESULT_INTS), dtype=torch.int32)
+    r[0, 0], r[0, 1], r[0, 3] = len(forced), 7, len(forced)
+    r[0, 4:4 + len(forced)] = torch.tensor(forced)
+    B.vs_commit(eng.model, eng.kv, batch, r.cuda().data_ptr(), eng.stream)
+    torch.cuda.synchronize()
+    for l in range(CFG.n_layers):
+        k2, v2 = G.kv_slots(eng, seq, l, [P0 + 1 + i for i in range(len(forced))])
+        assert np.array_equal(k2, before[l][0]) and np.array_equal(v2, before[l][1])
+    P, pending, committed = eng.state()
+    assert P[seq] == P0 + len(forced) + 1 and pending[seq] == 7 and committed[seq] == P[seq] + 1
+    B.vs_seq_close(eng.kv, seq)
+
+
+def test_stochastic_accept_parity(eng):
+    """Accept decisions on identical logits with shared uniforms equal the
+    oracle's accept_or_reject, except decisions flagged as near-ties."""
+    rng = np.random.default_rng(7)
+    n_seq, k, V = 8, 4, CFG.vocab
+    M = n_seq * (k + 1)
+    zt = (rng.standard_normal((M, V)) * 2.0).astype(np.float32)
+    zd = (zt + rng.standard_normal((M, V)).astype(np.float32) * 0.7).astype(np.float32)
+    toks = np.zeros(M, dtype=np.int32)
+    U = np.stack([G.uniforms(i, 3) for i in range(n_seq)])
+    T = 1.0
+    for i in range(n_seq):
+        for s in range(k):
+            r = i * (k + 1) + s
+            toks[r + 1] = spec.sample_index(spec.probs(zd[r], T), U[i][s])
+    seqs = [eng.open(100) for _ in range(n_seq)]
+    batch = B.make_batch(seqs, [k + 1] * n_seq)
+    res = torch.zeros((n_seq, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    dzt, dzd, dtok, du = (torch.from_numpy(zt).cuda(), torch.from_numpy(zd).cuda(), G.i32(toks),
+                          G.f64(U.reshape(-1)))
+    B.vs_accept(eng.model, batch, B.VS_SAMPLE, T, dtok.data_ptr(), dzt.data_ptr(), dzd.data_ptr(), du.data_ptr(),
+                res.data_ptr(), eng.stream)
+    got = G.result_rows(res, n_seq)
+    for i in range(n_seq):
+        rs = slice(i * (k + 1), (i + 1) * (k + 1))
+        pr = [spec.probs(z, T) for z in zt[rs].astype(np.float64)]
+        qr = [spec.probs(z, T) for z in zd[rs].astype(np.float64)]
+        a, y, flags = spec.accept_stochastic_chain(list(toks[rs]), pr, qr, U[i])
+        if flags:
+            continue
+        assert (got[i][0], got[i][1]) == (a, y), (i, got[i], a, y)
+    for s in seqs:
+        B.vs_seq_close(eng.kv, s)

@@ -1,0 +1,1114 @@
+// C ABI of the verify-step library: argument validation, buffer layout and
+// the order of kernel launches for prefill, draft, verify, accept and commit.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "misc.h"
+
+using namespace vs;
+
+namespace {
+
+thread_local std::string g_err;
+
+vs_status fail(vs_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Mat {
+  uint16_t* w = nullptr;
+  int n_tiles = 0, k_steps = 0;
+  size_t bytes() const { return (size_t)n_tiles * k_steps * 1024; }
+};
+
+// Layout of the packed weight buffer (offsets in bytes, 256-aligned).
+struct WeightLayout {
+  size_t embed, g_final, head, total;
+  std::vector<size_t> qkv, o, gu, down, g_attn, g_ffn;
+};
+
+bool shape_ok(const vs_model_cfg* c, std::string* why) {
+  auto bad = [&](const char* s) {
+    if (why) *why = s;
+    return false;
+  };
+  if (c->n_layers < 1 || c->d_model < 32 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 16 ||
+      c->d_ffn < 32 || c->vocab < 16)
+    return bad("sizes must be positive (d_model, d_ffn >= 32, head_dim >= 16, vocab >= 16)");
+  if (c->exit_layer < 0 || c->exit_layer > c->n_layers) return bad("exit_layer must lie in [0, n_layers]");
+  if (c->d_model % 256 != 0) return bad("d_model must be a multiple of 256");
+  if (c->d_ffn % 32 != 0) return bad("d_ffn must be a multiple of 32");
+  if (c->head_dim % 16 != 0 || c->head_dim > 128) return bad("head_dim must be a multiple of 16, at most 128");
+  if (c->n_heads % c->n_kv_heads != 0) return bad("n_heads must be a multiple of n_kv_heads");
+  if ((c->n_heads * c->head_dim) % 32 != 0) return bad("n_heads*head_dim must be a multiple of 32");
+  if (c->vocab % 16 != 0) return bad("vocab must be a multiple of 16");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return bad("rms_eps > 0 and rope_theta > 1 required");
+  return true;
+}
+
+WeightLayout weight_layout(const vs_model_cfg* c) {
+  WeightLayout L;
+  const size_t d = c->d_model, hd = c->head_dim, H = c->n_heads, Hkv = c->n_kv_heads, F = c->d_ffn, V = c->vocab;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    size_t o = off;
+    off = align256(off + b);
+    return o;
+  };
+  L.embed = take(V * d * 2);
+  for (int l = 0; l < c->n_layers; ++l) {
+    L.qkv.push_back(take((H + 2 * Hkv) * hd * d * 2));
+    L.o.push_back(take(d * H * hd * 2));
+    L.gu.push_back(take(2 * F * d * 2));
+    L.down.push_back(take(d * F * 2));
+    L.g_attn.push_back(take(d * 4));
+    L.g_ffn.push_back(take(d * 4));
+  }
+  L.g_final = take(d * 4);
+  L.head = take(V * d * 2);
+  L.total = off;
+  return L;
+}
+
+constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
+constexpr int kCounters = 65536;
+
+struct WsLayout {
+  size_t h, xa_h, xa_o, xa_act, ss, q, part, cnt, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
+};
+
+WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
+  WsLayout w;
+  const size_t d = c->d_model, hd = c->head_dim, H = c->n_heads, F = c->d_ffn, V = c->vocab;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    size_t o = off;
+    off = align256(off + b);
+    return o;
+  };
+  w.h = take(R * d * 4);
+  w.xa_h = take(R * d * 4);
+  w.xa_o = take(R * H * hd * 4);
+  w.xa_act = take(R * F * 4);
+  w.ss = take(R * (d / 16) * 4);
+  w.q = take(R * H * hd * 4);
+  w.part = take(kAttnPartFloats * 4);
+  w.cnt = take(kCounters * 4);
+  w.amax_val = take(R * (V / 16) * 4);
+  w.amax_idx = take(R * (V / 16) * 4);
+  w.logits = take(R * V * 4);
+  w.dlogits = take(R * V * 4);
+  w.hidden = take(R * d * 4);
+  w.tokens = take(R * 4);
+  w.st_mx = take(R * 4);
+  w.st_amax = take(R * 4);
+  w.st_second = take(R * 4);
+  w.st_sum = take(R * 8);
+  w.dst_mx = take(R * 4);
+  w.dst_amax = take(R * 4);
+  w.dst_sum = take(R * 8);
+  w.result = take((size_t)S * VS_RESULT_INTS * 4);
+  w.total = off;
+  return w;
+}
+
+enum Family { F_QKV = 0, F_O, F_GU, F_DOWN, F_HEAD, F_ATTN, F_SMALL, F_COUNT };
+const char* kFamilyNames[F_COUNT] = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention",
+                                     "small"};
+
+struct Timed {
+  int fam;
+  hipEvent_t a, b;
+  double bytes;
+};
+
+}  // namespace
+
+struct vs_model {
+  vs_model_cfg c;
+  WeightLayout wl;
+  char* wbase = nullptr;
+  std::vector<Mat> qkv, o, gu, down;
+  std::vector<float*> g_attn, g_ffn;
+  uint16_t* embed = nullptr;
+  float* g_final = nullptr;
+  Mat head;
+  int max_rows = 0, max_seqs = 0, max_ctx = 0;
+  WsLayout wsl;
+  char* ws = nullptr;
+  float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
+  uint16_t *xa_h, *xa_o, *xa_act;
+  int *cnt, *amax_idx, *tokens, *st_amax, *dst_amax, *result;
+  double *st_sum, *dst_sum;
+  int ss_groups = 0;       // groups of the last producer of ss
+  int head_groups = 0;     // groups of the last head pass
+  int head_rows = 0;
+  // timing
+  bool stats_on = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<Timed> timed;
+  double acc_ms[F_COUNT] = {0};
+  double acc_bytes[F_COUNT] = {0};
+  int64_t acc_n[F_COUNT] = {0};
+};
+
+struct vs_kv {
+  vs_model* m = nullptr;
+  char* base = nullptr;
+  int n_blocks = 0, max_seqs = 0, bps = 0;
+  std::vector<uint16_t*> k, v;
+  uint16_t** d_kptr = nullptr;
+  uint16_t** d_vptr = nullptr;
+  int *P = nullptr, *pending = nullptr, *committed = nullptr, *bt = nullptr;
+  std::vector<int> free_blocks;
+  std::vector<std::vector<int>> blocks;
+  std::vector<int> open, cap, P_ub, prefilled;
+};
+
+namespace {
+
+hipStream_t S(void* st) { return reinterpret_cast<hipStream_t>(st); }
+
+vs_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return VS_OK;
+}
+
+hipEvent_t next_event(vs_model* m) {
+  if (m->ev_used == m->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    m->ev_pool.push_back(e);
+  }
+  return m->ev_pool[m->ev_used++];
+}
+
+// Brackets one launch with events when timing is enabled.
+template <typename F>
+void timed(vs_model* m, int fam, double bytes, hipStream_t st, F launch) {
+  if (!m->stats_on) {
+    launch();
+    return;
+  }
+  hipEvent_t a = next_event(m), b = next_event(m);
+  if (!a || !b) {
+    launch();
+    return;
+  }
+  hipEventRecord(a, st);
+  launch();
+  hipEventRecord(b, st);
+  m->timed.push_back(Timed{fam, a, b, bytes});
+}
+
+KvView kv_view(vs_kv* kv, int layer) {
+  KvView v;
+  v.k = kv->k[layer];
+  v.v = kv->v[layer];
+  v.P = kv->P;
+  v.bt = kv->bt;
+  v.bps = kv->bps;
+  return v;
+}
+
+GemmArgs gemm_base(vs_model* m, const Mat& W, const uint16_t* xa, int M) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.W = W.w;
+  g.n_tiles = W.n_tiles;
+  g.k_steps = W.k_steps;
+  g.xa = xa;
+  g.M = M;
+  g.inv_d = 1.0f / (float)m->c.d_model;
+  g.eps = m->c.rms_eps;
+  g.d = m->c.d_model;
+  g.out_row_identity = 1;
+  return g;
+}
+
+double gemm_bytes(const Mat& W, int M) {
+  return (double)W.bytes() + (double)M * W.k_steps * 32 * 4 + (double)M * W.n_tiles * 16 * 4;
+}
+
+// Loads rows (embedding of token ids, or hidden rows) into the residual
+// stream with the next consumer's gain g.
+void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const int* src_rows, const float* g,
+               hipStream_t st) {
+  LoadArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = M;
+  a.d = m->c.d_model;
+  a.V = m->c.vocab;
+  a.tokens = tokens;
+  a.embed = m->embed;
+  a.hidden = hidden;
+  a.src_identity = src_rows == nullptr;
+  if (src_rows)
+    for (int i = 0; i < M; ++i) a.src_row[i] = src_rows[i];
+  a.h = m->h;
+  a.xa = m->xa_h;
+  a.g = g;
+  a.ss = m->ss;
+  timed(m, F_SMALL, (double)M * m->c.d_model * 10, st, [&] { launch_load_rows(a, st); });
+  m->ss_groups = (m->c.d_model + 255) / 256;
+}
+
+int ctx_bound(vs_kv* kv, const RowMap& rm) {
+  int p = 0;
+  for (int i = 0; i < rm.n_seq; ++i) p = std::max(p, kv->P_ub[rm.seq[i]]);
+  return p;
+}
+
+void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t st) {
+  const vs_model_cfg& c = m->c;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = rm;
+  a.kv = kv_view(kv, layer);
+  a.q = m->q;
+  a.H = c.n_heads;
+  a.Hkv = c.n_kv_heads;
+  a.hd = c.head_dim;
+  a.scale = 1.0f / std::sqrt((float)c.head_dim);
+  int max_nr = 0;
+  for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
+  const int G = c.n_heads / c.n_kv_heads;
+  const int nq = max_nr * G;
+  a.n_qg = (nq + 63) / 64;
+  a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
+  const int P = ctx_bound(kv, rm);
+  const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
+  int n_split = 0;
+  a.kps = kChunk;
+  if (P > 0) {
+    const int max_split = (P + kChunk - 1) / kChunk;
+    int want = std::max(1, 1024 / std::max(1, units) - 1);
+    // partial-buffer budget
+    const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
+    const int budget = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units) - 1);
+    want = std::min(want, budget);
+    n_split = std::min(max_split, want);
+    a.kps = ((P + n_split - 1) / n_split + kChunk - 1) / kChunk * kChunk;
+    n_split = (P + a.kps - 1) / a.kps;
+  }
+  a.n_split = n_split;
+  a.part = m->part;
+  a.counters = m->cnt;
+  a.xa_o = m->xa_o;
+  a.M = rm.M;
+  double bytes = 0;
+  for (int i = 0; i < rm.n_seq; ++i)
+    bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
+             c.head_dim * 4;
+  timed(m, F_ATTN, bytes, st, [&] { launch_attention(a, st); });
+}
+
+// Layers [start, end) over rows already loaded into h / xa_h / ss.
+void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hipStream_t st, float* h_copy,
+                const int* copy_rows) {
+  const vs_model_cfg& c = m->c;
+  const int M = rm.M;
+  for (int l = start; l < end; ++l) {
+    {
+      GemmArgs g = gemm_base(m, m->qkv[l], m->xa_h, M);
+      g.ss = m->ss;
+      g.ss_groups = m->ss_groups;
+      g.rows = rm;
+      g.kv = kv_view(kv, l);
+      g.q = m->q;
+      g.H = c.n_heads;
+      g.Hkv = c.n_kv_heads;
+      g.hd = c.head_dim;
+      g.theta = c.rope_theta;
+      timed(m, F_QKV, gemm_bytes(m->qkv[l], M), st, [&] { launch_gemm(g, EPI_QKV, st); });
+    }
+    attention(m, kv, rm, l, st);
+    {
+      GemmArgs g = gemm_base(m, m->o[l], m->xa_o, M);
+      g.h = m->h;
+      g.xa_next = m->xa_h;
+      g.g_next = m->g_ffn[l];
+      g.ss_out = m->ss;
+      int groups = 0;
+      timed(m, F_O, gemm_bytes(m->o[l], M), st, [&] { groups = launch_gemm(g, EPI_RESID, st); });
+      m->ss_groups = groups;
+    }
+    {
+      GemmArgs g = gemm_base(m, m->gu[l], m->xa_h, M);
+      g.ss = m->ss;
+      g.ss_groups = m->ss_groups;
+      g.xa_act = m->xa_act;
+      timed(m, F_GU, gemm_bytes(m->gu[l], M), st, [&] { launch_gemm(g, EPI_SWIGLU, st); });
+    }
+    {
+      GemmArgs g = gemm_base(m, m->down[l], m->xa_act, M);
+      g.h = m->h;
+      g.xa_next = m->xa_h;
+      g.g_next = (l + 1 < end) ? m->g_attn[l + 1] : m->g_final;
+      g.ss_out = m->ss;
+      if (l + 1 == end && h_copy != nullptr) {
+        g.h_copy = h_copy;
+        for (int i = 0; i < M; ++i) g.out_row[i] = copy_rows ? copy_rows[i] : i;
+      }
+      int groups = 0;
+      timed(m, F_DOWN, gemm_bytes(m->down[l], M), st, [&] { groups = launch_gemm(g, EPI_RESID, st); });
+      m->ss_groups = groups;
+    }
+  }
+}
+
+// Final norm + head over the rows in h (xa_h already carries g_final).
+void run_head(vs_model* m, int M, float* logits, const int* out_rows, hipStream_t st) {
+  GemmArgs g = gemm_base(m, m->head, m->xa_h, M);
+  g.ss = m->ss;
+  g.ss_groups = m->ss_groups;
+  g.logits = logits;
+  g.V = m->c.vocab;
+  g.amax_val = m->amax_val;
+  g.amax_idx = m->amax_idx;
+  if (out_rows) {
+    g.out_row_identity = 0;
+    for (int i = 0; i < M; ++i) g.out_row[i] = out_rows[i];
+  }
+  int groups = 0;
+  timed(m, F_HEAD, gemm_bytes(m->head, M), st, [&] { groups = launch_gemm(g, EPI_LOGITS, st); });
+  m->head_groups = groups;
+  m->head_rows = M;
+}
+
+vs_status batch_rowmap(vs_kv* kv, const vs_batch* b, RowMap* rm) {
+  if (b == nullptr || b->seq == nullptr || b->n_rows == nullptr) return fail(VS_E_INVAL, "batch: null pointer");
+  if (b->n_seq < 1 || b->n_seq > kMaxSeq) return fail(VS_E_SHAPE, "batch: n_seq %d not in [1, %d]", b->n_seq, kMaxSeq);
+  memset(rm, 0, sizeof(*rm));
+  rm->n_seq = b->n_seq;
+  int M = 0;
+  for (int i = 0; i < b->n_seq; ++i) {
+    const int s = b->seq[i];
+    if (s < 0 || s >= kv->max_seqs || !kv->open[s]) return fail(VS_E_STATE, "batch: sequence %d is not open", s);
+    for (int j = 0; j < i; ++j)
+      if (b->seq[j] == s) return fail(VS_E_INVAL, "batch: sequence %d listed twice", s);
+    if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows)
+      return fail(VS_E_SHAPE, "batch: %d rows for sequence %d (1..%d allowed)", b->n_rows[i], s, kMaxRows);
+    rm->seq[i] = s;
+    rm->row_start[i] = M;
+    M += b->n_rows[i];
+  }
+  rm->row_start[b->n_seq] = M;
+  if (M > kv->m->max_rows) return fail(VS_E_SHAPE, "batch: %d rows exceed the model's max_rows %d", M, kv->m->max_rows);
+  if (M > kMaxRows) return fail(VS_E_SHAPE, "batch: %d rows in one pass exceed %d", M, kMaxRows);
+  rm->M = M;
+  rm->depth = b->d_depth;
+  rm->mask = b->d_mask;
+  return VS_OK;
+}
+
+// Attention partials need (splits + 1) records per (sequence, KV head, query
+// group); at least two splits must fit.
+vs_status check_attn_budget(vs_model* m, const RowMap& rm) {
+  int max_nr = 0;
+  for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
+  const int G = m->c.n_heads / m->c.n_kv_heads;
+  const int nq = max_nr * G, n_qg = (nq + 63) / 64, qg = (nq + n_qg - 1) / n_qg;
+  const size_t need = (size_t)rm.n_seq * m->c.n_kv_heads * n_qg * qg * (m->c.head_dim + 2) * 2;
+  if (need > kAttnPartFloats) return fail(VS_E_SHAPE, "pass too wide for the attention workspace");
+  return VS_OK;
+}
+
+vs_status check_capacity(vs_kv* kv, const RowMap& rm) {
+  vs_status rc = check_attn_budget(kv->m, rm);
+  if (rc != VS_OK) return rc;
+  for (int i = 0; i < rm.n_seq; ++i) {
+    const int s = rm.seq[i];
+    const int last = kv->P_ub[s] + rm.win + rm.idx_off + (rm.row_start[i + 1] - rm.row_start[i]) - 1;
+    if (last >= kv->cap[s])
+      return fail(VS_E_NOKV, "sequence %d: slot %d beyond its capacity %d", s, last, kv->cap[s]);
+  }
+  return VS_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+const char* vs_last_error(void) { return g_err.c_str(); }
+
+size_t vs_weight_bytes(const vs_model_cfg* cfg) {
+  if (cfg == nullptr || !shape_ok(cfg, nullptr)) return 0;
+  return weight_layout(cfg).total;
+}
+
+size_t vs_workspace_bytes(const vs_model_cfg* cfg, int32_t max_rows, int32_t max_seqs, int32_t max_ctx) {
+  if (cfg == nullptr || !shape_ok(cfg, nullptr) || max_rows < 1 || max_seqs < 1 || max_ctx < 1) return 0;
+  return ws_layout(cfg, max_rows, max_seqs).total;
+}
+
+size_t vs_kv_bytes(const vs_model_cfg* cfg, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq) {
+  if (cfg == nullptr || !shape_ok(cfg, nullptr) || n_blocks < 1 || max_seqs < 1 || max_blocks_per_seq < 1) return 0;
+  const size_t pool = align256((size_t)n_blocks * cfg->n_kv_heads * kBlock * cfg->head_dim * 2);
+  return pool * 2 * cfg->n_layers + align256((size_t)cfg->n_layers * 2 * sizeof(void*)) +
+         align256((size_t)max_seqs * 4) * 3 + align256((size_t)max_seqs * max_blocks_per_seq * 4);
+}
+
+vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_workspace, int32_t max_rows,
+                          int32_t max_seqs, int32_t max_ctx, void* stream, vs_model** out) {
+  if (cfg == nullptr || out == nullptr || d_weights == nullptr || d_workspace == nullptr)
+    return fail(VS_E_INVAL, "vs_model_create: null argument");
+  std::string why;
+  if (!shape_ok(cfg, &why)) return fail(VS_E_SHAPE, "vs_model_create: %s", why.c_str());
+  if (max_rows < 1 || max_rows > kMaxRows * kMaxSeq || max_seqs < 1 || max_seqs > kMaxSeq || max_ctx < 1)
+    return fail(VS_E_SHAPE, "vs_model_create: limits out of range");
+  vs_model* m = new vs_model();
+  m->c = *cfg;
+  m->wl = weight_layout(cfg);
+  m->wbase = static_cast<char*>(d_weights);
+  const int d = cfg->d_model, hd = cfg->head_dim, H = cfg->n_heads, Hkv = cfg->n_kv_heads, F = cfg->d_ffn;
+  auto mat = [&](size_t off, int N, int K) {
+    Mat w;
+    w.w = reinterpret_cast<uint16_t*>(m->wbase + off);
+    w.n_tiles = N / 16;
+    w.k_steps = K / 32;
+    return w;
+  };
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    m->qkv.push_back(mat(m->wl.qkv[l], (H + 2 * Hkv) * hd, d));
+    m->o.push_back(mat(m->wl.o[l], d, H * hd));
+    m->gu.push_back(mat(m->wl.gu[l], 2 * F, d));
+    m->down.push_back(mat(m->wl.down[l], d, F));
+    m->g_attn.push_back(reinterpret_cast<float*>(m->wbase + m->wl.g_attn[l]));
+    m->g_ffn.push_back(reinterpret_cast<float*>(m->wbase + m->wl.g_ffn[l]));
+  }
+  m->embed = reinterpret_cast<uint16_t*>(m->wbase + m->wl.embed);
+  m->g_final = reinterpret_cast<float*>(m->wbase + m->wl.g_final);
+  m->head = mat(m->wl.head, cfg->vocab, d);
+  m->max_rows = std::min<int>(max_rows, kMaxRows);
+  m->max_seqs = max_seqs;
+  m->max_ctx = max_ctx;
+  m->wsl = ws_layout(cfg, max_rows, max_seqs);
+  m->ws = static_cast<char*>(d_workspace);
+  char* w = m->ws;
+  m->h = reinterpret_cast<float*>(w + m->wsl.h);
+  m->xa_h = reinterpret_cast<uint16_t*>(w + m->wsl.xa_h);
+  m->xa_o = reinterpret_cast<uint16_t*>(w + m->wsl.xa_o);
+  m->xa_act = reinterpret_cast<uint16_t*>(w + m->wsl.xa_act);
+  m->ss = reinterpret_cast<float*>(w + m->wsl.ss);
+  m->q = reinterpret_cast<float*>(w + m->wsl.q);
+  m->part = reinterpret_cast<float*>(w + m->wsl.part);
+  m->cnt = reinterpret_cast<int*>(w + m->wsl.cnt);
+  m->amax_val = reinterpret_cast<float*>(w + m->wsl.amax_val);
+  m->amax_idx = reinterpret_cast<int*>(w + m->wsl.amax_idx);
+  m->logits = reinterpret_cast<float*>(w + m->wsl.logits);
+  m->dlogits = reinterpret_cast<float*>(w + m->wsl.dlogits);
+  m->hidden = reinterpret_cast<float*>(w + m->wsl.hidden);
+  m->tokens = reinterpret_cast<int*>(w + m->wsl.tokens);
+  m->st_mx = reinterpret_cast<float*>(w + m->wsl.st_mx);
+  m->st_amax = reinterpret_cast<int*>(w + m->wsl.st_amax);
+  m->st_second = reinterpret_cast<float*>(w + m->wsl.st_second);
+  m->st_sum = reinterpret_cast<double*>(w + m->wsl.st_sum);
+  m->dst_mx = reinterpret_cast<float*>(w + m->wsl.dst_mx);
+  m->dst_amax = reinterpret_cast<int*>(w + m->wsl.dst_amax);
+  m->dst_sum = reinterpret_cast<double*>(w + m->wsl.dst_sum);
+  m->result = reinterpret_cast<int*>(w + m->wsl.result);
+  // attention workgroups may use up to the full LDS of a CU
+  attn_init();
+  launch_fill_i32(m->cnt, 0, kCounters, S(stream));
+  vs_status rc = check_launch("vs_model_create");
+  if (rc != VS_OK) {
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return VS_OK;
+}
+
+vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const void* d_src, void* stream) {
+  if (m == nullptr || d_src == nullptr) return fail(VS_E_INVAL, "vs_model_set_tensor: null argument");
+  if (tensor < 0 || tensor >= VS_T_COUNT) return fail(VS_E_INVAL, "vs_model_set_tensor: bad tensor id %d", tensor);
+  const vs_model_cfg& c = m->c;
+  const bool per_layer = !(tensor == VS_T_EMBED || tensor == VS_T_FINAL_NORM || tensor == VS_T_HEAD);
+  if (per_layer && (layer < 0 || layer >= c.n_layers))
+    return fail(VS_E_INVAL, "vs_model_set_tensor: layer %d out of range", layer);
+  const int d = c.d_model, hd = c.head_dim, H = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn, V = c.vocab;
+  const uint16_t* src = static_cast<const uint16_t*>(d_src);
+  hipStream_t st = S(stream);
+  PackArgs p;
+  memset(&p, 0, sizeof(p));
+  p.src = src;
+  p.hd = hd;
+  auto pack = [&](const Mat& W, int rows, int K, int row_off, int map) {
+    p.dst = W.w;
+    p.rows = rows;
+    p.K = K;
+    p.k_steps = K / 32;
+    p.row_off = row_off;
+    p.map = map;
+    launch_pack(p, st);
+  };
+  switch (tensor) {
+    case VS_T_EMBED:
+      hipMemcpyAsync(m->embed, src, (size_t)V * d * 2, hipMemcpyDeviceToDevice, st);
+      break;
+    case VS_T_ATTN_NORM: launch_bf16_to_f32(src, m->g_attn[layer], d, st); break;
+    case VS_T_FFN_NORM: launch_bf16_to_f32(src, m->g_ffn[layer], d, st); break;
+    case VS_T_FINAL_NORM: launch_bf16_to_f32(src, m->g_final, d, st); break;
+    case VS_T_WQ: pack(m->qkv[layer], H * hd, d, 0, PACK_HEADS); break;
+    case VS_T_WK: pack(m->qkv[layer], Hkv * hd, d, H * hd, PACK_HEADS); break;
+    case VS_T_WV: pack(m->qkv[layer], Hkv * hd, d, (H + Hkv) * hd, PACK_HEADS); break;
+    case VS_T_WO: pack(m->o[layer], d, H * hd, 0, PACK_IDENTITY); break;
+    case VS_T_W_GATE: pack(m->gu[layer], F, d, 0, PACK_EVEN); break;
+    case VS_T_W_UP: pack(m->gu[layer], F, d, 0, PACK_ODD); break;
+    case VS_T_W_DOWN: pack(m->down[layer], d, F, 0, PACK_IDENTITY); break;
+    case VS_T_HEAD: pack(m->head, V, d, 0, PACK_IDENTITY); break;
+  }
+  return check_launch("vs_model_set_tensor");
+}
+
+void vs_model_destroy(vs_model* m) {
+  if (!m) return;
+  for (auto e : m->ev_pool) hipEventDestroy(e);
+  delete m;
+}
+
+vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq,
+                       void* stream, vs_kv** out) {
+  if (m == nullptr || d_kv == nullptr || out == nullptr) return fail(VS_E_INVAL, "vs_kv_create: null argument");
+  if (n_blocks < 1 || max_seqs < 1 || max_seqs > 4096 || max_blocks_per_seq < 1)
+    return fail(VS_E_SHAPE, "vs_kv_create: limits out of range");
+  const vs_model_cfg& c = m->c;
+  vs_kv* kv = new vs_kv();
+  kv->m = m;
+  kv->base = static_cast<char*>(d_kv);
+  kv->n_blocks = n_blocks;
+  kv->max_seqs = max_seqs;
+  kv->bps = max_blocks_per_seq;
+  const size_t pool = align256((size_t)n_blocks * c.n_kv_heads * kBlock * c.head_dim * 2);
+  size_t off = 0;
+  for (int l = 0; l < c.n_layers; ++l) {
+    kv->k.push_back(reinterpret_cast<uint16_t*>(kv->base + off));
+    off += pool;
+    kv->v.push_back(reinterpret_cast<uint16_t*>(kv->base + off));
+    off += pool;
+  }
+  kv->d_kptr = reinterpret_cast<uint16_t**>(kv->base + off);
+  kv->d_vptr = kv->d_kptr + c.n_layers;
+  off += align256((size_t)c.n_layers * 2 * sizeof(void*));
+  kv->P = reinterpret_cast<int*>(kv->base + off);
+  off += align256((size_t)max_seqs * 4);
+  kv->pending = reinterpret_cast<int*>(kv->base + off);
+  off += align256((size_t)max_seqs * 4);
+  kv->committed = reinterpret_cast<int*>(kv->base + off);
+  off += align256((size_t)max_seqs * 4);
+  kv->bt = reinterpret_cast<int*>(kv->base + off);
+  std::vector<uint16_t*> ptrs(kv->k);
+  ptrs.insert(ptrs.end(), kv->v.begin(), kv->v.end());
+  hipStream_t st = S(stream);
+  hipError_t e = hipMemcpyAsync(kv->d_kptr, ptrs.data(), ptrs.size() * sizeof(void*), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host vector goes out of scope
+  if (e != hipSuccess) {
+    delete kv;
+    return fail(VS_E_DEVICE, "vs_kv_create: %s", hipGetErrorString(e));
+  }
+  launch_fill_i32(kv->P, 0, max_seqs, st);
+  launch_fill_i32(kv->pending, -1, max_seqs, st);
+  launch_fill_i32(kv->committed, 0, max_seqs, st);
+  launch_fill_i32(kv->bt, 0, (size_t)max_seqs * max_blocks_per_seq, st);
+  for (int b = n_blocks - 1; b >= 0; --b) kv->free_blocks.push_back(b);
+  kv->blocks.resize(max_seqs);
+  kv->open.assign(max_seqs, 0);
+  kv->cap.assign(max_seqs, 0);
+  kv->P_ub.assign(max_seqs, 0);
+  kv->prefilled.assign(max_seqs, 0);
+  vs_status rc = check_launch("vs_kv_create");
+  if (rc != VS_OK) {
+    delete kv;
+    return rc;
+  }
+  *out = kv;
+  return VS_OK;
+}
+
+void vs_kv_destroy(vs_kv* kv) { delete kv; }
+
+vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id) {
+  if (kv == nullptr || seq_id == nullptr) return fail(VS_E_INVAL, "vs_seq_open: null argument");
+  if (max_len < 1) return fail(VS_E_INVAL, "vs_seq_open: max_len %d", max_len);
+  const int nb = (max_len + kBlock - 1) / kBlock;
+  if (nb > kv->bps) return fail(VS_E_NOKV, "vs_seq_open: %d blocks exceed %d per sequence", nb, kv->bps);
+  if ((int)kv->free_blocks.size() < nb) return fail(VS_E_NOKV, "vs_seq_open: pool has %zu free blocks, %d needed",
+                                                    kv->free_blocks.size(), nb);
+  int s = -1;
+  for (int i = 0; i < kv->max_seqs; ++i)
+    if (!kv->open[i]) {
+      s = i;
+      break;
+    }
+  if (s < 0) return fail(VS_E_NOKV, "vs_seq_open: all %d sequence slots in use", kv->max_seqs);
+  std::vector<int>& bl = kv->blocks[s];
+  bl.clear();
+  for (int i = 0; i < nb; ++i) {
+    bl.push_back(kv->free_blocks.back());
+    kv->free_blocks.pop_back();
+  }
+  hipStream_t st = S(stream);
+  for (int first = 0; first < nb; first += 256) {
+    BlockSetArgs a;
+    memset(&a, 0, sizeof(a));
+    a.bt = kv->bt;
+    a.bps = kv->bps;
+    a.seq = s;
+    a.first = first;
+    a.n = std::min(256, nb - first);
+    a.reset_state = first == 0;
+    a.P = kv->P;
+    a.pending = kv->pending;
+    a.committed = kv->committed;
+    for (int i = 0; i < a.n; ++i) a.ids[i] = bl[first + i];
+    launch_set_blocks(a, st);
+  }
+  vs_status rc = check_launch("vs_seq_open");
+  if (rc != VS_OK) return rc;
+  kv->open[s] = 1;
+  kv->cap[s] = nb * kBlock;
+  kv->P_ub[s] = 0;
+  kv->prefilled[s] = 0;
+  *seq_id = s;
+  return VS_OK;
+}
+
+vs_status vs_seq_close(vs_kv* kv, int32_t seq_id) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_close: null argument");
+  if (seq_id < 0 || seq_id >= kv->max_seqs || !kv->open[seq_id])
+    return fail(VS_E_STATE, "vs_seq_close: sequence %d is not open", seq_id);
+  for (int b : kv->blocks[seq_id]) kv->free_blocks.push_back(b);
+  kv->blocks[seq_id].clear();
+  kv->open[seq_id] = 0;
+  return VS_OK;
+}
+
+vs_status vs_kv_state(vs_kv* kv, int32_t** d_P, int32_t** d_pending, int32_t** d_committed) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_kv_state: null argument");
+  if (d_P) *d_P = kv->P;
+  if (d_pending) *d_pending = kv->pending;
+  if (d_committed) *d_committed = kv->committed;
+  return VS_OK;
+}
+
+vs_status vs_kv_layer(vs_kv* kv, int32_t layer, void** d_k, void** d_v, int32_t** d_block_table) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_kv_layer: null argument");
+  if (layer < 0 || layer >= kv->m->c.n_layers) return fail(VS_E_INVAL, "vs_kv_layer: layer %d", layer);
+  if (d_k) *d_k = kv->k[layer];
+  if (d_v) *d_v = kv->v[layer];
+  if (d_block_table) *d_block_table = kv->bt;
+  return VS_OK;
+}
+
+vs_status vs_kv_sync(vs_kv* kv, void* stream) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_kv_sync: null argument");
+  std::vector<int> P(kv->max_seqs);
+  hipError_t e = hipMemcpyAsync(P.data(), kv->P, kv->max_seqs * 4, hipMemcpyDeviceToHost, S(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_kv_sync: %s", hipGetErrorString(e));
+  for (int s = 0; s < kv->max_seqs; ++s)
+    if (kv->open[s]) kv->P_ub[s] = P[s];
+  return VS_OK;
+}
+
+vs_status vs_forward_layers(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start, int32_t end,
+                            const int32_t* d_tokens, const float* d_hidden_in, float* d_hidden_out, void* stream) {
+  if (m == nullptr || kv == nullptr) return fail(VS_E_INVAL, "vs_forward_layers: null handle");
+  if (start < 0 || end > m->c.n_layers || start > end) return fail(VS_E_INVAL, "vs_forward_layers: bad layer range");
+  if (start == 0 && d_tokens == nullptr) return fail(VS_E_INVAL, "vs_forward_layers: tokens needed at start 0");
+  if (start > 0 && d_hidden_in == nullptr) return fail(VS_E_INVAL, "vs_forward_layers: hidden rows needed");
+  RowMap rm;
+  vs_status rc = batch_rowmap(kv, b, &rm);
+  if (rc != VS_OK) return rc;
+  if ((rc = check_capacity(kv, rm)) != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  const float* g0 = start < end ? m->g_attn[start] : m->g_final;
+  load_rows(m, rm.M, start == 0 ? d_tokens : nullptr, d_hidden_in, nullptr, g0, st);
+  run_layers(m, kv, rm, start, end, st, nullptr, nullptr);
+  if (d_hidden_out) launch_copy_rows(m->h, d_hidden_out, rm.M, m->c.d_model, st);
+  return check_launch("vs_forward_layers");
+}
+
+vs_status vs_head(vs_model* m, int32_t M, const float* d_hidden, float* d_logits, void* stream) {
+  if (m == nullptr || d_hidden == nullptr || d_logits == nullptr) return fail(VS_E_INVAL, "vs_head: null argument");
+  if (M < 1 || M > m->max_rows) return fail(VS_E_SHAPE, "vs_head: %d rows", M);
+  hipStream_t st = S(stream);
+  load_rows(m, M, nullptr, d_hidden, nullptr, m->g_final, st);
+  run_head(m, M, d_logits, nullptr, st);
+  return check_launch("vs_head");
+}
+
+vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t mode,
+                     float temp, const double* d_u, float* d_logits_last, void* stream) {
+  if (m == nullptr || kv == nullptr || d_tokens == nullptr) return fail(VS_E_INVAL, "vs_prefill: null argument");
+  if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_prefill: sequence not open");
+  if (kv->prefilled[seq]) return fail(VS_E_STATE, "vs_prefill: sequence %d already prefilled", seq);
+  if (n < 1) return fail(VS_E_INVAL, "vs_prefill: n = %d", n);
+  if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "vs_prefill: mode %d", mode);
+  if (mode == VS_SAMPLE && (d_u == nullptr || !(temp > 0.f))) return fail(VS_E_INVAL, "vs_prefill: sampling needs u, T>0");
+  if (n + 1 > kv->cap[seq]) return fail(VS_E_NOKV, "vs_prefill: %d tokens exceed capacity %d", n, kv->cap[seq]);
+  hipStream_t st = S(stream);
+  const int chunk = std::min(kMaxRows, m->max_rows);
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int nc = std::min(chunk, n - c0);
+    RowMap rm;
+    memset(&rm, 0, sizeof(rm));
+    rm.n_seq = 1;
+    rm.M = nc;
+    rm.seq[0] = seq;
+    rm.row_start[1] = nc;
+    load_rows(m, nc, d_tokens + c0, nullptr, nullptr, m->g_attn[0], st);
+    run_layers(m, kv, rm, 0, m->c.n_layers, st, nullptr, nullptr);
+    const bool last = c0 + nc == n;
+    if (last) run_head(m, nc, m->logits, nullptr, st);
+    launch_advance(kv->P, kv->committed, seq, nc, nc + (last ? 1 : 0), st);
+    kv->P_ub[seq] += nc;
+    if (last) {
+      PickArgs p;
+      memset(&p, 0, sizeof(p));
+      p.n = 1;
+      p.mode = mode;
+      p.temp = temp;
+      p.slot = 32;
+      p.pending = kv->pending;
+      p.amax_val = m->amax_val;
+      p.amax_idx = m->amax_idx;
+      p.groups = m->head_groups;
+      p.Mprev = nc;
+      p.logits = m->logits;
+      p.V = m->c.vocab;
+      p.u = d_u;
+      p.tokens = kv->pending;
+      p.seq[0] = seq;
+      p.src[0] = nc - 1;
+      p.lrow[0] = nc - 1;
+      p.uidx[0] = 0;
+      p.dst[0] = seq;
+      launch_pick(p, st);
+      if (d_logits_last)
+        hipMemcpyAsync(d_logits_last, m->logits + (size_t)(nc - 1) * m->c.vocab, (size_t)m->c.vocab * 4,
+                       hipMemcpyDeviceToDevice, st);
+    }
+  }
+  kv->prefilled[seq] = 1;
+  return check_launch("vs_prefill");
+}
+
+}  // extern "C"
+
+namespace {
+
+vs_status validate_chain(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int32_t* k, int mode,
+                         float temp, const double* d_u, int* M_out) {
+  if (n_seq < 1 || n_seq > kMaxSeq) return fail(VS_E_SHAPE, "n_seq %d not in [1, %d]", n_seq, kMaxSeq);
+  if (seq == nullptr || k == nullptr) return fail(VS_E_INVAL, "null seq or k");
+  if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "mode %d", mode);
+  if (mode == VS_SAMPLE && (d_u == nullptr || !(temp > 0.f))) return fail(VS_E_INVAL, "sampling needs u and T > 0");
+  int M = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int s = seq[i];
+    if (s < 0 || s >= kv->max_seqs || !kv->open[s]) return fail(VS_E_STATE, "sequence %d is not open", s);
+    if (!kv->prefilled[s]) return fail(VS_E_STATE, "sequence %d has no prefill", s);
+    for (int j = 0; j < i; ++j)
+      if (seq[j] == s) return fail(VS_E_INVAL, "sequence %d listed twice", s);
+    if (k[i] < 0 || k[i] > VS_MAX_K) return fail(VS_E_INVAL, "k = %d not in [0, %d]", k[i], VS_MAX_K);
+    if (kv->P_ub[s] + k[i] + 1 > kv->cap[s]) return fail(VS_E_NOKV, "sequence %d: capacity %d reached", s, kv->cap[s]);
+    M += k[i] + 1;
+  }
+  if (M > m->max_rows || M > kMaxRows) return fail(VS_E_SHAPE, "%d verify rows exceed max_rows %d", M, m->max_rows);
+  *M_out = M;
+  return VS_OK;
+}
+
+void chain_batch_rowmap(const int n_seq, const int32_t* seq, const int32_t* k, RowMap* rm) {
+  memset(rm, 0, sizeof(*rm));
+  rm->n_seq = n_seq;
+  int M = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    rm->seq[i] = seq[i];
+    rm->row_start[i] = M;
+    M += k[i] + 1;
+  }
+  rm->row_start[n_seq] = M;
+  rm->M = M;
+}
+
+void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int32_t* k, int mode, float temp,
+                const double* d_u, int32_t* d_tokens, float* d_hidden_L, float* d_draft_logits, hipStream_t st) {
+  const int L = m->c.exit_layer;
+  std::vector<int> vstart(n_seq);
+  int kmax = 0, M = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    vstart[i] = M;
+    M += k[i] + 1;
+    kmax = std::max(kmax, (int)k[i]);
+  }
+  std::vector<int> prev;  // active sequences (indices) of the previous step
+  for (int s = 0; s <= kmax; ++s) {
+    std::vector<int> act;
+    for (int i = 0; i < n_seq; ++i)
+      if (k[i] >= s) act.push_back(i);
+    const int Ma = (int)act.size();
+    PickArgs p;
+    memset(&p, 0, sizeof(p));
+    p.n = Ma;
+    p.mode = mode;
+    p.temp = temp;
+    p.slot = s - 1;
+    p.pending = kv->pending;
+    p.amax_val = m->amax_val;
+    p.amax_idx = m->amax_idx;
+    p.groups = m->head_groups;
+    p.Mprev = (int)prev.size();
+    p.logits = d_draft_logits;
+    p.V = m->c.vocab;
+    p.u = d_u;
+    p.tokens = d_tokens;
+    std::vector<int> rows_src(Ma), rows_out(Ma), logit_rows(Ma);
+    for (int a = 0; a < Ma; ++a) {
+      const int i = act[a];
+      p.seq[a] = seq[i];
+      p.src[a] = -1;
+      if (s > 0)
+        for (int b = 0; b < (int)prev.size(); ++b)
+          if (prev[b] == i) p.src[a] = b;
+      p.lrow[a] = vstart[i] + s - 1;
+      p.uidx[a] = i;
+      p.dst[a] = vstart[i] + s;
+      rows_src[a] = vstart[i] + s;
+      logit_rows[a] = k[i] > s ? vstart[i] + s : -1;
+    }
+    timed(m, F_SMALL, 0, st, [&] { launch_pick(p, st); });
+    RowMap rm;
+    memset(&rm, 0, sizeof(rm));
+    rm.n_seq = Ma;
+    rm.M = Ma;
+    rm.idx_off = s;
+    for (int a = 0; a < Ma; ++a) {
+      rm.seq[a] = seq[act[a]];
+      rm.row_start[a] = a;
+    }
+    rm.row_start[Ma] = Ma;
+    load_rows(m, Ma, d_tokens, nullptr, rows_src.data(), L > 0 ? m->g_attn[0] : m->g_final, st);
+    if (L > 0) {
+      run_layers(m, kv, rm, 0, L, st, d_hidden_L, rows_src.data());
+    } else {
+      for (int a = 0; a < Ma; ++a)  // with L = 0 the layer-L input is the embedding itself
+        hipMemcpyAsync(d_hidden_L + (size_t)rows_src[a] * m->c.d_model, m->h + (size_t)a * m->c.d_model,
+                       (size_t)m->c.d_model * 4, hipMemcpyDeviceToDevice, st);
+    }
+    bool need_head = false;
+    for (int a = 0; a < Ma; ++a) need_head |= k[act[a]] > s;
+    if (need_head) run_head(m, Ma, d_draft_logits, logit_rows.data(), st);
+    prev = act;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+vs_status vs_draft(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
+                   float temp, const double* d_u, int32_t* d_tokens, float* d_hidden_L, float* d_draft_logits,
+                   void* stream) {
+  if (m == nullptr || kv == nullptr || d_tokens == nullptr || d_hidden_L == nullptr)
+    return fail(VS_E_INVAL, "vs_draft: null argument");
+  int M = 0;
+  vs_status rc = validate_chain(m, kv, n_seq, seq, k, mode, temp, d_u, &M);
+  if (rc != VS_OK) return rc;
+  if (mode == VS_SAMPLE && d_draft_logits == nullptr) return fail(VS_E_INVAL, "vs_draft: sampling needs draft logits");
+  draft_impl(m, kv, n_seq, seq, k, mode, temp, d_u, d_tokens, d_hidden_L, d_draft_logits, S(stream));
+  return check_launch("vs_draft");
+}
+
+vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_layer, const int32_t* d_tokens,
+                    const float* d_hidden_in, float* d_logits, void* stream) {
+  if (m == nullptr || kv == nullptr || d_logits == nullptr) return fail(VS_E_INVAL, "vs_verify: null argument");
+  if (start_layer < 0 || start_layer > m->c.n_layers) return fail(VS_E_INVAL, "vs_verify: start_layer %d", start_layer);
+  if (start_layer == 0 && d_tokens == nullptr) return fail(VS_E_INVAL, "vs_verify: tokens needed at start 0");
+  if (start_layer > 0 && d_hidden_in == nullptr) return fail(VS_E_INVAL, "vs_verify: hidden rows needed");
+  RowMap rm;
+  vs_status rc = batch_rowmap(kv, b, &rm);
+  if (rc != VS_OK) return rc;
+  if ((rc = check_capacity(kv, rm)) != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  const int N = m->c.n_layers;
+  load_rows(m, rm.M, start_layer == 0 ? d_tokens : nullptr, d_hidden_in, nullptr,
+            start_layer < N ? m->g_attn[start_layer] : m->g_final, st);
+  run_layers(m, kv, rm, start_layer, N, st, nullptr, nullptr);
+  run_head(m, rm.M, d_logits, nullptr, st);
+  return check_launch("vs_verify");
+}
+
+vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
+                    const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                    void* stream) {
+  if (m == nullptr || d_tokens == nullptr || d_logits == nullptr || d_result == nullptr || b == nullptr ||
+      b->seq == nullptr || b->n_rows == nullptr)
+    return fail(VS_E_INVAL, "vs_accept: null argument");
+  if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "vs_accept: mode %d", mode);
+  if (b->n_seq < 1 || b->n_seq > kMaxSeq) return fail(VS_E_SHAPE, "vs_accept: n_seq %d", b->n_seq);
+  if (mode == VS_SAMPLE) {
+    if (d_draft_logits == nullptr || d_u == nullptr || !(temp > 0.f))
+      return fail(VS_E_INVAL, "vs_accept: sampling needs draft logits, u and T > 0");
+    if (b->d_mask != nullptr || b->d_depth != nullptr) return fail(VS_E_INVAL, "vs_accept: sampling is chain-only");
+  }
+  RowMap rm;
+  memset(&rm, 0, sizeof(rm));
+  rm.n_seq = b->n_seq;
+  int M = 0;
+  for (int i = 0; i < b->n_seq; ++i) {
+    if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows) return fail(VS_E_SHAPE, "vs_accept: rows %d", b->n_rows[i]);
+    rm.seq[i] = b->seq[i];
+    rm.row_start[i] = M;
+    M += b->n_rows[i];
+  }
+  rm.row_start[b->n_seq] = M;
+  rm.M = M;
+  rm.mask = b->d_mask;
+  rm.depth = b->d_depth;
+  if (M > m->max_rows) return fail(VS_E_SHAPE, "vs_accept: %d rows exceed max_rows", M);
+  hipStream_t st = S(stream);
+  StatsArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.logits = d_logits;
+  sa.V = m->c.vocab;
+  sa.temp = mode == VS_SAMPLE ? temp : 1.0f;
+  sa.mx = m->st_mx;
+  sa.amax = m->st_amax;
+  sa.second = m->st_second;
+  sa.sumexp = mode == VS_SAMPLE ? m->st_sum : nullptr;
+  timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&] { launch_row_stats(sa, M, st); });
+  if (mode == VS_SAMPLE) {
+    StatsArgs da = sa;
+    da.logits = d_draft_logits;
+    da.mx = m->dst_mx;
+    da.amax = m->dst_amax;
+    da.second = nullptr;
+    da.sumexp = m->dst_sum;
+    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&] { launch_row_stats(da, M, st); });
+  }
+  AcceptArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = rm;
+  a.mode = mode;
+  a.temp = temp;
+  a.tokens = d_tokens;
+  a.logits = d_logits;
+  a.dlogits = d_draft_logits;
+  a.mx = m->st_mx;
+  a.amax = m->st_amax;
+  a.second = m->st_second;
+  a.sumexp = m->st_sum;
+  a.dmx = m->dst_mx;
+  a.dsumexp = m->dst_sum;
+  a.V = m->c.vocab;
+  a.u = d_u;
+  a.result = d_result;
+  timed(m, F_SMALL, 0, st, [&] { launch_accept(a, st); });
+  return check_launch("vs_accept");
+}
+
+vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_result, void* stream) {
+  if (m == nullptr || kv == nullptr || d_result == nullptr) return fail(VS_E_INVAL, "vs_commit: null argument");
+  RowMap rm;
+  vs_status rc = batch_rowmap(kv, b, &rm);
+  if (rc != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  CommitArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = rm;
+  a.result = d_result;
+  a.P = kv->P;
+  a.pending = kv->pending;
+  a.committed = kv->committed;
+  a.bt = kv->bt;
+  a.bps = kv->bps;
+  a.kpool = kv->d_kptr;
+  a.vpool = kv->d_vptr;
+  a.n_layers = m->c.n_layers;
+  a.Hkv = m->c.n_kv_heads;
+  a.hd = m->c.head_dim;
+  if (b->d_mask != nullptr) timed(m, F_SMALL, 0, st, [&] { launch_compact(a, st); });
+  timed(m, F_SMALL, 0, st, [&] { launch_commit(a, st); });
+  for (int i = 0; i < rm.n_seq; ++i) kv->P_ub[rm.seq[i]] += rm.row_start[i + 1] - rm.row_start[i];
+  return check_launch("vs_commit");
+}
+
+vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
+                  float temp, const double* d_u, int32_t* d_tokens, int32_t* d_result, void* stream) {
+  if (m == nullptr || kv == nullptr || d_tokens == nullptr || d_result == nullptr)
+    return fail(VS_E_INVAL, "vs_step: null argument");
+  int M = 0;
+  vs_status rc = validate_chain(m, kv, n_seq, seq, k, mode, temp, d_u, &M);
+  if (rc != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  draft_impl(m, kv, n_seq, seq, k, mode, temp, d_u, d_tokens, m->hidden, m->dlogits, st);
+  std::vector<int> rows(n_seq);
+  for (int i = 0; i < n_seq; ++i) rows[i] = k[i] + 1;
+  vs_batch b{n_seq, seq, rows.data(), nullptr, nullptr};
+  const int L = m->c.exit_layer;
+  if ((rc = vs_verify(m, kv, &b, L, d_tokens, m->hidden, m->logits, stream)) != VS_OK) return rc;
+  if ((rc = vs_accept(m, &b, mode, temp, d_tokens, m->logits, m->dlogits, d_u, d_result, stream)) != VS_OK) return rc;
+  return vs_commit(m, kv, &b, d_result, stream);
+}
+
+vs_status vs_stats_enable(vs_model* m, int32_t on) {
+  if (m == nullptr) return fail(VS_E_INVAL, "vs_stats_enable: null model");
+  m->stats_on = on != 0;
+  return VS_OK;
+}
+
+vs_status vs_stats_reset(vs_model* m) {
+  if (m == nullptr) return fail(VS_E_INVAL, "vs_stats_reset: null model");
+  for (const Timed& t : m->timed) hipEventSynchronize(t.b);
+  m->timed.clear();
+  m->ev_used = 0;
+  for (int f = 0; f < F_COUNT; ++f) m->acc_ms[f] = m->acc_bytes[f] = 0, m->acc_n[f] = 0;
+  return VS_OK;
+}
+
+vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* n_out) {
+  if (m == nullptr || out == nullptr || n_out == nullptr) return fail(VS_E_INVAL, "vs_stats_read: null argument");
+  for (const Timed& t : m->timed) {
+    if (hipEventSynchronize(t.b) != hipSuccess) return fail(VS_E_DEVICE, "vs_stats_read: event sync failed");
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, t.a, t.b);
+    m->acc_ms[t.fam] += ms;
+    m->acc_bytes[t.fam] += t.bytes;
+    m->acc_n[t.fam] += 1;
+  }
+  m->timed.clear();
+  m->ev_used = 0;
+  int n = 0;
+  for (int f = 0; f < F_COUNT && n < max; ++f) {
+    memset(&out[n], 0, sizeof(out[n]));
+    snprintf(out[n].name, sizeof(out[n].name), "%s", kFamilyNames[f]);
+    out[n].launches = m->acc_n[f];
+    out[n].total_ms = m->acc_ms[f];
+    out[n].bytes = m->acc_bytes[f];
+    ++n;
+  }
+  *n_out = n;
+  return VS_OK;
+}
+
+}  // extern "C"

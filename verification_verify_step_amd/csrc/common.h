@@ -1,0 +1,86 @@
+// Internal types and device helpers of the verify-step library (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vstep.h"
+
+namespace vs {
+
+constexpr int kMaxSeq = VS_MAX_SEQS;
+constexpr int kMaxRows = VS_MAX_ROWS;
+constexpr int kBlock = 16;    // KV tokens per block
+constexpr int kChunk = 64;    // keys per attention sub-chunk
+
+// --------------------------------------------------------------------------
+// Rows of one pass (passed by value to the kernels that place rows).
+// Sequence i owns rows [row_start[i], row_start[i+1]); its row m has in-round
+// index idx = idx_off + m - row_start[i], KV slot P + win + idx and position
+// P + depth (depth = idx for a chain).  Visible keys: slots < P, plus slots
+// P + win + j for every bit j of the row's mask.
+struct RowMap {
+  int n_seq;
+  int M;
+  int idx_off;
+  int win;
+  int seq[kMaxSeq];
+  int row_start[kMaxSeq + 1];
+  const int* depth;       // device [M] or null
+  const uint64_t* mask;   // device [M] or null
+};
+
+struct KvView {
+  uint16_t* k;            // layer pool [n_blocks][Hkv][16][hd] bf16
+  uint16_t* v;
+  const int* P;           // [max_seqs]
+  const int* bt;          // [max_seqs][bps]
+  int bps;
+};
+
+// --------------------------------------------------------------------------
+// bf16 helpers (bit patterns in uint16_t).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// The activation side of a GEMM is stored split into two bf16 parts
+// (hi = bf16(x), lo = bf16(x - hi)) so that bf16 MFMA keeps ~16 bits of the
+// fp32 activation.  Layout of a [M][K] activation: for k-step s = k/32,
+// quad j = (k%32)/8, row m: 32 bytes = 8 hi then 8 lo bf16 at
+//   ((s*4 + j) * M + m) * 16 (in bf16 units).
+__device__ __forceinline__ size_t xa_index(int k, int m, int M) {
+  return ((size_t)((k >> 5) * 4 + ((k >> 3) & 3)) * M + m) * 16 + (k & 7);
+}
+__device__ __forceinline__ void xa_store(uint16_t* xa, int k, int m, int M, float v) {
+  const uint16_t hi = f2bf(v);
+  const uint16_t lo = f2bf(v - bf2f(hi));
+  const size_t i = xa_index(k, m, M);
+  xa[i] = hi;
+  xa[i + 8] = lo;
+}
+
+// Row placement helpers for kernels that read a RowMap.
+__device__ __forceinline__ int row_seq_index(const RowMap& rm, int m) {
+  int i = 0;
+  while (i + 1 < rm.n_seq && rm.row_start[i + 1] <= m) ++i;
+  return i;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace vs

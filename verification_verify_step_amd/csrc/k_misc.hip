@@ -1,0 +1,441 @@
+// Small kernels of the round: weight packing, row loading (embedding or
+// hidden rows), per-row vocabulary statistics, draft-token selection and
+// sampling, acceptance, and commit / tree compaction (gfx950).
+#include <climits>
+
+#include "misc.h"
+
+namespace vs {
+
+// ---------------------------------------------------------------------------
+// Weight packing: canonical row-major [rows][K] bf16 -> MFMA B fragments.
+// Canonical row r lands on packed row p = row_off + map(r); fragment
+// (tile, kstep) holds lane l = (p%16) + 16*j with k = 32*kstep + 8*j .. +8.
+__global__ void pack_kernel(PackArgs a) {
+  const size_t total = (size_t)a.rows * a.k_steps * 4;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(e % 4);
+    const int s = (int)((e / 4) % a.k_steps);
+    const int r = (int)(e / ((size_t)4 * a.k_steps));
+    int p;
+    if (a.map == PACK_HEADS) {  // pair (i, i + hd/2) of each head side by side
+      const int h = r / a.hd, i = r % a.hd, half = a.hd / 2;
+      p = h * a.hd + (i < half ? 2 * i : 2 * (i - half) + 1);
+    } else if (a.map == PACK_EVEN) {
+      p = 2 * r;
+    } else if (a.map == PACK_ODD) {
+      p = 2 * r + 1;
+    } else {
+      p = r;
+    }
+    p += a.row_off;
+    const int tile = p / 16, lane = (p % 16) + 16 * j;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.src + (size_t)r * a.K + 32 * s + 8 * j);
+    *reinterpret_cast<uint4*>(a.dst + (((size_t)tile * a.k_steps + s) * 64 + lane) * 8) = v;
+  }
+}
+
+void launch_pack(const PackArgs& a, hipStream_t st) {
+  const size_t total = (size_t)a.rows * a.k_steps * 4;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+}
+
+__global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf2f(src[i]);
+}
+void launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t st) {
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, src, dst, n);
+}
+
+__global__ void fill_i32_kernel(int* p, int v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+void launch_fill_i32(int* p, int v, size_t n, hipStream_t st) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, v, n);
+}
+
+__global__ void set_blocks_kernel(BlockSetArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.n) a.bt[a.seq * a.bps + a.first + i] = a.ids[i];
+  if (i == 0 && a.reset_state) {
+    a.P[a.seq] = 0;
+    a.pending[a.seq] = -1;
+    a.committed[a.seq] = 0;
+  }
+}
+void launch_set_blocks(const BlockSetArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(set_blocks_kernel, dim3(1), dim3(256), 0, st, a);
+}
+
+// ---------------------------------------------------------------------------
+// Row loading: h[m] = embed[token] (or a given hidden row); the next
+// consumer's activation (h * g) as split-bf16 fragments; per 256-column group
+// sums of h^2 for the fused RMSNorm.
+__global__ __launch_bounds__(256) void load_rows_kernel(LoadArgs a) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float wsum[4][kMaxRows];
+  for (int m = 0; m < a.M; ++m) {
+    float v = 0.f;
+    if (n < a.d) {
+      const int src = a.src_identity ? m : a.src_row[m];
+      if (a.tokens != nullptr) {
+        const int t = min(max(a.tokens[src], 0), a.V - 1);  // never read outside the table
+        v = bf2f(a.embed[(size_t)t * a.d + n]);
+      } else {
+        v = a.hidden[(size_t)src * a.d + n];
+      }
+      a.h[(size_t)m * a.d + n] = v;
+      xa_store(a.xa, n, m, a.M, v * a.g[n]);
+    }
+    const float s = wave_sum(v * v);
+    if (lane == 0) wsum[wave][m] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < a.M) {
+    const int m = threadIdx.x;
+    a.ss[blockIdx.x * a.M + m] = ((wsum[0][m] + wsum[1][m]) + wsum[2][m]) + wsum[3][m];
+  }
+}
+void launch_load_rows(const LoadArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(load_rows_kernel, dim3((a.d + 255) / 256), dim3(256), 0, st, a);
+}
+
+__global__ void copy_rows_kernel(const float* src, float* dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+void launch_copy_rows(const float* src, float* dst, int M, int d, hipStream_t st) {
+  const size_t n = (size_t)M * d;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, n);
+}
+
+// ---------------------------------------------------------------------------
+// Block-level reductions (256 threads) in a fixed order.
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+};
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  if (a.v1 > b.v1 || (a.v1 == b.v1 && a.i1 < b.i1)) {
+    r.v1 = a.v1;
+    r.i1 = a.i1;
+    r.v2 = fmaxf(a.v2, b.v1);
+  } else {
+    r.v1 = b.v1;
+    r.i1 = b.i1;
+    r.v2 = fmaxf(b.v2, a.v1);
+  }
+  return r;
+}
+__device__ Top2 block_top2(Top2 t) {
+  __shared__ Top2 sh[256];
+  sh[threadIdx.x] = t;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] = top2_merge(sh[threadIdx.x], sh[threadIdx.x + o]);
+    __syncthreads();
+  }
+  const Top2 r = sh[0];
+  __syncthreads();
+  return r;
+}
+__device__ double block_sum_d(double v) {
+  __shared__ double sh[256];
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// Per-row statistics of logits: max, argmax (lowest id on ties), second
+// largest value, and S = sum exp((z - max)/T) in fp64 when requested.
+__device__ void row_stats(const float* z, int V, float temp, float* mx, int* amax, float* second, double* sumexp) {
+  Top2 t{-INFINITY, INT_MAX, -INFINITY};
+  for (int j = threadIdx.x; j < V; j += 256) t = top2_merge(t, Top2{z[j], j, -INFINITY});
+  t = block_top2(t);
+  if (threadIdx.x == 0) {
+    *mx = t.v1;
+    *amax = t.i1;
+    if (second) *second = t.v2;
+  }
+  if (sumexp != nullptr) {
+    const double inv_t = 1.0 / (double)temp;
+    const int per = (V + 255) / 256;
+    const int j0 = min(V, (int)threadIdx.x * per), j1 = min(V, j0 + per);
+    double s = 0.0;
+    for (int j = j0; j < j1; ++j) s += exp(((double)z[j] - (double)t.v1) * inv_t);
+    s = block_sum_d(s);
+    if (threadIdx.x == 0) *sumexp = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void row_stats_kernel(StatsArgs a) {
+  const int m = blockIdx.x;
+  row_stats(a.logits + (size_t)m * a.V, a.V, a.temp, a.mx + m, a.amax + m, a.second ? a.second + m : nullptr,
+            a.sumexp ? a.sumexp + m : nullptr);
+}
+void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
+  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(256), 0, st, a);
+}
+
+// Inverse-CDF draw from weights w_j = weight(j) >= 0 (fp64), ids ascending:
+// the smallest j with u*S < C_j, else the largest j with w_j > 0.  Each thread
+// owns a contiguous chunk of ids; chunk sums are prefixed in thread order.
+template <typename F>
+__device__ int block_sample(int V, double u, F weight) {
+  __shared__ double csum[256];
+  __shared__ double s_total;
+  __shared__ int s_pick, s_last;
+  const int per = (V + 255) / 256;
+  const int j0 = min(V, (int)threadIdx.x * per), j1 = min(V, j0 + per);
+  double s = 0.0;
+  int last = -1;
+  for (int j = j0; j < j1; ++j) {
+    const double w = weight(j);
+    s += w;
+    if (w > 0.0) last = j;
+  }
+  csum[threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    s_pick = INT_MAX;
+    s_last = -1;
+  }
+  __syncthreads();
+  atomicMax(&s_last, last);
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int t = 0; t < 256; ++t) {
+      const double c = csum[t];
+      csum[t] = acc;
+      acc += c;
+    }
+    s_total = acc;
+  }
+  __syncthreads();
+  const double target = u * s_total;
+  double c = csum[threadIdx.x];
+  for (int j = j0; j < j1; ++j) {
+    c += weight(j);
+    if (target < c) {
+      atomicMin(&s_pick, j);
+      break;
+    }
+  }
+  __syncthreads();
+  const int pick = s_pick == INT_MAX ? s_last : s_pick;
+  __syncthreads();
+  return pick;
+}
+
+// Softmax-at-T weight of id j of a logits row: exp((z_j - max)/T), fp64.
+struct SoftW {
+  const float* z;
+  double mx, inv_t;
+  __device__ double operator()(int j) const { return exp(((double)z[j] - mx) * inv_t); }
+};
+
+// ---------------------------------------------------------------------------
+// Draft-token selection (one workgroup per sequence).
+__global__ __launch_bounds__(256) void pick_kernel(PickArgs a) {
+  const int i = blockIdx.x;
+  int tok;
+  if (a.src[i] < 0) {
+    tok = a.pending[a.seq[i]];
+  } else if (a.mode == VS_GREEDY) {
+    Top2 t{-INFINITY, INT_MAX, -INFINITY};
+    for (int g = threadIdx.x; g < a.groups; g += 256) {
+      const int e = g * a.Mprev + a.src[i];
+      t = top2_merge(t, Top2{a.amax_val[e], a.amax_idx[e], -INFINITY});
+    }
+    t = block_top2(t);
+    tok = t.i1;
+  } else {
+    const float* z = a.logits + (size_t)a.lrow[i] * a.V;
+    __shared__ float s_mx;
+    __shared__ int s_am;
+    row_stats(z, a.V, a.temp, &s_mx, &s_am, nullptr, nullptr);
+    __syncthreads();
+    SoftW w{z, (double)s_mx, 1.0 / (double)a.temp};
+    tok = block_sample(a.V, a.u[(size_t)a.uidx[i] * VS_N_UNIFORMS + a.slot], w);
+  }
+  if (threadIdx.x == 0) a.tokens[a.dst[i]] = tok;
+}
+void launch_pick(const PickArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(pick_kernel, dim3(a.n), dim3(256), 0, st, a);
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance (one workgroup per sequence).
+__device__ __forceinline__ int row_parent(const RowMap& rm, int r0, int c) {
+  if (rm.mask == nullptr) return c - 1;
+  const uint64_t anc = rm.mask[r0 + c] & ~(1ull << c);
+  return anc == 0 ? -1 : 63 - __clzll((long long)anc);
+}
+
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  const int i = blockIdx.x;
+  const int r0 = a.rows.row_start[i];
+  const int nr = a.rows.row_start[i + 1] - r0;
+  int* res = a.result + i * VS_RESULT_INTS;
+  if (a.mode == VS_GREEDY) {
+    if (threadIdx.x == 0) {
+      int cur = 0, n_path = 0, flags = 0;
+      int path[VS_RESULT_INTS - 4];
+      while (true) {
+        if (a.mx[r0 + cur] - a.second[r0 + cur] < 4e-2f) flags |= 1;
+        const int t = a.amax[r0 + cur];
+        int nxt = -1;
+        for (int c = cur + 1; c < nr; ++c)
+          if (row_parent(a.rows, r0, c) == cur && a.tokens[r0 + c] == t) {
+            nxt = c;
+            break;
+          }
+        if (nxt < 0 || n_path >= VS_RESULT_INTS - 4) break;
+        path[n_path++] = nxt;
+        cur = nxt;
+      }
+      res[0] = n_path;
+      res[1] = a.amax[r0 + cur];
+      res[2] = flags;
+      res[3] = n_path;
+      for (int j = 0; j < VS_RESULT_INTS - 4; ++j) res[4 + j] = j < n_path ? path[j] : -1;
+    }
+    return;
+  }
+  // Stochastic chain: rows r0 .. r0+k, row j judges token of row j+1.
+  const int k = nr - 1;
+  const double inv_t = 1.0 / (double)a.temp;
+  const double* u = a.u + (size_t)i * VS_N_UNIFORMS;
+  __shared__ int s_a, s_flags, s_reject;
+  if (threadIdx.x == 0) {
+    int acc = 0, flags = 0, reject = -1;
+    for (int j = 0; j < k; ++j) {
+      const int r = r0 + j;
+      const int d = a.tokens[r + 1];
+      const double p = exp(((double)a.logits[(size_t)r * a.V + d] - (double)a.mx[r]) * inv_t) / a.sumexp[r];
+      const double q = exp(((double)a.dlogits[(size_t)r * a.V + d] - (double)a.dmx[r]) * inv_t) / a.dsumexp[r];
+      const double ratio = q > 0.0 ? p / q : 0.0;
+      const double uj = u[16 + j];
+      if (fabs(ratio - uj) < 1e-3) flags |= 1;
+      if (uj < fmin(1.0, ratio)) {
+        ++acc;
+        continue;
+      }
+      reject = j;
+      break;
+    }
+    s_a = acc;
+    s_flags = flags;
+    s_reject = reject;
+  }
+  __syncthreads();
+  const int reject = s_reject;
+  int y;
+  if (reject < 0) {
+    const int r = r0 + k;
+    SoftW w{a.logits + (size_t)r * a.V, (double)a.mx[r], inv_t};
+    y = block_sample(a.V, u[32], w);
+  } else {
+    const int r = r0 + reject;
+    const float* zt = a.logits + (size_t)r * a.V;
+    const float* zd = a.dlogits + (size_t)r * a.V;
+    const double mt = a.mx[r], md = a.dmx[r], st = a.sumexp[r], sd = a.dsumexp[r];
+    auto resid = [&](int j) -> double {
+      const double p = exp(((double)zt[j] - mt) * inv_t) / st;
+      const double q = exp(((double)zd[j] - md) * inv_t) / sd;
+      return p > q ? p - q : 0.0;
+    };
+    double part = 0.0;
+    for (int j = threadIdx.x; j < a.V; j += 256) part += resid(j);
+    const double tot = block_sum_d(part);
+    if (tot > 0.0) {
+      y = block_sample(a.V, u[32], resid);
+    } else {
+      SoftW w{zt, mt, inv_t};
+      y = block_sample(a.V, u[32], w);
+    }
+  }
+  if (threadIdx.x == 0) {
+    res[0] = s_a;
+    res[1] = y;
+    res[2] = s_flags;
+    res[3] = s_a;
+    for (int j = 0; j < VS_RESULT_INTS - 4; ++j) res[4 + j] = j < s_a ? j + 1 : -1;
+  }
+}
+void launch_accept(const AcceptArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(a.rows.n_seq), dim3(256), 0, st, a);
+}
+
+// ---------------------------------------------------------------------------
+// Tree compaction: K/V of accepted path rows P + path[j] -> P + 1 + j in
+// every layer.  Sources increase along the path and never lie below their
+// destination, so copying j in increasing order per element is safe.
+__global__ void compact_kernel(CommitArgs a) {
+  const int i = blockIdx.x;
+  const int layer = blockIdx.y / 2, is_v = blockIdx.y % 2;
+  const int* res = a.result + i * VS_RESULT_INTS;
+  const int nr = a.rows.row_start[i + 1] - a.rows.row_start[i];
+  const int n_path = min(max(res[3], 0), nr - 1);
+  const int sq = a.rows.seq[i];
+  const int P = a.P[sq];
+  uint16_t* pool = is_v ? a.vpool[layer] : a.kpool[layer];
+  const int per_slot = a.Hkv * a.hd / 8;  // 16-byte pieces of one slot
+  for (int e = threadIdx.x; e < per_slot; e += blockDim.x) {
+    const int kvh = e / (a.hd / 8), part = e % (a.hd / 8);
+    for (int j = 0; j < n_path; ++j) {
+      const int r = res[4 + j];
+      if (r < 1 || r >= nr) break;  // a path row outside this sequence's rows
+      const int src = P + r, dst = P + 1 + j;
+      if (src == dst) continue;
+      const int bs = a.bt[sq * a.bps + src / kBlock], bd = a.bt[sq * a.bps + dst / kBlock];
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          pool + (((size_t)bs * a.Hkv + kvh) * kBlock + src % kBlock) * a.hd + part * 8);
+      *reinterpret_cast<uint4*>(pool + (((size_t)bd * a.Hkv + kvh) * kBlock + dst % kBlock) * a.hd + part * 8) = v;
+    }
+  }
+}
+void launch_compact(const CommitArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(compact_kernel, dim3(a.rows.n_seq, 2 * a.n_layers), dim3(256), 0, st, a);
+}
+
+__global__ void commit_kernel(CommitArgs a) {
+  const int i = threadIdx.x;
+  if (i >= a.rows.n_seq) return;
+  const int* res = a.result + i * VS_RESULT_INTS;
+  const int sq = a.rows.seq[i];
+  a.P[sq] += res[0] + 1;
+  a.pending[sq] = res[1];
+  a.committed[sq] += res[0] + 1;
+}
+void launch_commit(const CommitArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, a);
+}
+
+__global__ void advance_kernel(int* P, int* committed, int seq, int dP, int dC) {
+  if (threadIdx.x == 0) {
+    P[seq] += dP;
+    committed[seq] += dC;
+  }
+}
+void launch_advance(int* P, int* committed, int seq, int dP, int dC, hipStream_t st) {
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, st, P, committed, seq, dP, dC);
+}
+
+}  // namespace vs

@@ -1,0 +1,115 @@
+// Argument structs and launchers of the round's small kernels (internal).
+#pragma once
+#include "common.h"
+
+namespace vs {
+
+enum PackMap { PACK_IDENTITY = 0, PACK_HEADS = 1, PACK_EVEN = 2, PACK_ODD = 3 };
+
+struct PackArgs {
+  const uint16_t* src;  // canonical [rows][K]
+  uint16_t* dst;        // packed matrix
+  int rows, K, k_steps, row_off, map, hd;
+};
+
+struct BlockSetArgs {
+  int* bt;
+  int bps, seq, first, n, reset_state;
+  int* P;
+  int* pending;
+  int* committed;
+  int ids[256];
+};
+
+struct LoadArgs {
+  int M, d, V;
+  const int* tokens;      // token ids (embedding) or null
+  const uint16_t* embed;  // [V][d] bf16
+  const float* hidden;    // hidden rows when tokens == null
+  int src_identity;
+  int src_row[kMaxRows];
+  float* h;
+  uint16_t* xa;
+  const float* g;
+  float* ss;              // [ceil(d/256)][M]
+};
+
+struct StatsArgs {
+  const float* logits;
+  int V;
+  float temp;
+  float* mx;
+  int* amax;
+  float* second;
+  double* sumexp;         // null: skip
+};
+
+// Draft-token selection for one draft step: sequence i writes
+// tokens[dst[i]] = pending (src == -1), the argmax of row src[i] of the head
+// partials (greedy) or a draw from softmax(logits row / T) with
+// u[i * 48 + slot] (sample).
+struct PickArgs {
+  int n;
+  int mode;
+  float temp;
+  int slot;
+  const int* pending;
+  const float* amax_val;
+  const int* amax_idx;
+  int groups, Mprev;
+  const float* logits;    // sample: rows of the previous head pass
+  int V;
+  const double* u;
+  int* tokens;
+  int seq[kMaxSeq];
+  int src[kMaxSeq];       // previous-pass row, or -1 for the pending token
+  int lrow[kMaxSeq];      // logits row (sample)
+  int uidx[kMaxSeq];      // index of the sequence in the uniforms array
+  int dst[kMaxSeq];
+};
+
+struct AcceptArgs {
+  RowMap rows;            // rows of the verify pass (masks define parents)
+  int mode;
+  float temp;
+  const int* tokens;
+  const float* logits;    // target logits [M][V]
+  const float* dlogits;   // draft logits [M][V] (sample)
+  const float* mx;        // target row stats
+  const int* amax;
+  const float* second;
+  const double* sumexp;
+  const float* dmx;       // draft row stats
+  const double* dsumexp;
+  int V;
+  const double* u;        // [n_seq][48]
+  int* result;            // [n_seq][24]
+};
+
+struct CommitArgs {
+  RowMap rows;
+  const int* result;
+  int* P;
+  int* pending;
+  int* committed;
+  const int* bt;
+  int bps;
+  uint16_t** kpool;       // [n_layers] device array of layer K pools
+  uint16_t** vpool;
+  int n_layers, Hkv, hd;
+};
+
+void launch_pack(const PackArgs& a, hipStream_t st);
+void launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t st);
+void launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
+void launch_set_blocks(const BlockSetArgs& a, hipStream_t st);
+void launch_load_rows(const LoadArgs& a, hipStream_t st);
+void launch_copy_rows(const float* src, float* dst, int M, int d, hipStream_t st);
+void launch_row_stats(const StatsArgs& a, int M, hipStream_t st);
+void launch_pick(const PickArgs& a, hipStream_t st);
+void launch_accept(const AcceptArgs& a, hipStream_t st);
+void launch_compact(const CommitArgs& a, hipStream_t st);
+void launch_commit(const CommitArgs& a, hipStream_t st);
+void launch_advance(int* P, int* committed, int seq, int dP, int dC, hipStream_t st);
+
+}  // namespace vs
