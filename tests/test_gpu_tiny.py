@@ -20,7 +20,7 @@ CFG = TINY
 
 @pytest.fixture(scope="module")
 def eng():
-    return G.engine(CFG, force_host=True, max_rows=64, max_seqs=8, max_ctx=512)
+    return G.engine(CFG, force_host=True, max_rows=64, max_seqs=16, max_ctx=512)
 
 
 @pytest.fixture(scope="module")
@@ -65,6 +65,7 @@ def test_prefill_logits_and_kv(eng, dec):
         assert np.abs(v - Vo[:, :64]).max() <= 0.05 * max(1.0, np.abs(Vo[:, :64]).max())
         # stored values are bf16 and mostly identical to the oracle's bf16 rounding
         assert np.mean(k == Ko[:, :64]) > 0.9
+    B.vs_seq_close(eng.kv, seq)
 
 
 @pytest.mark.parametrize("eps", [None, 0.0, 0.5])

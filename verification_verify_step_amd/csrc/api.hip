@@ -526,7 +526,12 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->dst_sum = reinterpret_cast<double*>(w + m->wsl.dst_sum);
   m->result = reinterpret_cast<int*>(w + m->wsl.result);
   // attention workgroups may use up to the full LDS of a CU
-  attn_init();
+  hipError_t ae = attn_init();
+  if (ae != hipSuccess) {
+    delete m;
+    (void)hipGetLastError();
+    return fail(VS_E_DEVICE, "vs_model_create: attention LDS limit: %s", hipGetErrorString(ae));
+  }
   launch_fill_i32(m->cnt, 0, kCounters, S(stream));
   vs_status rc = check_launch("vs_model_create");
   if (rc != VS_OK) {

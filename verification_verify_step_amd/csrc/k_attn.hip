@@ -209,9 +209,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   if (tid == 0) a.counters[unit] = 0;
 }
 
-void attn_init() {
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                      160 * 1024);
+hipError_t attn_init() {
+  // largest launch: 64 query vectors of 128 dims, ~81 KB
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             96 * 1024);
 }
 
 void launch_attention(const AttnArgs& a, hipStream_t st) {

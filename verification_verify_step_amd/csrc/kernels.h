@@ -63,6 +63,6 @@ struct AttnArgs {
   int M;
 };
 void launch_attention(const AttnArgs& a, hipStream_t st);
-void attn_init();  // lets the attention kernel use the whole LDS of a CU
+hipError_t attn_init();  // lets the attention kernel use more than 64 KB of LDS
 
 }  // namespace vs
