@@ -1,0 +1,300 @@
+"""Benchmark of the speculative-decoding round on one MI355X.
+
+Workload (default): the 7B Llama-shape chain round: 32 layers, d 4096, 32x128
+MHA, FFN 11008, V 32000, bf16 weights N(0, 0.02) from seed, prompt of 1024
+uniform-random ids, draft = first 12 layers + head with KV reuse, chain k = 5,
+greedy, batch 1.  One step = one round: draft (5 steps + finishing pass),
+verify (layers 12..31 + head over 6 rows), accept, commit.
+
+Printed JSON line:
+  value          verified tokens/s (committed tokens of the timed rounds / time)
+  roofline       the dominant kernel family (by time) against HBM peak, from
+                 HIP events around every launch on the library's stream
+  verify_step_*  verify + accept + commit per round: ms, algorithmic GB/s,
+                 fraction of the 8 TB/s peak
+  cpu_baseline   the CPU oracle on a bounded sample of the same round
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_chain_k5")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the AR and calibrated-acceptance runs")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers timed per kind in the CPU sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (to scale the HBM byte counters)")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 512 MiB, three times: what FETCH_SIZE
+    and WRITE_SIZE read for it (per dispatch) against 512 MiB gives the scale
+    of those counters."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n}))
+
+
+def layer_bytes(c):
+    d, hd, H, Hkv, F = c.d_model, c.head_dim, c.n_heads, c.n_kv_heads, c.d_ffn
+    return 2 * (d * (H + 2 * Hkv) * hd + H * hd * d + 3 * d * F)
+
+
+def verify_step_bytes(c, P, M):
+    """Algorithmic HBM bytes of one verify step: weights of layers L..N-1 and
+    the head read once, the committed KV of those layers read once, the
+    in-round KV written, hidden rows and logits."""
+    nl = c.n_layers - c.exit_layer
+    kv_row = c.n_kv_heads * c.head_dim * 2 * 2  # K and V, bf16
+    return (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * (P + M) * kv_row + nl * M * kv_row
+            + M * c.d_model * 4 * 2 + M * c.vocab * 4)
+
+
+def cpu_baseline(w, P, n_layers_sample):
+    """The oracle as it stands on a bounded sample of one round: n verify
+    layers (k+1 rows at context P), n draft layers (1 row), the head on k+1
+    rows and on 1 row; the round time is extrapolated by layer count."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.decoder import Decoder, KVCache, Row
+    from synth.model_weights import SynthWeights
+
+    c = w.model
+    k = w.k
+    weights = SynthWeights(c, precision="bf16", cache=True)
+    dec = Decoder(c, weights)
+    rng = np.random.default_rng(0)
+    cache = KVCache(c, P + k + 2, kv_round="bf16")
+    draft_layers = list(range(n_layers_sample))
+    verify_layers = list(range(c.exit_layer, c.exit_layer + n_layers_sample))
+    for l in draft_layers + verify_layers:  # stand-in committed context
+        K, V = cache.get(0, l)
+        K[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+        V[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+    for l in draft_layers + verify_layers:  # generate weights before timing
+        for t in range(1, 10):
+            weights.get(t, l)
+    weights.get(10), weights.get(11)
+    rows6 = [Row(0, P + i, P + i, np.arange(P + i + 1)) for i in range(k + 1)]
+    rows1 = [Row(0, P, P, np.arange(P + 1))]
+    h6 = rng.standard_normal((k + 1, c.d_model))
+    h1 = h6[:1].copy()
+    t0 = time.perf_counter()
+    for l in verify_layers:
+        dec.layer(l, cache, rows6, h6)
+    t_v = (time.perf_counter() - t0) / len(verify_layers)
+    t0 = time.perf_counter()
+    for l in draft_layers:
+        dec.layer(l, cache, rows1, h1)
+    t_d = (time.perf_counter() - t0) / len(draft_layers)
+    t0 = time.perf_counter()
+    dec.head(h6)
+    t_h6 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    dec.head(h1)
+    t_h1 = time.perf_counter() - t0
+    nv = c.n_layers - c.exit_layer
+    round_s = (k + 1) * c.exit_layer * t_d + k * t_h1 + nv * t_v + t_h6
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 1.0 / round_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 numpy oracle: {len(verify_layers)} verify layers ({k + 1} rows, context {P}, "
+                       f"random committed KV), {len(draft_layers)} draft layers (1 row), head on {k + 1} and 1 rows; "
+                       f"round = {k + 1}x{c.exit_layer} draft layers + {k} draft heads + {nv} verify layers + "
+                       f"1 verify head, one committed token per round as on the GPU (acceptance ~0)"),
+            "round_s": round_s, "verify_step_s": nv * t_v + t_h6}
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1 (multi-GPU sharding is "
+                                   "described in DESIGN.md and not built)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from synth import gpu_weights
+    from synth.workloads import WORKLOADS
+    import synth
+    from verification_verify_step_amd import binding as B
+    from verification_verify_step_amd.runtime import Engine
+
+    w = WORKLOADS[args.workload]
+    c, k = w.model, w.k
+    P0 = w.prompt_len
+    rounds = args.warmup + 3 * args.steps
+    cap = P0 + 2 + (rounds + args.steps + 8) * (k + 1) + 128
+    e = Engine(c, max_rows=64, max_seqs=4, max_ctx=cap, max_blocks_per_seq=(cap + 15) // 16 + 1)
+    t_load = time.time()
+    gpu_weights.load(e, c)
+    t_load = time.time() - t_load
+    prompt = synth.tokens(synth.SEED_PROMPTS, synth.stream_prompt(0), c.vocab, P0)
+    dprompt = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+    st = e.stream
+
+    def open_prefilled():
+        s = e.open(cap)
+        B.vs_prefill(e.model, e.kv, s, dprompt.data_ptr(), P0, B.VS_GREEDY, 1.0, None, None, st)
+        e.sync()
+        return s
+
+    seq = open_prefilled()
+    M = k + 1
+    toks = torch.empty(64, dtype=torch.int32, device="cuda")
+    hidden = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
+    logits = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+    res = torch.zeros((rounds, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    batch = B.make_batch([seq], [M])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+
+    def one_round(r, s=seq, b=batch):
+        B.vs_draft(e.model, e.kv, [s], [k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), hidden.data_ptr(), None, st)
+        ev[r][0].record()
+        B.vs_verify(e.model, e.kv, b, c.exit_layer, toks.data_ptr(), hidden.data_ptr(), logits.data_ptr(), st)
+        rp = res[r].data_ptr()
+        B.vs_accept(e.model, b, B.VS_GREEDY, 1.0, toks.data_ptr(), logits.data_ptr(), None, None, rp, st)
+        B.vs_commit(e.model, e.kv, b, rp, st)
+        ev[r][1].record()
+
+    for r in range(args.warmup):
+        one_round(r)
+    e.sync()
+    torch.cuda.synchronize()
+
+    def timed_region(first, mask):
+        """args.steps rounds; library event brackets on the families in mask."""
+        B.vs_stats_reset(e.model)
+        B.vs_stats_enable(e.model, mask)
+        p0 = e.state()[0][seq]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for r in range(first, first + args.steps):
+            one_round(r)
+        t1.record()
+        torch.cuda.synchronize()
+        B.vs_stats_enable(e.model, 0)
+        r_host = res.cpu().numpy()
+        committed = int(sum(r_host[r][0] + 1 for r in range(first, first + args.steps)))
+        accepted = int(sum(r_host[r][0] for r in range(first, first + args.steps)))
+        p1 = e.state()[0][seq]
+        assert p1 == p0 + committed, (p0, p1, committed)
+        v_ms = float(np.mean([ev[r][0].elapsed_time(ev[r][1]) for r in range(first, first + args.steps)]))
+        e.sync()
+        return t0.elapsed_time(t1), committed, accepted, v_ms, p0, B.vs_stats_read(e.model)
+
+    # A: clean (no per-launch events) -> headline numbers
+    total_ms, committed, accepted, v_ms, P_start, _ = timed_region(args.warmup, 0)
+    # B: every family bracketed -> per-family table, dominant family
+    _, _, _, _, _, stats = timed_region(args.warmup + args.steps, -1)
+    fam = {n: s for n, s in stats.items() if n != "small" and s[0] > 0}
+    dom = max(fam, key=lambda n: fam[n][1])
+    # C: only the dominant family bracketed -> its average launch duration
+    _, _, _, _, _, stats_c = timed_region(args.warmup + 2 * args.steps, 1 << B.STAT_FAMILIES.index(dom))
+    n_l, ms_l, by_l = stats_c[dom]
+    achieved = (by_l / n_l) / (ms_l / n_l * 1e-3) / 1e9
+    P_mid = P_start + committed // 2
+    v_bytes = verify_step_bytes(c, P_mid, M)
+    out = {
+        "metric": "verified tokens/s at 7B-shape batch 1; verify-step HBM GB/s vs peak",
+        "value": committed / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random-init N(0,0.02) bf16 weights, uniform-random prompt ids, seeded)",
+        "config": {"workload": w.name, "layers": c.n_layers, "d_model": c.d_model, "heads": c.n_heads,
+                   "head_dim": c.head_dim, "d_ffn": c.d_ffn, "vocab": c.vocab, "exit_layer": c.exit_layer,
+                   "k": k, "batch": w.batch, "prompt": P0, "mode": w.mode},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launches": n_l, "avg_launch_us": ms_l / n_l * 1e3, "bytes_per_launch": by_l / n_l},
+        "verify_step_ms": v_ms,
+        "verify_step_gbs": v_bytes / (v_ms * 1e-3) / 1e9,
+        "verify_step_frac_of_peak": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "verify_step_bytes": v_bytes,
+        "alpha": accepted / (args.steps * k),
+        "tokens_per_round": committed / args.steps,
+        "kernel_families_bracketed": {n: {"launches": s[0], "avg_us": s[1] / s[0] * 1e3 if s[0] else None,
+                                          "gbs": (s[2] / (s[1] * 1e-3) / 1e9) if s[1] else None}
+                                      for n, s in stats.items()},
+        "weights_load_s": t_load,
+    }
+    if not args.no_extras:
+        # plain greedy AR on the same kernels: the pending token through all layers
+        sB = open_prefilled()
+        bB = B.make_batch([sB], [1])
+        pend = B.vs_kv_state(e.kv)[1] + 4 * sB
+        zz = torch.empty((1, c.vocab), dtype=torch.float32, device="cuda")
+        rr = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+
+        def ar_step():
+            B.vs_verify(e.model, e.kv, bB, 0, pend, None, zz.data_ptr(), st)
+            B.vs_accept(e.model, bB, B.VS_GREEDY, 1.0, pend, zz.data_ptr(), None, None, rr.data_ptr(), st)
+            B.vs_commit(e.model, e.kv, bB, rr.data_ptr(), st)
+
+        for _ in range(args.warmup):
+            ar_step()
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        for _ in range(args.steps):
+            ar_step()
+        torch.cuda.synchronize()
+        out["ar_tokens_per_s"] = args.steps / (time.perf_counter() - a0)
+        B.vs_seq_close(e.kv, sB)
+        # acceptance-calibrated synthetic model: W_o, W_down of layers >= L
+        # scaled by 0 (same bytes, target == draft, every draft accepted)
+        for l in range(c.exit_layer, c.n_layers):
+            for t in (synth.T_WO, synth.T_W_DOWN):
+                src = gpu_weights.device_bits(c, t, l, e.device, st, eps=0.0)
+                e.set_tensor(t, l, src)
+        sC = open_prefilled()
+        bC = B.make_batch([sC], [M])
+        for r in range(min(args.warmup, rounds)):
+            one_round(r, sC, bC)
+        torch.cuda.synchronize()
+        Pc = e.state()[0][sC]
+        a0 = time.perf_counter()
+        n_cal = min(args.steps, rounds - args.warmup)
+        for r in range(args.warmup, args.warmup + n_cal):
+            one_round(r, sC, bC)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - a0
+        Pc2 = e.state()[0][sC]
+        out["calibrated_alpha1"] = {"tokens_per_s": (Pc2 - Pc) / dt, "tokens_per_round": (Pc2 - Pc) / n_cal,
+                                    "note": "synthetic model with upper-layer W_o and W_down zeroed (same bytes)"}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, P0, args.cpu_layers)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

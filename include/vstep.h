@@ -130,8 +130,9 @@ vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
 /* Device pointers of the per-sequence state arrays [max_seqs]:
  * P (KV length), pending token, committed count (read-only for callers). */
 vs_status vs_kv_state(vs_kv* kv, int32_t** d_P, int32_t** d_pending, int32_t** d_committed);
-/* Device pointers of layer `layer`'s K and V pools [n_blocks][Hkv][16][hd]
- * and the block table [max_seqs][max_blocks_per_seq] (int32). */
+/* Device pointers of layer `layer`'s K pool [n_blocks][Hkv][16 keys][hd],
+ * V pool [n_blocks][Hkv][hd][16 keys] (bf16) and the block table
+ * [max_seqs][max_blocks_per_seq] (int32). */
 vs_status vs_kv_layer(vs_kv* kv, int32_t layer, void** d_k, void** d_v, int32_t** d_block_table);
 /* Host-side upper bound of P for a sequence (exact after vs_kv_sync). */
 vs_status vs_kv_sync(vs_kv* kv, void* stream); /* blocks: reads P back */
@@ -191,16 +192,20 @@ vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_
 vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
                   float temp, const double* d_u, int32_t* d_tokens, int32_t* d_result, void* stream);
 
-/* Per-kernel-family timing, measured with HIP events around every launch on
- * the launching stream while enabled (adds event records between kernels).
- * vs_stats_read synchronises. */
+/* Per-kernel-family timing with HIP events on the launching stream, for the
+ * selected families only.  `mask` selects families by bit, in the order vs_stats_read
+ * reports them: gemm_qkv, gemm_o, gemm_gate_up, gemm_down, gemm_head,
+ * attention+combine, small; 0 disables, -1 selects all.  While a mask is
+ * set every launch gets an end event timestamped by the kernel itself, and a
+ * selected launch is charged from the previous launch's end to its own end:
+ * its run time plus the launch gap before it.  vs_stats_read synchronises. */
 typedef struct vs_kernel_stat {
   char name[32];
   int64_t launches;
   double total_ms;
   double bytes; /* algorithmic HBM bytes of all timed launches */
 } vs_kernel_stat;
-vs_status vs_stats_enable(vs_model* m, int32_t on);
+vs_status vs_stats_enable(vs_model* m, int32_t mask);
 vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* n_out);
 vs_status vs_stats_reset(vs_model* m);
 

@@ -1,0 +1,131 @@
+"""GPU parity at the full 7B shape (32 layers, d 4096, 32x128 heads, FFN
+11008, V 32000, bf16) with the benchmark's launch configuration: prompt 1024,
+chain k = 5, exit layer 12.  The oracle cannot run 1024-token prefills at
+this size, so it checks sampled outputs one layer at a time: given the GPU's
+layer input and committed KV, the oracle recomputes the layer (and the head)
+in float64.  Properties that hold at any size are checked end to end:
+speculative tokens == greedy AR tokens, first-L KV identity, accept
+decisions on identical logits."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spec
+from oracle.decoder import Decoder, KVCache
+from synth.model_weights import SynthWeights
+from synth.workloads import LLAMA7B
+from tests import gpu_common as G
+from verification_verify_step_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+CFG = LLAMA7B
+P0, K = 1024, 5
+M = K + 1
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    e = G.engine(CFG, max_rows=64, max_seqs=4, max_ctx=1600)
+    p = G.prompt(CFG, P0, req=0)
+    seq = e.open(1500)
+    B.vs_prefill(e.model, e.kv, seq, G.i32(p).data_ptr(), P0, B.VS_GREEDY, 1.0, None, None, e.stream)
+    toks = torch.empty(M, dtype=torch.int32, device="cuda")
+    hL = torch.empty((M, CFG.d_model), dtype=torch.float32, device="cuda")
+    B.vs_draft(e.model, e.kv, [seq], [K], B.VS_GREEDY, 1.0, None, toks.data_ptr(), hL.data_ptr(), None, e.stream)
+    torch.cuda.synchronize()
+    return {"e": e, "seq": seq, "prompt": p, "toks": toks, "hL": hL, "batch": B.make_batch([seq], [M])}
+
+
+def _forward(e, batch, start, end, toks, hin):
+    out = torch.empty((M, CFG.d_model), dtype=torch.float32, device="cuda")
+    B.vs_forward_layers(e.model, e.kv, batch, start, end, toks.data_ptr(), hin.data_ptr() if hin is not None else None,
+                        out.data_ptr(), e.stream)
+    return out
+
+
+def _oracle_layer(e, seq, l, X, P):
+    dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
+    cache = KVCache(CFG, P + M + 1)
+    k, v = G.kv_slots(e, seq, l, np.arange(P))
+    Kc, Vc = cache.get(0, l)
+    Kc[:, :P], Vc[:, :P] = k, v
+    rows = spec.chain_rows(0, P, M)
+    return dec.layer(l, cache, rows, X.astype(np.float64)), dec
+
+
+@pytest.mark.parametrize("layer", [12, 21, 31])
+def test_layer_parity(ctx, layer):
+    e, seq = ctx["e"], ctx["seq"]
+    P = e.state()[0][seq]
+    X = ctx["hL"] if layer == CFG.exit_layer else _forward(e, ctx["batch"], CFG.exit_layer, layer, ctx["toks"],
+                                                           ctx["hL"])
+    Y = _forward(e, ctx["batch"], layer, layer + 1, ctx["toks"], X)
+    torch.cuda.synchronize()
+    Yo, _ = _oracle_layer(e, seq, layer, X.cpu().numpy(), P)
+    Yg = Y.cpu().numpy().astype(np.float64)
+    scale = np.abs(Yo).max()
+    err = np.abs(Yg - Yo).max()
+    assert err <= 1e-3 * scale + 1e-4, (layer, err, scale)
+
+
+def test_head_parity_and_greedy_accept(ctx):
+    e, seq = ctx["e"], ctx["seq"]
+    Y = _forward(e, ctx["batch"], CFG.exit_layer, CFG.n_layers, ctx["toks"], ctx["hL"])
+    z = torch.empty((M, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_head(e.model, M, Y.data_ptr(), z.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
+    zo = dec.head(Y.cpu().numpy().astype(np.float64))
+    zg = z.cpu().numpy().astype(np.float64)
+    assert np.abs(zg - zo).max() <= G.LOGIT_TOL, np.abs(zg - zo).max()
+    # accept on identical logits: bit-exact with the oracle's greedy rule
+    res = torch.zeros((4, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    B.vs_accept(e.model, ctx["batch"], B.VS_GREEDY, 1.0, ctx["toks"].data_ptr(), z.data_ptr(), None, None,
+                res.data_ptr(), e.stream)
+    a, y, _, path = G.result_rows(res, 1)[0]
+    oa, oy = spec.accept_greedy_chain(ctx["toks"].cpu().tolist(), zg.astype(np.float32))
+    assert (a, y) == (oa, oy) and path == list(range(1, a + 1))
+
+
+def test_first_L_kv_identity(ctx):
+    """The draft's first-L KV (k+1 sequential one-row passes) equals one batched
+    pass over the same k+1 rows, bit for bit."""
+    e, seq = ctx["e"], ctx["seq"]
+    P = e.state()[0][seq]
+    before = [G.kv_slots(e, seq, l, np.arange(P, P + M)) for l in (0, 5, CFG.exit_layer - 1)]
+    _forward(e, ctx["batch"], 0, CFG.exit_layer, ctx["toks"], None)
+    torch.cuda.synchronize()
+    after = [G.kv_slots(e, seq, l, np.arange(P, P + M)) for l in (0, 5, CFG.exit_layer - 1)]
+    for (k1, v1), (k2, v2) in zip(before, after):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_spec_equals_ar(ctx):
+    e = ctx["e"]
+    p = ctx["prompt"]
+    n_new = 24
+    sA = e.open(1500)
+    B.vs_prefill(e.model, e.kv, sA, G.i32(p).data_ptr(), P0, B.VS_GREEDY, 1.0, None, None, e.stream)
+    toks = torch.empty(64, dtype=torch.int32, device="cuda")
+    res = torch.zeros((4, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    out_spec = [e.state()[1][sA]]
+    while len(out_spec) < n_new:
+        B.vs_step(e.model, e.kv, [sA], [K], B.VS_GREEDY, 1.0, None, toks.data_ptr(), res.data_ptr(), e.stream)
+        a, y, _, _ = G.result_rows(res, 1)[0]
+        out_spec += toks[:K + 1].cpu().tolist()[1:a + 1] + [y]
+        e.sync()
+    B.vs_seq_close(e.kv, sA)
+    sB = e.open(1500)
+    B.vs_prefill(e.model, e.kv, sB, G.i32(p).data_ptr(), P0, B.VS_GREEDY, 1.0, None, None, e.stream)
+    pend = B.vs_kv_state(e.kv)[1] + 4 * sB
+    batch = B.make_batch([sB], [1])
+    z = torch.empty((1, CFG.vocab), dtype=torch.float32, device="cuda")
+    out_ar = [e.state()[1][sB]]
+    while len(out_ar) < n_new:
+        B.vs_verify(e.model, e.kv, batch, 0, pend, None, z.data_ptr(), e.stream)
+        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, pend, z.data_ptr(), None, None, res.data_ptr(), e.stream)
+        B.vs_commit(e.model, e.kv, batch, res.data_ptr(), e.stream)
+        out_ar.append(G.result_rows(res, 1)[0][1])
+    B.vs_seq_close(e.kv, sB)
+    assert out_spec[:n_new] == out_ar[:n_new]

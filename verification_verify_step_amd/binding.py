@@ -224,8 +224,14 @@ def vs_step(model, kv, seqs, ks, mode, temp, d_u, d_tokens, d_result, stream):
                                     stream))
 
 
-def vs_stats_enable(model, on):
-    _check("vs_stats_enable", lib().vs_stats_enable(model, 1 if on else 0))
+STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention+combine", "small"]
+
+
+def vs_stats_enable(model, mask):
+    """mask: int bitmask over STAT_FAMILIES, True for all, False/0 for none."""
+    if mask is True:
+        mask = -1
+    _check("vs_stats_enable", lib().vs_stats_enable(model, int(mask)))
 
 
 def vs_stats_reset(model):

@@ -54,7 +54,7 @@ bool shape_ok(const vs_model_cfg* c, std::string* why) {
   if (c->head_dim % 16 != 0 || c->head_dim > 128) return bad("head_dim must be a multiple of 16, at most 128");
   if (c->n_heads % c->n_kv_heads != 0) return bad("n_heads must be a multiple of n_kv_heads");
   if ((c->n_heads * c->head_dim) % 32 != 0) return bad("n_heads*head_dim must be a multiple of 32");
-  if (c->vocab % 16 != 0) return bad("vocab must be a multiple of 16");
+  if (c->vocab % 16 != 0 || c->vocab > 32768) return bad("vocab must be a multiple of 16, at most 32768");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return bad("rms_eps > 0 and rope_theta > 1 required");
   return true;
 }
@@ -84,10 +84,9 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
 }
 
 constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
-constexpr int kCounters = 65536;
 
 struct WsLayout {
-  size_t h, xa_h, xa_o, xa_act, ss, q, part, cnt, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
+  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
       st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
 };
 
@@ -106,8 +105,8 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.xa_act = take(R * F * 4);
   w.ss = take(R * (d / 16) * 4);
   w.q = take(R * H * hd * 4);
+  w.rope = take(R * (hd / 2) * 8);
   w.part = take(kAttnPartFloats * 4);
-  w.cnt = take(kCounters * 4);
   w.amax_val = take(R * (V / 16) * 4);
   w.amax_idx = take(R * (V / 16) * 4);
   w.logits = take(R * V * 4);
@@ -127,8 +126,8 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
 }
 
 enum Family { F_QKV = 0, F_O, F_GU, F_DOWN, F_HEAD, F_ATTN, F_SMALL, F_COUNT };
-const char* kFamilyNames[F_COUNT] = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention",
-                                     "small"};
+const char* kFamilyNames[F_COUNT] = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head",
+                                     "attention+combine", "small"};
 
 struct Timed {
   int fam;
@@ -152,15 +151,17 @@ struct vs_model {
   char* ws = nullptr;
   float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   uint16_t *xa_h, *xa_o, *xa_act;
-  int *cnt, *amax_idx, *tokens, *st_amax, *dst_amax, *result;
+  float2* rope;
+  int *amax_idx, *tokens, *st_amax, *dst_amax, *result;
   double *st_sum, *dst_sum;
   int ss_groups = 0;       // groups of the last producer of ss
   int head_groups = 0;     // groups of the last head pass
   int head_rows = 0;
   // timing
-  bool stats_on = false;
+  int stats_mask = 0;  // families timed with events (bit f)
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
+  hipEvent_t prev_end = nullptr;  // end event of the last timed launch
   std::vector<Timed> timed;
   double acc_ms[F_COUNT] = {0};
   double acc_bytes[F_COUNT] = {0};
@@ -199,22 +200,30 @@ hipEvent_t next_event(vs_model* m) {
   return m->ev_pool[m->ev_used++];
 }
 
-// Brackets one launch with events when timing is enabled.
+// Launch timing while a stats mask is set: every launch gets an end event
+// timestamped by the kernel itself (GEMM and attention launches take it
+// through hipExtLaunchKernelGGL; other launches get a marker right after), and
+// a launch of a selected family is charged from the previous launch's end to
+// its own end: its run time plus the launch gap before it.
 template <typename F>
 void timed(vs_model* m, int fam, double bytes, hipStream_t st, F launch) {
-  if (!m->stats_on) {
-    launch();
+  if (m->stats_mask == 0) {
+    launch(nullptr, nullptr);
     return;
   }
-  hipEvent_t a = next_event(m), b = next_event(m);
-  if (!a || !b) {
-    launch();
+  hipEvent_t b = next_event(m);
+  if (!b) {
+    launch(nullptr, nullptr);
     return;
   }
-  hipEventRecord(a, st);
-  launch();
-  hipEventRecord(b, st);
-  m->timed.push_back(Timed{fam, a, b, bytes});
+  if (fam == F_SMALL) {
+    launch(nullptr, nullptr);
+    (void)hipEventRecord(b, st);
+  } else {
+    launch(nullptr, b);
+  }
+  if ((m->stats_mask >> fam & 1) && m->prev_end != nullptr) m->timed.push_back(Timed{fam, m->prev_end, b, bytes});
+  m->prev_end = b;
 }
 
 KvView kv_view(vs_kv* kv, int layer) {
@@ -249,7 +258,7 @@ double gemm_bytes(const Mat& W, int M) {
 // Loads rows (embedding of token ids, or hidden rows) into the residual
 // stream with the next consumer's gain g.
 void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const int* src_rows, const float* g,
-               hipStream_t st) {
+               hipStream_t st, const RowMap* rows = nullptr, const int* P = nullptr) {
   LoadArgs a;
   memset(&a, 0, sizeof(a));
   a.M = M;
@@ -265,7 +274,14 @@ void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const
   a.xa = m->xa_h;
   a.g = g;
   a.ss = m->ss;
-  timed(m, F_SMALL, (double)M * m->c.d_model * 10, st, [&] { launch_load_rows(a, st); });
+  if (rows != nullptr) {  // the pass runs layers: build its RoPE table
+    a.rope = m->rope;
+    a.P = P;
+    a.rows = *rows;
+    a.half = m->c.head_dim / 2;
+    a.theta = m->c.rope_theta;
+  }
+  timed(m, F_SMALL, (double)M * m->c.d_model * 10, st, [&](hipEvent_t, hipEvent_t) { launch_load_rows(a, st); });
   m->ss_groups = (m->c.d_model + 255) / 256;
 }
 
@@ -290,33 +306,36 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
   const int G = c.n_heads / c.n_kv_heads;
   const int nq = max_nr * G;
-  a.n_qg = (nq + 63) / 64;
+  a.n_qg = (nq + kAttnQG - 1) / kAttnQG;
   a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
   const int P = ctx_bound(kv, rm);
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
+  // One 32-key step per wave while that stays under ~2048 waves (all KV loads
+  // in flight at once), else longer splits; bounded by the partials buffer and
+  // the combine's split capacity.
   int n_split = 0;
-  a.kps = kChunk;
+  a.kps = 32;
   if (P > 0) {
-    const int max_split = (P + kChunk - 1) / kChunk;
-    int want = std::max(1, 1024 / std::max(1, units) - 1);
-    // partial-buffer budget
+    const int max_split = (P + 31) / 32;
+    int want = std::max(1, 2048 / std::max(1, units));
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
     const int budget = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units) - 1);
     want = std::min(want, budget);
+    want = std::min(want, kAttnCombineMax - 1);
     n_split = std::min(max_split, want);
-    a.kps = ((P + n_split - 1) / n_split + kChunk - 1) / kChunk * kChunk;
+    a.kps = ((P + n_split - 1) / n_split + 31) / 32 * 32;
     n_split = (P + a.kps - 1) / a.kps;
   }
   a.n_split = n_split;
   a.part = m->part;
-  a.counters = m->cnt;
   a.xa_o = m->xa_o;
   a.M = rm.M;
+  a.use_mfma = 1;
   double bytes = 0;
   for (int i = 0; i < rm.n_seq; ++i)
     bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
              c.head_dim * 4;
-  timed(m, F_ATTN, bytes, st, [&] { launch_attention(a, st); });
+  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention(a, st, e0, e1); });
 }
 
 // Layers [start, end) over rows already loaded into h / xa_h / ss.
@@ -335,8 +354,8 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.H = c.n_heads;
       g.Hkv = c.n_kv_heads;
       g.hd = c.head_dim;
-      g.theta = c.rope_theta;
-      timed(m, F_QKV, gemm_bytes(m->qkv[l], M), st, [&] { launch_gemm(g, EPI_QKV, st); });
+      g.rope = m->rope;
+      timed(m, F_QKV, gemm_bytes(m->qkv[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { launch_gemm(g, EPI_QKV, st, e0, e1); });
     }
     attention(m, kv, rm, l, st);
     {
@@ -346,7 +365,7 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.g_next = m->g_ffn[l];
       g.ss_out = m->ss;
       int groups = 0;
-      timed(m, F_O, gemm_bytes(m->o[l], M), st, [&] { groups = launch_gemm(g, EPI_RESID, st); });
+      timed(m, F_O, gemm_bytes(m->o[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_RESID, st, e0, e1); });
       m->ss_groups = groups;
     }
     {
@@ -354,7 +373,7 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.ss = m->ss;
       g.ss_groups = m->ss_groups;
       g.xa_act = m->xa_act;
-      timed(m, F_GU, gemm_bytes(m->gu[l], M), st, [&] { launch_gemm(g, EPI_SWIGLU, st); });
+      timed(m, F_GU, gemm_bytes(m->gu[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { launch_gemm(g, EPI_SWIGLU, st, e0, e1); });
     }
     {
       GemmArgs g = gemm_base(m, m->down[l], m->xa_act, M);
@@ -367,7 +386,7 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
         for (int i = 0; i < M; ++i) g.out_row[i] = copy_rows ? copy_rows[i] : i;
       }
       int groups = 0;
-      timed(m, F_DOWN, gemm_bytes(m->down[l], M), st, [&] { groups = launch_gemm(g, EPI_RESID, st); });
+      timed(m, F_DOWN, gemm_bytes(m->down[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_RESID, st, e0, e1); });
       m->ss_groups = groups;
     }
   }
@@ -387,7 +406,7 @@ void run_head(vs_model* m, int M, float* logits, const int* out_rows, hipStream_
     for (int i = 0; i < M; ++i) g.out_row[i] = out_rows[i];
   }
   int groups = 0;
-  timed(m, F_HEAD, gemm_bytes(m->head, M), st, [&] { groups = launch_gemm(g, EPI_LOGITS, st); });
+  timed(m, F_HEAD, gemm_bytes(m->head, M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_LOGITS, st, e0, e1); });
   m->head_groups = groups;
   m->head_rows = M;
 }
@@ -424,7 +443,7 @@ vs_status check_attn_budget(vs_model* m, const RowMap& rm) {
   int max_nr = 0;
   for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
   const int G = m->c.n_heads / m->c.n_kv_heads;
-  const int nq = max_nr * G, n_qg = (nq + 63) / 64, qg = (nq + n_qg - 1) / n_qg;
+  const int nq = max_nr * G, n_qg = (nq + kAttnQG - 1) / kAttnQG, qg = (nq + n_qg - 1) / n_qg;
   const size_t need = (size_t)rm.n_seq * m->c.n_kv_heads * n_qg * qg * (m->c.head_dim + 2) * 2;
   if (need > kAttnPartFloats) return fail(VS_E_SHAPE, "pass too wide for the attention workspace");
   return VS_OK;
@@ -509,8 +528,8 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->xa_act = reinterpret_cast<uint16_t*>(w + m->wsl.xa_act);
   m->ss = reinterpret_cast<float*>(w + m->wsl.ss);
   m->q = reinterpret_cast<float*>(w + m->wsl.q);
+  m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
   m->part = reinterpret_cast<float*>(w + m->wsl.part);
-  m->cnt = reinterpret_cast<int*>(w + m->wsl.cnt);
   m->amax_val = reinterpret_cast<float*>(w + m->wsl.amax_val);
   m->amax_idx = reinterpret_cast<int*>(w + m->wsl.amax_idx);
   m->logits = reinterpret_cast<float*>(w + m->wsl.logits);
@@ -532,7 +551,6 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
     (void)hipGetLastError();
     return fail(VS_E_DEVICE, "vs_model_create: attention LDS limit: %s", hipGetErrorString(ae));
   }
-  launch_fill_i32(m->cnt, 0, kCounters, S(stream));
   vs_status rc = check_launch("vs_model_create");
   if (rc != VS_OK) {
     delete m;
@@ -746,7 +764,7 @@ vs_status vs_forward_layers(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t s
   if ((rc = check_capacity(kv, rm)) != VS_OK) return rc;
   hipStream_t st = S(stream);
   const float* g0 = start < end ? m->g_attn[start] : m->g_final;
-  load_rows(m, rm.M, start == 0 ? d_tokens : nullptr, d_hidden_in, nullptr, g0, st);
+  load_rows(m, rm.M, start == 0 ? d_tokens : nullptr, d_hidden_in, nullptr, g0, st, &rm, kv->P);
   run_layers(m, kv, rm, start, end, st, nullptr, nullptr);
   if (d_hidden_out) launch_copy_rows(m->h, d_hidden_out, rm.M, m->c.d_model, st);
   return check_launch("vs_forward_layers");
@@ -780,7 +798,7 @@ vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_token
     rm.M = nc;
     rm.seq[0] = seq;
     rm.row_start[1] = nc;
-    load_rows(m, nc, d_tokens + c0, nullptr, nullptr, m->g_attn[0], st);
+    load_rows(m, nc, d_tokens + c0, nullptr, nullptr, m->g_attn[0], st, &rm, kv->P);
     run_layers(m, kv, rm, 0, m->c.n_layers, st, nullptr, nullptr);
     const bool last = c0 + nc == n;
     if (last) run_head(m, nc, m->logits, nullptr, st);
@@ -901,7 +919,7 @@ void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int
       rows_src[a] = vstart[i] + s;
       logit_rows[a] = k[i] > s ? vstart[i] + s : -1;
     }
-    timed(m, F_SMALL, 0, st, [&] { launch_pick(p, st); });
+    timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_pick(p, st); });
     RowMap rm;
     memset(&rm, 0, sizeof(rm));
     rm.n_seq = Ma;
@@ -912,7 +930,7 @@ void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int
       rm.row_start[a] = a;
     }
     rm.row_start[Ma] = Ma;
-    load_rows(m, Ma, d_tokens, nullptr, rows_src.data(), L > 0 ? m->g_attn[0] : m->g_final, st);
+    load_rows(m, Ma, d_tokens, nullptr, rows_src.data(), L > 0 ? m->g_attn[0] : m->g_final, st, &rm, kv->P);
     if (L > 0) {
       run_layers(m, kv, rm, 0, L, st, d_hidden_L, rows_src.data());
     } else {
@@ -957,7 +975,7 @@ vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_lay
   hipStream_t st = S(stream);
   const int N = m->c.n_layers;
   load_rows(m, rm.M, start_layer == 0 ? d_tokens : nullptr, d_hidden_in, nullptr,
-            start_layer < N ? m->g_attn[start_layer] : m->g_final, st);
+            start_layer < N ? m->g_attn[start_layer] : m->g_final, st, &rm, kv->P);
   run_layers(m, kv, rm, start_layer, N, st, nullptr, nullptr);
   run_head(m, rm.M, d_logits, nullptr, st);
   return check_launch("vs_verify");
@@ -1001,7 +1019,7 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
   sa.amax = m->st_amax;
   sa.second = m->st_second;
   sa.sumexp = mode == VS_SAMPLE ? m->st_sum : nullptr;
-  timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&] { launch_row_stats(sa, M, st); });
+  timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(sa, M, st); });
   if (mode == VS_SAMPLE) {
     StatsArgs da = sa;
     da.logits = d_draft_logits;
@@ -1009,7 +1027,7 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
     da.amax = m->dst_amax;
     da.second = nullptr;
     da.sumexp = m->dst_sum;
-    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&] { launch_row_stats(da, M, st); });
+    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(da, M, st); });
   }
   AcceptArgs a;
   memset(&a, 0, sizeof(a));
@@ -1028,7 +1046,7 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
   a.V = m->c.vocab;
   a.u = d_u;
   a.result = d_result;
-  timed(m, F_SMALL, 0, st, [&] { launch_accept(a, st); });
+  timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_accept(a, st); });
   return check_launch("vs_accept");
 }
 
@@ -1052,8 +1070,8 @@ vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_
   a.n_layers = m->c.n_layers;
   a.Hkv = m->c.n_kv_heads;
   a.hd = m->c.head_dim;
-  if (b->d_mask != nullptr) timed(m, F_SMALL, 0, st, [&] { launch_compact(a, st); });
-  timed(m, F_SMALL, 0, st, [&] { launch_commit(a, st); });
+  if (b->d_mask != nullptr) timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_compact(a, st); });
+  timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_commit(a, st); });
   for (int i = 0; i < rm.n_seq; ++i) kv->P_ub[rm.seq[i]] += rm.row_start[i + 1] - rm.row_start[i];
   return check_launch("vs_commit");
 }
@@ -1078,7 +1096,8 @@ vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, con
 
 vs_status vs_stats_enable(vs_model* m, int32_t on) {
   if (m == nullptr) return fail(VS_E_INVAL, "vs_stats_enable: null model");
-  m->stats_on = on != 0;
+  m->stats_mask = on;
+  m->prev_end = nullptr;
   return VS_OK;
 }
 
@@ -1087,6 +1106,7 @@ vs_status vs_stats_reset(vs_model* m) {
   for (const Timed& t : m->timed) hipEventSynchronize(t.b);
   m->timed.clear();
   m->ev_used = 0;
+  m->prev_end = nullptr;
   for (int f = 0; f < F_COUNT; ++f) m->acc_ms[f] = m->acc_bytes[f] = 0, m->acc_n[f] = 0;
   return VS_OK;
 }
@@ -1103,6 +1123,7 @@ vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* 
   }
   m->timed.clear();
   m->ev_used = 0;
+  m->prev_end = nullptr;
   int n = 0;
   for (int f = 0; f < F_COUNT && n < max; ++f) {
     memset(&out[n], 0, sizeof(out[n]));

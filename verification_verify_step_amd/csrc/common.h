@@ -7,6 +7,8 @@
 
 namespace vs {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kMaxSeq = VS_MAX_SEQS;
 constexpr int kMaxRows = VS_MAX_ROWS;
 constexpr int kBlock = 16;    // KV tokens per block

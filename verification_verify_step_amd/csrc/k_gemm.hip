@@ -22,7 +22,6 @@ namespace vs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -90,11 +89,64 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     }
   };
 
+  // RMSNorm scale of the input rows from the producer's per-group sums of
+  // squares: loaded before the weight prologue (so waiting for them leaves the
+  // weight loads in flight) and reduced in a fixed order through LDS.
+  constexpr int NT = NW * 64;
+  constexpr int kSS = 2048;             // sums held by the fast path
+  constexpr int RSS = kSS / NT;
+  __shared__ float rs[kMaxRows];
+  __shared__ float sstmp[kSS];
+  const int tid = threadIdx.x;
+  const int n_ss = a.ss != nullptr ? a.ss_groups * M : 0;
+  // Row m's sum is (S_0 + S_1) + (S_2 + S_3) with S_q = sum of groups g = q mod 4
+  // in increasing g: the order does not depend on M, so a row's scale (and
+  // everything after it) is the same whichever rows share the pass.
+  constexpr int kQ = 4;
+  auto first_level = [&](auto val) {
+    float s = 0.f;
+    if (tid < kQ * M) {
+      const int m = tid % M;
+      for (int g = tid / M; g < a.ss_groups; g += kQ) s += val(g * M + m);
+    }
+    return s;
+  };
+  auto finish_rs = [&]() {
+    __syncthreads();
+    if (tid < M) {
+      const float t = (sstmp[tid] + sstmp[M + tid]) + (sstmp[2 * M + tid] + sstmp[3 * M + tid]);
+      rs[tid] = 1.0f / sqrtf(t * a.inv_d + a.eps);
+    }
+  };
+  if (n_ss > kSS) {  // many sums (large M): reduce straight from memory, before the weight stream starts
+    const float s = first_level([&](int e) { return a.ss[e]; });
+    sstmp[tid] = s;
+    finish_rs();
+  } else if (n_ss == 0 && tid < M) {
+    rs[tid] = 1.0f;
+  }
+  float ssv[RSS];
+#pragma unroll
+  for (int j = 0; j < RSS; ++j) {
+    const int e = tid + j * NT;
+    ssv[j] = (n_ss <= kSS && e < n_ss) ? a.ss[e] : 0.f;
+  }
+
   // Software pipeline: PD k-steps of loads in flight ahead of the MFMAs.
   // (unconditional, clamped to a valid k-step: a branch here would make the
   // loop's wait counts conservative)
 #pragma unroll
   for (int p = 0; p < PD; ++p) load(p, max(0, min(s0 + p, a.k_steps - 1)));
+
+  if (n_ss > 0 && n_ss <= kSS) {
+#pragma unroll
+    for (int j = 0; j < RSS; ++j) sstmp[tid + j * NT] = ssv[j];
+    __syncthreads();
+    const float s = first_level([&](int e) { return sstmp[e]; });
+    __syncthreads();
+    sstmp[tid] = s;
+    finish_rs();
+  }
   int i = 0;
   for (; i + 2 * PD <= n; i += PD) {
 #pragma unroll
@@ -116,7 +168,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 
   // ---- cross-wave reduction through LDS (fixed order) ----
   __shared__ float red[NW * NTW * MT * 256];
-  __shared__ float rs[kMaxRows];
   __shared__ float rowtmp[kMaxRows * NTW * 16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -124,17 +175,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     for (int t = 0; t < NTW; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[(((wave * NTW + t) * MT + mt) * 64 + lane) * 4 + r] = acc[mt][t][r];
-
-  const int tid = threadIdx.x;
-  if (tid < M) {
-    float scale = 1.0f;
-    if (a.ss != nullptr) {
-      float s = 0.f;
-      for (int g = 0; g < a.ss_groups; ++g) s += a.ss[g * M + tid];
-      scale = 1.0f / sqrtf(s * a.inv_d + a.eps);
-    }
-    rs[tid] = scale;
-  }
   __syncthreads();
 
   auto result = [&](int m, int c) -> float {
@@ -164,16 +204,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       a.ss_out[blockIdx.x * M + tid] = s;
     }
   } else if constexpr (EPI == EPI_QKV) {
-    __shared__ int s_pos[kMaxRows], s_slot[kMaxRows], s_seq[kMaxRows];
+    __shared__ int s_slot[kMaxRows], s_seq[kMaxRows];
     if (tid < M) {
       const int i = row_seq_index(a.rows, tid);
       const int sq = a.rows.seq[i];
       const int idx = a.rows.idx_off + tid - a.rows.row_start[i];
-      const int depth = a.rows.depth ? a.rows.depth[tid] : idx;
-      const int P = a.kv.P[sq];
       s_seq[tid] = sq;
-      s_slot[tid] = P + a.rows.win + idx;
-      s_pos[tid] = P + depth;
+      s_slot[tid] = a.kv.P[sq] + a.rows.win + idx;
     }
     __syncthreads();
     const int hd = a.hd, half = hd >> 1;
@@ -187,12 +224,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const int ci = (nn % hd) >> 1;
       float o0 = y0, o1 = y1;
       if (hb < a.H + a.Hkv) {
-        const double inv_freq = pow((double)a.theta, -2.0 * (double)ci / (double)hd);
-        const double ang = (double)s_pos[m] * inv_freq;
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        o0 = (float)((double)y0 * cs - (double)y1 * sn);
-        o1 = (float)((double)y1 * cs + (double)y0 * sn);
+        const float2 r = a.rope[m * half + ci];
+        o0 = y0 * r.x - y1 * r.y;
+        o1 = y1 * r.x + y0 * r.y;
       }
       if (hb < a.H) {
         float* qo = a.q + ((size_t)m * a.H + hb) * hd;
@@ -203,9 +237,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
         const int slot = s_slot[m];
         const int blk = a.kv.bt[s_seq[m] * a.kv.bps + slot / kBlock];
-        uint16_t* dst = (is_k ? a.kv.k : a.kv.v) + (((size_t)blk * a.Hkv + kvh) * kBlock + (slot % kBlock)) * hd;
-        dst[ci] = f2bf(o0);
-        dst[ci + half] = f2bf(o1);
+        const size_t head = ((size_t)blk * a.Hkv + kvh) * kBlock * hd;
+        if (is_k) {  // K rows: [16 keys][hd]
+          uint16_t* dst = a.kv.k + head + (size_t)(slot % kBlock) * hd;
+          dst[ci] = f2bf(o0);
+          dst[ci + half] = f2bf(o1);
+        } else {     // V columns: [hd][16 keys]
+          uint16_t* dst = a.kv.v + head + (slot % kBlock);
+          dst[(size_t)ci * kBlock] = f2bf(o0);
+          dst[(size_t)(ci + half) * kBlock] = f2bf(o1);
+        }
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -243,37 +284,74 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
 }
 
-int gemm_groups(int n_tiles) {
-  return (n_tiles % 2 == 0 && n_tiles / 2 >= 384) ? n_tiles / 2 : n_tiles;
+GemmCfg gemm_cfg(int id) {
+  static const GemmCfg t[kGemmCfgs] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
+  return t[(id > 0 && id < kGemmCfgs) ? id : 0];
+}
+
+// Measured on MI355X at M <= 16 (7B shapes): one n-tile per workgroup is best;
+// 4 waves for the wide matrices (QKV, gate/up, head: >= 512 tiles), 8-16 waves
+// splitting K for the narrow ones (O, down: 256 tiles).  Larger M prefers two
+// n-tiles per workgroup (half the activation traffic per weight byte).
+int gemm_pick(int n_tiles, int k_steps, int M) {
+  if (M > 16) return n_tiles % 2 == 0 ? 4 : 1;  // (2,4) / (1,4)
+  if (n_tiles >= 512) return 1;                  // (1,4)
+  return k_steps >= 256 ? 3 : 2;                 // (1,16) / (1,8)
+}
+
+struct Ev {
+  hipEvent_t a, b;
+};
+
+template <int EPI, int MT, int NTW, int NW>
+static void go(const GemmArgs& a, hipStream_t st, Ev ev) {
+  constexpr int PD = MT >= 4 ? (NTW == 2 ? 2 : 4) : (NTW == 2 ? 4 : 8);
+  if (ev.a != nullptr || ev.b != nullptr)
+    hipExtLaunchKernelGGL((gemm_kernel<MT, NTW, NW, PD, EPI>), dim3(a.n_tiles / NTW), dim3(NW * 64), 0, st, ev.a,
+                          ev.b, 0, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MT, NTW, NW, PD, EPI>), dim3(a.n_tiles / NTW), dim3(NW * 64), 0, st, a);
+}
+
+template <int EPI, int MT>
+static void launch_mt(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
+  switch (cfg) {
+    case 1: go<EPI, MT, 1, 4>(a, st, ev); break;
+    case 2: go<EPI, MT, 1, 8>(a, st, ev); break;
+    case 3:
+      if constexpr (MT <= 2) go<EPI, MT, 1, 16>(a, st, ev);
+      else go<EPI, MT, 1, 8>(a, st, ev);
+      break;
+    case 4: go<EPI, MT, 2, 4>(a, st, ev); break;
+    case 5: go<EPI, MT, 2, 8>(a, st, ev); break;
+    default:
+      if constexpr (MT <= 1) go<EPI, MT, 2, 16>(a, st, ev);
+      else go<EPI, MT, 2, 8>(a, st, ev);
+      break;
+  }
 }
 
 template <int EPI>
-static void launch_epi(const GemmArgs& a, hipStream_t st, int groups) {
+static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
   const int mt = (a.M + 15) / 16;
-  const bool wide = groups * 2 == a.n_tiles;
-  dim3 grid(groups);
-#define VS_GEMM(MT, NTW, NW, PD) hipLaunchKernelGGL((gemm_kernel<MT, NTW, NW, PD, EPI>), grid, dim3(NW * 64), 0, st, a)
-  if (wide) {
-    if (mt == 1) VS_GEMM(1, 2, 4, 4);
-    else if (mt == 2) VS_GEMM(2, 2, 4, 4);
-    else VS_GEMM(4, 2, 4, 2);
-  } else {
-    if (mt == 1) VS_GEMM(1, 1, 8, 8);
-    else if (mt == 2) VS_GEMM(2, 1, 8, 4);
-    else VS_GEMM(4, 1, 8, 4);
-  }
-#undef VS_GEMM
+  if (mt == 1) launch_mt<EPI, 1>(a, cfg, st, ev);
+  else if (mt == 2) launch_mt<EPI, 2>(a, cfg, st, ev);
+  else launch_mt<EPI, 4>(a, cfg, st, ev);
 }
 
-int launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
-  const int groups = gemm_groups(a.n_tiles);
+int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const Ev ev{ev0, ev1};
+  int cfg = a.cfg > 0 ? a.cfg : gemm_pick(a.n_tiles, a.k_steps, a.M);
+  if (gemm_cfg(cfg).ntw == 2 && a.n_tiles % 2 != 0) cfg = 2;
+  // configurations whose reduction buffer would not fit fall back inside launch_mt
+  int ntw = gemm_cfg(cfg).ntw;
   switch (epi) {
-    case EPI_RESID: launch_epi<EPI_RESID>(a, st, groups); break;
-    case EPI_QKV: launch_epi<EPI_QKV>(a, st, groups); break;
-    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, st, groups); break;
-    default: launch_epi<EPI_LOGITS>(a, st, groups); break;
+    case EPI_RESID: launch_epi<EPI_RESID>(a, cfg, st, ev); break;
+    case EPI_QKV: launch_epi<EPI_QKV>(a, cfg, st, ev); break;
+    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, cfg, st, ev); break;
+    default: launch_epi<EPI_LOGITS>(a, cfg, st, ev); break;
   }
-  return groups;
+  return a.n_tiles / ntw;
 }
 
 }  // namespace vs

@@ -102,6 +102,19 @@ __global__ __launch_bounds__(256) void load_rows_kernel(LoadArgs a) {
     const int m = threadIdx.x;
     a.ss[blockIdx.x * a.M + m] = ((wsum[0][m] + wsum[1][m]) + wsum[2][m]) + wsum[3][m];
   }
+  if (a.rope != nullptr && blockIdx.x == 0) {
+    // angles in fp64: position up to ~1e4 times frequencies down to 1e-4
+    for (int e = threadIdx.x; e < a.M * a.half; e += 256) {
+      const int m = e / a.half, i = e % a.half;
+      const int si = row_seq_index(a.rows, m);
+      const int idx = a.rows.idx_off + m - a.rows.row_start[si];
+      const int pos = a.P[a.rows.seq[si]] + (a.rows.depth ? a.rows.depth[m] : idx);
+      const double ang = (double)pos * pow((double)a.theta, -(double)i / (double)a.half);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      a.rope[e] = make_float2((float)cs, (float)sn);
+    }
+  }
 }
 void launch_load_rows(const LoadArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(load_rows_kernel, dim3((a.d + 255) / 256), dim3(256), 0, st, a);
@@ -165,6 +178,33 @@ __device__ double block_sum_d(double v) {
 
 // Per-row statistics of logits: max, argmax (lowest id on ties), second
 // largest value, and S = sum exp((z - max)/T) in fp64 when requested.
+template <int NT>
+__device__ Top2 block_top2_n(Top2 t) {
+  __shared__ Top2 sh[NT];
+  sh[threadIdx.x] = t;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] = top2_merge(sh[threadIdx.x], sh[threadIdx.x + o]);
+    __syncthreads();
+  }
+  const Top2 r = sh[0];
+  __syncthreads();
+  return r;
+}
+template <int NT>
+__device__ double block_sum_n(double v) {
+  __shared__ double sh[NT];
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
 __device__ void row_stats(const float* z, int V, float temp, float* mx, int* amax, float* second, double* sumexp) {
   Top2 t{-INFINITY, INT_MAX, -INFINITY};
   for (int j = threadIdx.x; j < V; j += 256) t = top2_merge(t, Top2{z[j], j, -INFINITY});
@@ -185,13 +225,39 @@ __device__ void row_stats(const float* z, int V, float temp, float* mx, int* ama
   }
 }
 
-__global__ __launch_bounds__(256) void row_stats_kernel(StatsArgs a) {
+// One 1024-thread workgroup per row; each thread keeps its contiguous slice of
+// the row in registers (all loads in flight at once).
+constexpr int kStatsThreads = 1024;
+constexpr int kStatsPer = 32;  // rows up to 32768 logits
+__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a) {
   const int m = blockIdx.x;
-  row_stats(a.logits + (size_t)m * a.V, a.V, a.temp, a.mx + m, a.amax + m, a.second ? a.second + m : nullptr,
-            a.sumexp ? a.sumexp + m : nullptr);
+  const float* z = a.logits + (size_t)m * a.V;
+  const int j0 = threadIdx.x * kStatsPer;
+  float v[kStatsPer];
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) v[q] = j0 + q < a.V ? z[j0 + q] : -INFINITY;
+  Top2 t{-INFINITY, INT_MAX, -INFINITY};
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q)
+    if (j0 + q < a.V) t = top2_merge(t, Top2{v[q], j0 + q, -INFINITY});
+  t = block_top2_n<kStatsThreads>(t);
+  if (threadIdx.x == 0) {
+    a.mx[m] = t.v1;
+    a.amax[m] = t.i1;
+    if (a.second) a.second[m] = t.v2;
+  }
+  if (a.sumexp != nullptr) {
+    const double inv_t = 1.0 / (double)a.temp;
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q)
+      if (j0 + q < a.V) s += exp(((double)v[q] - (double)t.v1) * inv_t);
+    s = block_sum_n<kStatsThreads>(s);
+    if (threadIdx.x == 0) a.sumexp[m] = s;
+  }
 }
 void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
-  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(256), 0, st, a);
+  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
 }
 
 // Inverse-CDF draw from weights w_j = weight(j) >= 0 (fp64), ids ascending:
@@ -385,8 +451,9 @@ void launch_accept(const AcceptArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Tree compaction: K/V of accepted path rows P + path[j] -> P + 1 + j in
-// every layer.  Sources increase along the path and never lie below their
-// destination, so copying j in increasing order per element is safe.
+// every layer (K rows [16][hd] per block and head, V columns [hd][16]).
+// Sources increase along the path and never lie below their destination, so
+// copying j in increasing order per element is safe.
 __global__ void compact_kernel(CommitArgs a) {
   const int i = blockIdx.x;
   const int layer = blockIdx.y / 2, is_v = blockIdx.y % 2;
@@ -396,18 +463,20 @@ __global__ void compact_kernel(CommitArgs a) {
   const int sq = a.rows.seq[i];
   const int P = a.P[sq];
   uint16_t* pool = is_v ? a.vpool[layer] : a.kpool[layer];
-  const int per_slot = a.Hkv * a.hd / 8;  // 16-byte pieces of one slot
-  for (int e = threadIdx.x; e < per_slot; e += blockDim.x) {
-    const int kvh = e / (a.hd / 8), part = e % (a.hd / 8);
+  const size_t head = (size_t)kBlock * a.hd;  // elements per (block, kv head)
+  for (int e = threadIdx.x; e < a.Hkv * a.hd; e += blockDim.x) {  // one (kv head, dim) per thread
+    const int kvh = e / a.hd, d = e % a.hd;
     for (int j = 0; j < n_path; ++j) {
       const int r = res[4 + j];
       if (r < 1 || r >= nr) break;  // a path row outside this sequence's rows
       const int src = P + r, dst = P + 1 + j;
       if (src == dst) continue;
-      const int bs = a.bt[sq * a.bps + src / kBlock], bd = a.bt[sq * a.bps + dst / kBlock];
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          pool + (((size_t)bs * a.Hkv + kvh) * kBlock + src % kBlock) * a.hd + part * 8);
-      *reinterpret_cast<uint4*>(pool + (((size_t)bd * a.Hkv + kvh) * kBlock + dst % kBlock) * a.hd + part * 8) = v;
+      const size_t bs = ((size_t)a.bt[sq * a.bps + src / kBlock] * a.Hkv + kvh) * head;
+      const size_t bd = ((size_t)a.bt[sq * a.bps + dst / kBlock] * a.Hkv + kvh) * head;
+      if (is_v)
+        pool[bd + (size_t)d * kBlock + dst % kBlock] = pool[bs + (size_t)d * kBlock + src % kBlock];
+      else
+        pool[bd + (size_t)(dst % kBlock) * a.hd + d] = pool[bs + (size_t)(src % kBlock) * a.hd + d];
     }
   }
 }

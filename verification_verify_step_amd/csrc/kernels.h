@@ -1,5 +1,7 @@
 // Launch interfaces of the library's kernels (internal).
 #pragma once
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace vs {
@@ -31,7 +33,8 @@ struct GemmArgs {
   KvView kv;
   float* q;
   int H, Hkv, hd;
-  float theta;
+  const float2* rope;    // [M][hd/2] (cos, sin) of each row's position
+
   // EPI_SWIGLU
   uint16_t* xa_act;
   // EPI_LOGITS: logits[out_row[m]][V]; per-group argmax partials
@@ -41,11 +44,20 @@ struct GemmArgs {
   int* amax_idx;
   int out_row_identity;
   int out_row[kMaxRows];
+  int cfg;               // launch configuration (0: chosen from the shape), see gemm_cfg()
 };
 
-// Returns the number of workgroups launched (= ss groups for EPI_RESID).
-int launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
-int gemm_groups(int n_tiles);
+// Launch configurations: n-tiles per workgroup (NTW) x waves per workgroup
+// (NW, splitting K).  Returns the number of workgroups launched (= the ss
+// groups an EPI_RESID launch writes).
+struct GemmCfg {
+  int ntw, nw;
+};
+constexpr int kGemmCfgs = 7;
+GemmCfg gemm_cfg(int id);
+int gemm_pick(int n_tiles, int k_steps, int M);
+// ev0/ev1 (optional): events timestamped at the kernel's own start and end.
+int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 struct AttnArgs {
   RowMap rows;
@@ -54,15 +66,17 @@ struct AttnArgs {
   int H, Hkv, hd;
   float scale;
   int n_split;      // committed-key splits; split n_split is the in-round window
-  int kps;          // keys per committed split (multiple of kChunk)
+  int kps;          // keys per committed split (multiple of 32)
   int qg_size;      // query vectors per workgroup
   int n_qg;
   float* part;      // partials: per (i, kvh, qg, split): qg_size x (hd + 2) floats
-  int* counters;    // per (i, kvh, qg)
   uint16_t* xa_o;
   int M;
+  int use_mfma;     // MFMA score/PV path (head_dim 64 or 128)
 };
-void launch_attention(const AttnArgs& a, hipStream_t st);
+void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+constexpr int kAttnCombineMax = 1024;  // n_split + 1 must not exceed this
+constexpr int kAttnQG = 32;            // query vectors per query group
 hipError_t attn_init();  // lets the attention kernel use more than 64 KB of LDS
 
 }  // namespace vs

@@ -32,6 +32,12 @@ struct LoadArgs {
   uint16_t* xa;
   const float* g;
   float* ss;              // [ceil(d/256)][M]
+  // RoPE table of the pass rows: rope[m][i] = (cos, sin) of pos_m * theta^(-2i/hd)
+  float2* rope;           // null: not needed
+  const int* P;           // sequence KV lengths
+  RowMap rows;
+  int half;
+  float theta;
 };
 
 struct StatsArgs {
