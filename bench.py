@@ -54,6 +54,28 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n}))
 
 
+def pmc_traffic(workload, family):
+    """HBM bytes per launch of `family` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy's readings), or
+    None when there is none or the GEMM kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k, v = line.rsplit(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("k_gemm.hip", "kernels.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "verification_verify_step_amd", "csrc", f), "rb").read())
+    if kv.get("sources_sha256_16") != h.hexdigest()[:16]:
+        return None
+    v = kv.get(f"traffic_bytes_per_launch {family}")
+    return float(v) if v is not None else None
+
+
 def layer_bytes(c):
     d, hd, H, Hkv, F = c.d_model, c.head_dim, c.n_heads, c.n_kv_heads, c.d_ffn
     return 2 * (d * (H + 2 * Hkv) * hd + H * hd * d + 3 * d * F)
@@ -235,7 +257,7 @@ def main():
                    "head_dim": c.head_dim, "d_ffn": c.d_ffn, "vocab": c.vocab, "exit_layer": c.exit_layer,
                    "k": k, "batch": w.batch, "prompt": P0, "mode": w.mode},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic(w.name, dom),
                      "launches": n_l, "avg_launch_us": ms_l / n_l * 1e3, "bytes_per_launch": by_l / n_l},
         "verify_step_ms": v_ms,
         "verify_step_gbs": v_bytes / (v_ms * 1e-3) / 1e9,

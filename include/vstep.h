@@ -195,10 +195,10 @@ vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, con
 /* Per-kernel-family timing with HIP events on the launching stream, for the
  * selected families only.  `mask` selects families by bit, in the order vs_stats_read
  * reports them: gemm_qkv, gemm_o, gemm_gate_up, gemm_down, gemm_head,
- * attention+combine, small; 0 disables, -1 selects all.  While a mask is
+ * attention, small; 0 disables, -1 selects all.  While a mask is
  * set every launch gets an end event timestamped by the kernel itself, and a
- * selected launch is charged from the previous launch's end to its own end:
- * its run time plus the launch gap before it.  vs_stats_read synchronises. */
+ * selected launch is charged from the later of the previous launch's end and
+ * its own start event to its end.  vs_stats_read synchronises. */
 typedef struct vs_kernel_stat {
   char name[32];
   int64_t launches;

@@ -224,7 +224,7 @@ def vs_step(model, kv, seqs, ks, mode, temp, d_u, d_tokens, d_result, stream):
                                     stream))
 
 
-STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention+combine", "small"]
+STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention", "small"]
 
 
 def vs_stats_enable(model, mask):

@@ -86,7 +86,7 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
 constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
 
 struct WsLayout {
-  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
+  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, attn_cnt, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
       st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
 };
 
@@ -107,6 +107,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.q = take(R * H * hd * 4);
   w.rope = take(R * (hd / 2) * 8);
   w.part = take(kAttnPartFloats * 4);
+  w.attn_cnt = take(kAttnMaxUnits * 4);
   w.amax_val = take(R * (V / 16) * 4);
   w.amax_idx = take(R * (V / 16) * 4);
   w.logits = take(R * V * 4);
@@ -127,11 +128,11 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
 
 enum Family { F_QKV = 0, F_O, F_GU, F_DOWN, F_HEAD, F_ATTN, F_SMALL, F_COUNT };
 const char* kFamilyNames[F_COUNT] = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head",
-                                     "attention+combine", "small"};
+                                     "attention", "small"};
 
 struct Timed {
   int fam;
-  hipEvent_t a, b;
+  hipEvent_t prev, a, b;  // previous launch's end; this kernel's start and end (a may be null)
   double bytes;
 };
 
@@ -149,6 +150,7 @@ struct vs_model {
   int max_rows = 0, max_seqs = 0, max_ctx = 0;
   WsLayout wsl;
   char* ws = nullptr;
+  unsigned* attn_cnt;
   float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
@@ -201,18 +203,23 @@ hipEvent_t next_event(vs_model* m) {
 }
 
 // Launch timing while a stats mask is set: every launch gets an end event
-// timestamped by the kernel itself (GEMM and attention launches take it
-// through hipExtLaunchKernelGGL; other launches get a marker right after), and
-// a launch of a selected family is charged from the previous launch's end to
-// its own end: its run time plus the launch gap before it.
+// timestamped by the kernel itself (GEMM and attention launches take their
+// start and end events through hipExtLaunchKernelGGL; other launches get a
+// marker right after), and a launch of a selected family is charged from the
+// later of the previous launch's end and its own start event to its end.
+// Back to back, the start event can be stamped before the previous kernel
+// has drained, so the previous end bounds it; with idle time between
+// launches, the start event does.
 template <typename F>
 void timed(vs_model* m, int fam, double bytes, hipStream_t st, F launch) {
   if (m->stats_mask == 0) {
     launch(nullptr, nullptr);
     return;
   }
+  const bool sel = (m->stats_mask >> fam & 1) && fam != F_SMALL && m->prev_end != nullptr;
+  hipEvent_t a = sel ? next_event(m) : nullptr;
   hipEvent_t b = next_event(m);
-  if (!b) {
+  if (!b || (sel && !a)) {
     launch(nullptr, nullptr);
     return;
   }
@@ -220,9 +227,9 @@ void timed(vs_model* m, int fam, double bytes, hipStream_t st, F launch) {
     launch(nullptr, nullptr);
     (void)hipEventRecord(b, st);
   } else {
-    launch(nullptr, b);
+    launch(a, b);
   }
-  if ((m->stats_mask >> fam & 1) && m->prev_end != nullptr) m->timed.push_back(Timed{fam, m->prev_end, b, bytes});
+  if ((m->stats_mask >> fam & 1) && m->prev_end != nullptr) m->timed.push_back(Timed{fam, m->prev_end, a, b, bytes});
   m->prev_end = b;
 }
 
@@ -312,22 +319,26 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
   // One 32-key step per wave while that stays under ~2048 waves (all KV loads
   // in flight at once), else longer splits; bounded by the partials buffer and
-  // the combine's split capacity.
+  // by the combine's capacity (workgroups per unit x query vectors).
   int n_split = 0;
   a.kps = 32;
   if (P > 0) {
     const int max_split = (P + 31) / 32;
     int want = std::max(1, 2048 / std::max(1, units));
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
-    const int budget = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units) - 1);
-    want = std::min(want, budget);
-    want = std::min(want, kAttnCombineMax - 1);
-    n_split = std::min(max_split, want);
+    const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
+    const int max_wg = std::min(budget_wg, kAttnCombineSlots / a.qg_size);
+    want = std::min(want, max_wg * kAttnWaves - 1);
+    n_split = std::min(max_split, std::max(1, want));
     a.kps = ((P + n_split - 1) / n_split + 31) / 32 * 32;
     n_split = (P + a.kps - 1) / a.kps;
   }
   a.n_split = n_split;
+  const int wpb = (n_split + 1 + kAttnWaves - 1) / kAttnWaves;
   a.part = m->part;
+  a.ml_off = (size_t)units * wpb * a.qg_size * c.head_dim;
+  a.ml_off += a.ml_off & 1;
+  a.cnt = m->attn_cnt;
   a.xa_o = m->xa_o;
   a.M = rm.M;
   a.use_mfma = 1;
@@ -446,6 +457,8 @@ vs_status check_attn_budget(vs_model* m, const RowMap& rm) {
   const int nq = max_nr * G, n_qg = (nq + kAttnQG - 1) / kAttnQG, qg = (nq + n_qg - 1) / n_qg;
   const size_t need = (size_t)rm.n_seq * m->c.n_kv_heads * n_qg * qg * (m->c.head_dim + 2) * 2;
   if (need > kAttnPartFloats) return fail(VS_E_SHAPE, "pass too wide for the attention workspace");
+  if ((size_t)rm.n_seq * m->c.n_kv_heads * n_qg > (size_t)kAttnMaxUnits)
+    return fail(VS_E_SHAPE, "pass has more attention units than the %d counters", kAttnMaxUnits);
   return VS_OK;
 }
 
@@ -530,6 +543,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->q = reinterpret_cast<float*>(w + m->wsl.q);
   m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
   m->part = reinterpret_cast<float*>(w + m->wsl.part);
+  m->attn_cnt = reinterpret_cast<unsigned*>(w + m->wsl.attn_cnt);
   m->amax_val = reinterpret_cast<float*>(w + m->wsl.amax_val);
   m->amax_idx = reinterpret_cast<int*>(w + m->wsl.amax_idx);
   m->logits = reinterpret_cast<float*>(w + m->wsl.logits);
@@ -544,12 +558,14 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->dst_amax = reinterpret_cast<int*>(w + m->wsl.dst_amax);
   m->dst_sum = reinterpret_cast<double*>(w + m->wsl.dst_sum);
   m->result = reinterpret_cast<int*>(w + m->wsl.result);
-  // attention workgroups may use up to the full LDS of a CU
-  hipError_t ae = attn_init();
+  // the attention kernel's arrival counters start at zero and every launch
+  // leaves them at zero
+  hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
+  if (ae == hipSuccess) ae = attn_init();
   if (ae != hipSuccess) {
     delete m;
     (void)hipGetLastError();
-    return fail(VS_E_DEVICE, "vs_model_create: attention LDS limit: %s", hipGetErrorString(ae));
+    return fail(VS_E_DEVICE, "vs_model_create: attention set-up: %s", hipGetErrorString(ae));
   }
   vs_status rc = check_launch("vs_model_create");
   if (rc != VS_OK) {
@@ -1116,7 +1132,9 @@ vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* 
   for (const Timed& t : m->timed) {
     if (hipEventSynchronize(t.b) != hipSuccess) return fail(VS_E_DEVICE, "vs_stats_read: event sync failed");
     float ms = 0.f;
-    hipEventElapsedTime(&ms, t.a, t.b);
+    (void)hipEventElapsedTime(&ms, t.prev, t.b);
+    float own = 0.f;
+    if (t.a != nullptr && hipEventElapsedTime(&own, t.a, t.b) == hipSuccess) ms = std::min(ms, own);
     m->acc_ms[t.fam] += ms;
     m->acc_bytes[t.fam] += t.bytes;
     m->acc_n[t.fam] += 1;

@@ -14,14 +14,25 @@
 //
 // Work split: a wave owns one split of the keys (a range of committed keys,
 // or the in-round window) of one (sequence, KV head, query group) and keeps
-// its own online softmax: no block barriers, no K/V staging.  Per 32-key
-// step: S for two 16-key tiles (bf16 16x16x32 MFMA, the query split into bf16
-// hi + lo parts so scores keep fp32 precision), masking, softmax update in
-// fp32, P through a small per-wave LDS scratch into A-operand order (again
-// split hi/lo), then O += P.V.  The next step's K/V loads are in flight while
-// the current one computes.  Each split writes (max, sum, unnormalised o); a
-// second kernel combines the splits in a fixed order and writes the result
-// as split-bf16 activation fragments for the O projection.
+// its own online softmax, with no K/V staging.  Per 32-key step: S for two
+// 16-key tiles (bf16 16x16x32 MFMA, the query split into bf16 hi + lo parts so
+// scores keep fp32 precision), masking, softmax update in fp32, P through a
+// small per-wave LDS scratch into A-operand order (again split hi/lo), then
+// O += P.V.  The next step's K/V loads are in flight while the current one
+// computes.
+//
+// Combining the splits happens in the same launch.  The four waves of a
+// workgroup merge their (max, sum, o) in LDS in a fixed order, (0,2) and
+// (1,3) then the two results.  Wave 0 publishes the merged partial with
+// device-coherent stores (they write through this XCD's L2).  Thread 0 then
+// counts the workgroup in on a per-unit counter.  The last workgroup of a
+// unit to arrive reads every partial with device-coherent loads, sums them
+// in workgroup order, and writes the result as split-bf16 activation
+// fragments for the O projection; it also resets the counter to zero.  The
+// result does not depend on which workgroup arrives last.  No agent-scope
+// fence is used: a fence would write back or invalidate the whole L2.
+// Ordering comes from the workgroup fence before the count.  It waits until
+// the device-coherent stores have completed.
 #include "kernels.h"
 
 namespace vs {
@@ -32,7 +43,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStep = 32;           // keys per step
-constexpr int kCombineMax = 1024;   // splits combined by one workgroup
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -53,20 +63,27 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
+// Query vectors of a unit: vector gq of the query group maps to row
+// r0 + gq % nr and head kvh*G + gq / nr.
 template <int MTQ, int HD>
 __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   constexpr int KSQ = HD / 32;  // k-steps of S over head dims
   constexpr int NDT = HD / 16;  // 16-dim output tiles
   constexpr int QR = MTQ * 16;
   constexpr int PS = kStep + 4;  // P scratch row stride (floats)
-  __shared__ float Pl[kWaves][QR * PS];
+  constexpr int NO = MTQ * NDT * 4;  // o values per lane
+  constexpr int NML = MTQ * 4;       // (max, sum) pairs per lane
+  constexpr int PL_FLOATS = kWaves * QR * PS;
+  constexpr int XO_FLOATS = 2 * NO * 64, XML_FLOATS = 2 * NML * 64 * 2;
+  __shared__ float smem[PL_FLOATS + XO_FLOATS + XML_FLOATS];
+  __shared__ int last_wg;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_parts = a.n_split + 1;
-  const int wpb = (n_parts + kWaves - 1) / kWaves;  // workgroups per (sequence, kv head, query group)
+  const int wpb = (n_parts + kWaves - 1) / kWaves;  // workgroups per unit
   const int i = blockIdx.x / wpb;
-  const int split = (blockIdx.x % wpb) * kWaves + wave;
-  if (split >= n_parts) return;  // whole wave; no block-level barriers below
+  const int wgi = blockIdx.x % wpb;
+  const int split = wgi * kWaves + wave;
   const int kvh = blockIdx.y, qg = blockIdx.z;
   const int sq = a.rows.seq[i];
   const int r0 = a.rows.row_start[i];
@@ -74,6 +91,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   const int G = a.H / a.Hkv;
   const int q0 = qg * a.qg_size;
   const int nq = max(0, min(a.qg_size, nr * G - q0));
+  if (nq == 0) return;  // whole unit: nothing to attend for this query group
+  const int unit = (i * a.Hkv + kvh) * a.n_qg + qg;
+  const bool active = split < n_parts;
   const int P = a.kv.P[sq];
   const int W = a.rows.idx_off + nr;  // in-round keys present: window indices 0..W-1
   const bool window = split == a.n_split;
@@ -89,54 +109,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   const int mrow = lane & 15, kq = lane >> 4;
   const size_t head_stride = (size_t)kBlock * HD;  // elements per (block, kv head)
 
-  // query fragments (A operand of S), pre-scaled and split hi/lo
-  u32x4 qh[MTQ][KSQ], ql[MTQ][KSQ];
-  uint64_t qmask[MTQ][4];  // visibility masks of the 4 rows this lane holds in S
-#pragma unroll
-  for (int mt = 0; mt < MTQ; ++mt) {
-    const int qv = mt * 16 + mrow;
-    const int gq = q0 + min(qv, max(nq - 1, 0));
-    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
-#pragma unroll
-    for (int s = 0; s < KSQ; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = qv < nq ? src[32 * s + 8 * kq + e] * a.scale : 0.f;
-      split8(x, qh[mt][s], ql[mt][s]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = mt * 16 + 4 * kq + r;
-      uint64_t mk = 0;
-      if (row < nq) {
-        const int rl = (q0 + row) % nr;
-        const int idx = a.rows.idx_off + rl;
-        mk = a.rows.mask ? a.rows.mask[r0 + rl] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
-      }
-      qmask[mt][r] = mk;
-    }
-  }
-
-  float mrun[MTQ][4], lrun[MTQ][4];
-  f32x4 oacc[MTQ][NDT];
-#pragma unroll
-  for (int mt = 0; mt < MTQ; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mrun[mt][r] = -INFINITY;
-      lrun[mt][r] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) oacc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   // Steps of 32 keys aligned to blocks: [base, base+32) covers slots of two
   // blocks.  A committed split's steps and block-table entries follow from
   // the split index alone (P only masks), so its first K/V loads do not wait
   // for P.  K of the next step is requested right after this step's S, V of
   // the next step right after this step's P.V.
   const int first = window ? (key_lo / kStep) * kStep : split * a.kps;
-  const int last = window ? key_hi : split * a.kps + a.kps;  // exclusive
+  const int last = !active ? first : window ? key_hi : split * a.kps + a.kps;  // exclusive
   u32x4 kb[2][KSQ], vb[NDT];
   int nb0 = 0, nb1 = 0;  // blocks of the step being loaded
   auto blocks_of = [&](int base) {
@@ -157,10 +136,65 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     for (int t = 0; t < NDT; ++t)
       vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (size_t)(16 * t + mrow) * kBlock));
   };
-  float* pw = Pl[wave];
-  blocks_of(first);
-  load_k();
-  load_v();
+
+  // Request order: block-table entries of the first step, the query vectors
+  // and masks, then the first K/V step (which waits only for the table
+  // entries); the queries are split while K/V are in flight.
+  if (active) blocks_of(first);
+  float4 qraw[MTQ][KSQ][2];
+  uint64_t qmask[MTQ][4];  // visibility masks of the 4 rows this lane holds in S
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+    const int qv = mt * 16 + mrow;
+    const int gq = q0 + min(qv, nq - 1);
+    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
+#pragma unroll
+    for (int s = 0; s < KSQ; ++s) {
+      qraw[mt][s][0] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq);
+      qraw[mt][s][1] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mt * 16 + 4 * kq + r;
+      const int rl = (q0 + min(row, nq - 1)) % nr;
+      const int idx = a.rows.idx_off + rl;
+      const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + rl] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+      qmask[mt][r] = row < nq ? mk : 0ull;
+    }
+  }
+  if (active) {  // a wave past the last split only takes part in the merge
+    load_k();
+    load_v();
+  }
+  // query fragments (A operand of S), pre-scaled and split hi/lo
+  u32x4 qh[MTQ][KSQ], ql[MTQ][KSQ];
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+    const bool qok = mt * 16 + mrow < nq;
+#pragma unroll
+    for (int s = 0; s < KSQ; ++s) {
+      const float4 u = qraw[mt][s][0], v = qraw[mt][s][1];
+      const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = qok ? x[e] * a.scale : 0.f;
+      split8(y, qh[mt][s], ql[mt][s]);
+    }
+  }
+
+  float mrun[MTQ][4], lrun[MTQ][4];
+  f32x4 oacc[MTQ][NDT];
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mrun[mt][r] = -INFINITY;
+      lrun[mt][r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float* pw = smem + wave * QR * PS;
   for (int base = first; base < last; base += kStep) {
     const bool more = base + kStep < last;
     if (more) blocks_of(base + kStep);
@@ -226,81 +260,154 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     if (more) load_v();
   }
 
-  // partials: lane holds rows 16mt + 4(lane/16) + r, dims 16t + lane%16
-  const int unit = (i * a.Hkv + kvh) * a.n_qg + qg;
-  const size_t rec = (size_t)HD + 2;
-  float* part = a.part + ((size_t)unit * n_parts + split) * a.qg_size * rec;
-#pragma unroll
-  for (int mt = 0; mt < MTQ; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = mt * 16 + 4 * kq + r;
-      if (row < nq) {
-        float* pp = part + (size_t)row * rec;
-        if (mrow == 0) {
-          pp[0] = mrun[mt][r];
-          pp[1] = lrun[mt][r];
-        }
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) pp[2 + 16 * t + mrow] = oacc[mt][t][r];
-      }
-    }
-}
 
-// Combines the split partials of one query vector of one (sequence, KV head,
-// query group): workgroup = (unit, query vector), thread = head dim.  The
-// (max, sum) of every split go through LDS, then each thread sums its dim
-// over the splits in split order with all loads issued up front.
-constexpr int kCombineThreads = 128;
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const AttnArgs a) {
-  __shared__ float mls[kCombineMax], wts[kCombineMax];
-  const int unit = blockIdx.x, qv = blockIdx.y;
-  const int qg = unit % a.n_qg;
-  const int kvh = (unit / a.n_qg) % a.Hkv;
-  const int i = unit / (a.n_qg * a.Hkv);
-  const int hd = a.hd, QG = a.qg_size;
-  const int r0 = a.rows.row_start[i];
-  const int nr = a.rows.row_start[i + 1] - r0;
-  const int G = a.H / a.Hkv;
-  const int q0 = qg * QG;
-  const int nq = max(0, min(QG, nr * G - q0));
-  if (qv >= nq) return;  // whole workgroup
-  const int n_parts = a.n_split + 1;
-  const size_t rec = (size_t)hd + 2, stride = (size_t)QG * rec;
-  const float* base = a.part + (size_t)unit * n_parts * stride + (size_t)qv * rec;
-  // the (max, sum) of every split and this thread's first block of o values
-  // are requested in the same round
-  constexpr int kB = 32;
-  const int dd = threadIdx.x;
-  const float* pp = base + 2 + min(dd, hd - 1);
-  float x[kB];
+  // ---- merge the four waves' partials: (0 with 2, 1 with 3), then (0 with 1)
+  float* xo = smem + PL_FLOATS;            // [2][NO][64]
+  float2* xml = reinterpret_cast<float2*>(xo + XO_FLOATS);  // [2][NML][64]
+  auto put = [&](int slot) {
 #pragma unroll
-  for (int e = 0; e < kB; ++e) x[e] = e < n_parts ? pp[(size_t)e * stride] : 0.f;
-  for (int sp = threadIdx.x; sp < n_parts; sp += kCombineThreads) {
-    mls[sp] = base[sp * stride];
-    wts[sp] = base[sp * stride + 1];
+    for (int mt = 0; mt < MTQ; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xml[(slot * NML + mt * 4 + r) * 64 + lane] = make_float2(mrun[mt][r], lrun[mt][r]);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) xo[(slot * NO + (mt * NDT + t) * 4 + r) * 64 + lane] = oacc[mt][t][r];
+      }
+  };
+  auto merge = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 o2 = xml[(slot * NML + mt * 4 + r) * 64 + lane];
+        const float m1 = mrun[mt][r];
+        const float mn = fmaxf(m1, o2.x);
+        const float c1 = m1 == -INFINITY ? 0.f : expf(m1 - mn);
+        const float c2 = o2.x == -INFINITY ? 0.f : expf(o2.x - mn);
+        mrun[mt][r] = mn;
+        lrun[mt][r] = lrun[mt][r] * c1 + o2.y * c2;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+          oacc[mt][t][r] = oacc[mt][t][r] * c1 + xo[(slot * NO + (mt * NDT + t) * 4 + r) * 64 + lane] * c2;
+      }
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) merge(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+
+  const size_t QG = a.qg_size;
+  float* po = a.part;                                            // [units][wpb][QG][HD]
+  uint64_t* pml = reinterpret_cast<uint64_t*>(a.part + a.ml_off);  // [units][wpb][QG] (max, sum)
+  if (wave == 0) {
+    merge(0);
+    if (wpb == 1) {  // the only workgroup of its unit: write the result
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = mt * 16 + 4 * kq + r;
+          if (row < nq) {
+            const int gq = q0 + row;
+            const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) xa_store(a.xa_o, h * HD + 16 * t + mrow, m, a.M, oacc[mt][t][r] / lrun[mt][r]);
+          }
+        }
+    } else {
+      const size_t rec = (size_t)unit * wpb + wgi;
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = mt * 16 + 4 * kq + r;
+          if (row < nq) {
+            float* dst = po + (rec * QG + row) * HD + mrow;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t)
+              __hip_atomic_store(dst + 16 * t, oacc[mt][t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (mrow == 0) {
+              const uint64_t b = (uint64_t)__float_as_uint(mrun[mt][r]) |
+                                 ((uint64_t)__float_as_uint(lrun[mt][r]) << 32);
+              __hip_atomic_store(pml + rec * QG + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+    }
+  }
+  if (wpb == 1) return;
+  // the partial stores have completed before the workgroup is counted in
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(a.cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int is_last = old == (unsigned)(wpb - 1);
+    if (is_last) __hip_atomic_store(a.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_wg = is_last;
   }
   __syncthreads();
-  float mx = -INFINITY;
-  for (int sp = 0; sp < n_parts; ++sp)
-    if (wts[sp] > 0.f) mx = fmaxf(mx, mls[sp]);
-  float tot = 0.f;
-  for (int sp = 0; sp < n_parts; ++sp)
-    if (wts[sp] > 0.f) tot += wts[sp] * expf(mls[sp] - mx);
-  float o = 0.f;
-  for (int b = 0; b < n_parts; b += kB) {  // splits summed in order
-    if (b > 0) {
+  if (!last_wg) return;
+
+  // ---- last workgroup of the unit: combine the wpb partials in workgroup
+  // order.  Thread = one pair of dims of one query vector (two pairs when the
+  // unit has more than kThreads of them); its o pairs and (max, sum) values
+  // are requested together, then merged one partial after another.
+  constexpr int HP = HD / 2;  // dim pairs
+  constexpr int kCB = 12;     // partials requested per batch
+  const size_t rec0 = (size_t)unit * wpb;
+  const uint64_t* po2 = reinterpret_cast<const uint64_t*>(po);
+  const int npair = nq * HP;
+  for (int p = threadIdx.x; p < npair; p += 2 * kThreads) {
+    const bool two = p + kThreads < npair;
+    int r[2], c[2];
+    float mr[2], lr[2], o0[2], o1[2];
 #pragma unroll
-      for (int e = 0; e < kB; ++e) x[e] = b + e < n_parts ? pp[(size_t)(b + e) * stride] : 0.f;
+    for (int j = 0; j < 2; ++j) {
+      const int pj = min(p + j * kThreads, npair - 1);
+      r[j] = pj / HP;
+      c[j] = pj - r[j] * HP;
+      mr[j] = -INFINITY;
+      lr[j] = o0[j] = o1[j] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < wpb; sp0 += kCB) {
+      uint64_t xo[2][kCB], xm[2][kCB];
+#pragma unroll
+      for (int e = 0; e < kCB; ++e) {
+        const size_t sp = rec0 + min(sp0 + e, wpb - 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          xo[j][e] = __hip_atomic_load(po2 + (sp * QG + r[j]) * HP + c[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          xm[j][e] = __hip_atomic_load(pml + sp * QG + r[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kCB; ++e) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float m2 = __uint_as_float((uint32_t)xm[j][e]);
+          const float l2 = __uint_as_float((uint32_t)(xm[j][e] >> 32));
+          if (sp0 + e < wpb && l2 > 0.f) {  // a partial that saw no key has l = 0
+            const float mn = fmaxf(mr[j], m2);
+            const float c1 = mr[j] == -INFINITY ? 0.f : expf(mr[j] - mn);
+            const float c2 = expf(m2 - mn);
+            lr[j] = lr[j] * c1 + l2 * c2;
+            o0[j] = o0[j] * c1 + __uint_as_float((uint32_t)xo[j][e]) * c2;
+            o1[j] = o1[j] * c1 + __uint_as_float((uint32_t)(xo[j][e] >> 32)) * c2;
+            mr[j] = mn;
+          }
+        }
+      }
     }
 #pragma unroll
-    for (int e = 0; e < kB; ++e)
-      if (b + e < n_parts && wts[b + e] > 0.f) o += x[e] * expf(mls[b + e] - mx);
-  }
-  if (dd < hd) {
-    const int gq = q0 + qv;
-    const int m = r0 + gq % nr, h = kvh * G + gq / nr;
-    xa_store(a.xa_o, h * hd + dd, m, a.M, o / tot);
+    for (int j = 0; j < 2; ++j)
+      if (j == 0 || two) {
+        const int gq = q0 + r[j];
+        const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+        xa_store(a.xa_o, h * HD + 2 * c[j], m, a.M, o0[j] / lr[j]);
+        xa_store(a.xa_o, h * HD + 2 * c[j] + 1, m, a.M, o1[j] / lr[j]);
+      }
   }
 }
 
@@ -313,8 +420,8 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
   const int mtq = (a.qg_size + 15) / 16;  // at most 2 (query groups hold <= kAttnQG vectors)
 #define VS_ATT(MTQ, HD)                                                                                     \
   do {                                                                                                      \
-    if (ev0 != nullptr)                                                                                     \
-      hipExtLaunchKernelGGL((attn_kernel<MTQ, HD>), grid, dim3(kThreads), 0, st, ev0, nullptr, 0, a);       \
+    if (ev0 != nullptr || ev1 != nullptr)                                                                   \
+      hipExtLaunchKernelGGL((attn_kernel<MTQ, HD>), grid, dim3(kThreads), 0, st, ev0, ev1, 0, a);           \
     else                                                                                                    \
       hipLaunchKernelGGL((attn_kernel<MTQ, HD>), grid, dim3(kThreads), 0, st, a);                           \
   } while (0)
@@ -326,11 +433,6 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
     else VS_ATT(2, 64);
   }
 #undef VS_ATT
-  const dim3 cgrid(a.rows.n_seq * a.Hkv * a.n_qg, a.qg_size);
-  if (ev1 != nullptr)
-    hipExtLaunchKernelGGL(attn_combine_kernel, cgrid, dim3(kCombineThreads), 0, st, nullptr, ev1, 0, a);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel, cgrid, dim3(kCombineThreads), 0, st, a);
 }
 
 }  // namespace vs

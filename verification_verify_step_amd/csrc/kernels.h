@@ -69,14 +69,22 @@ struct AttnArgs {
   int kps;          // keys per committed split (multiple of 32)
   int qg_size;      // query vectors per workgroup
   int n_qg;
-  float* part;      // partials: per (i, kvh, qg, split): qg_size x (hd + 2) floats
+  // Partials of the workgroups of a unit (sequence, kv head, query group):
+  // o at part[((unit * wpb + wg) * qg_size + v) * hd + dim], (max, sum) as a
+  // float pair at part[ml_off + 2 * ((unit * wpb + wg) * qg_size + v)].
+  float* part;
+  size_t ml_off;    // floats; even
+  unsigned* cnt;    // per-unit arrival counters, zero between launches
   uint16_t* xa_o;
   int M;
   int use_mfma;     // MFMA score/PV path (head_dim 64 or 128)
 };
+// One launch: splits, in-workgroup merge, and the last workgroup's combine.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-constexpr int kAttnCombineMax = 1024;  // n_split + 1 must not exceed this
-constexpr int kAttnQG = 32;            // query vectors per query group
-hipError_t attn_init();  // lets the attention kernel use more than 64 KB of LDS
+constexpr int kAttnQG = 32;              // query vectors per query group
+constexpr int kAttnCombineSlots = 1024;  // workgroups per unit x query vectors per group, at most
+constexpr int kAttnWaves = 4;            // splits per workgroup
+constexpr int kAttnMaxUnits = 16384;     // arrival counters
+hipError_t attn_init();
 
 }  // namespace vs
