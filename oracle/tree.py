@@ -83,7 +83,12 @@ def build_tree(expand, root_token, topk=5, depth=4, keep=63):
         if not frontier:
             break
     kept = _top_keep(nodes, keep)
-    # level order: depth, then the parent's row, then child rank
+    return nodes, level_order(nodes, kept, depth)
+
+
+def level_order(nodes, kept, depth):
+    """The root, then the kept nodes in level order: depth, then the
+    parent's row, then child rank."""
     row_of = {0: 0}
     order = [0]
     for d in range(1, depth + 1):
@@ -92,7 +97,7 @@ def build_tree(expand, root_token, topk=5, depth=4, keep=63):
         for i in level:
             row_of[i] = len(order)
             order.append(i)
-    return nodes, order
+    return order
 
 
 def ancestors_or_self(nodes, i):
