@@ -164,6 +164,27 @@ vs_status vs_draft(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, co
                    float temp, const double* d_u, int32_t* d_tokens, float* d_hidden_L, float* d_draft_logits,
                    void* stream);
 
+/* Tree draft of one sequence ("FlashSpec" page, lnrk.cn/news/47842, §2.2,
+ * §3.2; the shape is this library's reading of its 63-node tree): the root
+ * is the pending token; every expanded node gets its `topk` most probable
+ * children under softmax(z/temp) of the draft (layers 0..L-1 + final norm +
+ * head, probabilities in fp64); a path's score is the product of the
+ * probabilities along it; the kept set is the top `keep` non-root nodes by
+ * (score desc, depth asc, creation order), grown level by level to `depth`
+ * levels, expanding at each level only the kept nodes of that depth.
+ * Outputs the verify rows (R = 1 + keep, root first, level order: depth,
+ * then the parent's row, then child rank; rows past the kept nodes, if any,
+ * are padding that sees only itself): d_tokens [R], d_depth [R],
+ * d_mask [R] (ancestor-or-self bits over rows), d_parent [R] (parent's row,
+ * -1 for the root and padding), d_hidden_L [R][d] (layer-L input of each
+ * row; the rows' first-L KV is written at slots P + row).  d_level_logits
+ * (optional) [depth][R][V] receives each level pass's head output.
+ * Limits: topk <= 8, depth <= 8, 1 + keep <= 64 and <= max_rows, at most
+ * 1024 nodes; the sequence needs capacity P + R. */
+vs_status vs_draft_tree(vs_model* m, vs_kv* kv, int32_t seq, int32_t topk, int32_t depth, int32_t keep, float temp,
+                        int32_t* d_tokens, int32_t* d_depth, uint64_t* d_mask, int32_t* d_parent, float* d_hidden_L,
+                        float* d_level_logits, void* stream);
+
 /* Verify: layers start_layer..N-1 over the batch rows (input hidden_L rows,
  * or token ids when start_layer == 0), then the head -> d_logits [M][V]. */
 vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_layer, const int32_t* d_tokens,

@@ -129,3 +129,23 @@ def test_spec_equals_ar(ctx):
         out_ar.append(G.result_rows(res, 1)[0][1])
     B.vs_seq_close(e.kv, sB)
     assert out_spec[:n_new] == out_ar[:n_new]
+
+
+def test_verify_pass_is_bit_reproducible(ctx):
+    """The same verify pass (layers L..N-1 + head, 6 rows, and the 1-row pass
+    of a draft step) repeated 25 times gives bit-identical logits: the
+    attention's split combine reads only partials completed in the same
+    launch, in a fixed order."""
+    e, seq = ctx["e"], ctx["seq"]
+    for rows in (M, 1):
+        batch = B.make_batch([seq], [rows])
+        ref = None
+        for _ in range(25):
+            y = torch.empty((rows, CFG.vocab), dtype=torch.float32, device="cuda")
+            B.vs_verify(e.model, e.kv, batch, CFG.exit_layer, ctx["toks"].data_ptr(), ctx["hL"].data_ptr(),
+                        y.data_ptr(), e.stream)
+            if ref is None:
+                ref = y
+            else:
+                assert torch.equal(y, ref)
+        torch.cuda.synchronize()

@@ -18,7 +18,7 @@ VS_MAX_ROWS, VS_MAX_SEQS, VS_MAX_K, VS_N_UNIFORMS, VS_RESULT_INTS = 64, 64, 16, 
 EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
     "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
-    "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_verify", "vs_accept", "vs_commit",
+    "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_commit",
     "vs_step", "vs_stats_enable", "vs_stats_read", "vs_stats_reset",
 ]
 
@@ -82,6 +82,7 @@ def lib():
             "vs_forward_layers": (I32, [VP, VP, P(vs_batch), I32, I32, VP, VP, VP, VP]),
             "vs_head": (I32, [VP, I32, VP, VP, VP]),
             "vs_draft": (I32, [VP, VP, I32, pI, pI, I32, F, VP, VP, VP, VP, VP]),
+            "vs_draft_tree": (I32, [VP, VP, I32, I32, I32, I32, F, VP, VP, VP, VP, VP, VP, VP]),
             "vs_verify": (I32, [VP, VP, P(vs_batch), I32, VP, VP, VP, VP]),
             "vs_accept": (I32, [VP, P(vs_batch), I32, F, VP, VP, VP, VP, VP, VP]),
             "vs_commit": (I32, [VP, VP, P(vs_batch), VP, VP]),
@@ -203,6 +204,12 @@ def vs_head(model, M, d_hidden, d_logits, stream):
 def vs_draft(model, kv, seqs, ks, mode, temp, d_u, d_tokens, d_hidden_L, d_draft_logits, stream):
     _check("vs_draft", lib().vs_draft(model, kv, len(seqs), _i32(seqs), _i32(ks), mode, temp, d_u, d_tokens,
                                       d_hidden_L, d_draft_logits, stream))
+
+
+def vs_draft_tree(model, kv, seq, topk, depth, keep, temp, d_tokens, d_depth, d_mask, d_parent, d_hidden_L,
+                  d_level_logits, stream):
+    _check("vs_draft_tree", lib().vs_draft_tree(model, kv, seq, topk, depth, keep, temp, d_tokens, d_depth, d_mask,
+                                                d_parent, d_hidden_L, d_level_logits, stream))
 
 
 def vs_verify(model, kv, batch, start_layer, d_tokens, d_hidden_in, d_logits, stream):

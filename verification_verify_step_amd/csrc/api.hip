@@ -84,9 +84,11 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
 }
 
 constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
+// tree drafting state: node arrays (4 int + 1 double per node), meta, row arrays
+constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows * 24;
 
 struct WsLayout {
-  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, attn_cnt, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
+  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
       st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
 };
 
@@ -108,6 +110,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.rope = take(R * (hd / 2) * 8);
   w.part = take(kAttnPartFloats * 4);
   w.attn_cnt = take(kAttnMaxUnits * 4);
+  w.tree = take(kTreeBytes);
   w.amax_val = take(R * (V / 16) * 4);
   w.amax_idx = take(R * (V / 16) * 4);
   w.logits = take(R * V * 4);
@@ -151,6 +154,7 @@ struct vs_model {
   WsLayout wsl;
   char* ws = nullptr;
   unsigned* attn_cnt;
+  TreeArgs tree;          // device pointers of the tree drafting state
   float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
@@ -544,6 +548,22 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
   m->part = reinterpret_cast<float*>(w + m->wsl.part);
   m->attn_cnt = reinterpret_cast<unsigned*>(w + m->wsl.attn_cnt);
+  {
+    char* t = w + m->wsl.tree;
+    memset(&m->tree, 0, sizeof(m->tree));
+    m->tree.score = reinterpret_cast<double*>(t);
+    t += (size_t)kTreeNodes * 8;
+    m->tree.tok = reinterpret_cast<int*>(t);
+    m->tree.parent = m->tree.tok + kTreeNodes;
+    m->tree.depth = m->tree.parent + kTreeNodes;
+    m->tree.rank = m->tree.depth + kTreeNodes;
+    m->tree.meta = m->tree.rank + kTreeNodes;
+    m->tree.row_mask = reinterpret_cast<uint64_t*>(m->tree.meta + 64);
+    m->tree.row_tok = reinterpret_cast<int*>(m->tree.row_mask + kMaxRows);
+    m->tree.row_depth = m->tree.row_tok + kMaxRows;
+    m->tree.row_node = m->tree.row_depth + kMaxRows;
+    m->tree.row_parent = m->tree.row_node + kMaxRows;
+  }
   m->amax_val = reinterpret_cast<float*>(w + m->wsl.amax_val);
   m->amax_idx = reinterpret_cast<int*>(w + m->wsl.amax_idx);
   m->logits = reinterpret_cast<float*>(w + m->wsl.logits);
@@ -961,9 +981,86 @@ void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int
   }
 }
 
+// Tree draft of one sequence: level passes (layers 0..L-1 + head over the
+// root and the kept nodes) grow the tree; a final first-L pass over the
+// final rows writes their KV at slots P + row and their layer-L inputs.
+void draft_tree_impl(vs_model* m, vs_kv* kv, int seq, int topk, int depth, int keep, float temp, int32_t* d_tokens,
+                     int32_t* d_depth, uint64_t* d_mask, int32_t* d_parent, float* d_hidden_L, float* d_level_logits,
+                     hipStream_t st) {
+  const int L = m->c.exit_layer, V = m->c.vocab, R = 1 + keep;
+  TreeArgs ta = m->tree;
+  ta.R = R;
+  ta.max_depth = depth;
+  ta.topk = topk;
+  ta.keep = keep;
+  ta.pending = kv->pending;
+  ta.seq = seq;
+  ta.V = V;
+  ta.temp = temp;
+  RowMap rm;
+  memset(&rm, 0, sizeof(rm));
+  rm.n_seq = 1;
+  rm.M = R;
+  rm.seq[0] = seq;
+  rm.row_start[1] = R;
+  rm.depth = ta.row_depth;
+  rm.mask = ta.row_mask;
+  const float* g0 = L > 0 ? m->g_attn[0] : m->g_final;
+  for (int lev = 0; lev <= depth; ++lev) {
+    ta.level = lev;
+    const bool last = lev == depth;
+    if (last) {
+      ta.out_tok = d_tokens;
+      ta.out_depth = d_depth;
+      ta.out_mask = d_mask;
+      ta.out_parent = d_parent;
+    }
+    timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_tree_select(ta, st); });
+    load_rows(m, R, ta.row_tok, nullptr, nullptr, g0, st, &rm, kv->P);
+    if (L > 0) run_layers(m, kv, rm, 0, L, st, last ? d_hidden_L : nullptr, nullptr);
+    if (last) {
+      if (L == 0) launch_copy_rows(m->h, d_hidden_L, R, m->c.d_model, st);
+      break;
+    }
+    float* z = d_level_logits != nullptr ? d_level_logits + (size_t)lev * R * V : m->dlogits;
+    run_head(m, R, z, nullptr, st);
+    ta.logits = z;
+    timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_tree_expand(ta, st); });
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+vs_status vs_draft_tree(vs_model* m, vs_kv* kv, int32_t seq, int32_t topk, int32_t depth, int32_t keep, float temp,
+                        int32_t* d_tokens, int32_t* d_depth, uint64_t* d_mask, int32_t* d_parent, float* d_hidden_L,
+                        float* d_level_logits, void* stream) {
+  if (m == nullptr || kv == nullptr || d_tokens == nullptr || d_depth == nullptr || d_mask == nullptr ||
+      d_parent == nullptr || d_hidden_L == nullptr)
+    return fail(VS_E_INVAL, "vs_draft_tree: null argument");
+  if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_draft_tree: sequence %d is not open", seq);
+  if (!kv->prefilled[seq]) return fail(VS_E_STATE, "vs_draft_tree: sequence %d has no prefill", seq);
+  if (topk < 1 || topk > kTreeMaxTopk) return fail(VS_E_INVAL, "vs_draft_tree: topk %d not in [1, %d]", topk, kTreeMaxTopk);
+  if (depth < 1 || depth > kTreeMaxDepth)
+    return fail(VS_E_INVAL, "vs_draft_tree: depth %d not in [1, %d]", depth, kTreeMaxDepth);
+  if (keep < 1 || 1 + keep > kMaxRows || 1 + keep > m->max_rows)
+    return fail(VS_E_SHAPE, "vs_draft_tree: %d kept nodes need %d rows (max_rows %d)", keep, 1 + keep, m->max_rows);
+  if (1 + (size_t)topk * (1 + (size_t)(depth - 1) * keep) > (size_t)kTreeNodes)
+    return fail(VS_E_SHAPE, "vs_draft_tree: expansion may exceed %d nodes", kTreeNodes);
+  if (!(temp > 0.f)) return fail(VS_E_INVAL, "vs_draft_tree: temperature must be positive");
+  RowMap rm;
+  memset(&rm, 0, sizeof(rm));
+  rm.n_seq = 1;
+  rm.M = 1 + keep;
+  rm.seq[0] = seq;
+  rm.row_start[1] = 1 + keep;
+  vs_status rc = check_capacity(kv, rm);
+  if (rc != VS_OK) return rc;
+  draft_tree_impl(m, kv, seq, topk, depth, keep, temp, d_tokens, d_depth, d_mask, d_parent, d_hidden_L, d_level_logits,
+                  S(stream));
+  return check_launch("vs_draft_tree");
+}
 
 vs_status vs_draft(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
                    float temp, const double* d_u, int32_t* d_tokens, float* d_hidden_L, float* d_draft_logits,

@@ -31,8 +31,8 @@
 // fragments for the O projection; it also resets the counter to zero.  The
 // result does not depend on which workgroup arrives last.  No agent-scope
 // fence is used: a fence would write back or invalidate the whole L2.
-// Ordering comes from the workgroup fence before the count.  It waits until
-// the device-coherent stores have completed.
+// Ordering comes from waiting on the vector memory counter before the count,
+// so the device-coherent stores have completed.
 #include "kernels.h"
 
 namespace vs {
@@ -338,8 +338,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     }
   }
   if (wpb == 1) return;
-  // the partial stores have completed before the workgroup is counted in
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // The partial stores must have completed (written through to device
+  // scope) before the workgroup is counted in.  A workgroup-scope fence does
+  // not wait for stores on this target, so wait on the vector memory counter
+  // itself (it counts stores too); the clobber keeps the compiler from
+  // moving memory operations across the wait.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old = __hip_atomic_fetch_add(a.cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -105,6 +105,42 @@ struct CommitArgs {
   int n_layers, Hkv, hd;
 };
 
+// Tree drafting state (one sequence).  Nodes are numbered in creation order
+// (root = 0); the verify rows are the root and the kept nodes in level order.
+constexpr int kTreeNodes = 1024;
+constexpr int kTreeMaxDepth = 8;
+constexpr int kTreeMaxTopk = 8;
+struct TreeArgs {
+  int* tok;               // node arrays [kTreeNodes]
+  int* parent;
+  int* depth;
+  int* rank;
+  double* score;          // product of the draft probabilities along the path
+  int* meta;              // [0] nodes, [1] frontier rows, [2] first frontier row, [3] real rows
+  int* row_tok;           // pass rows [R]
+  int* row_depth;
+  uint64_t* row_mask;
+  int* row_node;
+  int* row_parent;
+  int R;                  // rows of every pass (1 + keep)
+  int level;              // select: rows for expanding this depth (== max_depth: final layout)
+  int max_depth, topk, keep;
+  const int* pending;     // root token = pending[seq]
+  int seq;
+  // expand
+  const float* logits;    // head output of the pass [R][V]
+  int V;
+  float temp;
+  // final layout copies (optional)
+  int* out_tok;
+  int* out_depth;
+  uint64_t* out_mask;
+  int* out_parent;
+};
+
+void launch_tree_select(const TreeArgs& a, hipStream_t st);
+void launch_tree_expand(const TreeArgs& a, hipStream_t st);
+
 void launch_pack(const PackArgs& a, hipStream_t st);
 void launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t st);
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
