@@ -58,6 +58,7 @@ typedef int32_t vs_status;
 #define VS_SAMPLE 1
 
 #define VS_MAX_ROWS 64     /* rows per sequence per pass (uint64 masks) */
+#define VS_MAX_PASS_ROWS 1088  /* rows per pass over all sequences (64 sequences x 17) */
 #define VS_MAX_SEQS 64     /* sequences per pass */
 #define VS_MAX_K 16        /* chain draft length */
 #define VS_N_UNIFORMS 48   /* per sequence per round: 0..k-1 draft, 16.. accept, 32 residual/bonus */
@@ -126,6 +127,12 @@ void vs_kv_destroy(vs_kv* kv);
 /* Open a sequence able to hold max_len KV slots (prompt + generated tokens
  * + in-round scratch); reserves its blocks from the pool up front. */
 vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id);
+/* Declare a context the caller wrote itself: the K/V of slots 0..P-1 of
+ * every layer are already in the sequence's blocks (layout of vs_kv_layer),
+ * and the sequence continues with `pending` at position P (committed =
+ * P + 1), as after a prefill of P + 1 tokens.  For a freshly opened
+ * sequence; P below its capacity. */
+vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream);
 vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
 /* Device pointers of the per-sequence state arrays [max_seqs]:
  * P (KV length), pending token, committed count (read-only for callers). */

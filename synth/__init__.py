@@ -37,6 +37,19 @@ def stream_uniform(request, rnd):
     return 0x40000000 + request * 0x10000 + rnd
 
 
+SEED_WORKLOAD = 0x5EED0004  # per-request context lengths and draft lengths of ragged batches
+SEED_KV = 0x5EED0005        # committed K/V written straight into the cache by the generator
+
+
+def stream_workload(what):
+    return 0x60000000 + what
+
+
+def stream_kv(layer, kind):
+    """kind 0 = K pool, 1 = V pool of a layer."""
+    return 0x70000000 + layer * 2 + kind
+
+
 def _lib():
     global _host
     if _host is None:

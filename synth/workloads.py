@@ -57,3 +57,20 @@ WORKLOADS = {
                                     temperature=1.0, new_tokens=1,
                                     extra={"ctx_min": 512, "ctx_max": 8192, "k_min": 2, "k_max": 16, "block": 16}),
 }
+
+
+def ragged_batch(w):
+    """Per-request context lengths uniform in [ctx_min, ctx_max] and draft
+    lengths uniform in [k_min, k_max] (inclusive), drawn from the workload
+    seed: (contexts, draft lengths, pending tokens), one entry per request."""
+    import numpy as np
+
+    import synth
+    e = w.extra
+    n = w.batch
+    u_ctx = synth.uniforms(synth.SEED_WORKLOAD, synth.stream_workload(0), n)
+    u_k = synth.uniforms(synth.SEED_WORKLOAD, synth.stream_workload(1), n)
+    ctx = (e["ctx_min"] + np.floor(u_ctx * (e["ctx_max"] - e["ctx_min"] + 1))).astype(np.int64)
+    ks = (e["k_min"] + np.floor(u_k * (e["k_max"] - e["k_min"] + 1))).astype(np.int64)
+    pend = synth.tokens(synth.SEED_WORKLOAD, synth.stream_workload(2), w.model.vocab, n)
+    return [int(c) for c in ctx], [int(k) for k in ks], [int(t) for t in pend]

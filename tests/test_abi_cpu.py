@@ -23,6 +23,16 @@ def test_header_and_binding_agree():
     assert sorted(B.EXPORTS) == _declared()
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(VS_[A-Z_0-9]+)\s+(-?\d+)", text))
+    for name, val in defs.items():
+        if hasattr(B, name):
+            assert getattr(B, name) == int(val), name
+    for name in ("VS_MAX_ROWS", "VS_MAX_SEQS", "VS_MAX_K", "VS_N_UNIFORMS", "VS_RESULT_INTS", "VS_MAX_PASS_ROWS"):
+        assert name in defs and getattr(B, name) == int(defs[name]), name
+
+
 def test_library_exports_every_symbol():
     L = B.lib()
     for name in _declared():

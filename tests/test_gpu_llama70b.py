@@ -1,0 +1,173 @@
+"""GPU parity at the 70B shape on one GPU: 80 layers, d 8192, 64 query / 8 KV
+heads x 128, FFN 28672, V 32000, bf16, paged KV (block 16), draft = first 24
+layers; 32 requests with contexts uniform in [512, 8192] and draft lengths
+uniform in [2, 16] (about 330 verify rows per pass).  The committed KV is
+written straight into the cache by the seeded generator (N(0, 1) bf16)
+instead of 32 prefills of up to 8192 tokens.  The oracle checks sampled
+outputs: one verify layer of three requests (shortest, middle, longest
+context) from the GPU's layer input and committed KV, the head on sampled
+rows, and the greedy accept of every request on the GPU's logits; draft
+tokens are the argmax of their draft logits, and the draft's first-L KV
+matches a batched first-L pass within bf16 rounding."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import spec
+from oracle.decoder import Decoder, KVCache
+from synth.model_weights import SynthWeights
+from synth.workloads import LLAMA70B, WORKLOADS, ragged_batch
+from tests import gpu_common as G
+from verification_verify_step_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+CFG = LLAMA70B
+W = WORKLOADS["llama70b_ragged_b32"]
+CTX, KS, PEND = ragged_batch(W)
+N = len(CTX)
+ROWS = [k + 1 for k in KS]
+M = sum(ROWS)
+START = np.concatenate([[0], np.cumsum(ROWS)]).astype(int)
+MAX_CTX = max(CTX) + 64
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    bps = (MAX_CTX + 15) // 16 + 2
+    n_blocks = sum((c + 64 + 15) // 16 for c in CTX) + 16
+    e = G.engine(CFG, max_rows=M, max_seqs=N, max_ctx=MAX_CTX, n_blocks=n_blocks, max_blocks_per_seq=bps)
+    st = e.stream
+    for layer in range(CFG.n_layers):
+        K, V, _ = e.kv_layer(layer)
+        synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 0), K.numel(), K.data_ptr(), st, std=1.0)
+        synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 1), V.numel(), V.data_ptr(), st, std=1.0)
+    seqs = []
+    for i in range(N):
+        s = e.open(CTX[i] + 48)
+        B.vs_seq_assume(e.kv, s, CTX[i], PEND[i], st)
+        seqs.append(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(70)
+    hL = torch.from_numpy(rng.standard_normal((M, CFG.d_model)).astype(np.float32)).cuda()
+    toks = torch.from_numpy(rng.integers(0, CFG.vocab, M).astype(np.int32)).cuda()
+    batch = B.make_batch(seqs, ROWS)
+    yield {"e": e, "seqs": seqs, "hL": hL, "toks": toks, "batch": batch}
+    for s in seqs:
+        B.vs_seq_close(e.kv, s)
+
+
+def _forward(e, batch, start, end, toks, hin):
+    out = torch.empty((M, CFG.d_model), dtype=torch.float32, device="cuda")
+    B.vs_forward_layers(e.model, e.kv, batch, start, end, toks.data_ptr(), hin.data_ptr() if hin is not None else None,
+                        out.data_ptr(), e.stream)
+    return out
+
+
+def test_state_after_assume(ctx):
+    P, pending, committed = ctx["e"].state()
+    for i, s in enumerate(ctx["seqs"]):
+        assert P[s] == CTX[i] and pending[s] == PEND[i] and committed[s] == CTX[i] + 1
+
+
+@pytest.mark.parametrize("layer", [CFG.exit_layer, 50])
+def test_verify_layer_parity_ragged(ctx, layer):
+    e, seqs, batch = ctx["e"], ctx["seqs"], ctx["batch"]
+    X = ctx["hL"] if layer == CFG.exit_layer else _forward(e, batch, CFG.exit_layer, layer, ctx["toks"], ctx["hL"])
+    Y = _forward(e, batch, layer, layer + 1, ctx["toks"], X)
+    torch.cuda.synchronize()
+    Xh, Yh = X.cpu().numpy().astype(np.float64), Y.cpu().numpy().astype(np.float64)
+    dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
+    order = np.argsort(CTX)
+    for i in (int(order[0]), int(order[N // 2]), int(order[-1])):
+        P = CTX[i]
+        cache = KVCache(CFG, P + ROWS[i] + 1)
+        k, v = G.kv_slots(e, seqs[i], layer, np.arange(P))
+        Kc, Vc = cache.get(0, layer)
+        Kc[:, :P], Vc[:, :P] = k, v
+        rs = slice(START[i], START[i + 1])
+        Yo = dec.layer(layer, cache, spec.chain_rows(0, P, ROWS[i]), Xh[rs])
+        scale = np.abs(Yo).max()
+        err = np.abs(Yh[rs] - Yo).max()
+        assert err <= 1e-3 * scale + 1e-4, (layer, i, P, err, scale)
+
+
+def test_head_and_ragged_greedy_accept(ctx):
+    """Verify over all rows; head of sampled rows vs the oracle; draft tokens
+    set so that request i's first i % (K_i + 1) drafts match the target's
+    argmax and the next one does not: the accepted lengths, bonus tokens and
+    the committed state follow the oracle's greedy rule."""
+    e, seqs, batch = ctx["e"], ctx["seqs"], ctx["batch"]
+    Y = _forward(e, batch, CFG.exit_layer, CFG.n_layers, ctx["toks"], ctx["hL"])
+    z = torch.empty((M, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_head(e.model, M, Y.data_ptr(), z.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    zg = z.cpu().numpy()
+    sample = [0, 5, M // 2, M - 1]
+    dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
+    zo = dec.head(Y.cpu().numpy().astype(np.float64)[sample])
+    assert np.abs(zg[sample].astype(np.float64) - zo).max() <= G.LOGIT_TOL
+    toks = ctx["toks"].cpu().numpy().copy()
+    want = []
+    for i in range(N):
+        r0, k = START[i], KS[i]
+        a = i % (k + 1)
+        for j in range(1, k + 1):
+            am = int(np.argmax(zg[r0 + j - 1]))
+            toks[r0 + j] = am if j <= a else (am + 1) % CFG.vocab
+        want.append(spec.accept_greedy_chain(list(toks[r0:r0 + k + 1]), zg[r0:r0 + k + 1]))
+    dt = G.i32(toks)
+    res = torch.zeros((N, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    P0 = [e.state()[0][s] for s in seqs]
+    B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, dt.data_ptr(), z.data_ptr(), None, None, res.data_ptr(), e.stream)
+    B.vs_commit(e.model, e.kv, batch, res.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    got = G.result_rows(res, N)
+    P, pending, committed = e.state()
+    for i, s in enumerate(seqs):
+        a, y = want[i]
+        assert (got[i][0], got[i][1]) == (a, y), (i, got[i][:2], a, y)
+        assert a == i % (KS[i] + 1)
+        assert P[s] == P0[i] + a + 1 and pending[s] == y and committed[s] == P[s] + 1
+
+
+def test_ragged_draft(ctx):
+    """A greedy draft with per-request lengths K_i: every draft token is the
+    argmax of the draft logits that produced it, and the first-L KV it wrote
+    matches one batched first-L pass over the same rows.  Late draft steps
+    carry fewer requests, and the attention's key splits follow the pass's
+    shape (units and longest context), so the comparison allows the bf16
+    rounding of the stored K/V to differ by one step where the fp32 values
+    straddle a rounding boundary."""
+    e, seqs = ctx["e"], ctx["seqs"]
+    toks = torch.empty(M, dtype=torch.int32, device="cuda")
+    hL = torch.empty((M, CFG.d_model), dtype=torch.float32, device="cuda")
+    zd = torch.empty((M, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_draft(e.model, e.kv, seqs, KS, B.VS_GREEDY, 1.0, None, toks.data_ptr(), hL.data_ptr(), zd.data_ptr(),
+               e.stream)
+    torch.cuda.synchronize()
+    t = toks.cpu().numpy()
+    zdh = zd.cpu().numpy()
+    P, pending, _ = e.state()
+    for i, s in enumerate(seqs):
+        r0 = START[i]
+        assert t[r0] == pending[s]
+        for j in range(KS[i]):
+            row = zdh[r0 + j]
+            if not G.near_tie(row):
+                assert t[r0 + j + 1] == int(np.argmax(row)), (i, j)
+    layers = [0, CFG.exit_layer - 1]
+    slots = {i: np.arange(P[s], P[s] + ROWS[i]) for i, s in enumerate(seqs)}
+    pick = [0, N // 2, N - 1]
+    before = {(i, l): G.kv_slots(e, seqs[i], l, slots[i]) for i in pick for l in layers}
+    batch = B.make_batch(seqs, ROWS)
+    _forward(e, batch, 0, CFG.exit_layer, toks, None)
+    torch.cuda.synchronize()
+    for i in pick:
+        for l in layers:
+            k2, v2 = G.kv_slots(e, seqs[i], l, slots[i])
+            k1, v1 = before[(i, l)]
+            for x1, x2 in ((k1, k2), (v1, v2)):
+                assert np.allclose(x1, x2, rtol=2.0 ** -7, atol=1e-3), (i, l, np.abs(x1 - x2).max())
+                assert np.mean(x1 == x2) > 0.9, (i, l, np.mean(x1 == x2))

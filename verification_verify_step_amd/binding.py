@@ -12,12 +12,13 @@ LIB_PATH = os.path.join(_HERE, "libvstep.so")
 VS_OK, VS_E_INVAL, VS_E_SHAPE, VS_E_NOKV, VS_E_STATE, VS_E_DEVICE = 0, -1, -2, -3, -4, -5
 VS_GREEDY, VS_SAMPLE = 0, 1
 VS_MAX_ROWS, VS_MAX_SEQS, VS_MAX_K, VS_N_UNIFORMS, VS_RESULT_INTS = 64, 64, 16, 48, 24
+VS_MAX_PASS_ROWS = 1088
 (VS_T_EMBED, VS_T_ATTN_NORM, VS_T_WQ, VS_T_WK, VS_T_WV, VS_T_WO, VS_T_FFN_NORM, VS_T_W_GATE, VS_T_W_UP, VS_T_W_DOWN,
  VS_T_FINAL_NORM, VS_T_HEAD) = range(12)
 
 EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
-    "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
+    "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_commit",
     "vs_step", "vs_stats_enable", "vs_stats_read", "vs_stats_reset",
 ]
@@ -74,6 +75,7 @@ def lib():
             "vs_kv_create": (I32, [VP, VP, I32, I32, I32, VP, P(VP)]),
             "vs_kv_destroy": (None, [VP]),
             "vs_seq_open": (I32, [VP, I32, VP, pI]),
+            "vs_seq_assume": (I32, [VP, I32, I32, I32, VP]),
             "vs_seq_close": (I32, [VP, I32]),
             "vs_kv_state": (I32, [VP, P(VP), P(VP), P(VP)]),
             "vs_kv_layer": (I32, [VP, I32, P(VP), P(VP), P(VP)]),
@@ -154,6 +156,10 @@ def vs_seq_open(kv, max_len, stream):
     sid = ctypes.c_int32()
     _check("vs_seq_open", lib().vs_seq_open(kv, max_len, stream, ctypes.byref(sid)))
     return sid.value
+
+
+def vs_seq_assume(kv, seq, P, pending, stream):
+    _check("vs_seq_assume", lib().vs_seq_assume(kv, seq, P, pending, stream))
 
 
 def vs_seq_close(kv, seq):

@@ -88,7 +88,7 @@ constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention par
 constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows * 24;
 
 struct WsLayout {
-  size_t h, xa_h, xa_o, xa_act, ss, q, rope, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
+  size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
       st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
 };
 
@@ -108,6 +108,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.ss = take(R * (d / 16) * 4);
   w.q = take(R * H * hd * 4);
   w.rope = take(R * (hd / 2) * 8);
+  w.kvrow = take(R * 4);
   w.part = take(kAttnPartFloats * 4);
   w.attn_cnt = take(kAttnMaxUnits * 4);
   w.tree = take(kTreeBytes);
@@ -158,6 +159,7 @@ struct vs_model {
   float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
+  int* kvrow;
   int *amax_idx, *tokens, *st_amax, *dst_amax, *result;
   double *st_sum, *dst_sum;
   int ss_groups = 0;       // groups of the last producer of ss
@@ -255,6 +257,8 @@ GemmArgs gemm_base(vs_model* m, const Mat& W, const uint16_t* xa, int M) {
   g.k_steps = W.k_steps;
   g.xa = xa;
   g.M = M;
+  g.m0 = 0;
+  g.ld = M;
   g.inv_d = 1.0f / (float)m->c.d_model;
   g.eps = m->c.rms_eps;
   g.d = m->c.d_model;
@@ -266,10 +270,35 @@ double gemm_bytes(const Mat& W, int M) {
   return (double)W.bytes() + (double)M * W.k_steps * 32 * 4 + (double)M * W.n_tiles * 16 * 4;
 }
 
+// One GEMM of a pass.  A pass of more than kMaxRows rows runs as launches of
+// kMaxRows rows (row offset m0, row stride = the pass's rows) that all use
+// one launch configuration, so the per-workgroup norm sums of an EPI_RESID
+// product keep one layout.  out_rows (optional): destination row of each
+// pass row (h_copy / logits).  Returns the number of workgroups of a launch.
+int run_gemm(vs_model* m, GemmArgs g, int epi, int fam, const Mat& W, hipStream_t st, const int* out_rows) {
+  const int M = g.M;
+  g.m0 = 0;
+  g.ld = M;
+  if (M > kMaxRows) g.cfg = gemm_pick(W.n_tiles, W.k_steps, kMaxRows);
+  int groups = 0;
+  for (int m0 = 0; m0 < M; m0 += kMaxRows) {
+    GemmArgs c = g;
+    c.m0 = m0;
+    c.M = std::min(kMaxRows, M - m0);
+    if (out_rows != nullptr) {
+      c.out_row_identity = 0;
+      for (int i = 0; i < c.M; ++i) c.out_row[i] = out_rows[m0 + i];
+    }
+    timed(m, fam, gemm_bytes(W, c.M), st,
+          [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(c, epi, st, e0, e1); });
+  }
+  return groups;
+}
+
 // Loads rows (embedding of token ids, or hidden rows) into the residual
 // stream with the next consumer's gain g.
 void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const int* src_rows, const float* g,
-               hipStream_t st, const RowMap* rows = nullptr, const int* P = nullptr) {
+               hipStream_t st, const RowMap* rows = nullptr, const vs_kv* kv = nullptr) {
   LoadArgs a;
   memset(&a, 0, sizeof(a));
   a.M = M;
@@ -279,15 +308,18 @@ void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const
   a.embed = m->embed;
   a.hidden = hidden;
   a.src_identity = src_rows == nullptr;
-  if (src_rows)
-    for (int i = 0; i < M; ++i) a.src_row[i] = src_rows[i];
+  if (src_rows)  // row gathers come from draft steps: one row per sequence
+    for (int i = 0; i < M && i < kMaxRows; ++i) a.src_row[i] = src_rows[i];
   a.h = m->h;
   a.xa = m->xa_h;
   a.g = g;
   a.ss = m->ss;
   if (rows != nullptr) {  // the pass runs layers: build its RoPE table
     a.rope = m->rope;
-    a.P = P;
+    a.P = kv->P;
+    a.bt = kv->bt;
+    a.bps = kv->bps;
+    a.kvrow = m->kvrow;
     a.rows = *rows;
     a.half = m->c.head_dim / 2;
     a.theta = m->c.rope_theta;
@@ -322,13 +354,14 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   const int P = ctx_bound(kv, rm);
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
   // One 32-key step per wave while that stays under ~2048 waves (all KV loads
-  // in flight at once), else longer splits; bounded by the partials buffer and
-  // by the combine's capacity (workgroups per unit x query vectors).
+  // in flight at once), else longer splits of at most ~1024 keys; bounded by
+  // the partials buffer and by the combine's capacity (workgroups per unit x
+  // query vectors).
   int n_split = 0;
   a.kps = 32;
   if (P > 0) {
     const int max_split = (P + 31) / 32;
-    int want = std::max(1, 2048 / std::max(1, units));
+    int want = std::max({1, 2048 / std::max(1, units), (P + 1023) / 1024});
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
     const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
     const int max_wg = std::min(budget_wg, kAttnCombineSlots / a.qg_size);
@@ -370,7 +403,8 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.Hkv = c.n_kv_heads;
       g.hd = c.head_dim;
       g.rope = m->rope;
-      timed(m, F_QKV, gemm_bytes(m->qkv[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { launch_gemm(g, EPI_QKV, st, e0, e1); });
+      g.kvrow = m->kvrow;
+      run_gemm(m, g, EPI_QKV, F_QKV, m->qkv[l], st, nullptr);
     }
     attention(m, kv, rm, l, st);
     {
@@ -379,16 +413,14 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.xa_next = m->xa_h;
       g.g_next = m->g_ffn[l];
       g.ss_out = m->ss;
-      int groups = 0;
-      timed(m, F_O, gemm_bytes(m->o[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_RESID, st, e0, e1); });
-      m->ss_groups = groups;
+      m->ss_groups = run_gemm(m, g, EPI_RESID, F_O, m->o[l], st, nullptr);
     }
     {
       GemmArgs g = gemm_base(m, m->gu[l], m->xa_h, M);
       g.ss = m->ss;
       g.ss_groups = m->ss_groups;
       g.xa_act = m->xa_act;
-      timed(m, F_GU, gemm_bytes(m->gu[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { launch_gemm(g, EPI_SWIGLU, st, e0, e1); });
+      run_gemm(m, g, EPI_SWIGLU, F_GU, m->gu[l], st, nullptr);
     }
     {
       GemmArgs g = gemm_base(m, m->down[l], m->xa_act, M);
@@ -396,13 +428,14 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.xa_next = m->xa_h;
       g.g_next = (l + 1 < end) ? m->g_attn[l + 1] : m->g_final;
       g.ss_out = m->ss;
-      if (l + 1 == end && h_copy != nullptr) {
+      const bool copy = l + 1 == end && h_copy != nullptr;
+      std::vector<int> rows;
+      if (copy) {
         g.h_copy = h_copy;
-        for (int i = 0; i < M; ++i) g.out_row[i] = copy_rows ? copy_rows[i] : i;
+        rows.resize(M);
+        for (int i = 0; i < M; ++i) rows[i] = copy_rows ? copy_rows[i] : i;
       }
-      int groups = 0;
-      timed(m, F_DOWN, gemm_bytes(m->down[l], M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_RESID, st, e0, e1); });
-      m->ss_groups = groups;
+      m->ss_groups = run_gemm(m, g, EPI_RESID, F_DOWN, m->down[l], st, copy ? rows.data() : nullptr);
     }
   }
 }
@@ -416,13 +449,7 @@ void run_head(vs_model* m, int M, float* logits, const int* out_rows, hipStream_
   g.V = m->c.vocab;
   g.amax_val = m->amax_val;
   g.amax_idx = m->amax_idx;
-  if (out_rows) {
-    g.out_row_identity = 0;
-    for (int i = 0; i < M; ++i) g.out_row[i] = out_rows[i];
-  }
-  int groups = 0;
-  timed(m, F_HEAD, gemm_bytes(m->head, M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, EPI_LOGITS, st, e0, e1); });
-  m->head_groups = groups;
+  m->head_groups = run_gemm(m, g, EPI_LOGITS, F_HEAD, m->head, st, out_rows);
   m->head_rows = M;
 }
 
@@ -445,7 +472,7 @@ vs_status batch_rowmap(vs_kv* kv, const vs_batch* b, RowMap* rm) {
   }
   rm->row_start[b->n_seq] = M;
   if (M > kv->m->max_rows) return fail(VS_E_SHAPE, "batch: %d rows exceed the model's max_rows %d", M, kv->m->max_rows);
-  if (M > kMaxRows) return fail(VS_E_SHAPE, "batch: %d rows in one pass exceed %d", M, kMaxRows);
+  if (M > kMaxPassRows) return fail(VS_E_SHAPE, "batch: %d rows in one pass exceed %d", M, kMaxPassRows);
   rm->M = M;
   rm->depth = b->d_depth;
   rm->mask = b->d_mask;
@@ -508,7 +535,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
     return fail(VS_E_INVAL, "vs_model_create: null argument");
   std::string why;
   if (!shape_ok(cfg, &why)) return fail(VS_E_SHAPE, "vs_model_create: %s", why.c_str());
-  if (max_rows < 1 || max_rows > kMaxRows * kMaxSeq || max_seqs < 1 || max_seqs > kMaxSeq || max_ctx < 1)
+  if (max_rows < 1 || max_rows > kMaxPassRows || max_seqs < 1 || max_seqs > kMaxSeq || max_ctx < 1)
     return fail(VS_E_SHAPE, "vs_model_create: limits out of range");
   vs_model* m = new vs_model();
   m->c = *cfg;
@@ -533,7 +560,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->embed = reinterpret_cast<uint16_t*>(m->wbase + m->wl.embed);
   m->g_final = reinterpret_cast<float*>(m->wbase + m->wl.g_final);
   m->head = mat(m->wl.head, cfg->vocab, d);
-  m->max_rows = std::min<int>(max_rows, kMaxRows);
+  m->max_rows = max_rows;
   m->max_seqs = max_seqs;
   m->max_ctx = max_ctx;
   m->wsl = ws_layout(cfg, max_rows, max_seqs);
@@ -546,6 +573,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->ss = reinterpret_cast<float*>(w + m->wsl.ss);
   m->q = reinterpret_cast<float*>(w + m->wsl.q);
   m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
+  m->kvrow = reinterpret_cast<int*>(w + m->wsl.kvrow);
   m->part = reinterpret_cast<float*>(w + m->wsl.part);
   m->attn_cnt = reinterpret_cast<unsigned*>(w + m->wsl.attn_cnt);
   {
@@ -750,6 +778,20 @@ vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id)
   return VS_OK;
 }
 
+vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_assume: null argument");
+  if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_seq_assume: sequence %d is not open", seq);
+  if (kv->prefilled[seq]) return fail(VS_E_STATE, "vs_seq_assume: sequence %d already holds a context", seq);
+  if (P < 0 || P >= kv->cap[seq]) return fail(VS_E_NOKV, "vs_seq_assume: length %d outside the capacity %d", P, kv->cap[seq]);
+  if (pending < 0 || pending >= kv->m->c.vocab) return fail(VS_E_INVAL, "vs_seq_assume: pending token %d", pending);
+  launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, S(stream));
+  vs_status rc = check_launch("vs_seq_assume");
+  if (rc != VS_OK) return rc;
+  kv->P_ub[seq] = P;
+  kv->prefilled[seq] = 1;
+  return VS_OK;
+}
+
 vs_status vs_seq_close(vs_kv* kv, int32_t seq_id) {
   if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_close: null argument");
   if (seq_id < 0 || seq_id >= kv->max_seqs || !kv->open[seq_id])
@@ -800,7 +842,7 @@ vs_status vs_forward_layers(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t s
   if ((rc = check_capacity(kv, rm)) != VS_OK) return rc;
   hipStream_t st = S(stream);
   const float* g0 = start < end ? m->g_attn[start] : m->g_final;
-  load_rows(m, rm.M, start == 0 ? d_tokens : nullptr, d_hidden_in, nullptr, g0, st, &rm, kv->P);
+  load_rows(m, rm.M, start == 0 ? d_tokens : nullptr, d_hidden_in, nullptr, g0, st, &rm, kv);
   run_layers(m, kv, rm, start, end, st, nullptr, nullptr);
   if (d_hidden_out) launch_copy_rows(m->h, d_hidden_out, rm.M, m->c.d_model, st);
   return check_launch("vs_forward_layers");
@@ -834,7 +876,7 @@ vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_token
     rm.M = nc;
     rm.seq[0] = seq;
     rm.row_start[1] = nc;
-    load_rows(m, nc, d_tokens + c0, nullptr, nullptr, m->g_attn[0], st, &rm, kv->P);
+    load_rows(m, nc, d_tokens + c0, nullptr, nullptr, m->g_attn[0], st, &rm, kv);
     run_layers(m, kv, rm, 0, m->c.n_layers, st, nullptr, nullptr);
     const bool last = c0 + nc == n;
     if (last) run_head(m, nc, m->logits, nullptr, st);
@@ -892,7 +934,7 @@ vs_status validate_chain(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, 
     if (kv->P_ub[s] + k[i] + 1 > kv->cap[s]) return fail(VS_E_NOKV, "sequence %d: capacity %d reached", s, kv->cap[s]);
     M += k[i] + 1;
   }
-  if (M > m->max_rows || M > kMaxRows) return fail(VS_E_SHAPE, "%d verify rows exceed max_rows %d", M, m->max_rows);
+  if (M > m->max_rows || M > kMaxPassRows) return fail(VS_E_SHAPE, "%d verify rows exceed max_rows %d", M, m->max_rows);
   *M_out = M;
   return VS_OK;
 }
@@ -966,7 +1008,7 @@ void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int
       rm.row_start[a] = a;
     }
     rm.row_start[Ma] = Ma;
-    load_rows(m, Ma, d_tokens, nullptr, rows_src.data(), L > 0 ? m->g_attn[0] : m->g_final, st, &rm, kv->P);
+    load_rows(m, Ma, d_tokens, nullptr, rows_src.data(), L > 0 ? m->g_attn[0] : m->g_final, st, &rm, kv);
     if (L > 0) {
       run_layers(m, kv, rm, 0, L, st, d_hidden_L, rows_src.data());
     } else {
@@ -1016,7 +1058,7 @@ void draft_tree_impl(vs_model* m, vs_kv* kv, int seq, int topk, int depth, int k
       ta.out_parent = d_parent;
     }
     timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_tree_select(ta, st); });
-    load_rows(m, R, ta.row_tok, nullptr, nullptr, g0, st, &rm, kv->P);
+    load_rows(m, R, ta.row_tok, nullptr, nullptr, g0, st, &rm, kv);
     if (L > 0) run_layers(m, kv, rm, 0, L, st, last ? d_hidden_L : nullptr, nullptr);
     if (last) {
       if (L == 0) launch_copy_rows(m->h, d_hidden_L, R, m->c.d_model, st);
@@ -1088,7 +1130,7 @@ vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_lay
   hipStream_t st = S(stream);
   const int N = m->c.n_layers;
   load_rows(m, rm.M, start_layer == 0 ? d_tokens : nullptr, d_hidden_in, nullptr,
-            start_layer < N ? m->g_attn[start_layer] : m->g_final, st, &rm, kv->P);
+            start_layer < N ? m->g_attn[start_layer] : m->g_final, st, &rm, kv);
   run_layers(m, kv, rm, start_layer, N, st, nullptr, nullptr);
   run_head(m, rm.M, d_logits, nullptr, st);
   return check_launch("vs_verify");

@@ -10,7 +10,8 @@ namespace vs {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxSeq = VS_MAX_SEQS;
-constexpr int kMaxRows = VS_MAX_ROWS;
+constexpr int kMaxRows = VS_MAX_ROWS;          // per sequence per pass; also per GEMM launch
+constexpr int kMaxPassRows = VS_MAX_PASS_ROWS;  // per pass
 constexpr int kBlock = 16;    // KV tokens per block
 constexpr int kChunk = 64;    // keys per attention sub-chunk
 
@@ -52,18 +53,19 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // The activation side of a GEMM is stored split into two bf16 parts
 // (hi = bf16(x), lo = bf16(x - hi)) so that bf16 MFMA keeps ~16 bits of the
-// fp32 activation.  Layout of a [M][K] activation: for k-step s = k/32,
-// quad j = (k%32)/8, row m: 32 bytes = 8 hi then 8 lo bf16 at
-//   ((s*4 + j) * M + m) * 16 (in bf16 units).
-__device__ __forceinline__ size_t xa_index(int k, int m, int M) {
-  return ((size_t)((k >> 5) * 4 + ((k >> 3) & 3)) * M + m) * 16 + (k & 7);
+// fp32 activation.  Layout of a [M][K] activation: for k-step s = k/32, part
+// p (0 = hi, 1 = lo), quad j = (k%32)/8, row m: 8 bf16 at
+//   (((s*2 + p)*4 + j) * M + m) * 8.
+// One k-step's hi parts are contiguous (then its lo parts), so the GEMM's
+// 16-byte fragment loads of one part touch 4*M*16 contiguous bytes.
+__device__ __forceinline__ size_t xa_index(int k, int m, int M, int part) {
+  return ((size_t)(((k >> 5) * 2 + part) * 4 + ((k >> 3) & 3)) * M + m) * 8 + (k & 7);
 }
 __device__ __forceinline__ void xa_store(uint16_t* xa, int k, int m, int M, float v) {
   const uint16_t hi = f2bf(v);
   const uint16_t lo = f2bf(v - bf2f(hi));
-  const size_t i = xa_index(k, m, M);
-  xa[i] = hi;
-  xa[i + 8] = lo;
+  xa[xa_index(k, m, M, 0)] = hi;
+  xa[xa_index(k, m, M, 1)] = lo;
 }
 
 // Row placement helpers for kernels that read a RowMap.

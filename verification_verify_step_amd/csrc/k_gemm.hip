@@ -33,7 +33,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tile0 = blockIdx.x * NTW;
-  const int M = a.M;
+  const int M = a.M, m0 = a.m0, ld = a.ld;
   const int per = (a.k_steps + NW - 1) / NW;
   const int s0 = min(wave * per, a.k_steps);
   const int s1 = min(s0 + per, a.k_steps);
@@ -70,9 +70,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     for (int t = 0; t < NTW; ++t) wb[p][t] = __builtin_nontemporal_load(wbase[t] + (size_t)s * 64);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4* px = xbase + ((size_t)(s * 4 + kq) * M + row_ld[mt]) * 2;
-      xh[p][mt] = px[0];
-      xl[p][mt] = px[1];
+      xh[p][mt] = xbase[(size_t)((s * 2) * 4 + kq) * ld + m0 + row_ld[mt]];
+      xl[p][mt] = xbase[(size_t)((s * 2 + 1) * 4 + kq) * ld + m0 + row_ld[mt]];
     }
   };
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -107,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     float s = 0.f;
     if (tid < kQ * M) {
       const int m = tid % M;
-      for (int g = tid / M; g < a.ss_groups; g += kQ) s += val(g * M + m);
+      for (int g = tid / M; g < a.ss_groups; g += kQ) s += val(g, m);
     }
     return s;
   };
@@ -119,7 +118,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     }
   };
   if (n_ss > kSS) {  // many sums (large M): reduce straight from memory, before the weight stream starts
-    const float s = first_level([&](int e) { return a.ss[e]; });
+    const float s = first_level([&](int g, int m) { return a.ss[(size_t)g * ld + m0 + m]; });
     sstmp[tid] = s;
     finish_rs();
   } else if (n_ss == 0 && tid < M) {
@@ -129,7 +128,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < RSS; ++j) {
     const int e = tid + j * NT;
-    ssv[j] = (n_ss <= kSS && e < n_ss) ? a.ss[e] : 0.f;
+    ssv[j] = (n_ss <= kSS && e < n_ss) ? a.ss[(size_t)(e / M) * ld + m0 + e % M] : 0.f;
+  }
+
+  // Operands of the epilogue that do not depend on the product are requested
+  // now, so the epilogue waits on no memory: residual rows and the next
+  // norm's gains (residual), RoPE pairs and KV destinations (QKV).  Indexes
+  // are clamped to valid entries; entries past M * NC are never used.
+  constexpr int NC = NTW * 16;
+  constexpr int EP = (kMaxRows * NC + NT - 1) / NT;
+  constexpr int EQ = (kMaxRows * NC / 2 + NT - 1) / NT;
+  float pre_h[EPI == EPI_RESID ? EP : 1], pre_g[EPI == EPI_RESID ? EP : 1];
+  float2 pre_rope[EPI == EPI_QKV ? EQ : 1];
+  int pre_kv[EPI == EPI_QKV ? EQ : 1];
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+      const int idx = min(tid + j * NT, M * NC - 1);
+      const int m = idx / NC, nn = tile0 * 16 + idx % NC;
+      pre_h[j] = a.h[(size_t)(m0 + m) * a.d + nn];
+      pre_g[j] = a.g_next[nn];
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    const int half = a.hd >> 1;
+#pragma unroll
+    for (int j = 0; j < EQ; ++j) {
+      const int idx = min(tid + j * NT, M * (NC / 2) - 1);
+      const int m = idx / (NC / 2), nn = tile0 * 16 + 2 * (idx % (NC / 2));
+      pre_rope[j] = a.rope[(size_t)(m0 + m) * half + ((nn % a.hd) >> 1)];
+      pre_kv[j] = a.kvrow[m0 + m];
+    }
   }
 
   // Software pipeline: PD k-steps of loads in flight ahead of the MFMAs.
@@ -137,12 +165,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   // loop's wait counts conservative)
 #pragma unroll
   for (int p = 0; p < PD; ++p) load(p, max(0, min(s0 + p, a.k_steps - 1)));
-
+  // the norm scale is reduced while the first weight loads are in flight
   if (n_ss > 0 && n_ss <= kSS) {
 #pragma unroll
     for (int j = 0; j < RSS; ++j) sstmp[tid + j * NT] = ssv[j];
     __syncthreads();
-    const float s = first_level([&](int e) { return sstmp[e]; });
+    const float s = first_level([&](int g, int m) { return sstmp[g * M + m]; });
     __syncthreads();
     sstmp[tid] = s;
     finish_rs();
@@ -185,67 +213,64 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     for (int w = 0; w < NW; ++w) y += red[((w * NTW + t) * MT + mt) * 256 + src];
     return y;
   };
-  constexpr int NC = NTW * 16;
 
   if constexpr (EPI == EPI_RESID) {
-    for (int idx = tid; idx < M * NC; idx += NW * 64) {
-      const int m = idx / NC, c = idx % NC;
-      const int nn = tile0 * 16 + c;
-      const float hv = a.h[(size_t)m * a.d + nn] + result(m, c);
-      a.h[(size_t)m * a.d + nn] = hv;
-      if (a.h_copy != nullptr) a.h_copy[(size_t)a.out_row[m] * a.d + nn] = hv;
-      xa_store(a.xa_next, nn, m, M, hv * a.g_next[nn]);
-      rowtmp[m * NC + c] = hv * hv;
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+      const int idx = tid + j * NT;
+      if (idx < M * NC) {
+        const int m = idx / NC, c = idx % NC;
+        const int nn = tile0 * 16 + c;
+        const float hv = pre_h[j] + result(m, c);
+        a.h[(size_t)(m0 + m) * a.d + nn] = hv;
+        if (a.h_copy != nullptr) a.h_copy[(size_t)a.out_row[m] * a.d + nn] = hv;
+        xa_store(a.xa_next, nn, m0 + m, ld, hv * pre_g[j]);
+        rowtmp[m * NC + c] = hv * hv;
+      }
     }
     __syncthreads();
     if (tid < M) {
       float s = 0.f;
       for (int c = 0; c < NC; ++c) s += rowtmp[tid * NC + c];
-      a.ss_out[blockIdx.x * M + tid] = s;
+      a.ss_out[(size_t)blockIdx.x * ld + m0 + tid] = s;
     }
   } else if constexpr (EPI == EPI_QKV) {
-    __shared__ int s_slot[kMaxRows], s_seq[kMaxRows];
-    if (tid < M) {
-      const int i = row_seq_index(a.rows, tid);
-      const int sq = a.rows.seq[i];
-      const int idx = a.rows.idx_off + tid - a.rows.row_start[i];
-      s_seq[tid] = sq;
-      s_slot[tid] = a.kv.P[sq] + a.rows.win + idx;
-    }
-    __syncthreads();
     const int hd = a.hd, half = hd >> 1;
-    for (int idx = tid; idx < M * (NC / 2); idx += NW * 64) {
-      const int m = idx / (NC / 2), pr = idx % (NC / 2);
-      const int c = 2 * pr;
-      const int nn = tile0 * 16 + c;  // packed column: pair (i, i + hd/2) of one head
-      const float y0 = result(m, c) * rs[m];
-      const float y1 = result(m, c + 1) * rs[m];
-      const int hb = nn / hd;
-      const int ci = (nn % hd) >> 1;
-      float o0 = y0, o1 = y1;
-      if (hb < a.H + a.Hkv) {
-        const float2 r = a.rope[m * half + ci];
-        o0 = y0 * r.x - y1 * r.y;
-        o1 = y1 * r.x + y0 * r.y;
-      }
-      if (hb < a.H) {
-        float* qo = a.q + ((size_t)m * a.H + hb) * hd;
-        qo[ci] = o0;
-        qo[ci + half] = o1;
-      } else {
-        const bool is_k = hb < a.H + a.Hkv;
-        const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
-        const int slot = s_slot[m];
-        const int blk = a.kv.bt[s_seq[m] * a.kv.bps + slot / kBlock];
-        const size_t head = ((size_t)blk * a.Hkv + kvh) * kBlock * hd;
-        if (is_k) {  // K rows: [16 keys][hd]
-          uint16_t* dst = a.kv.k + head + (size_t)(slot % kBlock) * hd;
-          dst[ci] = f2bf(o0);
-          dst[ci + half] = f2bf(o1);
-        } else {     // V columns: [hd][16 keys]
-          uint16_t* dst = a.kv.v + head + (slot % kBlock);
-          dst[(size_t)ci * kBlock] = f2bf(o0);
-          dst[(size_t)(ci + half) * kBlock] = f2bf(o1);
+#pragma unroll
+    for (int j = 0; j < EQ; ++j) {
+      const int idx = tid + j * NT;
+      if (idx < M * (NC / 2)) {
+        const int m = idx / (NC / 2), pr = idx % (NC / 2);
+        const int c = 2 * pr;
+        const int nn = tile0 * 16 + c;  // packed column: pair (i, i + hd/2) of one head
+        const float y0 = result(m, c) * rs[m];
+        const float y1 = result(m, c + 1) * rs[m];
+        const int hb = nn / hd;
+        const int ci = (nn % hd) >> 1;
+        float o0 = y0, o1 = y1;
+        if (hb < a.H + a.Hkv) {
+          const float2 r = pre_rope[j];
+          o0 = y0 * r.x - y1 * r.y;
+          o1 = y1 * r.x + y0 * r.y;
+        }
+        if (hb < a.H) {
+          float* qo = a.q + ((size_t)(m0 + m) * a.H + hb) * hd;
+          qo[ci] = o0;
+          qo[ci + half] = o1;
+        } else {
+          const bool is_k = hb < a.H + a.Hkv;
+          const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
+          const int dst = pre_kv[j];  // block * 16 + offset in the block
+          const size_t head = ((size_t)(dst / kBlock) * a.Hkv + kvh) * kBlock * hd;
+          if (is_k) {  // K rows: [16 keys][hd]
+            uint16_t* kp = a.kv.k + head + (size_t)(dst % kBlock) * hd;
+            kp[ci] = f2bf(o0);
+            kp[ci + half] = f2bf(o1);
+          } else {     // V columns: [hd][16 keys]
+            uint16_t* vp = a.kv.v + head + (dst % kBlock);
+            vp[(size_t)ci * kBlock] = f2bf(o0);
+            vp[(size_t)(ci + half) * kBlock] = f2bf(o1);
+          }
         }
       }
     }
@@ -256,14 +281,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const float g = result(m, 2 * pr) * rs[m];
       const float u = result(m, 2 * pr + 1) * rs[m];
       const float act = g / (1.0f + expf(-g)) * u;
-      xa_store(a.xa_act, f, m, M, act);
+      xa_store(a.xa_act, f, m0 + m, ld, act);
     }
   } else {  // EPI_LOGITS
     for (int idx = tid; idx < M * NC; idx += NW * 64) {
       const int m = idx / NC, c = idx % NC;
       const int nn = tile0 * 16 + c;
       const float z = result(m, c) * rs[m];
-      const int orow = a.out_row_identity ? m : a.out_row[m];
+      const int orow = a.out_row_identity ? m0 + m : a.out_row[m];
       if (a.logits != nullptr && orow >= 0) a.logits[(size_t)orow * a.V + nn] = z;
       rowtmp[m * NC + c] = z;
     }
@@ -278,25 +303,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           bi = c;
         }
       }
-      a.amax_val[blockIdx.x * M + tid] = best;
-      a.amax_idx[blockIdx.x * M + tid] = tile0 * 16 + bi;
+      a.amax_val[(size_t)blockIdx.x * ld + m0 + tid] = best;
+      a.amax_idx[(size_t)blockIdx.x * ld + m0 + tid] = tile0 * 16 + bi;
     }
   }
 }
 
 GemmCfg gemm_cfg(int id) {
-  static const GemmCfg t[kGemmCfgs] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
+  static const GemmCfg t[kGemmCfgs] = {{0, 0}, {1, 4}, {1, 8}, {2, 4}, {2, 8}};
   return t[(id > 0 && id < kGemmCfgs) ? id : 0];
 }
 
-// Measured on MI355X at M <= 16 (7B shapes): one n-tile per workgroup is best;
-// 4 waves for the wide matrices (QKV, gate/up, head: >= 512 tiles), 8-16 waves
-// splitting K for the narrow ones (O, down: 256 tiles).  Larger M prefers two
-// n-tiles per workgroup (half the activation traffic per weight byte).
+// The number of waves splitting K fixes the order of every column's sum, so
+// it depends on the matrix only, never on M: a row's result is then the same
+// whichever rows share its pass.  Measured on MI355X (7B shapes): 4 waves for
+// the wide matrices (>= 512 n-tiles: QKV, gate/up, head, and every 70B
+// matrix), two n-tiles per workgroup above 16 rows (half the activation
+// traffic per weight byte); 8 waves and one n-tile for the narrow ones
+// (O and down at d = 4096), at every M.
 int gemm_pick(int n_tiles, int k_steps, int M) {
-  if (M > 16) return n_tiles % 2 == 0 ? 4 : 1;  // (2,4) / (1,4)
-  if (n_tiles >= 512) return 1;                  // (1,4)
-  return k_steps >= 256 ? 3 : 2;                 // (1,16) / (1,8)
+  (void)k_steps;
+  if (n_tiles < 512) return 2;                    // (1,8)
+  return (M > 16 && n_tiles % 2 == 0) ? 3 : 1;    // (2,4) / (1,4)
 }
 
 struct Ev {
@@ -318,16 +346,8 @@ static void launch_mt(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
   switch (cfg) {
     case 1: go<EPI, MT, 1, 4>(a, st, ev); break;
     case 2: go<EPI, MT, 1, 8>(a, st, ev); break;
-    case 3:
-      if constexpr (MT <= 2) go<EPI, MT, 1, 16>(a, st, ev);
-      else go<EPI, MT, 1, 8>(a, st, ev);
-      break;
-    case 4: go<EPI, MT, 2, 4>(a, st, ev); break;
-    case 5: go<EPI, MT, 2, 8>(a, st, ev); break;
-    default:
-      if constexpr (MT <= 1) go<EPI, MT, 2, 16>(a, st, ev);
-      else go<EPI, MT, 2, 8>(a, st, ev);
-      break;
+    case 3: go<EPI, MT, 2, 4>(a, st, ev); break;
+    default: go<EPI, MT, 2, 8>(a, st, ev); break;
   }
 }
 
@@ -341,8 +361,8 @@ static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
 
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const Ev ev{ev0, ev1};
-  int cfg = a.cfg > 0 ? a.cfg : gemm_pick(a.n_tiles, a.k_steps, a.M);
-  if (gemm_cfg(cfg).ntw == 2 && a.n_tiles % 2 != 0) cfg = 2;
+  int cfg = (a.cfg > 0 && a.cfg < kGemmCfgs) ? a.cfg : gemm_pick(a.n_tiles, a.k_steps, a.M);
+  if (gemm_cfg(cfg).ntw == 2 && a.n_tiles % 2 != 0) cfg -= 2;  // same waves, one n-tile
   // configurations whose reduction buffer would not fit fall back inside launch_mt
   int ntw = gemm_cfg(cfg).ntw;
   switch (epi) {

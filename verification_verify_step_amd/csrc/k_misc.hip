@@ -73,6 +73,15 @@ void launch_set_blocks(const BlockSetArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(set_blocks_kernel, dim3(1), dim3(256), 0, st, a);
 }
 
+__global__ void set_state_kernel(int* P, int* pending, int* committed, int seq, int p, int pend) {
+  P[seq] = p;
+  pending[seq] = pend;
+  committed[seq] = p + 1;
+}
+void launch_set_state(int* P, int* pending, int* committed, int seq, int p, int pend, hipStream_t st) {
+  hipLaunchKernelGGL(set_state_kernel, dim3(1), dim3(1), 0, st, P, pending, committed, seq, p, pend);
+}
+
 // ---------------------------------------------------------------------------
 // Row loading: h[m] = embed[token] (or a given hidden row); the next
 // consumer's activation (h * g) as split-bf16 fragments; per 256-column group
@@ -81,26 +90,31 @@ __global__ __launch_bounds__(256) void load_rows_kernel(LoadArgs a) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float wsum[4][kMaxRows];
-  for (int m = 0; m < a.M; ++m) {
-    float v = 0.f;
-    if (n < a.d) {
-      const int src = a.src_identity ? m : a.src_row[m];
-      if (a.tokens != nullptr) {
-        const int t = min(max(a.tokens[src], 0), a.V - 1);  // never read outside the table
-        v = bf2f(a.embed[(size_t)t * a.d + n]);
-      } else {
-        v = a.hidden[(size_t)src * a.d + n];
+  for (int r0 = 0; r0 < a.M; r0 += kMaxRows) {  // rows in groups of kMaxRows
+    const int nr = min(kMaxRows, a.M - r0);
+    for (int mm = 0; mm < nr; ++mm) {
+      const int m = r0 + mm;
+      float v = 0.f;
+      if (n < a.d) {
+        const int src = a.src_identity ? m : a.src_row[mm];
+        if (a.tokens != nullptr) {
+          const int t = min(max(a.tokens[src], 0), a.V - 1);  // never read outside the table
+          v = bf2f(a.embed[(size_t)t * a.d + n]);
+        } else {
+          v = a.hidden[(size_t)src * a.d + n];
+        }
+        a.h[(size_t)m * a.d + n] = v;
+        xa_store(a.xa, n, m, a.M, v * a.g[n]);
       }
-      a.h[(size_t)m * a.d + n] = v;
-      xa_store(a.xa, n, m, a.M, v * a.g[n]);
+      const float s = wave_sum(v * v);
+      if (lane == 0) wsum[wave][mm] = s;
     }
-    const float s = wave_sum(v * v);
-    if (lane == 0) wsum[wave][m] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x < a.M) {
-    const int m = threadIdx.x;
-    a.ss[blockIdx.x * a.M + m] = ((wsum[0][m] + wsum[1][m]) + wsum[2][m]) + wsum[3][m];
+    __syncthreads();
+    if (threadIdx.x < nr) {
+      const int mm = threadIdx.x;
+      a.ss[(size_t)blockIdx.x * a.M + r0 + mm] = ((wsum[0][mm] + wsum[1][mm]) + wsum[2][mm]) + wsum[3][mm];
+    }
+    __syncthreads();
   }
   if (a.rope != nullptr && blockIdx.x == 0) {
     // angles in fp64: position up to ~1e4 times frequencies down to 1e-4
@@ -113,6 +127,12 @@ __global__ __launch_bounds__(256) void load_rows_kernel(LoadArgs a) {
       double sn, cs;
       sincos(ang, &sn, &cs);
       a.rope[e] = make_float2((float)cs, (float)sn);
+    }
+    for (int m = threadIdx.x; m < a.M; m += 256) {
+      const int si = row_seq_index(a.rows, m);
+      const int sq = a.rows.seq[si];
+      const int slot = a.P[sq] + a.rows.win + a.rows.idx_off + m - a.rows.row_start[si];
+      a.kvrow[m] = a.bt[(size_t)sq * a.bps + slot / kBlock] * kBlock + slot % kBlock;
     }
   }
 }

@@ -14,7 +14,8 @@ struct GemmArgs {
   const uint16_t* W;     // packed fragments [n_tiles][k_steps][64 lanes][8]
   int n_tiles, k_steps;
   const uint16_t* xa;    // activation fragments, see xa_index()
-  int M;
+  int M;                 // rows computed by this launch: pass rows m0 .. m0+M-1
+  int m0, ld;            // first row; rows of the whole pass (row stride of every row-indexed array)
   // RMSNorm scale of the input rows: rs[m] = 1/sqrt(sum_g ss[g*M+m] / d + eps)
   const float* ss;       // null: no norm scale
   int ss_groups;
@@ -34,10 +35,11 @@ struct GemmArgs {
   float* q;
   int H, Hkv, hd;
   const float2* rope;    // [M][hd/2] (cos, sin) of each row's position
+  const int* kvrow;      // [M] KV destination: block * 16 + slot % 16
 
   // EPI_SWIGLU
   uint16_t* xa_act;
-  // EPI_LOGITS: logits[out_row[m]][V]; per-group argmax partials
+  // EPI_LOGITS: logits[out_row[m]][V] (out_row relative to m0); per-group argmax partials
   float* logits;
   int V;
   float* amax_val;
@@ -53,7 +55,7 @@ struct GemmArgs {
 struct GemmCfg {
   int ntw, nw;
 };
-constexpr int kGemmCfgs = 7;
+constexpr int kGemmCfgs = 5;
 GemmCfg gemm_cfg(int id);
 int gemm_pick(int n_tiles, int k_steps, int M);
 // ev0/ev1 (optional): events timestamped at the kernel's own start and end.

@@ -38,6 +38,11 @@ struct LoadArgs {
   RowMap rows;
   int half;
   float theta;
+  // KV destination of each row (block * 16 + slot % 16), the same in every
+  // layer's pool; written with the RoPE table
+  const int* bt;
+  int bps;
+  int* kvrow;
 };
 
 struct StatsArgs {
@@ -145,6 +150,7 @@ void launch_pack(const PackArgs& a, hipStream_t st);
 void launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t st);
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
 void launch_set_blocks(const BlockSetArgs& a, hipStream_t st);
+void launch_set_state(int* P, int* pending, int* committed, int seq, int p, int pend, hipStream_t st);
 void launch_load_rows(const LoadArgs& a, hipStream_t st);
 void launch_copy_rows(const float* src, float* dst, int M, int d, hipStream_t st);
 void launch_row_stats(const StatsArgs& a, int M, hipStream_t st);
