@@ -28,8 +28,17 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
                                                  0, 0);
 }
 
+// MT = 0 is the packed form for M <= 8: one 16-row A operand holds the hi
+// parts of the rows in A rows 0-7 and their lo parts in rows 8-15, so a
+// k-step takes one activation load and one MFMA; output rows m and m + 8 are
+// added per wave.  With MT >= 1 tiles the hi and lo parts accumulate
+// separately and are added per wave the same way, so a row's sum is grouped
+// identically whichever form computes it.
 template <int MT, int NTW, int NW, int PD, int EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
+  constexpr bool PK = MT == 0;
+  constexpr int T = PK ? 1 : MT;  // 16-row tiles
+  constexpr int TL = PK ? 1 : MT;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tile0 = blockIdx.x * NTW;
@@ -40,11 +49,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   const int n = s1 - s0;
   const int mrow = lane & 15, kq = lane >> 4;
 
-  f32x4 acc[MT][NTW];
+  f32x4 acc[T][NTW], acl[TL][NTW];  // hi (packed: hi and lo) and lo accumulators
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < T; ++mt)
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < TL; ++mt)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acl[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const u32x4* wbase[NTW];
 #pragma unroll
@@ -53,15 +66,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   const u32x4* xbase = reinterpret_cast<const u32x4*>(a.xa);
 
   u32x4 wb[PD][NTW];
-  u32x4 xh[PD][MT], xl[PD][MT];
+  u32x4 xh[PD][T], xl[PD][TL];
 
   // Rows >= M are loaded from row M-1 (no divergent branch, so the loads stay
   // in flight across iterations) and zeroed by a select before the MFMA.
-  bool row_ok[MT];
-  int row_ld[MT];
+  bool row_ok[T];
+  int row_ld[T];
+  const int part = PK ? (mrow >> 3) : 0;  // packed: A rows 8-15 carry the lo parts
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + mrow;
+  for (int mt = 0; mt < T; ++mt) {
+    const int m = PK ? (mrow & 7) : mt * 16 + mrow;
     row_ok[mt] = m < M;
     row_ld[mt] = min(m, M - 1);
   }
@@ -69,21 +83,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) wb[p][t] = __builtin_nontemporal_load(wbase[t] + (size_t)s * 64);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      xh[p][mt] = xbase[(size_t)((s * 2) * 4 + kq) * ld + m0 + row_ld[mt]];
-      xl[p][mt] = xbase[(size_t)((s * 2 + 1) * 4 + kq) * ld + m0 + row_ld[mt]];
+    for (int mt = 0; mt < T; ++mt) {
+      if constexpr (PK) {
+        xh[p][mt] = xbase[(size_t)((s * 2 + part) * 4 + kq) * ld + m0 + row_ld[mt]];
+      } else {
+        xh[p][mt] = xbase[(size_t)((s * 2) * 4 + kq) * ld + m0 + row_ld[mt]];
+        xl[p][mt] = xbase[(size_t)((s * 2 + 1) * 4 + kq) * ld + m0 + row_ld[mt]];
+      }
     }
   };
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto compute = [&](int p) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < T; ++mt) {
       const u32x4 ah = row_ok[mt] ? xh[p][mt] : zero4;
-      const u32x4 al = row_ok[mt] ? xl[p][mt] : zero4;
+      if constexpr (PK) {
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        acc[mt][t] = mfma(ah, wb[p][t], acc[mt][t]);
-        acc[mt][t] = mfma(al, wb[p][t], acc[mt][t]);
+        for (int t = 0; t < NTW; ++t) acc[mt][t] = mfma(ah, wb[p][t], acc[mt][t]);
+      } else {
+        const u32x4 al = row_ok[mt] ? xl[p][mt] : zero4;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          acc[mt][t] = mfma(ah, wb[p][t], acc[mt][t]);
+          acl[mt][t] = mfma(al, wb[p][t], acl[mt][t]);
+        }
       }
     }
   };
@@ -195,22 +218,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
 
   // ---- cross-wave reduction through LDS (fixed order) ----
-  __shared__ float red[NW * NTW * MT * 256];
+  __shared__ float red[NW * NTW * T * 256];
   __shared__ float rowtmp[kMaxRows * NTW * 16];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < T; ++mt)
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(((wave * NTW + t) * MT + mt) * 64 + lane) * 4 + r] = acc[mt][t][r];
+      for (int r = 0; r < 4; ++r)
+        red[(((wave * NTW + t) * T + mt) * 64 + lane) * 4 + r] =
+            PK ? acc[mt][t][r] : acc[mt][t][r] + acl[PK ? 0 : mt][t][r];
   __syncthreads();
 
   auto result = [&](int m, int c) -> float {
-    const int t = c >> 4, col = c & 15, mt = m >> 4, row = m & 15;
+    const int t = c >> 4, col = c & 15, mt = PK ? 0 : m >> 4, row = PK ? m : m & 15;
     const int src = ((row >> 2) * 16 + col) * 4 + (row & 3);
     float y = 0.f;
+    if constexpr (PK) {  // per wave: hi (row m) + lo (row m + 8), then over waves
+      const int src_lo = (((row + 8) >> 2) * 16 + col) * 4 + ((row + 8) & 3);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) y += red[((w * NTW + t) * MT + mt) * 256 + src];
+      for (int w = 0; w < NW; ++w) {
+        const float* tile = red + ((w * NTW + t) * T + mt) * 256;
+        y += tile[src] + tile[src_lo];
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) y += red[((w * NTW + t) * T + mt) * 256 + src];
+    }
     return y;
   };
 
@@ -354,7 +388,8 @@ static void launch_mt(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
 template <int EPI>
 static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
   const int mt = (a.M + 15) / 16;
-  if (mt == 1) launch_mt<EPI, 1>(a, cfg, st, ev);
+  if (a.M <= 8) launch_mt<EPI, 0>(a, cfg, st, ev);
+  else if (mt == 1) launch_mt<EPI, 1>(a, cfg, st, ev);
   else if (mt == 2) launch_mt<EPI, 2>(a, cfg, st, ev);
   else launch_mt<EPI, 4>(a, cfg, st, ev);
 }
