@@ -365,13 +365,13 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
     const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
     const int max_wg = std::min(budget_wg, kAttnCombineSlots / a.qg_size);
-    want = std::min(want, max_wg * kAttnWaves - 1);
+    want = std::min(want, max_wg * attn_waves(a.qg_size) - 1);
     n_split = std::min(max_split, std::max(1, want));
     a.kps = ((P + n_split - 1) / n_split + 31) / 32 * 32;
     n_split = (P + a.kps - 1) / a.kps;
   }
   a.n_split = n_split;
-  const int wpb = (n_split + 1 + kAttnWaves - 1) / kAttnWaves;
+  const int wpb = (n_split + 1 + attn_waves(a.qg_size) - 1) / attn_waves(a.qg_size);
   a.part = m->part;
   a.ml_off = (size_t)units * wpb * a.qg_size * c.head_dim;
   a.ml_off += a.ml_off & 1;

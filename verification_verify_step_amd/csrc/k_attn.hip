@@ -21,10 +21,11 @@
 // O += P.V.  The next step's K/V loads are in flight while the current one
 // computes.
 //
-// Combining the splits happens in the same launch.  The four waves of a
-// workgroup merge their (max, sum, o) in LDS in a fixed order, (0,2) and
-// (1,3) then the two results.  Wave 0 publishes the merged partial with
-// device-coherent stores (they write through this XCD's L2).  Thread 0 then
+// Combining the splits happens in the same launch.  The waves of a
+// workgroup put their (max, sum, o) in LDS; each wave then merges one slice
+// of the head dims over all of them in wave order and publishes that slice
+// of the workgroup's partial with device-coherent stores (they write
+// through this XCD's L2).  Thread 0 then
 // counts the workgroup in on a per-unit counter.  The last workgroup of a
 // unit to arrive reads every partial with device-coherent loads, sums them
 // in workgroup order, and writes the result as split-bf16 activation
@@ -40,8 +41,6 @@ namespace vs {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kStep = 32;           // keys per step
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -65,17 +64,18 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 
 // Query vectors of a unit: vector gq of the query group maps to row
 // r0 + gq % nr and head kvh*G + gq / nr.
-template <int MTQ, int HD>
-__global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
+template <int MTQ, int HD, int WV>
+__global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
+  constexpr int kWaves = WV, kThreads = WV * 64;
   constexpr int KSQ = HD / 32;  // k-steps of S over head dims
   constexpr int NDT = HD / 16;  // 16-dim output tiles
   constexpr int QR = MTQ * 16;
   constexpr int PS = kStep + 4;  // P scratch row stride (floats)
-  constexpr int NO = MTQ * NDT * 4;  // o values per lane
-  constexpr int NML = MTQ * 4;       // (max, sum) pairs per lane
   constexpr int PL_FLOATS = kWaves * QR * PS;
-  constexpr int XO_FLOATS = 2 * NO * 64, XML_FLOATS = 2 * NML * 64 * 2;
-  __shared__ float smem[PL_FLOATS + XO_FLOATS + XML_FLOATS];
+  constexpr int MG_FLOATS = WV * QR * HD + 2 * WV * QR + 2 * QR + WV * QR;
+  constexpr int SM_FLOATS = PL_FLOATS > MG_FLOATS ? PL_FLOATS : MG_FLOATS;
+  static_assert(SM_FLOATS >= 2 * kAttnCombineSlots + kAttnQG, "combine scratch");
+  __shared__ float smem[SM_FLOATS];
   __shared__ int last_wg;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -166,7 +166,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
     load_k();
     load_v();
   }
-  // query fragments (A operand of S), pre-scaled and split hi/lo
+  // query fragments (A operand of S), pre-scaled and split hi/lo.  Scores
+  // are kept in base-2 units (the scale carries log2 e), so every softmax
+  // exponential is one hardware exp2; max, sum and partials all use base 2.
+  const float qscale = a.scale * 1.4426950408889634f;
   u32x4 qh[MTQ][KSQ], ql[MTQ][KSQ];
 #pragma unroll
   for (int mt = 0; mt < MTQ; ++mt) {
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
       const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = qok ? x[e] * a.scale : 0.f;
+      for (int e = 0; e < 8; ++e) y[e] = qok ? x[e] * qscale : 0.f;
       split8(y, qh[mt][s], ql[mt][s]);
     }
   }
@@ -231,11 +234,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         const float mnew = fmaxf(mrun[mt][r], mx);
-        const float corr = (mrun[mt][r] == -INFINITY) ? 0.f : expf(mrun[mt][r] - mnew);
+        const float corr = (mrun[mt][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[mt][r] - mnew);
         float ps = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const float p = v[t] == -INFINITY ? 0.f : expf(v[t] - mnew);
+          const float p = v[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[t] - mnew);
           pw[row * PS + 16 * t + mrow] = p;
           ps += p;
         }
@@ -261,80 +264,71 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   }
 
 
-  // ---- merge the four waves' partials: (0 with 2, 1 with 3), then (0 with 1)
-  float* xo = smem + PL_FLOATS;            // [2][NO][64]
-  float2* xml = reinterpret_cast<float2*>(xo + XO_FLOATS);  // [2][NML][64]
-  auto put = [&](int slot) {
+  // ---- merge the waves' partials: every wave puts its (max, sum, o) in LDS;
+  // after one barrier wave w merges dims [w*DS, (w+1)*DS) of all WV partials
+  // in wave order and writes that slice of the workgroup's partial (or, for a
+  // unit of one workgroup, of the result).  The P scratch is reused.
+  constexpr int DS = HD / WV;       // dims merged by one wave
+  constexpr int NE = QR * DS / 64;  // (row, dim) entries per lane
+  static_assert((QR * DS) % 64 == 0, "merge entries");
+  float* xo = smem;                                              // [WV][QR][HD]
+  float2* xml = reinterpret_cast<float2*>(smem + WV * QR * HD);  // [WV][QR]
+  __syncthreads();  // every wave is done with the P scratch
 #pragma unroll
-    for (int mt = 0; mt < MTQ; ++mt)
+  for (int mt = 0; mt < MTQ; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xml[(slot * NML + mt * 4 + r) * 64 + lane] = make_float2(mrun[mt][r], lrun[mt][r]);
+    for (int r = 0; r < 4; ++r) {
+      const int row = mt * 16 + 4 * kq + r;
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) xo[(slot * NO + (mt * NDT + t) * 4 + r) * 64 + lane] = oacc[mt][t][r];
-      }
-  };
-  auto merge = [&](int slot) {
-#pragma unroll
-    for (int mt = 0; mt < MTQ; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 o2 = xml[(slot * NML + mt * 4 + r) * 64 + lane];
-        const float m1 = mrun[mt][r];
-        const float mn = fmaxf(m1, o2.x);
-        const float c1 = m1 == -INFINITY ? 0.f : expf(m1 - mn);
-        const float c2 = o2.x == -INFINITY ? 0.f : expf(o2.x - mn);
-        mrun[mt][r] = mn;
-        lrun[mt][r] = lrun[mt][r] * c1 + o2.y * c2;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-          oacc[mt][t][r] = oacc[mt][t][r] * c1 + xo[(slot * NO + (mt * NDT + t) * 4 + r) * 64 + lane] * c2;
-      }
-  };
-  if (wave >= 2) put(wave - 2);
+      for (int t = 0; t < NDT; ++t) xo[(wave * QR + row) * HD + 16 * t + mrow] = oacc[mt][t][r];
+      if (mrow == 0) xml[wave * QR + row] = make_float2(mrun[mt][r], lrun[mt][r]);
+    }
+  // per-row weights exp2(m_j - max) and merged (max, sum), once per row
+  float2* rw = xml + WV * QR;  // [QR]: (max, sum) of the merged partial
+  float* wts = reinterpret_cast<float*>(rw + QR);  // [WV][QR]
   __syncthreads();
-  if (wave < 2) merge(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
+  for (int row = threadIdx.x; row < QR; row += kThreads) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < WV; ++j) {
+      const float2 v = xml[j * QR + row];
+      if (v.y > 0.f) mx = fmaxf(mx, v.x);  // a partial that saw no key has sum 0
+    }
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < WV; ++j) {
+      const float2 v = xml[j * QR + row];
+      const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
+      wts[j * QR + row] = w;
+      l += w * v.y;
+    }
+    rw[row] = make_float2(mx, l);
+  }
   __syncthreads();
 
   const size_t QG = a.qg_size;
   float* po = a.part;                                            // [units][wpb][QG][HD]
   uint64_t* pml = reinterpret_cast<uint64_t*>(a.part + a.ml_off);  // [units][wpb][QG] (max, sum)
-  if (wave == 0) {
-    merge(0);
-    if (wpb == 1) {  // the only workgroup of its unit: write the result
+  const size_t rec = (size_t)unit * wpb + wgi;
 #pragma unroll
-      for (int mt = 0; mt < MTQ; ++mt)
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    const int row = e / DS, d = wave * DS + e % DS;
+    if (row < nq) {
+      float o = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = mt * 16 + 4 * kq + r;
-          if (row < nq) {
-            const int gq = q0 + row;
-            const int m = r0 + gq % nr, h = kvh * G + gq / nr;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t) xa_store(a.xa_o, h * HD + 16 * t + mrow, m, a.M, oacc[mt][t][r] / lrun[mt][r]);
-          }
+      for (int j = 0; j < WV; ++j) o += wts[j * QR + row] * xo[(j * QR + row) * HD + d];
+      const float2 ml = rw[row];
+      if (wpb == 1) {  // the only workgroup of its unit: write the result
+        const int gq = q0 + row;
+        xa_store(a.xa_o, (kvh * G + gq / nr) * HD + d, r0 + gq % nr, a.M, o / ml.y);
+      } else {
+        __hip_atomic_store(po + (rec * QG + row) * HD + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wave == 0 && e % DS == 0) {
+          const uint64_t b = (uint64_t)__float_as_uint(ml.x) | ((uint64_t)__float_as_uint(ml.y) << 32);
+          __hip_atomic_store(pml + rec * QG + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    } else {
-      const size_t rec = (size_t)unit * wpb + wgi;
-#pragma unroll
-      for (int mt = 0; mt < MTQ; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = mt * 16 + 4 * kq + r;
-          if (row < nq) {
-            float* dst = po + (rec * QG + row) * HD + mrow;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t)
-              __hip_atomic_store(dst + 16 * t, oacc[mt][t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (mrow == 0) {
-              const uint64_t b = (uint64_t)__float_as_uint(mrun[mt][r]) |
-                                 ((uint64_t)__float_as_uint(lrun[mt][r]) << 32);
-              __hip_atomic_store(pml + rec * QG + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
+      }
     }
   }
   if (wpb == 1) return;
@@ -355,63 +349,64 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(const AttnArgs a) {
   if (!last_wg) return;
 
   // ---- last workgroup of the unit: combine the wpb partials in workgroup
-  // order.  Thread = one pair of dims of one query vector (two pairs when the
-  // unit has more than kThreads of them); its o pairs and (max, sum) values
-  // are requested together, then merged one partial after another.
+  // order.  Each row's weights exp(m_j - max) and total are computed once in
+  // LDS; a thread then sums one pair of dims of one query vector over the
+  // partials.  Its first partials are requested before the weights exist.
   constexpr int HP = HD / 2;  // dim pairs
-  constexpr int kCB = 12;     // partials requested per batch
+  constexpr int kCB = 16;     // partials requested per batch
+  float2* cw = reinterpret_cast<float2*>(smem);  // [wpb][nq]: (max, sum) -> (weight, sum)
+  float* ctot = smem + 2 * kAttnCombineSlots;     // [nq]
   const size_t rec0 = (size_t)unit * wpb;
   const uint64_t* po2 = reinterpret_cast<const uint64_t*>(po);
   const int npair = nq * HP;
-  for (int p = threadIdx.x; p < npair; p += 2 * kThreads) {
-    const bool two = p + kThreads < npair;
-    int r[2], c[2];
-    float mr[2], lr[2], o0[2], o1[2];
+  uint64_t xc[kCB];
+  auto load_batch = [&](int p, int j0) {
+    const int pp = min(p, npair - 1);
+    const int r = pp / HP, c = pp - r * HP;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pj = min(p + j * kThreads, npair - 1);
-      r[j] = pj / HP;
-      c[j] = pj - r[j] * HP;
-      mr[j] = -INFINITY;
-      lr[j] = o0[j] = o1[j] = 0.f;
+    for (int e = 0; e < kCB; ++e)
+      xc[e] = __hip_atomic_load(po2 + ((rec0 + min(j0 + e, wpb - 1)) * QG + r) * HP + c, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+  };
+  load_batch(threadIdx.x, 0);
+  for (int e = threadIdx.x; e < wpb * nq; e += kThreads) {
+    const int j = e / nq, r = e - j * nq;
+    const uint64_t b = __hip_atomic_load(pml + (rec0 + j) * QG + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cw[e] = make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < nq; r += kThreads) {
+    float mx = -INFINITY;
+    for (int j = 0; j < wpb; ++j)
+      if (cw[j * nq + r].y > 0.f) mx = fmaxf(mx, cw[j * nq + r].x);
+    float tot = 0.f;
+    for (int j = 0; j < wpb; ++j) {
+      const float2 v = cw[j * nq + r];
+      const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
+      cw[j * nq + r].x = w;
+      tot += w * v.y;
     }
-    for (int sp0 = 0; sp0 < wpb; sp0 += kCB) {
-      uint64_t xo[2][kCB], xm[2][kCB];
+    ctot[r] = tot;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < npair; p += kThreads) {
+    const int r = p / HP, c = p - r * HP;
+    float o0 = 0.f, o1 = 0.f;
+    for (int j0 = 0; j0 < wpb; j0 += kCB) {
+      if (p != threadIdx.x || j0 > 0) load_batch(p, j0);
 #pragma unroll
-      for (int e = 0; e < kCB; ++e) {
-        const size_t sp = rec0 + min(sp0 + e, wpb - 1);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          xo[j][e] = __hip_atomic_load(po2 + (sp * QG + r[j]) * HP + c[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          xm[j][e] = __hip_atomic_load(pml + sp * QG + r[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int e = 0; e < kCB; ++e)
+        if (j0 + e < wpb) {
+          const float w = cw[(j0 + e) * nq + r].x;
+          o0 += w * __uint_as_float((uint32_t)xc[e]);
+          o1 += w * __uint_as_float((uint32_t)(xc[e] >> 32));
         }
-      }
-#pragma unroll
-      for (int e = 0; e < kCB; ++e) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float m2 = __uint_as_float((uint32_t)xm[j][e]);
-          const float l2 = __uint_as_float((uint32_t)(xm[j][e] >> 32));
-          if (sp0 + e < wpb && l2 > 0.f) {  // a partial that saw no key has l = 0
-            const float mn = fmaxf(mr[j], m2);
-            const float c1 = mr[j] == -INFINITY ? 0.f : expf(mr[j] - mn);
-            const float c2 = expf(m2 - mn);
-            lr[j] = lr[j] * c1 + l2 * c2;
-            o0[j] = o0[j] * c1 + __uint_as_float((uint32_t)xo[j][e]) * c2;
-            o1[j] = o1[j] * c1 + __uint_as_float((uint32_t)(xo[j][e] >> 32)) * c2;
-            mr[j] = mn;
-          }
-        }
-      }
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (j == 0 || two) {
-        const int gq = q0 + r[j];
-        const int m = r0 + gq % nr, h = kvh * G + gq / nr;
-        xa_store(a.xa_o, h * HD + 2 * c[j], m, a.M, o0[j] / lr[j]);
-        xa_store(a.xa_o, h * HD + 2 * c[j] + 1, m, a.M, o1[j] / lr[j]);
-      }
+    const float tot = ctot[r];
+    const int gq = q0 + r;
+    const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+    xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / tot);
+    xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot);
   }
 }
 
@@ -419,22 +414,23 @@ hipError_t attn_init() { return hipSuccess; }
 
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const int n_parts = a.n_split + 1;
-  const int wpb = (n_parts + kWaves - 1) / kWaves;
+  const int wv = attn_waves(a.qg_size);
+  const int wpb = (n_parts + wv - 1) / wv;
   dim3 grid(a.rows.n_seq * wpb, a.Hkv, a.n_qg);
   const int mtq = (a.qg_size + 15) / 16;  // at most 2 (query groups hold <= kAttnQG vectors)
-#define VS_ATT(MTQ, HD)                                                                                     \
+#define VS_ATT(MTQ, HD, WV)                                                                                 \
   do {                                                                                                      \
     if (ev0 != nullptr || ev1 != nullptr)                                                                   \
-      hipExtLaunchKernelGGL((attn_kernel<MTQ, HD>), grid, dim3(kThreads), 0, st, ev0, ev1, 0, a);           \
+      hipExtLaunchKernelGGL((attn_kernel<MTQ, HD, WV>), grid, dim3(WV * 64), 0, st, ev0, ev1, 0, a);        \
     else                                                                                                    \
-      hipLaunchKernelGGL((attn_kernel<MTQ, HD>), grid, dim3(kThreads), 0, st, a);                           \
+      hipLaunchKernelGGL((attn_kernel<MTQ, HD, WV>), grid, dim3(WV * 64), 0, st, a);                        \
   } while (0)
   if (a.hd == 128) {
-    if (mtq <= 1) VS_ATT(1, 128);
-    else VS_ATT(2, 128);
+    if (mtq <= 1) VS_ATT(1, 128, 8);
+    else VS_ATT(2, 128, 4);
   } else {
-    if (mtq <= 1) VS_ATT(1, 64);
-    else VS_ATT(2, 64);
+    if (mtq <= 1) VS_ATT(1, 64, 8);
+    else VS_ATT(2, 64, 4);
   }
 #undef VS_ATT
 }
