@@ -25,15 +25,15 @@
 // workgroup put their (max, sum, o) in LDS; each wave then merges one slice
 // of the head dims over all of them in wave order and publishes that slice
 // of the workgroup's partial with device-coherent stores (they write
-// through this XCD's L2).  Thread 0 then
-// counts the workgroup in on a per-unit counter.  The last workgroup of a
-// unit to arrive reads every partial with device-coherent loads, sums them
-// in workgroup order, and writes the result as split-bf16 activation
-// fragments for the O projection; it also resets the counter to zero.  The
-// result does not depend on which workgroup arrives last.  No agent-scope
-// fence is used: a fence would write back or invalidate the whole L2.
-// Ordering comes from waiting on the vector memory counter before the count,
-// so the device-coherent stores have completed.
+// through this XCD's L2).  Thread 0 then counts the workgroup in on a
+// per-unit counter.  The last workgroup of a unit to arrive reads every
+// partial with device-coherent loads, sums them in workgroup order, and
+// writes the result as split-bf16 activation fragments for the O
+// projection; it also resets the counter to zero.  The result does not
+// depend on which workgroup arrives last.  No agent-scope fence is used: a
+// fence would write back or invalidate the whole L2.  Ordering comes from
+// waiting on the vector memory counter before the count, so the
+// device-coherent stores have completed.
 #include "kernels.h"
 
 namespace vs {
@@ -72,9 +72,9 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   constexpr int QR = MTQ * 16;
   constexpr int PS = kStep + 4;  // P scratch row stride (floats)
   constexpr int PL_FLOATS = kWaves * QR * PS;
-  constexpr int MG_FLOATS = WV * QR * HD + 2 * WV * QR + 2 * QR + WV * QR;
+  constexpr int MG_FLOATS = WV * QR * (HD + 4) + 2 * WV * QR + 2 * QR + WV * QR;
   constexpr int SM_FLOATS = PL_FLOATS > MG_FLOATS ? PL_FLOATS : MG_FLOATS;
-  static_assert(SM_FLOATS >= 2 * kAttnCombineSlots + kAttnQG, "combine scratch");
+  static_assert(SM_FLOATS >= 3 * kAttnCombineSlots + kAttnQG, "combine scratch");
   __shared__ float smem[SM_FLOATS];
   __shared__ int last_wg;
 
@@ -264,30 +264,34 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   }
 
 
-  // ---- merge the waves' partials: every wave puts its (max, sum, o) in LDS;
-  // after one barrier wave w merges dims [w*DS, (w+1)*DS) of all WV partials
-  // in wave order and writes that slice of the workgroup's partial (or, for a
-  // unit of one workgroup, of the result).  The P scratch is reused.
-  constexpr int DS = HD / WV;       // dims merged by one wave
-  constexpr int NE = QR * DS / 64;  // (row, dim) entries per lane
-  static_assert((QR * DS) % 64 == 0, "merge entries");
-  float* xo = smem;                                              // [WV][QR][HD]
-  float2* xml = reinterpret_cast<float2*>(smem + WV * QR * HD);  // [WV][QR]
+  // ---- merge the waves' partials: every wave puts its (max, sum, o) for
+  // the rows below nq in LDS; the per-row weights exp2(m_j - max) and the
+  // merged (max, sum) are computed once per row; then wave w merges dims
+  // [w*DS, (w+1)*DS) of all WV partials in wave order and writes that slice
+  // of the workgroup's partial (or, for a unit of one workgroup, of the
+  // result).  The P scratch is reused; rows are padded so that the rows one
+  // lane group apart fall in different LDS banks.
+  constexpr int HDP = HD + 4;   // padded row stride (floats)
+  constexpr int DS = HD / WV;   // dims merged by one wave
+  float* xo = smem;                                               // [WV][QR][HDP]
+  float2* xml = reinterpret_cast<float2*>(smem + WV * QR * HDP);  // [WV][QR]
+  float* rl = reinterpret_cast<float*>(xml + WV * QR);            // [QR] merged sum
+  float* rm = rl + QR;                                            // [QR] merged max
+  float* wts = rm + QR;                                           // [WV][QR]
   __syncthreads();  // every wave is done with the P scratch
 #pragma unroll
   for (int mt = 0; mt < MTQ; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = mt * 16 + 4 * kq + r;
+      if (row < nq) {
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) xo[(wave * QR + row) * HD + 16 * t + mrow] = oacc[mt][t][r];
-      if (mrow == 0) xml[wave * QR + row] = make_float2(mrun[mt][r], lrun[mt][r]);
+        for (int t = 0; t < NDT; ++t) xo[(wave * QR + row) * HDP + 16 * t + mrow] = oacc[mt][t][r];
+        if (mrow == 0) xml[wave * QR + row] = make_float2(mrun[mt][r], lrun[mt][r]);
+      }
     }
-  // per-row weights exp2(m_j - max) and merged (max, sum), once per row
-  float2* rw = xml + WV * QR;  // [QR]: (max, sum) of the merged partial
-  float* wts = reinterpret_cast<float*>(rw + QR);  // [WV][QR]
   __syncthreads();
-  for (int row = threadIdx.x; row < QR; row += kThreads) {
+  for (int row = threadIdx.x; row < nq; row += kThreads) {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < WV; ++j) {
@@ -302,36 +306,33 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       wts[j * QR + row] = w;
       l += w * v.y;
     }
-    rw[row] = make_float2(mx, l);
+    rl[row] = l;
+    rm[row] = mx;
   }
   __syncthreads();
 
   const size_t QG = a.qg_size;
-  float* po = a.part;                                            // [units][wpb][QG][HD]
+  float* po = a.part;                                              // [units][wpb][QG][HD]
   uint64_t* pml = reinterpret_cast<uint64_t*>(a.part + a.ml_off);  // [units][wpb][QG] (max, sum)
   const size_t rec = (size_t)unit * wpb + wgi;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const int e = lane + 64 * i;
+  for (int e = lane; e < nq * DS; e += 64) {
     const int row = e / DS, d = wave * DS + e % DS;
-    if (row < nq) {
-      float o = 0.f;
+    float o = 0.f;
 #pragma unroll
-      for (int j = 0; j < WV; ++j) o += wts[j * QR + row] * xo[(j * QR + row) * HD + d];
-      const float2 ml = rw[row];
-      if (wpb == 1) {  // the only workgroup of its unit: write the result
-        const int gq = q0 + row;
-        xa_store(a.xa_o, (kvh * G + gq / nr) * HD + d, r0 + gq % nr, a.M, o / ml.y);
-      } else {
-        __hip_atomic_store(po + (rec * QG + row) * HD + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (wave == 0 && e % DS == 0) {
-          const uint64_t b = (uint64_t)__float_as_uint(ml.x) | ((uint64_t)__float_as_uint(ml.y) << 32);
-          __hip_atomic_store(pml + rec * QG + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+    for (int j = 0; j < WV; ++j) o += wts[j * QR + row] * xo[(j * QR + row) * HDP + d];
+    if (wpb == 1) {  // the only workgroup of its unit: write the result
+      const int gq = q0 + row;
+      xa_store(a.xa_o, (kvh * G + gq / nr) * HD + d, r0 + gq % nr, a.M, o / rl[row]);
+    } else {
+      __hip_atomic_store(po + (rec * QG + row) * HD + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (wpb == 1) return;
+  if (threadIdx.x < nq) {
+    const int row = threadIdx.x;
+    const uint64_t b = (uint64_t)__float_as_uint(rm[row]) | ((uint64_t)__float_as_uint(rl[row]) << 32);
+    __hip_atomic_store(pml + rec * QG + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // The partial stores must have completed (written through to device
   // scope) before the workgroup is counted in.  A workgroup-scope fence does
   // not wait for stores on this target, so wait on the vector memory counter
@@ -349,41 +350,47 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   if (!last_wg) return;
 
   // ---- last workgroup of the unit: combine the wpb partials in workgroup
-  // order.  Each row's weights exp(m_j - max) and total are computed once in
+  // order.  Each row's weights exp2(m_j - max) and total are computed once in
   // LDS; a thread then sums one pair of dims of one query vector over the
-  // partials.  Its first partials are requested before the weights exist.
+  // partials, with the loads of up to kCB partials in flight at once (the
+  // first batch is requested before the weights exist).
   constexpr int HP = HD / 2;  // dim pairs
+  constexpr int kCG = 8;      // partials per guarded group
   constexpr int kCB = 16;     // partials requested per batch
-  float2* cw = reinterpret_cast<float2*>(smem);  // [wpb][nq]: (max, sum) -> (weight, sum)
-  float* ctot = smem + 2 * kAttnCombineSlots;     // [nq]
-  const size_t rec0 = (size_t)unit * wpb;
-  const uint64_t* po2 = reinterpret_cast<const uint64_t*>(po);
+  float2* cml = reinterpret_cast<float2*>(smem);  // [wpb][nq] (max, sum)
+  float* cwt = smem + 2 * kAttnCombineSlots;      // [wpb][nq] weights
+  float* ctot = cwt + kAttnCombineSlots;          // [nq]
+  const uint64_t* src0 = reinterpret_cast<const uint64_t*>(po) + (size_t)unit * wpb * QG * HP;
+  const int S = (int)QG * HP;  // pairs between consecutive partials
   const int npair = nq * HP;
   uint64_t xc[kCB];
   auto load_batch = [&](int p, int j0) {
-    const int pp = min(p, npair - 1);
-    const int r = pp / HP, c = pp - r * HP;
+    const uint64_t* src = src0 + min(p, npair - 1);
 #pragma unroll
-    for (int e = 0; e < kCB; ++e)
-      xc[e] = __hip_atomic_load(po2 + ((rec0 + min(j0 + e, wpb - 1)) * QG + r) * HP + c, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+    for (int g = 0; g < kCB / kCG; ++g)
+      if (j0 + g * kCG < wpb) {
+#pragma unroll
+        for (int e = g * kCG; e < (g + 1) * kCG; ++e)
+          xc[e] = __hip_atomic_load(src + min(j0 + e, wpb - 1) * S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
   };
-  load_batch(threadIdx.x, 0);
+  if (threadIdx.x < npair) load_batch(threadIdx.x, 0);
   for (int e = threadIdx.x; e < wpb * nq; e += kThreads) {
     const int j = e / nq, r = e - j * nq;
-    const uint64_t b = __hip_atomic_load(pml + (rec0 + j) * QG + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    cw[e] = make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+    const uint64_t b = __hip_atomic_load(pml + ((size_t)unit * wpb + j) * QG + r, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    cml[e] = make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
   }
   __syncthreads();
   for (int r = threadIdx.x; r < nq; r += kThreads) {
     float mx = -INFINITY;
     for (int j = 0; j < wpb; ++j)
-      if (cw[j * nq + r].y > 0.f) mx = fmaxf(mx, cw[j * nq + r].x);
+      if (cml[j * nq + r].y > 0.f) mx = fmaxf(mx, cml[j * nq + r].x);
     float tot = 0.f;
     for (int j = 0; j < wpb; ++j) {
-      const float2 v = cw[j * nq + r];
+      const float2 v = cml[j * nq + r];
       const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
-      cw[j * nq + r].x = w;
+      cwt[j * nq + r] = w;
       tot += w * v.y;
     }
     ctot[r] = tot;
@@ -395,11 +402,15 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
     for (int j0 = 0; j0 < wpb; j0 += kCB) {
       if (p != threadIdx.x || j0 > 0) load_batch(p, j0);
 #pragma unroll
-      for (int e = 0; e < kCB; ++e)
-        if (j0 + e < wpb) {
-          const float w = cw[(j0 + e) * nq + r].x;
-          o0 += w * __uint_as_float((uint32_t)xc[e]);
-          o1 += w * __uint_as_float((uint32_t)(xc[e] >> 32));
+      for (int g = 0; g < kCB / kCG; ++g)
+        if (j0 + g * kCG < wpb) {
+#pragma unroll
+          for (int e = g * kCG; e < (g + 1) * kCG; ++e) {
+            const int j = j0 + e;
+            const float w = j < wpb ? cwt[j * nq + r] : 0.f;
+            o0 += w * __uint_as_float((uint32_t)xc[e]);
+            o1 += w * __uint_as_float((uint32_t)(xc[e] >> 32));
+          }
         }
     }
     const float tot = ctot[r];
