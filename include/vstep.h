@@ -220,6 +220,49 @@ vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_
 vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const int32_t* k, int32_t mode,
                   float temp, const double* d_u, int32_t* d_tokens, int32_t* d_result, void* stream);
 
+/* Confidence of the target over each sequence's verify block ("DSpark" page,
+ * §2.2): per sequence, the mean over its rows of p_top1 and of p_top1 - p_top2
+ * with p = softmax(logits row / temp), computed in fp64 from the fp32 logits.
+ * d_logits [M][V] in batch row order; d_conf [n_seq][2] (device, fp64):
+ * (mean top-1 probability, mean top-1 minus top-2 gap).  Asynchronous on the
+ * stream; errors: VS_E_INVAL (null pointer, temp <= 0), VS_E_SHAPE (batch). */
+vs_status vs_confidence(vs_model* m, const vs_batch* b, float temp, const float* d_logits, double* d_conf,
+                        void* stream);
+
+/* Confidence-scheduled draft length per request ("DSpark" page, §2.2-§2.3),
+ * host code only.  After a round with a accepted of k drafts:
+ *   ema <- 0.2 * a/k + 0.8 * ema                      (ema starts at 0.5)
+ *   C    = 0.4 * top1 + 0.3 * min(5 * gap, 1) + 0.3 * ema
+ *   k'   = clamp(int(min_k + (max_k - min_k) * (C - low) / (high - low)))
+ * and k' = min_k when the first draft was rejected (a == 0).  The caller owns
+ * the state structs (one per request); vs_sched_init sets ema = 0.5 and k to
+ * k0 clamped to [min_k, max_k].  Errors: VS_E_INVAL for a bad config
+ * (1 <= min_k <= max_k <= VS_MAX_K, low < high), a outside [0, k] or a
+ * non-finite confidence; the state is unchanged on error. */
+typedef struct vs_sched_cfg {
+  int32_t min_k, max_k; /* 2, 16 */
+  double low, high;     /* 0.3, 0.7 */
+} vs_sched_cfg;
+typedef struct vs_spec_state {
+  double ema;           /* moving average of the per-round acceptance a/k */
+  int32_t k;            /* draft length of the next round */
+  int32_t rounds;       /* rounds seen */
+  int32_t last_a;       /* accepted drafts of the last round (-1 before the first) */
+} vs_spec_state;
+vs_status vs_sched_init(const vs_sched_cfg* c, int32_t k0, vs_spec_state* s);
+vs_status vs_sched_update(const vs_sched_cfg* c, vs_spec_state* s, int32_t a, double avg_top1, double avg_gap);
+
+/* One greedy chain round of n_seq requests with per-request draft lengths
+ * states[i].k (vs_step), then vs_confidence over each request's k+1 verify
+ * rows, then vs_sched_update of every state.  Blocks until the round is done:
+ * h_result [n_seq][VS_RESULT_INTS] (host) receives d_result, and h_conf
+ * [n_seq][2] (host, may be NULL) the confidences.  d_tokens [sum k+1] and
+ * d_result [n_seq][VS_RESULT_INTS] are device buffers as for vs_step.
+ * Errors: as vs_step; VS_E_STATE when a state's k lies outside the schedule. */
+vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const vs_sched_cfg* c,
+                        vs_spec_state* states, int32_t* d_tokens, int32_t* d_result, int32_t* h_result,
+                        double* h_conf, void* stream);
+
 /* Per-kernel-family timing with HIP events on the launching stream, for the
  * selected families only.  `mask` selects families by bit, in the order vs_stats_read
  * reports them: gemm_qkv, gemm_o, gemm_gate_up, gemm_down, gemm_head,

@@ -26,6 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from . import formulas
 from .decoder import Row, softmax
 
 FLAG_BAND = 1e-3  # |p/q - u| below this marks an acceptance decision as a near-tie
@@ -206,3 +207,66 @@ def generate_spec(dec, cache, sid, prompt, n_new, k, exit_layer=None):
     while len(st.tokens) - len(prompt) < n_new:
         spec_round(dec, cache, st, k, exit_layer=exit_layer)
     return st.tokens[len(prompt):len(prompt) + n_new], st
+
+
+def row_confidence(z_rows, T=1.0):
+    """Confidence of the target over a verify block ("DSpark" page, §2.2): the
+    mean over the rows of the top-1 probability and of the top-1 minus top-2
+    probability, p = softmax(z/T) in float64."""
+    top1, gap = [], []
+    for z in z_rows:
+        p = np.sort(probs(z, T))[::-1]
+        top1.append(p[0])
+        gap.append(p[0] - p[1])
+    return float(np.mean(top1)), float(np.mean(gap))
+
+
+@dataclass
+class SchedState:
+    """Per-request draft-length state ("DSpark" page, §2.2-§2.3, and the
+    per-request state it asks the scheduler to keep): the draft length of the
+    next round and the moving average of the acceptance rate (starts at 0.5)."""
+    k: int
+    ema: float = 0.5
+
+
+SCHED = dict(min_k=2, max_k=16, low=0.3, high=0.7)
+
+
+def schedule_update(state, a, avg_top1, avg_gap, min_k=2, max_k=16, low=0.3, high=0.7):
+    """After a round with a accepted of state.k drafts: fold the round's
+    acceptance a/k into the average (weight 0.2), form the confidence C from
+    the target's mean top-1 probability, its mean top-1/top-2 gap and the
+    average, map C linearly onto [min_k, max_k]; a first-draft reject sends K
+    straight back to min_k (the page raises K only after a round that kept at
+    least one draft and lowers it at once after a first-token reject)."""
+    state.ema = 0.2 * (a / state.k) + 0.8 * state.ema
+    C = formulas.confidence(avg_top1, avg_gap, state.ema)
+    k = formulas.next_k(C, min_k, max_k, low, high)
+    state.k = min_k if a == 0 else k
+    return state.k, C
+
+
+def next_k_real(C, min_k=2, max_k=16, low=0.3, high=0.7):
+    """The unclamped, untruncated value that next_k truncates (for checks that
+    must know how close a decision was to the next integer)."""
+    return min_k + (max_k - min_k) * (C - low) / (high - low)
+
+
+def generate_scheduled(dec, cache, sid, prompt, n_new, k0, **sched):
+    """Greedy speculative decoding with the confidence-scheduled draft length:
+    each round drafts state.k tokens, verifies, accepts, commits, then updates
+    the state from the verify rows' confidence.  Returns (new tokens, the k of
+    every round, the (top1, gap, C) of every round, the state)."""
+    cfg = dict(SCHED, **sched)
+    st, _ = prefill(dec, cache, sid, prompt)
+    state = SchedState(max(cfg["min_k"], min(cfg["max_k"], k0)))
+    ks, confs = [], []
+    while len(st.tokens) - len(prompt) < n_new:
+        k = state.k
+        a, y, zt, _ = spec_round(dec, cache, st, k)
+        top1, gap = row_confidence(zt)
+        _, C = schedule_update(state, a, top1, gap, **cfg)
+        ks.append(k)
+        confs.append((top1, gap, C, a))
+    return st.tokens[len(prompt):len(prompt) + n_new], ks, confs, state

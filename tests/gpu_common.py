@@ -14,16 +14,16 @@ LOGIT_TOL = 2e-2  # max-abs logit agreement, bf16 weights/KV with fp32 accumulat
 NEAR_TIE = 4e-2   # a greedy choice whose top-1 - top-2 gap is below this may legitimately differ
 
 
-def engine(cfg, eps=None, force_host=False, **kw):
+def engine(cfg, eps=None, force_host=False, head_scale=None, **kw):
     e = Engine(cfg, **kw)
-    gpu_weights.load(e, cfg, eps=eps, force_host=force_host)
+    gpu_weights.load(e, cfg, eps=eps, force_host=force_host, head_scale=head_scale)
     return e
 
 
-def oracle_decoder(cfg, eps=None):
+def oracle_decoder(cfg, eps=None, head_scale=None):
     w = SynthWeights(cfg, precision="bf16")
-    if eps is not None:
-        w = gpu_weights.ScaledWeights(w, cfg, eps)
+    if eps is not None or head_scale is not None:
+        w = gpu_weights.ScaledWeights(w, cfg, eps, head_scale)
     return Decoder(cfg, w)
 
 
@@ -60,6 +60,8 @@ def result_rows(res, n_seq):
     return [(int(x[0]), int(x[1]), int(x[2]), [int(p) for p in x[4:4 + x[3]]]) for x in r]
 
 
-def near_tie(z):
+def near_tie(z, scale=1.0):
+    """Top-1 - top-2 below the band (times the head's scale, which scales the
+    logits and their rounding errors alike)."""
     s = np.sort(np.asarray(z, dtype=np.float64))
-    return s[-1] - s[-2] < NEAR_TIE
+    return s[-1] - s[-2] < NEAR_TIE * scale

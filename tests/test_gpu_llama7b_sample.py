@@ -134,6 +134,26 @@ def test_head_and_stochastic_accept(ctx):
     assert flagged <= 2
 
 
+def test_verify_confidence(ctx):
+    """vs_confidence on the verify logits of the 8 requests (5 rows each, full
+    vocabulary) equals the oracle's mean top-1 probability and mean top-1/top-2
+    gap of the same logits, at T = 1 and T = 0.7."""
+    e, batch = ctx["e"], ctx["batch"]
+    Y = _forward(e, batch, CFG.exit_layer, CFG.n_layers, ctx["toks"], ctx["hL"])
+    z = torch.empty((M, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_head(e.model, M, Y.data_ptr(), z.data_ptr(), e.stream)
+    conf = torch.zeros((N_REQ, 2), dtype=torch.float64, device="cuda")
+    for temp in (1.0, 0.7):
+        B.vs_confidence(e.model, batch, temp, z.data_ptr(), conf.data_ptr(), e.stream)
+        torch.cuda.synchronize()
+        got = conf.cpu().numpy()
+        zg = z.cpu().numpy().astype(np.float64)
+        for i in range(N_REQ):
+            # the ABI takes the temperature as a float: the oracle divides by that value
+            t1, g = spec.row_confidence(zg[i * (K + 1):(i + 1) * (K + 1)], float(np.float32(temp)))
+            assert abs(got[i, 0] - t1) <= 1e-10 and abs(got[i, 1] - g) <= 1e-10, (temp, i, got[i], t1, g)
+
+
 def test_rounds_keep_the_state_invariant(ctx):
     """Stochastic rounds through vs_step: every request advances by a + 1 and
     keeps committed == P + 1."""

@@ -20,7 +20,8 @@ EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
     "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_commit",
-    "vs_step", "vs_stats_enable", "vs_stats_read", "vs_stats_reset",
+    "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_stats_enable", "vs_stats_read",
+    "vs_stats_reset",
 ]
 
 
@@ -40,6 +41,16 @@ class vs_batch(ctypes.Structure):
     _fields_ = [("n_seq", ctypes.c_int32), ("seq", ctypes.POINTER(ctypes.c_int32)),
                 ("n_rows", ctypes.POINTER(ctypes.c_int32)), ("d_depth", ctypes.c_void_p),
                 ("d_mask", ctypes.c_void_p)]
+
+
+class vs_sched_cfg(ctypes.Structure):
+    _fields_ = [("min_k", ctypes.c_int32), ("max_k", ctypes.c_int32), ("low", ctypes.c_double),
+                ("high", ctypes.c_double)]
+
+
+class vs_spec_state(ctypes.Structure):
+    _fields_ = [("ema", ctypes.c_double), ("k", ctypes.c_int32), ("rounds", ctypes.c_int32),
+                ("last_a", ctypes.c_int32)]
 
 
 class vs_kernel_stat(ctypes.Structure):
@@ -89,6 +100,10 @@ def lib():
             "vs_accept": (I32, [VP, P(vs_batch), I32, F, VP, VP, VP, VP, VP, VP]),
             "vs_commit": (I32, [VP, VP, P(vs_batch), VP, VP]),
             "vs_step": (I32, [VP, VP, I32, pI, pI, I32, F, VP, VP, VP, VP]),
+            "vs_confidence": (I32, [VP, P(vs_batch), F, VP, VP, VP]),
+            "vs_sched_init": (I32, [P(vs_sched_cfg), I32, P(vs_spec_state)]),
+            "vs_sched_update": (I32, [P(vs_sched_cfg), P(vs_spec_state), I32, D, D]),
+            "vs_step_sched": (I32, [VP, VP, I32, pI, P(vs_sched_cfg), P(vs_spec_state), VP, VP, pI, P(D), VP]),
             "vs_stats_enable": (I32, [VP, I32]),
             "vs_stats_read": (I32, [VP, P(vs_kernel_stat), I32, pI]),
             "vs_stats_reset": (I32, [VP]),
@@ -235,6 +250,39 @@ def vs_commit(model, kv, batch, d_result, stream):
 def vs_step(model, kv, seqs, ks, mode, temp, d_u, d_tokens, d_result, stream):
     _check("vs_step", lib().vs_step(model, kv, len(seqs), _i32(seqs), _i32(ks), mode, temp, d_u, d_tokens, d_result,
                                     stream))
+
+
+def vs_confidence(model, batch, temp, d_logits, d_conf, stream):
+    _check("vs_confidence", lib().vs_confidence(model, ctypes.byref(batch), temp, d_logits, d_conf, stream))
+
+
+def sched_cfg(min_k=2, max_k=16, low=0.3, high=0.7):
+    return vs_sched_cfg(min_k, max_k, low, high)
+
+
+def vs_sched_init(cfg, k0):
+    s = vs_spec_state()
+    _check("vs_sched_init", lib().vs_sched_init(ctypes.byref(cfg), k0, ctypes.byref(s)))
+    return s
+
+
+def vs_sched_update(cfg, state, a, avg_top1, avg_gap):
+    """Updates `state` (a vs_spec_state) in place; returns the next k."""
+    _check("vs_sched_update", lib().vs_sched_update(ctypes.byref(cfg), ctypes.byref(state), a, avg_top1, avg_gap))
+    return state.k
+
+
+def vs_step_sched(model, kv, seqs, cfg, states, d_tokens, d_result, stream):
+    """One scheduled round; `states` is a ctypes array of vs_spec_state,
+    updated in place.  Returns (results [n][VS_RESULT_INTS], conf [n][2])."""
+    n = len(seqs)
+    h_res = (ctypes.c_int32 * (n * VS_RESULT_INTS))()
+    h_conf = (ctypes.c_double * (2 * n))()
+    _check("vs_step_sched", lib().vs_step_sched(model, kv, n, _i32(seqs), ctypes.byref(cfg), states, d_tokens,
+                                                d_result, h_res, h_conf, stream))
+    res = [list(h_res[i * VS_RESULT_INTS:(i + 1) * VS_RESULT_INTS]) for i in range(n)]
+    conf = [(h_conf[2 * i], h_conf[2 * i + 1]) for i in range(n)]
+    return res, conf
 
 
 STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention", "small"]

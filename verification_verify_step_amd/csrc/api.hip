@@ -89,7 +89,7 @@ constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows *
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -126,6 +126,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.dst_amax = take(R * 4);
   w.dst_sum = take(R * 8);
   w.result = take((size_t)S * VS_RESULT_INTS * 4);
+  w.conf = take((size_t)kMaxSeq * 2 * 8);
   w.total = off;
   return w;
 }
@@ -161,7 +162,7 @@ struct vs_model {
   float2* rope;
   int* kvrow;
   int *amax_idx, *tokens, *st_amax, *dst_amax, *result;
-  double *st_sum, *dst_sum;
+  double *st_sum, *dst_sum, *conf;
   int ss_groups = 0;       // groups of the last producer of ss
   int head_groups = 0;     // groups of the last head pass
   int head_rows = 0;
@@ -606,6 +607,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->dst_amax = reinterpret_cast<int*>(w + m->wsl.dst_amax);
   m->dst_sum = reinterpret_cast<double*>(w + m->wsl.dst_sum);
   m->result = reinterpret_cast<int*>(w + m->wsl.result);
+  m->conf = reinterpret_cast<double*>(w + m->wsl.conf);
   // the attention kernel's arrival counters start at zero and every launch
   // leaves them at zero
   hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
@@ -1247,6 +1249,131 @@ vs_status vs_step(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, con
   if ((rc = vs_verify(m, kv, &b, L, d_tokens, m->hidden, m->logits, stream)) != VS_OK) return rc;
   if ((rc = vs_accept(m, &b, mode, temp, d_tokens, m->logits, m->dlogits, d_u, d_result, stream)) != VS_OK) return rc;
   return vs_commit(m, kv, &b, d_result, stream);
+}
+
+// Row map of a chain or tree batch for the per-row kernels (accept, stats).
+static vs_status batch_rows(vs_model* m, const vs_batch* b, const char* name, RowMap* rm) {
+  if (b == nullptr || b->seq == nullptr || b->n_rows == nullptr) return fail(VS_E_INVAL, "%s: null batch", name);
+  if (b->n_seq < 1 || b->n_seq > kMaxSeq) return fail(VS_E_SHAPE, "%s: n_seq %d", name, b->n_seq);
+  memset(rm, 0, sizeof(*rm));
+  rm->n_seq = b->n_seq;
+  int M = 0;
+  for (int i = 0; i < b->n_seq; ++i) {
+    if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows) return fail(VS_E_SHAPE, "%s: rows %d", name, b->n_rows[i]);
+    rm->seq[i] = b->seq[i];
+    rm->row_start[i] = M;
+    M += b->n_rows[i];
+  }
+  rm->row_start[b->n_seq] = M;
+  rm->M = M;
+  rm->mask = b->d_mask;
+  rm->depth = b->d_depth;
+  if (M > m->max_rows) return fail(VS_E_SHAPE, "%s: %d rows exceed max_rows", name, M);
+  return VS_OK;
+}
+
+vs_status vs_confidence(vs_model* m, const vs_batch* b, float temp, const float* d_logits, double* d_conf,
+                        void* stream) {
+  if (m == nullptr || d_logits == nullptr || d_conf == nullptr) return fail(VS_E_INVAL, "vs_confidence: null argument");
+  if (!(temp > 0.f)) return fail(VS_E_INVAL, "vs_confidence: temperature %g", (double)temp);
+  RowMap rm;
+  vs_status rc = batch_rows(m, b, "vs_confidence", &rm);
+  if (rc != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  StatsArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.logits = d_logits;
+  sa.V = m->c.vocab;
+  sa.temp = temp;
+  sa.mx = m->st_mx;
+  sa.amax = m->st_amax;
+  sa.second = m->st_second;
+  sa.sumexp = m->st_sum;
+  timed(m, F_SMALL, (double)rm.M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(sa, rm.M, st); });
+  ConfArgs ca;
+  ca.rows = rm;
+  ca.mx = m->st_mx;
+  ca.second = m->st_second;
+  ca.sumexp = m->st_sum;
+  ca.temp = temp;
+  ca.conf = d_conf;
+  timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_confidence(ca, st); });
+  return check_launch("vs_confidence");
+}
+
+static vs_status check_sched(const vs_sched_cfg* c) {
+  if (c == nullptr) return fail(VS_E_INVAL, "schedule: null config");
+  if (c->min_k < 1 || c->max_k < c->min_k || c->max_k > VS_MAX_K)
+    return fail(VS_E_INVAL, "schedule: draft lengths [%d, %d] outside [1, %d]", c->min_k, c->max_k, VS_MAX_K);
+  if (!(c->low < c->high)) return fail(VS_E_INVAL, "schedule: thresholds %g >= %g", c->low, c->high);
+  return VS_OK;
+}
+
+vs_status vs_sched_init(const vs_sched_cfg* c, int32_t k0, vs_spec_state* s) {
+  vs_status rc = check_sched(c);
+  if (rc != VS_OK) return rc;
+  if (s == nullptr) return fail(VS_E_INVAL, "vs_sched_init: null state");
+  s->ema = 0.5;
+  s->k = std::min(c->max_k, std::max(c->min_k, k0));
+  s->rounds = 0;
+  s->last_a = -1;
+  return VS_OK;
+}
+
+vs_status vs_sched_update(const vs_sched_cfg* c, vs_spec_state* s, int32_t a, double avg_top1, double avg_gap) {
+#pragma clang fp contract(off)
+  vs_status rc = check_sched(c);
+  if (rc != VS_OK) return rc;
+  if (s == nullptr) return fail(VS_E_INVAL, "vs_sched_update: null state");
+  if (a < 0 || a > s->k) return fail(VS_E_INVAL, "vs_sched_update: %d accepted of %d drafts", a, s->k);
+  if (!std::isfinite(avg_top1) || !std::isfinite(avg_gap))
+    return fail(VS_E_INVAL, "vs_sched_update: confidence inputs not finite");
+  const double acc = (double)a / (double)s->k;
+  s->ema = 0.2 * acc + 0.8 * s->ema;
+  const double C = 0.4 * avg_top1 + 0.3 * std::fmin(avg_gap * 5.0, 1.0) + 0.3 * s->ema;
+  const double x = c->min_k + (c->max_k - c->min_k) * (C - c->low) / (c->high - c->low);
+  int nk = x >= (double)c->max_k ? c->max_k : x <= (double)c->min_k ? c->min_k : (int)x;
+  if (a == 0) nk = c->min_k;  // the first draft was rejected: back to the shortest block at once
+  s->k = nk;
+  s->last_a = a;
+  s->rounds += 1;
+  return VS_OK;
+}
+
+vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const vs_sched_cfg* c,
+                        vs_spec_state* states, int32_t* d_tokens, int32_t* d_result, int32_t* h_result, double* h_conf,
+                        void* stream) {
+  if (m == nullptr || kv == nullptr || seq == nullptr || states == nullptr || h_result == nullptr)
+    return fail(VS_E_INVAL, "vs_step_sched: null argument");
+  vs_status rc = check_sched(c);
+  if (rc != VS_OK) return rc;
+  if (n_seq < 1 || n_seq > kMaxSeq) return fail(VS_E_SHAPE, "vs_step_sched: n_seq %d", n_seq);
+  std::vector<int> k(n_seq), rows(n_seq);
+  for (int i = 0; i < n_seq; ++i) {
+    if (states[i].k < c->min_k || states[i].k > c->max_k)
+      return fail(VS_E_STATE, "vs_step_sched: sequence %d has draft length %d outside the schedule", i, states[i].k);
+    k[i] = states[i].k;
+    rows[i] = k[i] + 1;
+  }
+  if ((rc = vs_step(m, kv, n_seq, seq, k.data(), VS_GREEDY, 1.0f, nullptr, d_tokens, d_result, stream)) != VS_OK)
+    return rc;
+  vs_batch b{n_seq, seq, rows.data(), nullptr, nullptr};
+  if ((rc = vs_confidence(m, &b, 1.0f, m->logits, m->conf, stream)) != VS_OK) return rc;
+  hipStream_t st = S(stream);
+  std::vector<double> conf(2 * n_seq);
+  hipError_t e = hipMemcpyAsync(h_result, d_result, (size_t)n_seq * VS_RESULT_INTS * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(conf.data(), m->conf, conf.size() * 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_sched: %s", hipGetErrorString(e));
+  for (int i = 0; i < n_seq; ++i) {
+    if ((rc = vs_sched_update(c, &states[i], h_result[i * VS_RESULT_INTS], conf[2 * i], conf[2 * i + 1])) != VS_OK)
+      return rc;
+    if (h_conf != nullptr) {
+      h_conf[2 * i] = conf[2 * i];
+      h_conf[2 * i + 1] = conf[2 * i + 1];
+    }
+  }
+  return VS_OK;
 }
 
 vs_status vs_stats_enable(vs_model* m, int32_t on) {

@@ -517,6 +517,29 @@ void launch_commit(const CommitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, a);
 }
 
+// One thread per sequence; its rows are averaged in row order in fp64
+// ("DSpark" page, §2.2: the mean top-1 probability and the mean top-1 minus
+// top-2 gap over the verify block).
+__global__ void confidence_kernel(ConfArgs a) {
+  const int i = threadIdx.x;
+  if (i >= a.rows.n_seq) return;
+  const int r0 = a.rows.row_start[i], r1 = a.rows.row_start[i + 1];
+  const double inv_t = 1.0 / (double)a.temp;
+  double s1 = 0.0, sg = 0.0;
+  for (int r = r0; r < r1; ++r) {
+    const double p1 = 1.0 / a.sumexp[r];
+    const double p2 = exp(((double)a.second[r] - (double)a.mx[r]) * inv_t) / a.sumexp[r];
+    s1 += p1;
+    sg += p1 - p2;
+  }
+  const double n = (double)max(1, r1 - r0);
+  a.conf[2 * i] = s1 / n;
+  a.conf[2 * i + 1] = sg / n;
+}
+void launch_confidence(const ConfArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(confidence_kernel, dim3(1), dim3(kMaxSeq), 0, st, a);
+}
+
 __global__ void advance_kernel(int* P, int* committed, int seq, int dP, int dC) {
   if (threadIdx.x == 0) {
     P[seq] += dP;

@@ -110,6 +110,18 @@ struct CommitArgs {
   int n_layers, Hkv, hd;
 };
 
+// Target-model confidence of each sequence's verify rows: the mean over its
+// rows of p_top1 and of p_top1 - p_top2 under softmax(z / temp), from the
+// row statistics (max, second largest value, sum of exp((z - max) / temp)).
+struct ConfArgs {
+  RowMap rows;
+  const float* mx;
+  const float* second;
+  const double* sumexp;
+  float temp;
+  double* conf;           // [n_seq][2]
+};
+
 // Tree drafting state (one sequence).  Nodes are numbered in creation order
 // (root = 0); the verify rows are the root and the kept nodes in level order.
 constexpr int kTreeNodes = 1024;
@@ -159,5 +171,6 @@ void launch_accept(const AcceptArgs& a, hipStream_t st);
 void launch_compact(const CommitArgs& a, hipStream_t st);
 void launch_commit(const CommitArgs& a, hipStream_t st);
 void launch_advance(int* P, int* committed, int seq, int dP, int dC, hipStream_t st);
+void launch_confidence(const ConfArgs& a, hipStream_t st);
 
 }  // namespace vs
