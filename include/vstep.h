@@ -133,6 +133,14 @@ vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id)
  * P + 1), as after a prefill of P + 1 tokens.  For a freshly opened
  * sequence; P below its capacity. */
 vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream);
+/* Rewind a sequence that holds a context to its first P positions: KV of
+ * slots 0..P-1 is kept as it is, `pending` becomes the token at position P
+ * (no KV), committed = P + 1, and later slots become garbage.  P must not
+ * exceed the sequence's current KV length (the host checks it against its
+ * upper bound of that length; a P between the true length and that bound
+ * leaves garbage slots below P).  Errors: VS_E_STATE (not open, no context),
+ * VS_E_NOKV (P beyond the bound), VS_E_INVAL (token id). */
+vs_status vs_seq_rewind(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream);
 vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
 /* Device pointers of the per-sequence state arrays [max_seqs]:
  * P (KV length), pending token, committed count (read-only for callers). */

@@ -8,7 +8,11 @@ outputs: one verify layer of three requests (shortest, middle, longest
 context) from the GPU's layer input and committed KV, the head on sampled
 rows, and the greedy accept of every request on the GPU's logits; draft
 tokens are the argmax of their draft logits, and the draft's first-L KV
-matches a batched first-L pass within bf16 rounding."""
+matches a batched first-L pass within bf16 rounding.  Rounds: the
+confidence-scheduled draft length over several rounds of the whole batch
+(starting from the drawn K_r), against plain greedy AR from the same
+contexts, on this model and on a calibrated one (upper-layer W_o and W_down
+zeroed so every draft is accepted, LM head x4 so the confidence is high)."""
 import numpy as np
 import pytest
 import torch
@@ -30,14 +34,16 @@ N = len(CTX)
 ROWS = [k + 1 for k in KS]
 M = sum(ROWS)
 START = np.concatenate([[0], np.cumsum(ROWS)]).astype(int)
-MAX_CTX = max(CTX) + 64
+MAX_CTX = max(CTX) + 160
+ROUNDS = 3
 
 
 @pytest.fixture(scope="module")
 def ctx():
     bps = (MAX_CTX + 15) // 16 + 2
-    n_blocks = sum((c + 64 + 15) // 16 for c in CTX) + 16
-    e = G.engine(CFG, max_rows=M, max_seqs=N, max_ctx=MAX_CTX, n_blocks=n_blocks, max_blocks_per_seq=bps)
+    n_blocks = sum((c + 160 + 15) // 16 for c in CTX) + 16
+    e = G.engine(CFG, max_rows=N * (B.VS_MAX_K + 1), max_seqs=N, max_ctx=MAX_CTX, n_blocks=n_blocks,
+                 max_blocks_per_seq=bps)
     st = e.stream
     for layer in range(CFG.n_layers):
         K, V, _ = e.kv_layer(layer)
@@ -45,7 +51,7 @@ def ctx():
         synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 1), V.numel(), V.data_ptr(), st, std=1.0)
     seqs = []
     for i in range(N):
-        s = e.open(CTX[i] + 48)
+        s = e.open(CTX[i] + 150)
         B.vs_seq_assume(e.kv, s, CTX[i], PEND[i], st)
         seqs.append(s)
     torch.cuda.synchronize()
@@ -172,3 +178,103 @@ def test_ragged_draft(ctx):
                 err, scale = np.abs(x1 - x2).max(), np.abs(x1).max()
                 assert err <= 1e-2 * scale, (i, l, err, scale)
                 assert np.mean(x1 == x2) > 0.5, (i, l, np.mean(x1 == x2))
+
+
+def _reset(e, seqs):
+    """Back to the drawn contexts: the committed KV below P was never written
+    by the rounds, so rewinding P and the pending token restores the start."""
+    for i, s in enumerate(seqs):
+        B.vs_seq_rewind(e.kv, s, CTX[i], PEND[i], e.stream)
+    torch.cuda.synchronize()
+
+
+def _scheduled(e, seqs, rounds):
+    cfg = B.sched_cfg()
+    states = (B.vs_spec_state * N)()
+    for i in range(N):
+        states[i] = B.vs_sched_init(cfg, int(KS[i]))
+    mirror = [spec.SchedState(int(KS[i])) for i in range(N)]
+    toks = torch.zeros(N * (B.VS_MAX_K + 1), dtype=torch.int32, device="cuda")
+    res = torch.zeros((N, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    out = [[int(PEND[i])] for i in range(N)]
+    ks, accs = [], []
+    for r in range(rounds):
+        k_round = [states[i].k for i in range(N)]
+        got, conf = B.vs_step_sched(e.model, e.kv, seqs, cfg, states, toks.data_ptr(), res.data_ptr(), e.stream)
+        t = toks.cpu().numpy()
+        P, pending, committed = e.state()
+        r0 = 0
+        for i, s in enumerate(seqs):
+            a, y = got[i][0], got[i][1]
+            out[i] += [int(x) for x in t[r0 + 1:r0 + a + 1]] + [y]
+            r0 += k_round[i] + 1
+            assert P[s] == CTX[i] + len(out[i]) - 1 and pending[s] == y and committed[s] == P[s] + 1
+            nk, _ = spec.schedule_update(mirror[i], a, conf[i][0], conf[i][1])
+            assert states[i].k == nk and states[i].ema == mirror[i].ema, (r, i)
+        ks.append(k_round)
+        accs.append([got[i][0] for i in range(N)])
+    return out, ks, accs
+
+
+def _greedy_ar(e, seqs, n_new):
+    """Plain greedy AR of every request: the pending tokens through all layers
+    as one batch of single rows per step.  Returns tokens and logits rows."""
+    batch = B.make_batch(seqs, [1] * N)
+    z = torch.empty((N, CFG.vocab), dtype=torch.float32, device="cuda")
+    res = torch.zeros((N, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    out = [[int(PEND[i])] for i in range(N)]
+    zs = [[] for _ in range(N)]
+    for step in range(n_new):
+        pend = G.i32([e.state()[1][s] for s in seqs])
+        B.vs_verify(e.model, e.kv, batch, 0, pend.data_ptr(), None, z.data_ptr(), e.stream)
+        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, pend.data_ptr(), z.data_ptr(), None, None, res.data_ptr(),
+                    e.stream)
+        B.vs_commit(e.model, e.kv, batch, res.data_ptr(), e.stream)
+        zh = z.cpu().numpy()
+        for i, (a, y, _, _) in enumerate(G.result_rows(res, N)):
+            out[i].append(y)
+            zs[i].append(zh[i])
+    return out, zs
+
+
+def _compare_with_ar(e, seqs, out, head_scale=1.0):
+    n_new = max(len(o) for o in out) - 1
+    _reset(e, seqs)
+    ar, zs = _greedy_ar(e, seqs, n_new)
+    for i in range(N):
+        tie = next((j for j in range(len(out[i]) - 1) if G.near_tie(zs[i][j], head_scale)), len(out[i]) - 1)
+        assert out[i][:tie + 1] == ar[i][:tie + 1], (i, tie, out[i], ar[i])
+
+
+def test_scheduled_rounds_equal_ar(ctx):
+    """Three scheduled rounds of the 32 requests from their drawn K_r.  On
+    this random-weight model the target's distributions are nearly flat and
+    drafts are rejected, so k drops to 2 after the first round; the committed
+    tokens equal greedy AR from the same contexts."""
+    e, seqs = ctx["e"], ctx["seqs"]
+    _reset(e, seqs)
+    out, ks, accs = _scheduled(e, seqs, ROUNDS)
+    assert ks[0] == [int(k) for k in KS]
+    _compare_with_ar(e, seqs, out)
+
+
+def test_scheduled_rounds_calibrated(ctx):
+    """The calibrated model: W_o and W_down of the verify layers zeroed (the
+    target equals the draft, every draft is accepted) and the LM head scaled
+    by 4 (confident distributions): k climbs to the top of its range, and the
+    committed tokens still equal greedy AR of the same model.  The last test
+    of the module: it changes the weights."""
+    import synth
+    from synth import gpu_weights
+    e, seqs = ctx["e"], ctx["seqs"]
+    for l in range(CFG.exit_layer, CFG.n_layers):
+        for t in (synth.T_WO, synth.T_W_DOWN):
+            e.set_tensor(t, l, gpu_weights.device_bits(CFG, t, l, e.device, e.stream, eps=0.0))
+    e.set_tensor(synth.T_HEAD, 0, gpu_weights.device_bits(CFG, synth.T_HEAD, 0, e.device, e.stream, head_scale=4.0))
+    torch.cuda.synchronize()
+    _reset(e, seqs)
+    out, ks, accs = _scheduled(e, seqs, ROUNDS)
+    for r in range(ROUNDS):
+        assert accs[r] == ks[r], (r, accs[r], ks[r])  # target == draft: everything accepted
+    assert max(ks[-1]) == B.VS_MAX_K and np.mean(ks[-1]) > np.mean(ks[0]), (ks[0], ks[-1])
+    _compare_with_ar(e, seqs, out, head_scale=4.0)

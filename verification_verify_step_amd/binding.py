@@ -18,7 +18,7 @@ VS_MAX_PASS_ROWS = 1088
 
 EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
-    "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
+    "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_commit",
     "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_stats_enable", "vs_stats_read",
     "vs_stats_reset",
@@ -87,6 +87,7 @@ def lib():
             "vs_kv_destroy": (None, [VP]),
             "vs_seq_open": (I32, [VP, I32, VP, pI]),
             "vs_seq_assume": (I32, [VP, I32, I32, I32, VP]),
+            "vs_seq_rewind": (I32, [VP, I32, I32, I32, VP]),
             "vs_seq_close": (I32, [VP, I32]),
             "vs_kv_state": (I32, [VP, P(VP), P(VP), P(VP)]),
             "vs_kv_layer": (I32, [VP, I32, P(VP), P(VP), P(VP)]),
@@ -175,6 +176,10 @@ def vs_seq_open(kv, max_len, stream):
 
 def vs_seq_assume(kv, seq, P, pending, stream):
     _check("vs_seq_assume", lib().vs_seq_assume(kv, seq, P, pending, stream))
+
+
+def vs_seq_rewind(kv, seq, P, pending, stream):
+    _check("vs_seq_rewind", lib().vs_seq_rewind(kv, seq, P, pending, stream))
 
 
 def vs_seq_close(kv, seq):

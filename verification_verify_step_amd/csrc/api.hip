@@ -794,6 +794,20 @@ vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void
   return VS_OK;
 }
 
+vs_status vs_seq_rewind(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream) {
+  if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_rewind: null argument");
+  if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_seq_rewind: sequence %d is not open", seq);
+  if (!kv->prefilled[seq]) return fail(VS_E_STATE, "vs_seq_rewind: sequence %d holds no context", seq);
+  if (P < 0 || P > kv->P_ub[seq])
+    return fail(VS_E_NOKV, "vs_seq_rewind: length %d beyond the sequence's %d", P, kv->P_ub[seq]);
+  if (pending < 0 || pending >= kv->m->c.vocab) return fail(VS_E_INVAL, "vs_seq_rewind: pending token %d", pending);
+  launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, S(stream));
+  vs_status rc = check_launch("vs_seq_rewind");
+  if (rc != VS_OK) return rc;
+  kv->P_ub[seq] = P;
+  return VS_OK;
+}
+
 vs_status vs_seq_close(vs_kv* kv, int32_t seq_id) {
   if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_close: null argument");
   if (seq_id < 0 || seq_id >= kv->max_seqs || !kv->open[seq_id])
