@@ -124,7 +124,7 @@ def cpu_baseline(w, P, n_layers_sample):
     # repeat the sample until about 10 s of oracle work have been timed
     tv, td, th6, th1 = [], [], [], []
     spent, reps = 0.0, 0
-    while spent < 10.0 and reps < 40:
+    while spent < 10.0 and reps < 400:
         for l in verify_layers:
             t0 = time.perf_counter()
             dec.layer(l, cache, rows6, h6)
@@ -153,6 +153,33 @@ def cpu_baseline(w, P, n_layers_sample):
                        f"round = {k + 1}x{c.exit_layer} draft layers + {k} draft heads + {nv} verify layers + "
                        f"1 verify head, one committed token per round as on the GPU (acceptance ~0)"),
             "round_s": round_s, "verify_step_s": nv * t_v + t_h6, "timed_s": spent}
+
+
+def scheduled_rounds(e, B, open_prefilled, k0, steps, warmup):
+    """Greedy rounds of one sequence whose draft length follows the
+    confidence schedule (k in [2, 16], starting at k0): committed tokens per
+    second over `steps` rounds after `warmup` rounds, and the k it used."""
+    import torch
+    s = open_prefilled()
+    cfg = B.sched_cfg()
+    states = (B.vs_spec_state * 1)()
+    states[0] = B.vs_sched_init(cfg, k0)
+    toks = torch.empty(B.VS_MAX_K + 1, dtype=torch.int32, device="cuda")
+    res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        B.vs_step_sched(e.model, e.kv, [s], cfg, states, toks.data_ptr(), res.data_ptr(), e.stream)
+    P0 = e.state()[0][s]
+    ks = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ks.append(states[0].k)
+        B.vs_step_sched(e.model, e.kv, [s], cfg, states, toks.data_ptr(), res.data_ptr(), e.stream)
+    dt = time.perf_counter() - t0
+    P1 = e.state()[0][s]
+    B.vs_seq_close(e.kv, s)
+    return {"tokens_per_s": (P1 - P0) / dt, "tokens_per_round": (P1 - P0) / steps, "mean_k": sum(ks) / len(ks),
+            "k_first": ks[0], "k_last": ks[-1], "note": "k from the confidence schedule, starting at the bench k; "
+            "each round reads its result and confidence back to the host"}
 
 
 def main():
@@ -301,6 +328,8 @@ def main():
         torch.cuda.synchronize()
         out["ar_tokens_per_s"] = args.steps / (time.perf_counter() - a0)
         B.vs_seq_close(e.kv, sB)
+        # confidence-scheduled draft length ("DSpark" page, §2.2-§2.3) from k = 5
+        out["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
         # acceptance-calibrated synthetic model: W_o, W_down of layers >= L
         # scaled by 0 (same bytes, target == draft, every draft accepted)
         for l in range(c.exit_layer, c.n_layers):
@@ -322,6 +351,14 @@ def main():
         Pc2 = e.state()[0][sC]
         out["calibrated_alpha1"] = {"tokens_per_s": (Pc2 - Pc) / dt, "tokens_per_round": (Pc2 - Pc) / n_cal,
                                     "note": "synthetic model with upper-layer W_o and W_down zeroed (same bytes)"}
+        B.vs_seq_close(e.kv, sC)
+        out["calibrated_alpha1"]["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        # the same with the LM head x4: sharper distributions (the same argmax,
+        # so the same tokens), so the schedule sees a confident target
+        e.set_tensor(synth.T_HEAD, 0, gpu_weights.device_bits(c, synth.T_HEAD, 0, e.device, st, head_scale=4.0))
+        sched4 = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        sched4["note"] = "as above with the LM head scaled by 4 (same argmax everywhere)"
+        out["calibrated_alpha1"]["scheduled_head_x4"] = sched4
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, P0, args.cpu_layers)
     print(json.dumps(out))
