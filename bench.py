@@ -182,6 +182,48 @@ def scheduled_rounds(e, B, open_prefilled, k0, steps, warmup):
             "each round reads its result and confidence back to the host"}
 
 
+def dynamic_rounds(e, B, open_prefilled, k0, steps, warmup, c_draft):
+    """Greedy rounds of one sequence under the windowed dynamic k with the
+    context-cost cut-off at c_draft; a round with k = 0 is a plain decoding
+    step (the pending token through all layers).  Committed tokens per second
+    over `steps` rounds after `warmup` rounds, and the k it used."""
+    import torch
+    s = open_prefilled()
+    cfg = B.dynk_cfg()
+    st = B.vs_dynk_init(cfg, k0)
+    toks = torch.empty(B.VS_MAX_K + 1, dtype=torch.int32, device="cuda")
+    res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    z = torch.empty((1, e.cfg.vocab), dtype=torch.float32, device="cuda")
+    b1 = B.make_batch([s], [1])
+    pend = B.vs_kv_state(e.kv)[1] + 4 * s
+    state = {"k": st.k}
+
+    def one():
+        k = state["k"]
+        if k > 0:
+            B.vs_step(e.model, e.kv, [s], [k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), res.data_ptr(), e.stream)
+        else:
+            B.vs_verify(e.model, e.kv, b1, 0, pend, None, z.data_ptr(), e.stream)
+            B.vs_accept(e.model, b1, B.VS_GREEDY, 1.0, pend, z.data_ptr(), None, None, res.data_ptr(), e.stream)
+            B.vs_commit(e.model, e.kv, b1, res.data_ptr(), e.stream)
+        a = int(res[0, 0].item())  # the host needs a to pick the next k
+        state["k"] = B.vs_dynk_update(cfg, st, a, k, c_draft)
+        return k
+
+    for _ in range(warmup):
+        one()
+    P0 = e.state()[0][s]
+    t0 = time.perf_counter()
+    ks = [one() for _ in range(steps)]
+    dt = time.perf_counter() - t0
+    P1 = e.state()[0][s]
+    B.vs_seq_close(e.kv, s)
+    return {"tokens_per_s": (P1 - P0) / dt, "tokens_per_round": (P1 - P0) / steps, "mean_k": sum(ks) / len(ks),
+            "plain_steps": ks.count(0), "c_draft": c_draft,
+            "note": "windowed dynamic k (64 rounds, 0.85 / 0.7, k in [2, 8]) from the bench k, cut off by the "
+                    "speedup E(k)/(c k + 1) with c = exit layer / layers; k = 0 rounds are plain decoding steps"}
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -330,6 +372,9 @@ def main():
         B.vs_seq_close(e.kv, sB)
         # confidence-scheduled draft length ("DSpark" page, §2.2-§2.3) from k = 5
         out["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        # windowed dynamic k with the context-cost cut-off (self-speculative page, §3.2, §5.3)
+        out["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
+                                          c.exit_layer / c.n_layers)
         # acceptance-calibrated synthetic model: W_o, W_down of layers >= L
         # scaled by 0 (same bytes, target == draft, every draft accepted)
         for l in range(c.exit_layer, c.n_layers):
@@ -353,6 +398,8 @@ def main():
                                     "note": "synthetic model with upper-layer W_o and W_down zeroed (same bytes)"}
         B.vs_seq_close(e.kv, sC)
         out["calibrated_alpha1"]["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        out["calibrated_alpha1"]["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
+                                                               c.exit_layer / c.n_layers)
         # the same with the LM head x4: sharper distributions (the same argmax,
         # so the same tokens), so the schedule sees a confident target
         e.set_tensor(synth.T_HEAD, 0, gpu_weights.device_bits(c, synth.T_HEAD, 0, e.device, st, head_scale=4.0))

@@ -260,6 +260,37 @@ typedef struct vs_spec_state {
 vs_status vs_sched_init(const vs_sched_cfg* c, int32_t k0, vs_spec_state* s);
 vs_status vs_sched_update(const vs_sched_cfg* c, vs_spec_state* s, int32_t a, double avg_top1, double avg_gap);
 
+/* Windowed dynamic draft length with a context-cost cut-off (self-speculative
+ * decoding page, §3.2 and §5.3), host code only.  The state keeps the last
+ * `window` rounds' (accepted, drafted) counts; alpha = sum accepted / sum
+ * drafted over them.  After each round with drafts:
+ *   alpha > up   -> k + 1,   alpha < down -> k - 1,   k kept in [min_k, max_k]
+ * (the controller's k).  When c_draft > 0 (the cost of one draft step over
+ * one full forward at the current context) the next round's draft length is
+ * min(controller k, k_c) with k_c = the k in [1, max_k] that maximises
+ * E(k) / (c_draft * k + 1), E(k) = (1 - alpha^(k+1)) / (1 - alpha) (the
+ * smallest such k on ties); when k_c < min_k, or no k gives a speedup above
+ * 1, the next round is a plain decoding step (*k_next = 0), which leaves the
+ * window unchanged.  Errors: VS_E_INVAL for a bad config (1 <= window <=
+ * VS_DYNK_MAX_WINDOW, 1 <= min_k <= max_k <= VS_MAX_K, down <= up), a
+ * outside [0, k_used] or a negative k_used; the state is unchanged on error. */
+#define VS_DYNK_MAX_WINDOW 256
+typedef struct vs_dynk_cfg {
+  int32_t window;       /* 64 */
+  int32_t min_k, max_k; /* 2, 8 */
+  double up, down;      /* 0.85, 0.7 */
+} vs_dynk_cfg;
+typedef struct vs_dynk_state {
+  int32_t k;                            /* the controller's draft length */
+  int32_t n, head;                      /* rounds in the window, next slot */
+  int32_t a[VS_DYNK_MAX_WINDOW];        /* accepted drafts per round */
+  int32_t drafted[VS_DYNK_MAX_WINDOW];  /* drafts per round */
+  double alpha;                         /* window acceptance (1 before any round) */
+} vs_dynk_state;
+vs_status vs_dynk_init(const vs_dynk_cfg* c, int32_t k0, vs_dynk_state* s);
+vs_status vs_dynk_update(const vs_dynk_cfg* c, vs_dynk_state* s, int32_t a, int32_t k_used, double c_draft,
+                         int32_t* k_next);
+
 /* One greedy chain round of n_seq requests with per-request draft lengths
  * states[i].k (vs_step), then vs_confidence over each request's k+1 verify
  * rows, then vs_sched_update of every state.  Blocks until the round is done:

@@ -270,3 +270,40 @@ def generate_scheduled(dec, cache, sid, prompt, n_new, k0, **sched):
         ks.append(k)
         confs.append((top1, gap, C, a))
     return st.tokens[len(prompt):len(prompt) + n_new], ks, confs, state
+
+
+@dataclass
+class DynKState:
+    """Windowed dynamic draft length (self-speculative decoding page, §3.2):
+    the controller's k and the (accepted, drafted) counts of recent rounds."""
+    k: int
+    window: list = field(default_factory=list)
+    alpha: float = 1.0
+
+
+DYNK = dict(window=64, min_k=2, max_k=8, up=0.85, down=0.7)
+
+
+def dynk_update(state, a, k_used, c_draft=0.0, window=64, min_k=2, max_k=8, up=0.85, down=0.7):
+    """After a round that drafted k_used tokens and kept a of them: the
+    window's acceptance alpha = accepted / drafted over the last `window`
+    rounds; alpha above `up` adds one to k, below `down` takes one away, k
+    stays in [min_k, max_k] (§3.2; read as a check every round, like additive
+    increase / decrease).  With a draft cost c_draft > 0 (one draft step over
+    one full forward, §3.2 and §5.3), the next round drafts at most the k that
+    maximises E(k) / (c k + 1); if that k is below min_k, or no k beats plain
+    decoding, the next round is a plain decoding step (returns 0, §5.3).  A
+    round without drafts leaves the window as it is."""
+    if k_used > 0:
+        state.window = (state.window + [(a, k_used)])[-window:]
+        state.alpha = sum(x for x, _ in state.window) / sum(y for _, y in state.window)
+        if state.alpha > up:
+            state.k = min(max_k, state.k + 1)
+        elif state.alpha < down:
+            state.k = max(min_k, state.k - 1)
+    k_next = state.k
+    if c_draft > 0:
+        sp = {k: formulas.speedup_layer_skip(state.alpha, k, c_draft) for k in range(1, max_k + 1)}
+        best = max(sp, key=lambda k: (sp[k], -k))
+        k_next = 0 if (sp[best] <= 1.0 or best < min_k) else min(k_next, best)
+    return k_next

@@ -1,5 +1,7 @@
-"""Confidence-scheduled draft lengths over several rounds of a ragged batch
-("DSpark" page, §2.2-§2.3), through the C ABI, on the tiny decoder with
+"""Draft-length policies over several rounds, through the C ABI, on the tiny
+decoder.
+
+The confidence schedule ("DSpark" page, §2.2-§2.3) over a ragged batch, with
 W_o and W_down of the verify layers scaled by 0.5 (a synthetic model whose
 drafts are sometimes accepted) and the LM head scaled by 16 (sharper output
 distributions, the same argmax everywhere, so that the confidence, and with
@@ -10,7 +12,12 @@ it k, moves over its range).  Per round and request:
   are in step;
 * the committed tokens equal the oracle's greedy tokens (the method is
   lossless whatever k is) up to the first near-tie, and the k sequence equals
-  the oracle's until a decision lands within reach of rounding."""
+  the oracle's until a decision lands within reach of rounding.
+
+The windowed dynamic k with its context-cost cut-off (self-speculative
+decoding page, §3.2 and §5.3) over one request: the library's controller
+against the oracle's on the GPU's accepted counts, and the tokens against the
+oracle's greedy tokens, including the plain decoding steps it switches to."""
 import numpy as np
 import pytest
 import torch
@@ -116,3 +123,65 @@ def test_scheduled_rounds(eng):
     assert compared >= 2 * N_REQ
     for s in seqs:
         B.vs_seq_close(e.kv, s)
+
+
+@pytest.mark.parametrize("eps", [0.0, None])
+def test_dynamic_k_rounds(eps):
+    """Twelve rounds of one request with the windowed dynamic k and the
+    context-cost cut-off at c = L/N = 0.5 (the draft's share of the layers):
+    each next k equals the oracle controller fed the GPU's accepted counts; a
+    round with k = 0 is a plain decoding step.  With every draft accepted
+    (eps = 0) k climbs to 8; on the random model (drafts rejected) drafting
+    switches off.  The tokens equal the oracle's greedy tokens throughout."""
+    e = G.engine(CFG, eps=eps, force_host=True, max_rows=64, max_seqs=2, max_ctx=512)
+    p = G.prompt(CFG, 48, req=30)
+    seq = e.open(480)
+    t = G.i32(p)
+    B.vs_prefill(e.model, e.kv, seq, t.data_ptr(), len(p), B.VS_GREEDY, 1.0, None, None, e.stream)
+    torch.cuda.synchronize()
+    c_draft = CFG.exit_layer / CFG.n_layers
+    cfg = B.dynk_cfg()
+    lib = B.vs_dynk_init(cfg, 4)
+    ora = spec.DynKState(4)
+    toks = torch.zeros(B.VS_MAX_K + 1, dtype=torch.int32, device="cuda")
+    res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    z = torch.empty((1, CFG.vocab), dtype=torch.float32, device="cuda")
+    batch1 = B.make_batch([seq], [1])
+    pend_ptr = B.vs_kv_state(e.kv)[1] + 4 * seq
+    out = [e.state()[1][seq]]
+    k_next, ks = 4, []
+    for r in range(12):
+        ks.append(k_next)
+        if k_next > 0:
+            B.vs_step(e.model, e.kv, [seq], [k_next], B.VS_GREEDY, 1.0, None, toks.data_ptr(), res.data_ptr(),
+                      e.stream)
+            a, y, _, _ = G.result_rows(res, 1)[0]
+            out += [int(x) for x in toks[1:a + 1].cpu().tolist()] + [y]
+            k_used = k_next
+        else:
+            B.vs_verify(e.model, e.kv, batch1, 0, pend_ptr, None, z.data_ptr(), e.stream)
+            B.vs_accept(e.model, batch1, B.VS_GREEDY, 1.0, pend_ptr, z.data_ptr(), None, None, res.data_ptr(),
+                        e.stream)
+            B.vs_commit(e.model, e.kv, batch1, res.data_ptr(), e.stream)
+            a, y, _, _ = G.result_rows(res, 1)[0]
+            out.append(y)
+            k_used = 0
+        P, pending, committed = e.state()
+        assert P[seq] == len(p) + len(out) - 1 and pending[seq] == y and committed[seq] == P[seq] + 1
+        k_next = B.vs_dynk_update(cfg, lib, a, k_used, c_draft)
+        assert k_next == spec.dynk_update(ora, a, k_used, c_draft) and lib.k == ora.k and lib.alpha == ora.alpha
+    if eps == 0.0:
+        assert max(ks) == 8 and ks[:5] == [4, 5, 6, 7, 8], ks
+    else:
+        assert 0 in ks, ks
+    dec = G.oracle_decoder(CFG, eps=eps)
+    cache = KVCache(CFG, 512)
+    st, z0 = spec.prefill(dec, cache, 0, p)
+    ref, zs = [st.pending], [z0]
+    while len(ref) < len(out):
+        y, zz = spec.ar_step(dec, cache, st)
+        ref.append(y)
+        zs.append(zz)
+    tie = next((j for j in range(len(out)) if G.near_tie(zs[j])), len(out))
+    assert out[:tie + 1] == ref[:tie + 1], (tie, out, ref)
+    B.vs_seq_close(e.kv, seq)

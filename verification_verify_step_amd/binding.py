@@ -13,6 +13,7 @@ VS_OK, VS_E_INVAL, VS_E_SHAPE, VS_E_NOKV, VS_E_STATE, VS_E_DEVICE = 0, -1, -2, -
 VS_GREEDY, VS_SAMPLE = 0, 1
 VS_MAX_ROWS, VS_MAX_SEQS, VS_MAX_K, VS_N_UNIFORMS, VS_RESULT_INTS = 64, 64, 16, 48, 24
 VS_MAX_PASS_ROWS = 1088
+VS_DYNK_MAX_WINDOW = 256
 (VS_T_EMBED, VS_T_ATTN_NORM, VS_T_WQ, VS_T_WK, VS_T_WV, VS_T_WO, VS_T_FFN_NORM, VS_T_W_GATE, VS_T_W_UP, VS_T_W_DOWN,
  VS_T_FINAL_NORM, VS_T_HEAD) = range(12)
 
@@ -20,7 +21,8 @@ EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
     "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_commit",
-    "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_stats_enable", "vs_stats_read",
+    "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_dynk_init",
+    "vs_dynk_update", "vs_stats_enable", "vs_stats_read",
     "vs_stats_reset",
 ]
 
@@ -51,6 +53,17 @@ class vs_sched_cfg(ctypes.Structure):
 class vs_spec_state(ctypes.Structure):
     _fields_ = [("ema", ctypes.c_double), ("k", ctypes.c_int32), ("rounds", ctypes.c_int32),
                 ("last_a", ctypes.c_int32)]
+
+
+class vs_dynk_cfg(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("min_k", ctypes.c_int32), ("max_k", ctypes.c_int32),
+                ("up", ctypes.c_double), ("down", ctypes.c_double)]
+
+
+class vs_dynk_state(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("n", ctypes.c_int32), ("head", ctypes.c_int32),
+                ("a", ctypes.c_int32 * VS_DYNK_MAX_WINDOW), ("drafted", ctypes.c_int32 * VS_DYNK_MAX_WINDOW),
+                ("alpha", ctypes.c_double)]
 
 
 class vs_kernel_stat(ctypes.Structure):
@@ -105,6 +118,8 @@ def lib():
             "vs_sched_init": (I32, [P(vs_sched_cfg), I32, P(vs_spec_state)]),
             "vs_sched_update": (I32, [P(vs_sched_cfg), P(vs_spec_state), I32, D, D]),
             "vs_step_sched": (I32, [VP, VP, I32, pI, P(vs_sched_cfg), P(vs_spec_state), VP, VP, pI, P(D), VP]),
+            "vs_dynk_init": (I32, [P(vs_dynk_cfg), I32, P(vs_dynk_state)]),
+            "vs_dynk_update": (I32, [P(vs_dynk_cfg), P(vs_dynk_state), I32, I32, D, pI]),
             "vs_stats_enable": (I32, [VP, I32]),
             "vs_stats_read": (I32, [VP, P(vs_kernel_stat), I32, pI]),
             "vs_stats_reset": (I32, [VP]),
@@ -288,6 +303,25 @@ def vs_step_sched(model, kv, seqs, cfg, states, d_tokens, d_result, stream):
     res = [list(h_res[i * VS_RESULT_INTS:(i + 1) * VS_RESULT_INTS]) for i in range(n)]
     conf = [(h_conf[2 * i], h_conf[2 * i + 1]) for i in range(n)]
     return res, conf
+
+
+def dynk_cfg(window=64, min_k=2, max_k=8, up=0.85, down=0.7):
+    return vs_dynk_cfg(window, min_k, max_k, up, down)
+
+
+def vs_dynk_init(cfg, k0):
+    s = vs_dynk_state()
+    _check("vs_dynk_init", lib().vs_dynk_init(ctypes.byref(cfg), k0, ctypes.byref(s)))
+    return s
+
+
+def vs_dynk_update(cfg, state, a, k_used, c_draft=0.0):
+    """Updates `state` in place; returns the next round's draft length (0 =
+    a plain decoding step)."""
+    kn = ctypes.c_int32()
+    _check("vs_dynk_update", lib().vs_dynk_update(ctypes.byref(cfg), ctypes.byref(state), a, k_used, c_draft,
+                                                  ctypes.byref(kn)))
+    return kn.value
 
 
 STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention", "small"]

@@ -1354,6 +1354,68 @@ vs_status vs_sched_update(const vs_sched_cfg* c, vs_spec_state* s, int32_t a, do
   return VS_OK;
 }
 
+static vs_status check_dynk(const vs_dynk_cfg* c) {
+  if (c == nullptr) return fail(VS_E_INVAL, "dynamic k: null config");
+  if (c->window < 1 || c->window > VS_DYNK_MAX_WINDOW)
+    return fail(VS_E_INVAL, "dynamic k: window %d outside [1, %d]", c->window, VS_DYNK_MAX_WINDOW);
+  if (c->min_k < 1 || c->max_k < c->min_k || c->max_k > VS_MAX_K)
+    return fail(VS_E_INVAL, "dynamic k: draft lengths [%d, %d] outside [1, %d]", c->min_k, c->max_k, VS_MAX_K);
+  if (!(c->down <= c->up)) return fail(VS_E_INVAL, "dynamic k: thresholds %g > %g", c->down, c->up);
+  return VS_OK;
+}
+
+vs_status vs_dynk_init(const vs_dynk_cfg* c, int32_t k0, vs_dynk_state* s) {
+  vs_status rc = check_dynk(c);
+  if (rc != VS_OK) return rc;
+  if (s == nullptr) return fail(VS_E_INVAL, "vs_dynk_init: null state");
+  memset(s, 0, sizeof(*s));
+  s->k = std::min(c->max_k, std::max(c->min_k, k0));
+  s->alpha = 1.0;
+  return VS_OK;
+}
+
+vs_status vs_dynk_update(const vs_dynk_cfg* c, vs_dynk_state* s, int32_t a, int32_t k_used, double c_draft,
+                         int32_t* k_next) {
+#pragma clang fp contract(off)
+  vs_status rc = check_dynk(c);
+  if (rc != VS_OK) return rc;
+  if (s == nullptr || k_next == nullptr) return fail(VS_E_INVAL, "vs_dynk_update: null argument");
+  if (k_used < 0 || a < 0 || a > k_used)
+    return fail(VS_E_INVAL, "vs_dynk_update: %d accepted of %d drafts", a, k_used);
+  if (k_used > 0) {  // a speculative round: slide the window, then step k
+    s->a[s->head] = a;
+    s->drafted[s->head] = k_used;
+    s->head = (s->head + 1) % c->window;
+    s->n = std::min(s->n + 1, c->window);
+    int64_t sa = 0, sk = 0;
+    for (int j = 0; j < s->n; ++j) {  // the n most recent rounds, oldest first
+      const int slot = (s->head - s->n + j + 2 * c->window) % c->window;
+      sa += s->a[slot];
+      sk += s->drafted[slot];
+    }
+    s->alpha = (double)sa / (double)sk;
+    if (s->alpha > c->up) s->k = std::min(c->max_k, s->k + 1);
+    else if (s->alpha < c->down) s->k = std::max(c->min_k, s->k - 1);
+  }
+  int kn = s->k;
+  if (c_draft > 0.0) {
+    // k maximising E(k) / (c k + 1), E(k) = (1 - alpha^(k+1)) / (1 - alpha)
+    int best_k = 1;
+    double best = -1.0;
+    for (int k = 1; k <= c->max_k; ++k) {
+      const double e = s->alpha == 1.0 ? (double)(k + 1) : (1.0 - std::pow(s->alpha, k + 1)) / (1.0 - s->alpha);
+      const double sp = e / (c_draft * k + 1.0);
+      if (sp > best) {
+        best = sp;
+        best_k = k;
+      }
+    }
+    kn = (best <= 1.0 || best_k < c->min_k) ? 0 : std::min(kn, best_k);
+  }
+  *k_next = kn;
+  return VS_OK;
+}
+
 vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const vs_sched_cfg* c,
                         vs_spec_state* states, int32_t* d_tokens, int32_t* d_result, int32_t* h_result, double* h_conf,
                         void* stream) {
