@@ -224,6 +224,38 @@ def dynamic_rounds(e, B, open_prefilled, k0, steps, warmup, c_draft):
                     "speedup E(k)/(c k + 1) with c = exit layer / layers; k = 0 rounds are plain decoding steps"}
 
 
+def accept_timing(e, B, seq, M, V, k, reps=50):
+    """Average time of one stochastic accept call over the k+1 rows of one
+    sequence at the full vocabulary: plain, and with the target truncated to
+    its top-0.9 set (seeded normal logits)."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(9)
+    z = torch.from_numpy((rng.standard_normal((M, V)) * 4).astype(np.float32)).cuda()
+    zd = torch.from_numpy((rng.standard_normal((M, V)) * 4).astype(np.float32)).cuda()
+    toks = torch.from_numpy(rng.integers(0, V, M).astype(np.int32)).cuda()
+    u = torch.from_numpy(rng.random(B.VS_N_UNIFORMS)).cuda()
+    res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    b = B.make_batch([seq], [M])
+    out = {}
+    for name, call in (("sample", lambda: B.vs_accept(e.model, b, B.VS_SAMPLE, 1.0, toks.data_ptr(), z.data_ptr(),
+                                                      zd.data_ptr(), u.data_ptr(), res.data_ptr(), e.stream)),
+                       ("top_p_0.9", lambda: B.vs_accept_top_p(e.model, b, 1.0, 0.9, toks.data_ptr(), z.data_ptr(),
+                                                               zd.data_ptr(), u.data_ptr(), res.data_ptr(),
+                                                               e.stream))):
+        call()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            call()
+        t1.record()
+        torch.cuda.synchronize()
+        out[name] = t0.elapsed_time(t1) / reps * 1e3
+    out["rows"] = M
+    return out
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -375,6 +407,8 @@ def main():
         # windowed dynamic k with the context-cost cut-off (self-speculative page, §3.2, §5.3)
         out["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
                                           c.exit_layer / c.n_layers)
+        # stochastic accept of the k+1 verify rows, plain and with a top-p target
+        out["accept_us"] = accept_timing(e, B, seq, M, c.vocab, k)
         # acceptance-calibrated synthetic model: W_o, W_down of layers >= L
         # scaled by 0 (same bytes, target == draft, every draft accepted)
         for l in range(c.exit_layer, c.n_layers):

@@ -217,6 +217,20 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
                     const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
                     void* stream);
 
+/* Stochastic chain accept with a top-p target ("self-speculative" page,
+ * §3.4): the draft keeps its full distribution q (drafts are sampled from
+ * it), the target p = softmax(logits / temp) of each row is truncated to its
+ * top-p set and renormalised there, then the test of vs_accept runs with
+ * that p: accept iff u < min(1, p(d)/q(d)), residual max(0, p - q), bonus
+ * from the last row's truncated p.  The top-p set of a row is the shortest
+ * prefix, in order of (probability desc, id asc), whose probability reaches
+ * top_p.  top_p in (0, 1]; 1 is vs_accept.  Buffers, uniforms and result as
+ * for vs_accept in VS_SAMPLE mode; errors as vs_accept, VS_E_INVAL for
+ * top_p outside (0, 1]. */
+vs_status vs_accept_top_p(vs_model* m, const vs_batch* b, float temp, double top_p, const int32_t* d_tokens,
+                          const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                          void* stream);
+
 /* Commit: P += a + 1, pending = y, committed += a + 1.  For masks that are not
  * chains, first copies the K/V (all layers) of the accepted path rows
  * P + path[i] to slots P + 1 + i. */

@@ -74,6 +74,36 @@ def sample_index(w, u):
     return j
 
 
+def top_p_filter(p, top_p):
+    """The target truncated to its top-p set and renormalised there
+    ("self-speculative" page, §3.4): ids ordered by probability, highest
+    first, lower id first among equals; keep the shortest prefix whose
+    cumulative probability reaches top_p; zero elsewhere."""
+    p = np.asarray(p, dtype=np.float64)
+    order = sorted(range(len(p)), key=lambda j: (-p[j], j))
+    kept, c = [], 0.0
+    for j in order:
+        kept.append(j)
+        c += p[j]
+        if c >= top_p:
+            break
+    out = np.zeros_like(p)
+    out[kept] = p[kept]
+    return out / out.sum()
+
+
+def top_p_margin(p, top_p):
+    """How far the cumulative probabilities around the top-p boundary lie from
+    top_p (a boundary this close may fall one token either way under another
+    summation order)."""
+    p = np.asarray(p, dtype=np.float64)
+    order = sorted(range(len(p)), key=lambda j: (-p[j], j))
+    c = np.cumsum(p[order])
+    n = int(np.searchsorted(c >= top_p, True))
+    lo = abs(c[n - 1] - top_p) if n > 0 else np.inf
+    return min(lo, abs(c[n] - top_p))
+
+
 def chain_rows(sid, P, n, first=0):
     """Rows first..first+n-1 of a chain at P: position = slot = P+i; row i sees
     slots 0..P+i (committed context plus itself and earlier rows)."""

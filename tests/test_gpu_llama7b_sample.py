@@ -134,6 +134,81 @@ def test_head_and_stochastic_accept(ctx):
     assert flagged <= 2
 
 
+def test_top_p_accept(ctx):
+    """Accept with the target truncated to its top-0.9 set, on the verify
+    logits of the 8 requests (full vocabulary) and the draft logits: the
+    decisions equal the oracle's test against top_p_filter(p) with the same
+    uniforms, except flagged near-ties (ratio within 1e-3 of u, or a row
+    whose cumulative probability lies within 1e-9 of 0.9 at the boundary)."""
+    e, batch = ctx["e"], ctx["batch"]
+    Y = _forward(e, batch, CFG.exit_layer, CFG.n_layers, ctx["toks"], ctx["hL"])
+    z = torch.empty((M, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_head(e.model, M, Y.data_ptr(), z.data_ptr(), e.stream)
+    res = torch.zeros((N_REQ, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    du = G.f64(ctx["U"].reshape(-1))
+    top_p = 0.9
+    B.vs_accept_top_p(e.model, batch, T, top_p, ctx["toks"].data_ptr(), z.data_ptr(), ctx["zd"].data_ptr(),
+                      du.data_ptr(), res.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    got = G.result_rows(res, N_REQ)
+    zg = z.cpu().numpy().astype(np.float64)
+    zd = ctx["zd"].cpu().numpy().astype(np.float64)
+    toks = ctx["toks"].cpu().numpy()
+    flagged = 0
+    for i in range(N_REQ):
+        rs = slice(i * (K + 1), (i + 1) * (K + 1))
+        pr_full = [spec.probs(r, T) for r in zg[rs]]
+        if min(spec.top_p_margin(p, top_p) for p in pr_full) < 1e-9:
+            flagged += 1
+            continue
+        pr = [spec.top_p_filter(p, top_p) for p in pr_full]
+        qr = [spec.probs(r, T) for r in zd[rs]]
+        a, y, flags = spec.accept_stochastic_chain(list(toks[rs]), pr, qr, ctx["U"][i])
+        if flags:
+            flagged += 1
+            continue
+        assert (got[i][0], got[i][1]) == (a, y), (i, got[i], a, y)
+        assert pr[min(a, K)][y] > 0 or a < K  # the bonus comes from the truncated target
+    assert flagged <= 2
+
+
+@pytest.mark.parametrize("scale,top_p", [(1.0, 0.9), (4.0, 0.5), (8.0, 0.9), (8.0, 0.99)])
+def test_top_p_set_at_full_vocabulary(ctx, scale, top_p):
+    """The top-p set over 32000 ids, seen through the bonus draw of one-row
+    chains (no drafts): y is the oracle's inverse-CDF draw from the truncated
+    target with the same uniform.  Logits are seeded normals times a scale
+    (flat to sharp distributions, nuclei from a few ids to most of the
+    vocabulary).  Draws within 1e-9 (relative) of a CDF boundary and rows
+    whose cumulative probability lies within 1e-9 of top_p at the set's edge
+    are skipped."""
+    e = ctx["e"]
+    n = N_REQ
+    rng = np.random.default_rng(int(scale * 100 + top_p * 10))
+    zl = (rng.standard_normal((n, CFG.vocab)) * scale).astype(np.float32)
+    z = torch.from_numpy(zl).cuda()
+    U = rng.random((n, B.VS_N_UNIFORMS))
+    batch = B.make_batch(ctx["seqs"], [1] * n)
+    toks = G.i32(np.zeros(n, dtype=np.int32))
+    res = torch.zeros((n, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    B.vs_accept_top_p(e.model, batch, 1.0, top_p, toks.data_ptr(), z.data_ptr(), z.data_ptr(),
+                      G.f64(U.reshape(-1)).data_ptr(), res.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    got = G.result_rows(res, n)
+    checked = 0
+    for i in range(n):
+        p = spec.probs(zl[i].astype(np.float64), 1.0)
+        if spec.top_p_margin(p, top_p) < 1e-9:
+            continue
+        pt = spec.top_p_filter(p, top_p)
+        C = np.cumsum(pt)
+        if np.min(np.abs(C - U[i][spec.SLOT_RESAMPLE] * C[-1])) < CDF_BAND * C[-1]:
+            continue
+        assert got[i][0] == 0 and got[i][1] == spec.sample_index(pt, U[i][spec.SLOT_RESAMPLE]), (i, got[i])
+        assert pt[got[i][1]] > 0
+        checked += 1
+    assert checked >= n - 2
+
+
 def test_verify_confidence(ctx):
     """vs_confidence on the verify logits of the 8 requests (5 rows each, full
     vocabulary) equals the oracle's mean top-1 probability and mean top-1/top-2
@@ -184,6 +259,17 @@ def test_rejection_sampling_chi_square():
     """The first emitted token of a k = 1 round (the draft token if accepted,
     else the residual draw) is distributed as the target p, including ids
     where p or q is zero (1e5 seeded trials, 16 ids)."""
+    _chi_square_first_token(None)
+
+
+def test_rejection_sampling_top_p_chi_square():
+    """The same with the target truncated to its top-0.8 set on the verify
+    side (drafts still from the full q): the first token follows the
+    truncated target, ids outside the set never appear."""
+    _chi_square_first_token(0.8)
+
+
+def _chi_square_first_token(top_p):
     from scipy.stats import chi2
 
     n_seq = 32  # 2 rows each: the 64-row limit of one pass
@@ -196,6 +282,9 @@ def test_rejection_sampling_chi_square():
     zq = np.array([0.2, 1.5, 1.0, 0.5, -np.inf, 0.7, 1.0, 0.0, -np.inf, 2.0, 0.1, 0.3, 0.9, -0.3, 0.5, 1.1],
                   dtype=np.float32)
     p = spec.probs(zp.astype(np.float64), 1.0)
+    if top_p is not None:
+        assert spec.top_p_margin(p, top_p) > 1e-6
+        p = spec.top_p_filter(p, top_p)
     q = spec.probs(zq.astype(np.float64), 1.0)
     zt = torch.from_numpy(np.tile(zp, (2 * n_seq, 1))).cuda()
     zd = torch.from_numpy(np.tile(zq, (2 * n_seq, 1))).cuda()
@@ -209,8 +298,12 @@ def test_rejection_sampling_chi_square():
         toks = np.zeros(2 * n_seq, dtype=np.int32)
         toks[1::2] = d1
         U = rng.random((n_seq, B.VS_N_UNIFORMS))
-        B.vs_accept(e.model, batch, B.VS_SAMPLE, 1.0, G.i32(toks).data_ptr(), zt.data_ptr(), zd.data_ptr(),
-                    G.f64(U.reshape(-1)).data_ptr(), res.data_ptr(), e.stream)
+        if top_p is None:
+            B.vs_accept(e.model, batch, B.VS_SAMPLE, 1.0, G.i32(toks).data_ptr(), zt.data_ptr(), zd.data_ptr(),
+                        G.f64(U.reshape(-1)).data_ptr(), res.data_ptr(), e.stream)
+        else:
+            B.vs_accept_top_p(e.model, batch, 1.0, top_p, G.i32(toks).data_ptr(), zt.data_ptr(), zd.data_ptr(),
+                              G.f64(U.reshape(-1)).data_ptr(), res.data_ptr(), e.stream)
         r = res[:n_seq, :2].cpu().numpy()
         first = np.where(r[:, 0] >= 1, d1, r[:, 1])
         accepted += int((r[:, 0] >= 1).sum())

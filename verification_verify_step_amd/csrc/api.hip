@@ -89,7 +89,7 @@ constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows *
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -127,6 +127,9 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.dst_sum = take(R * 8);
   w.result = take((size_t)S * VS_RESULT_INTS * 4);
   w.conf = take((size_t)kMaxSeq * 2 * 8);
+  w.tp_key = take(R * 4);
+  w.tp_id = take(R * 4);
+  w.tp_mass = take(R * 8);
   w.total = off;
   return w;
 }
@@ -162,7 +165,9 @@ struct vs_model {
   float2* rope;
   int* kvrow;
   int *amax_idx, *tokens, *st_amax, *dst_amax, *result;
-  double *st_sum, *dst_sum, *conf;
+  double *st_sum, *dst_sum, *conf, *tp_mass;
+  unsigned* tp_key;
+  int* tp_id;
   int ss_groups = 0;       // groups of the last producer of ss
   int head_groups = 0;     // groups of the last head pass
   int head_rows = 0;
@@ -608,6 +613,9 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->dst_sum = reinterpret_cast<double*>(w + m->wsl.dst_sum);
   m->result = reinterpret_cast<int*>(w + m->wsl.result);
   m->conf = reinterpret_cast<double*>(w + m->wsl.conf);
+  m->tp_key = reinterpret_cast<unsigned*>(w + m->wsl.tp_key);
+  m->tp_id = reinterpret_cast<int*>(w + m->wsl.tp_id);
+  m->tp_mass = reinterpret_cast<double*>(w + m->wsl.tp_mass);
   // the attention kernel's arrival counters start at zero and every launch
   // leaves them at zero
   hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
@@ -1152,9 +1160,9 @@ vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_lay
   return check_launch("vs_verify");
 }
 
-vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
-                    const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
-                    void* stream) {
+static vs_status accept_impl(vs_model* m, const vs_batch* b, int32_t mode, float temp, double top_p,
+                             const int32_t* d_tokens, const float* d_logits, const float* d_draft_logits,
+                             const double* d_u, int32_t* d_result, void* stream) {
   if (m == nullptr || d_tokens == nullptr || d_logits == nullptr || d_result == nullptr || b == nullptr ||
       b->seq == nullptr || b->n_rows == nullptr)
     return fail(VS_E_INVAL, "vs_accept: null argument");
@@ -1200,8 +1208,26 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
     da.sumexp = m->dst_sum;
     timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(da, M, st); });
   }
+  const bool tp = top_p < 1.0;
+  if (tp) {
+    TopPArgs ta;
+    ta.logits = d_logits;
+    ta.V = m->c.vocab;
+    ta.temp = temp;
+    ta.top_p = top_p;
+    ta.mx = m->st_mx;
+    ta.key = m->tp_key;
+    ta.id = m->tp_id;
+    ta.mass = m->tp_mass;
+    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_top_p(ta, M, st); });
+  }
   AcceptArgs a;
   memset(&a, 0, sizeof(a));
+  if (tp) {
+    a.tp_key = m->tp_key;
+    a.tp_id = m->tp_id;
+    a.tp_mass = m->tp_mass;
+  }
   a.rows = rm;
   a.mode = mode;
   a.temp = temp;
@@ -1218,7 +1244,20 @@ vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, co
   a.u = d_u;
   a.result = d_result;
   timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_accept(a, st); });
-  return check_launch("vs_accept");
+  return check_launch(tp ? "vs_accept_top_p" : "vs_accept");
+}
+
+vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
+                    const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                    void* stream) {
+  return accept_impl(m, b, mode, temp, 1.0, d_tokens, d_logits, d_draft_logits, d_u, d_result, stream);
+}
+
+vs_status vs_accept_top_p(vs_model* m, const vs_batch* b, float temp, double top_p, const int32_t* d_tokens,
+                          const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                          void* stream) {
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(VS_E_INVAL, "vs_accept_top_p: top_p %g outside (0, 1]", top_p);
+  return accept_impl(m, b, VS_SAMPLE, temp, top_p, d_tokens, d_logits, d_draft_logits, d_u, d_result, stream);
 }
 
 vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_result, void* stream) {

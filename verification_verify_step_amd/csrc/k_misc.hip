@@ -280,6 +280,96 @@ void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
   if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
 }
 
+// Order-preserving 32-bit image of a float: a > b as floats iff key(a) >
+// key(b) as unsigned integers (for non-NaN values).
+__device__ __forceinline__ unsigned ord_key(float z) {
+  const unsigned u = __float_as_uint(z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// fp64 sum over a workgroup in a fixed order: lane 0 of each wave takes its
+// wave's butterfly sum, then every thread adds the wave sums in wave order.
+template <int NT>
+__device__ double block_sum_fixed(double v, double* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) s += sh[w];
+  __syncthreads();
+  return s;
+}
+
+// Top-p (nucleus) truncation of the target on the verify side ("self-
+// speculative" page, §3.4: the draft keeps its full distribution, the verify
+// truncates the target and renormalises on the kept set, then the ratio test
+// runs on the full draft distribution).  Tokens are ordered by (logit desc,
+// id asc), i.e. by probability; the kept set is the shortest prefix of that
+// order whose probability reaches top_p.  One workgroup per row holds the row
+// in registers.  A bisection over the 32-bit order keys finds the boundary
+// key (the largest key whose tail mass still reaches top_p), a second one over
+// the ids of the tokens tied at that key finds where the prefix ends among
+// them; each step is one fixed-order fp64 sum over the row.
+__global__ __launch_bounds__(kStatsThreads) void top_p_kernel(TopPArgs a) {
+  __shared__ double sh[kStatsThreads / 64];
+  const int m = blockIdx.x;
+  const float* z = a.logits + (size_t)m * a.V;
+  const int j0 = threadIdx.x * kStatsPer;
+  const double mx = a.mx[m], inv_t = 1.0 / (double)a.temp;
+  unsigned key[kStatsPer];
+  double e[kStatsPer];
+  double part = 0.0;
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) {
+    const bool in = j0 + q < a.V;
+    const float zv = in ? z[j0 + q] : -INFINITY;
+    key[q] = in ? ord_key(zv) : 0u;
+    e[q] = in ? exp(((double)zv - mx) * inv_t) : 0.0;
+    part += e[q];
+  }
+  const double total = block_sum_fixed<kStatsThreads>(part, sh);
+  const double thr = a.top_p * total;
+  // largest key kappa with sum_{key >= kappa} e >= thr (kappa = 0 qualifies)
+  uint64_t lo = 0, hi = 0xFFFFFFFFull;
+  while (lo < hi) {
+    const uint64_t mid = lo + (hi - lo + 1) / 2;
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) s += key[q] >= (unsigned)mid ? e[q] : 0.0;
+    if (block_sum_fixed<kStatsThreads>(s, sh) >= thr) lo = mid;
+    else hi = mid - 1;
+  }
+  const unsigned kap = (unsigned)lo;
+  double s_above = 0.0;
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) s_above += key[q] > kap ? e[q] : 0.0;
+  const double above = block_sum_fixed<kStatsThreads>(s_above, sh);
+  // smallest id iota with above + sum_{key == kappa, j <= iota} e >= thr
+  int ilo = 0, ihi = a.V - 1;
+  while (ilo < ihi) {
+    const int mid = (ilo + ihi) / 2;
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) s += (key[q] == kap && j0 + q <= mid) ? e[q] : 0.0;
+    if (above + block_sum_fixed<kStatsThreads>(s, sh) >= thr) ihi = mid;
+    else ilo = mid + 1;
+  }
+  double s_tie = 0.0;
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) s_tie += (key[q] == kap && j0 + q <= ilo) ? e[q] : 0.0;
+  const double kept = above + block_sum_fixed<kStatsThreads>(s_tie, sh);
+  if (threadIdx.x == 0) {
+    a.key[m] = kap;
+    a.id[m] = ilo;
+    a.mass[m] = kept;
+  }
+}
+void launch_top_p(const TopPArgs& a, int M, hipStream_t st) {
+  if (M > 0) hipLaunchKernelGGL(top_p_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
+}
+
 // Inverse-CDF draw from weights w_j = weight(j) >= 0 (fp64), ids ascending:
 // the smallest j with u*S < C_j, else the largest j with w_j > 0.  Each thread
 // owns a contiguous chunk of ids; chunk sums are prefixed in thread order.
@@ -404,17 +494,27 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     }
     return;
   }
-  // Stochastic chain: rows r0 .. r0+k, row j judges token of row j+1.
+  // Stochastic chain: rows r0 .. r0+k, row j judges token of row j+1.  With
+  // top-p the target of row r is exp((z - max)/T) on its kept set over the
+  // kept mass, and zero elsewhere.
   const int k = nr - 1;
   const double inv_t = 1.0 / (double)a.temp;
   const double* u = a.u + (size_t)i * VS_N_UNIFORMS;
+  const bool tp = a.tp_key != nullptr;
+  auto kept = [&](int r, int j, float zj) {
+    if (!tp) return true;
+    const unsigned kk = ord_key(zj);
+    return kk > a.tp_key[r] || (kk == a.tp_key[r] && j <= a.tp_id[r]);
+  };
   __shared__ int s_a, s_flags, s_reject;
   if (threadIdx.x == 0) {
     int acc = 0, flags = 0, reject = -1;
     for (int j = 0; j < k; ++j) {
       const int r = r0 + j;
       const int d = a.tokens[r + 1];
-      const double p = exp(((double)a.logits[(size_t)r * a.V + d] - (double)a.mx[r]) * inv_t) / a.sumexp[r];
+      const float zd_t = a.logits[(size_t)r * a.V + d];
+      const double p = kept(r, d, zd_t) ? exp(((double)zd_t - (double)a.mx[r]) * inv_t) / (tp ? a.tp_mass[r] : a.sumexp[r])
+                                        : 0.0;
       const double q = exp(((double)a.dlogits[(size_t)r * a.V + d] - (double)a.dmx[r]) * inv_t) / a.dsumexp[r];
       const double ratio = q > 0.0 ? p / q : 0.0;
       const double uj = u[16 + j];
@@ -435,15 +535,17 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   int y;
   if (reject < 0) {
     const int r = r0 + k;
-    SoftW w{a.logits + (size_t)r * a.V, (double)a.mx[r], inv_t};
+    const float* zt = a.logits + (size_t)r * a.V;
+    const double mt = a.mx[r];
+    auto w = [&](int j) -> double { return kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) : 0.0; };
     y = block_sample(a.V, u[32], w);
   } else {
     const int r = r0 + reject;
     const float* zt = a.logits + (size_t)r * a.V;
     const float* zd = a.dlogits + (size_t)r * a.V;
-    const double mt = a.mx[r], md = a.dmx[r], st = a.sumexp[r], sd = a.dsumexp[r];
+    const double mt = a.mx[r], md = a.dmx[r], st = tp ? a.tp_mass[r] : a.sumexp[r], sd = a.dsumexp[r];
     auto resid = [&](int j) -> double {
-      const double p = exp(((double)zt[j] - mt) * inv_t) / st;
+      const double p = kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) / st : 0.0;
       const double q = exp(((double)zd[j] - md) * inv_t) / sd;
       return p > q ? p - q : 0.0;
     };
@@ -453,7 +555,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     if (tot > 0.0) {
       y = block_sample(a.V, u[32], resid);
     } else {
-      SoftW w{zt, mt, inv_t};
+      auto w = [&](int j) -> double { return kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) : 0.0; };
       y = block_sample(a.V, u[32], w);
     }
   }

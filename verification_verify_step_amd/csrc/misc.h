@@ -95,6 +95,24 @@ struct AcceptArgs {
   int V;
   const double* u;        // [n_seq][48]
   int* result;            // [n_seq][24]
+  // top-p truncation of the target (null: none): token j of row r is kept
+  // iff key(z_j) > tp_key[r], or key(z_j) == tp_key[r] and j <= tp_id[r];
+  // tp_mass[r] = sum over the kept tokens of exp((z_j - max) / temp)
+  const unsigned* tp_key;
+  const int* tp_id;
+  const double* tp_mass;
+};
+
+// Top-p boundary of each row (see top_p_kernel).
+struct TopPArgs {
+  const float* logits;
+  int V;
+  float temp;
+  double top_p;
+  const float* mx;        // row maxima
+  unsigned* key;
+  int* id;
+  double* mass;
 };
 
 struct CommitArgs {
@@ -172,5 +190,6 @@ void launch_compact(const CommitArgs& a, hipStream_t st);
 void launch_commit(const CommitArgs& a, hipStream_t st);
 void launch_advance(int* P, int* committed, int seq, int dP, int dC, hipStream_t st);
 void launch_confidence(const ConfArgs& a, hipStream_t st);
+void launch_top_p(const TopPArgs& a, int M, hipStream_t st);
 
 }  // namespace vs
