@@ -224,6 +224,37 @@ def dynamic_rounds(e, B, open_prefilled, k0, steps, warmup, c_draft):
                     "speedup E(k)/(c k + 1) with c = exit layer / layers; k = 0 rounds are plain decoding steps"}
 
 
+def ngram_rounds(e, B, prompt, open_prefilled, steps, warmup, k_max=8):
+    """Greedy rounds of one sequence drafted by n-gram lookup over its own
+    history (1- to 3-grams, up to k_max copied tokens), verified through all
+    layers: committed tokens per second and the mean draft length."""
+    import torch
+    s = open_prefilled()
+    hist = [int(t) for t in prompt] + [e.state()[1][s]]
+    d_toks = torch.zeros(k_max + 1, dtype=torch.int32, device="cuda")
+    d_res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+
+    def one():
+        res, k = B.vs_step_ngram(e.model, e.kv, s, hist, 1 << 30, 1, 3, k_max, d_toks.data_ptr(), d_res.data_ptr(),
+                                 e.stream)
+        a, y = res[0], res[1]
+        hist.extend(d_toks[1:a + 1].cpu().tolist() + [y])
+        return k, a
+
+    for _ in range(warmup):
+        one()
+    P0 = e.state()[0][s]
+    t0 = time.perf_counter()
+    ka = [one() for _ in range(steps)]
+    dt = time.perf_counter() - t0
+    P1 = e.state()[0][s]
+    B.vs_seq_close(e.kv, s)
+    return {"tokens_per_s": (P1 - P0) / dt, "tokens_per_round": (P1 - P0) / steps,
+            "mean_k": sum(k for k, _ in ka) / steps, "accepted": sum(a for _, a in ka),
+            "note": "drafts copied from the sequence's own history (1- to 3-gram lookup, up to 8 tokens), verified "
+                    "through all layers; each round reads its result back to the host"}
+
+
 def accept_timing(e, B, seq, M, V, k, reps=50):
     """Average time of one stochastic accept call over the k+1 rows of one
     sequence at the full vocabulary: plain, and with the target truncated to
@@ -407,6 +438,8 @@ def main():
         # windowed dynamic k with the context-cost cut-off (self-speculative page, §3.2, §5.3)
         out["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
                                           c.exit_layer / c.n_layers)
+        # prompt-copy drafting with a full-depth verify
+        out["ngram"] = ngram_rounds(e, B, prompt, open_prefilled, args.steps, args.warmup)
         # stochastic accept of the k+1 verify rows, plain and with a top-p target
         out["accept_us"] = accept_timing(e, B, seq, M, c.vocab, k)
         # acceptance-calibrated synthetic model: W_o, W_down of layers >= L

@@ -305,6 +305,29 @@ vs_status vs_dynk_init(const vs_dynk_cfg* c, int32_t k0, vs_dynk_state* s);
 vs_status vs_dynk_update(const vs_dynk_cfg* c, vs_dynk_state* s, int32_t a, int32_t k_used, double c_draft,
                          int32_t* k_next);
 
+/* n-gram (prompt-copy) drafting ("self-speculative" page, §2.2: draft
+ * tokens copied from text that already appeared), host code only.  For g =
+ * max_ngram down to min_ngram, take the last g tokens of tokens[0..n) and
+ * find their latest earlier occurrence starting at i with i + g < limit,
+ * limit = min(n, search_len); the proposal is tokens[i + g .. min(i + g +
+ * k_max, limit)).  The first g that matches wins; *n_out = 0 when none does.
+ * out receives at most k_max ids.  Errors: VS_E_INVAL (null pointers,
+ * 1 <= min_ngram <= max_ngram, k_max in [0, VS_MAX_K], n >= 1). */
+vs_status vs_ngram_propose(const int32_t* tokens, int32_t n, int32_t search_len, int32_t min_ngram,
+                           int32_t max_ngram, int32_t k_max, int32_t* out, int32_t* n_out);
+
+/* One greedy round of one sequence with an n-gram draft and a full-depth
+ * verify (no draft model, so no first-L KV to reuse): h_history [n_hist]
+ * (host) is the sequence's committed tokens, its last one the pending token
+ * at position P.  Proposes d_1..d_k with vs_ngram_propose, writes [x,
+ * d_1..d_k] to d_tokens, runs vs_verify(start_layer 0) over the k+1 rows
+ * (k = 0 is a plain decoding step), vs_accept (greedy) and vs_commit, and
+ * blocks until h_result [VS_RESULT_INTS] holds the result; *k_out = k.
+ * Errors: as vs_ngram_propose and vs_verify. */
+vs_status vs_step_ngram(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* h_history, int32_t n_hist,
+                        int32_t search_len, int32_t min_ngram, int32_t max_ngram, int32_t k_max, int32_t* d_tokens,
+                        int32_t* d_result, int32_t* h_result, int32_t* k_out, void* stream);
+
 /* One greedy chain round of n_seq requests with per-request draft lengths
  * states[i].k (vs_step), then vs_confidence over each request's k+1 verify
  * rows, then vs_sched_update of every state.  Blocks until the round is done:

@@ -337,3 +337,33 @@ def dynk_update(state, a, k_used, c_draft=0.0, window=64, min_k=2, max_k=8, up=0
         best = max(sp, key=lambda k: (sp[k], -k))
         k_next = 0 if (sp[best] <= 1.0 or best < min_k) else min(k_next, best)
     return k_next
+
+
+def ngram_propose(history, search_len, min_ngram, max_ngram, k_max):
+    """Prompt-copy drafting ("self-speculative" page, §2.2: the next tokens
+    are assumed to have appeared already): the longest suffix of the history
+    (max_ngram down to min_ngram tokens) that occurs earlier, at its latest
+    earlier occurrence whose continuation starts inside the first search_len
+    tokens; the proposal is that continuation, at most k_max tokens and not
+    past search_len."""
+    n = len(history)
+    limit = min(n, search_len)
+    for g in range(min(max_ngram, n - 1), min_ngram - 1, -1):
+        suffix = list(history[n - g:])
+        starts = [i for i in range(0, limit - g) if list(history[i:i + g]) == suffix]
+        if starts:
+            i = max(starts)
+            return [int(t) for t in history[i + g:min(i + g + k_max, limit)]]
+    return []
+
+
+def ngram_round(dec, cache, st, k_max, search_len=None, min_ngram=1, max_ngram=3):
+    """One greedy round with an n-gram draft and a full-depth verify (start
+    layer 0: no first-L KV to reuse); no proposal is a plain decoding step."""
+    sl = len(st.tokens) if search_len is None else search_len
+    d = ngram_propose(st.tokens, sl, min_ngram, max_ngram, k_max)
+    toks = [st.pending] + d
+    z = verify_rows(dec, cache, chain_rows(st.sid, st.P, len(toks)), toks, 0)
+    a, y = accept_greedy_chain(toks, z)
+    commit_chain(cache, st, toks, a, y)
+    return d, a, y, z

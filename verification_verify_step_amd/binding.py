@@ -22,7 +22,7 @@ EXPORTS = [
     "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_accept_top_p", "vs_commit",
     "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_dynk_init",
-    "vs_dynk_update", "vs_stats_enable", "vs_stats_read",
+    "vs_dynk_update", "vs_ngram_propose", "vs_step_ngram", "vs_stats_enable", "vs_stats_read",
     "vs_stats_reset",
 ]
 
@@ -120,6 +120,8 @@ def lib():
             "vs_sched_update": (I32, [P(vs_sched_cfg), P(vs_spec_state), I32, D, D]),
             "vs_step_sched": (I32, [VP, VP, I32, pI, P(vs_sched_cfg), P(vs_spec_state), VP, VP, pI, P(D), VP]),
             "vs_dynk_init": (I32, [P(vs_dynk_cfg), I32, P(vs_dynk_state)]),
+            "vs_ngram_propose": (I32, [pI, I32, I32, I32, I32, I32, pI, pI]),
+            "vs_step_ngram": (I32, [VP, VP, I32, pI, I32, I32, I32, I32, I32, VP, VP, pI, pI, VP]),
             "vs_dynk_update": (I32, [P(vs_dynk_cfg), P(vs_dynk_state), I32, I32, D, pI]),
             "vs_stats_enable": (I32, [VP, I32]),
             "vs_stats_read": (I32, [VP, P(vs_kernel_stat), I32, pI]),
@@ -328,6 +330,24 @@ def vs_dynk_update(cfg, state, a, k_used, c_draft=0.0):
     _check("vs_dynk_update", lib().vs_dynk_update(ctypes.byref(cfg), ctypes.byref(state), a, k_used, c_draft,
                                                   ctypes.byref(kn)))
     return kn.value
+
+
+def vs_ngram_propose(tokens, search_len, min_ngram, max_ngram, k_max):
+    out = (ctypes.c_int32 * max(1, k_max))()
+    n = ctypes.c_int32()
+    _check("vs_ngram_propose", lib().vs_ngram_propose(_i32(tokens), len(tokens), search_len, min_ngram, max_ngram,
+                                                      k_max, out, ctypes.byref(n)))
+    return list(out[:n.value])
+
+
+def vs_step_ngram(model, kv, seq, history, search_len, min_ngram, max_ngram, k_max, d_tokens, d_result, stream):
+    """One n-gram round; returns (result row, k)."""
+    h_res = (ctypes.c_int32 * VS_RESULT_INTS)()
+    k = ctypes.c_int32()
+    _check("vs_step_ngram", lib().vs_step_ngram(model, kv, seq, _i32(history), len(history), search_len, min_ngram,
+                                                max_ngram, k_max, d_tokens, d_result, h_res, ctypes.byref(k),
+                                                stream))
+    return list(h_res), k.value
 
 
 STAT_FAMILIES = ["gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_head", "attention", "small"]

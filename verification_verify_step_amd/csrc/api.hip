@@ -1455,6 +1455,53 @@ vs_status vs_dynk_update(const vs_dynk_cfg* c, vs_dynk_state* s, int32_t a, int3
   return VS_OK;
 }
 
+vs_status vs_ngram_propose(const int32_t* tokens, int32_t n, int32_t search_len, int32_t min_ngram,
+                           int32_t max_ngram, int32_t k_max, int32_t* out, int32_t* n_out) {
+  if (tokens == nullptr || out == nullptr || n_out == nullptr) return fail(VS_E_INVAL, "vs_ngram_propose: null argument");
+  if (n < 1 || min_ngram < 1 || max_ngram < min_ngram || k_max < 0 || k_max > VS_MAX_K)
+    return fail(VS_E_INVAL, "vs_ngram_propose: n %d, n-gram [%d, %d], k_max %d", n, min_ngram, max_ngram, k_max);
+  *n_out = 0;
+  if (k_max == 0) return VS_OK;
+  const int limit = std::min(n, std::max(0, search_len));
+  for (int g = std::min(max_ngram, n - 1); g >= min_ngram; --g) {
+    const int32_t* suf = tokens + n - g;
+    for (int i = limit - g - 1; i >= 0; --i) {  // latest start with i + g < limit
+      if (std::memcmp(tokens + i, suf, (size_t)g * sizeof(int32_t)) != 0) continue;
+      const int end = std::min(i + g + k_max, limit);
+      for (int j = i + g; j < end; ++j) out[(*n_out)++] = tokens[j];
+      return VS_OK;
+    }
+  }
+  return VS_OK;
+}
+
+vs_status vs_step_ngram(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* h_history, int32_t n_hist,
+                        int32_t search_len, int32_t min_ngram, int32_t max_ngram, int32_t k_max, int32_t* d_tokens,
+                        int32_t* d_result, int32_t* h_result, int32_t* k_out, void* stream) {
+  if (m == nullptr || kv == nullptr || h_history == nullptr || d_tokens == nullptr || d_result == nullptr ||
+      h_result == nullptr || k_out == nullptr)
+    return fail(VS_E_INVAL, "vs_step_ngram: null argument");
+  int32_t rows[VS_MAX_K + 1];
+  int32_t k = 0;
+  vs_status rc = vs_ngram_propose(h_history, n_hist, search_len, min_ngram, max_ngram, k_max, rows + 1, &k);
+  if (rc != VS_OK) return rc;
+  rows[0] = h_history[n_hist - 1];
+  hipStream_t st = S(stream);
+  hipError_t e = hipMemcpyAsync(d_tokens, rows, (size_t)(k + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_ngram: %s", hipGetErrorString(e));
+  const int32_t n_rows = k + 1;
+  vs_batch b{1, &seq, &n_rows, nullptr, nullptr};
+  if ((rc = vs_verify(m, kv, &b, 0, d_tokens, nullptr, m->logits, stream)) != VS_OK) return rc;
+  if ((rc = vs_accept(m, &b, VS_GREEDY, 1.0f, d_tokens, m->logits, nullptr, nullptr, d_result, stream)) != VS_OK)
+    return rc;
+  if ((rc = vs_commit(m, kv, &b, d_result, stream)) != VS_OK) return rc;
+  e = hipMemcpyAsync(h_result, d_result, VS_RESULT_INTS * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_ngram: %s", hipGetErrorString(e));
+  *k_out = k;
+  return VS_OK;
+}
+
 vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* seq, const vs_sched_cfg* c,
                         vs_spec_state* states, int32_t* d_tokens, int32_t* d_result, int32_t* h_result, double* h_conf,
                         void* stream) {
