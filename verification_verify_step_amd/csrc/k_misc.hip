@@ -171,31 +171,6 @@ __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
   }
   return r;
 }
-__device__ Top2 block_top2(Top2 t) {
-  __shared__ Top2 sh[256];
-  sh[threadIdx.x] = t;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) sh[threadIdx.x] = top2_merge(sh[threadIdx.x], sh[threadIdx.x + o]);
-    __syncthreads();
-  }
-  const Top2 r = sh[0];
-  __syncthreads();
-  return r;
-}
-__device__ double block_sum_d(double v) {
-  __shared__ double sh[256];
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-
 // Per-row statistics of logits: max, argmax (lowest id on ties), second
 // largest value, and S = sum exp((z - max)/T) in fp64 when requested.
 template <int NT>
@@ -223,26 +198,6 @@ __device__ double block_sum_n(double v) {
   const double r = sh[0];
   __syncthreads();
   return r;
-}
-
-__device__ void row_stats(const float* z, int V, float temp, float* mx, int* amax, float* second, double* sumexp) {
-  Top2 t{-INFINITY, INT_MAX, -INFINITY};
-  for (int j = threadIdx.x; j < V; j += 256) t = top2_merge(t, Top2{z[j], j, -INFINITY});
-  t = block_top2(t);
-  if (threadIdx.x == 0) {
-    *mx = t.v1;
-    *amax = t.i1;
-    if (second) *second = t.v2;
-  }
-  if (sumexp != nullptr) {
-    const double inv_t = 1.0 / (double)temp;
-    const int per = (V + 255) / 256;
-    const int j0 = min(V, (int)threadIdx.x * per), j1 = min(V, j0 + per);
-    double s = 0.0;
-    for (int j = j0; j < j1; ++j) s += exp(((double)z[j] - (double)t.v1) * inv_t);
-    s = block_sum_d(s);
-    if (threadIdx.x == 0) *sumexp = s;
-  }
 }
 
 // One 1024-thread workgroup per row; each thread keeps its contiguous slice of
@@ -370,90 +325,103 @@ void launch_top_p(const TopPArgs& a, int M, hipStream_t st) {
   if (M > 0) hipLaunchKernelGGL(top_p_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
 }
 
-// Inverse-CDF draw from weights w_j = weight(j) >= 0 (fp64), ids ascending:
-// the smallest j with u*S < C_j, else the largest j with w_j > 0.  Each thread
-// owns a contiguous chunk of ids; chunk sums are prefixed in thread order.
-template <typename F>
-__device__ int block_sample(int V, double u, F weight) {
-  __shared__ double csum[256];
-  __shared__ double s_total;
+// Inverse-CDF draw from weights w_j >= 0 (fp64), ids ascending: the smallest
+// j with u*S < C_j, else the largest j with w_j > 0.  For 1024-thread
+// workgroups with the weights already in registers: thread t holds the
+// weights of ids t*kStatsPer ..
+// (t+1)*kStatsPer - 1 (zero past V), so each weight is computed once.  Chunk
+// sums in id order, an inclusive scan of them over each wave, the wave totals
+// in wave order: C_j = (sum of earlier chunks) + (the chunk's own running
+// sum).  Returns -1 when every weight is zero; *total receives S.
+__device__ int block_sample_reg(const double (&w)[kStatsPer], double u, double* total) {
+  __shared__ double wsum[kStatsThreads / 64];
   __shared__ int s_pick, s_last;
-  const int per = (V + 255) / 256;
-  const int j0 = min(V, (int)threadIdx.x * per), j1 = min(V, j0 + per);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j0 = t * kStatsPer;
   double s = 0.0;
   int last = -1;
-  for (int j = j0; j < j1; ++j) {
-    const double w = weight(j);
-    s += w;
-    if (w > 0.0) last = j;
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) {
+    s += w[q];
+    if (w[q] > 0.0) last = j0 + q;
   }
-  csum[threadIdx.x] = s;
-  if (threadIdx.x == 0) {
+  double incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  double excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.0;
+  if (lane == 63) wsum[wave] = incl;
+  if (t == 0) {
     s_pick = INT_MAX;
     s_last = -1;
   }
   __syncthreads();
   atomicMax(&s_last, last);
-  if (threadIdx.x == 0) {
-    double acc = 0.0;
-    for (int t = 0; t < 256; ++t) {
-      const double c = csum[t];
-      csum[t] = acc;
-      acc += c;
-    }
-    s_total = acc;
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kStatsThreads / 64; ++i) {
+    if (i == wave) base = tot;
+    tot += wsum[i];
   }
-  __syncthreads();
-  const double target = u * s_total;
-  double c = csum[threadIdx.x];
-  for (int j = j0; j < j1; ++j) {
-    c += weight(j);
+  const double target = u * tot;
+  double c = base + excl;
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) {
+    c += w[q];
     if (target < c) {
-      atomicMin(&s_pick, j);
+      atomicMin(&s_pick, j0 + q);
       break;
     }
   }
   __syncthreads();
   const int pick = s_pick == INT_MAX ? s_last : s_pick;
   __syncthreads();
-  return pick;
+  *total = tot;
+  return tot > 0.0 ? pick : -1;
 }
-
-// Softmax-at-T weight of id j of a logits row: exp((z_j - max)/T), fp64.
-struct SoftW {
-  const float* z;
-  double mx, inv_t;
-  __device__ double operator()(int j) const { return exp(((double)z[j] - mx) * inv_t); }
-};
 
 // ---------------------------------------------------------------------------
 // Draft-token selection (one workgroup per sequence).
-__global__ __launch_bounds__(256) void pick_kernel(PickArgs a) {
+__global__ __launch_bounds__(kStatsThreads) void pick_kernel(PickArgs a) {
   const int i = blockIdx.x;
   int tok;
   if (a.src[i] < 0) {
     tok = a.pending[a.seq[i]];
   } else if (a.mode == VS_GREEDY) {
     Top2 t{-INFINITY, INT_MAX, -INFINITY};
-    for (int g = threadIdx.x; g < a.groups; g += 256) {
+    for (int g = threadIdx.x; g < a.groups; g += kStatsThreads) {
       const int e = g * a.Mprev + a.src[i];
       t = top2_merge(t, Top2{a.amax_val[e], a.amax_idx[e], -INFINITY});
     }
-    t = block_top2(t);
+    t = block_top2_n<kStatsThreads>(t);
     tok = t.i1;
   } else {
+    // draw from softmax(z / T): the row in registers, its max, the weights
+    // exp((z - max) / T) once, then the inverse-CDF draw
     const float* z = a.logits + (size_t)a.lrow[i] * a.V;
-    __shared__ float s_mx;
-    __shared__ int s_am;
-    row_stats(z, a.V, a.temp, &s_mx, &s_am, nullptr, nullptr);
-    __syncthreads();
-    SoftW w{z, (double)s_mx, 1.0 / (double)a.temp};
-    tok = block_sample(a.V, a.u[(size_t)a.uidx[i] * VS_N_UNIFORMS + a.slot], w);
+    const int j0 = threadIdx.x * kStatsPer;
+    float v[kStatsPer];
+    Top2 t{-INFINITY, INT_MAX, -INFINITY};
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) {
+      v[q] = j0 + q < a.V ? z[j0 + q] : -INFINITY;
+      if (j0 + q < a.V) t = top2_merge(t, Top2{v[q], j0 + q, -INFINITY});
+    }
+    t = block_top2_n<kStatsThreads>(t);
+    const double mx = t.v1, inv_t = 1.0 / (double)a.temp;
+    double w[kStatsPer];
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) w[q] = j0 + q < a.V ? exp(((double)v[q] - mx) * inv_t) : 0.0;
+    double tot;
+    tok = block_sample_reg(w, a.u[(size_t)a.uidx[i] * VS_N_UNIFORMS + a.slot], &tot);
   }
   if (threadIdx.x == 0) a.tokens[a.dst[i]] = tok;
 }
 void launch_pick(const PickArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pick_kernel, dim3(a.n), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(pick_kernel, dim3(a.n), dim3(kStatsThreads), 0, st, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -464,7 +432,7 @@ __device__ __forceinline__ int row_parent(const RowMap& rm, int r0, int c) {
   return anc == 0 ? -1 : 63 - __clzll((long long)anc);
 }
 
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+__global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
   const int i = blockIdx.x;
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
@@ -533,30 +501,42 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   __syncthreads();
   const int reject = s_reject;
   int y;
-  if (reject < 0) {
-    const int r = r0 + k;
+  // weights of the draw in registers: thread t holds ids t*kStatsPer ..
+  const int j0 = threadIdx.x * kStatsPer;
+  double w[kStatsPer];
+  double tot;
+  auto target_weights = [&](int r) {  // exp((z - max)/T) on the (top-p) support
     const float* zt = a.logits + (size_t)r * a.V;
     const double mt = a.mx[r];
-    auto w = [&](int j) -> double { return kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) : 0.0; };
-    y = block_sample(a.V, u[32], w);
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) {
+      const int j = j0 + q;
+      w[q] = (j < a.V && kept(r, j, zt[j])) ? exp(((double)zt[j] - mt) * inv_t) : 0.0;
+    }
+  };
+  if (reject < 0) {
+    target_weights(r0 + k);
+    y = block_sample_reg(w, u[32], &tot);
   } else {
     const int r = r0 + reject;
     const float* zt = a.logits + (size_t)r * a.V;
     const float* zd = a.dlogits + (size_t)r * a.V;
     const double mt = a.mx[r], md = a.dmx[r], st = tp ? a.tp_mass[r] : a.sumexp[r], sd = a.dsumexp[r];
-    auto resid = [&](int j) -> double {
-      const double p = kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) / st : 0.0;
-      const double q = exp(((double)zd[j] - md) * inv_t) / sd;
-      return p > q ? p - q : 0.0;
-    };
-    double part = 0.0;
-    for (int j = threadIdx.x; j < a.V; j += 256) part += resid(j);
-    const double tot = block_sum_d(part);
-    if (tot > 0.0) {
-      y = block_sample(a.V, u[32], resid);
-    } else {
-      auto w = [&](int j) -> double { return kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) : 0.0; };
-      y = block_sample(a.V, u[32], w);
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q) {  // residual max(0, p - q)
+      const int j = j0 + q;
+      if (j < a.V) {
+        const double p = kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) / st : 0.0;
+        const double qd = exp(((double)zd[j] - md) * inv_t) / sd;
+        w[q] = p > qd ? p - qd : 0.0;
+      } else {
+        w[q] = 0.0;
+      }
+    }
+    y = block_sample_reg(w, u[32], &tot);
+    if (y < 0) {  // the residual vanished: draw from p
+      target_weights(r);
+      y = block_sample_reg(w, u[32], &tot);
     }
   }
   if (threadIdx.x == 0) {
@@ -568,7 +548,7 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
   }
 }
 void launch_accept(const AcceptArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(a.rows.n_seq), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(accept_kernel, dim3(a.rows.n_seq), dim3(kStatsThreads), 0, st, a);
 }
 
 // ---------------------------------------------------------------------------
