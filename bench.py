@@ -287,8 +287,120 @@ def accept_timing(e, B, seq, M, V, k, reps=50):
     return out
 
 
+def ragged_verify(args):
+    """The 70B ragged batch (32 requests, contexts U[512, 8192], drafts
+    U[2, 16]): the verify step (layers 24..79 + head over the drafted rows,
+    greedy accept, commit) timed with HIP events, reported against both
+    roofs: algorithmic HBM bytes (weights of the verify layers and the head
+    once, the committed KV once, in-round KV, hidden and logits) and
+    algorithmic MFMA flops (2 per weight per row).  The committed KV is drawn
+    by the generator (N(0, 1) bf16) rather than prefilled; draft rows are
+    random token ids with random layer-L inputs."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import gpu_weights
+    from synth.workloads import WORKLOADS, ragged_batch
+    from verification_verify_step_amd import binding as B
+    from verification_verify_step_amd.runtime import Engine
+
+    w = WORKLOADS[args.workload]
+    c = w.model
+    ctx, ks, pend = ragged_batch(w)
+    n = len(ctx)
+    rows = [int(k) + 1 for k in ks]
+    M = sum(rows)
+    max_ctx = int(max(ctx)) + 64
+    bps = (max_ctx + 15) // 16 + 2
+    e = Engine(c, max_rows=M, max_seqs=n, max_ctx=max_ctx, n_blocks=sum((int(x) + 64 + 15) // 16 for x in ctx) + 16,
+               max_blocks_per_seq=bps)
+    st = e.stream
+    t_load = time.time()
+    gpu_weights.load(e, c)
+    for layer in range(c.n_layers):
+        K, V, _ = e.kv_layer(layer)
+        synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 0), K.numel(), K.data_ptr(), st, std=1.0)
+        synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 1), V.numel(), V.data_ptr(), st, std=1.0)
+    seqs = []
+    for i in range(n):
+        s = e.open(int(ctx[i]) + 48)
+        B.vs_seq_assume(e.kv, s, int(ctx[i]), int(pend[i]), st)
+        seqs.append(s)
+    torch.cuda.synchronize()
+    t_load = time.time() - t_load
+    rng = np.random.default_rng(5)
+    hL = torch.from_numpy(rng.standard_normal((M, c.d_model)).astype(np.float32)).cuda()
+    toks = torch.from_numpy(rng.integers(0, c.vocab, M).astype(np.int32)).cuda()
+    z = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+    res = torch.zeros((n, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    batch = B.make_batch(seqs, rows)
+
+    def step():
+        B.vs_verify(e.model, e.kv, batch, c.exit_layer, toks.data_ptr(), hL.data_ptr(), z.data_ptr(), st)
+        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, toks.data_ptr(), z.data_ptr(), None, None, res.data_ptr(), st)
+        B.vs_commit(e.model, e.kv, batch, res.data_ptr(), st)
+
+    def rewind():
+        for i, s in enumerate(seqs):
+            B.vs_seq_rewind(e.kv, s, int(ctx[i]), int(pend[i]), st)
+
+    for _ in range(args.warmup):
+        step()
+        rewind()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        step()
+        t1.record()
+        rewind()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    ms = float(np.mean(times))
+    # one more step with every kernel family bracketed by events
+    B.vs_stats_reset(e.model)
+    B.vs_stats_enable(e.model, -1)
+    step()
+    torch.cuda.synchronize()
+    B.vs_stats_enable(e.model, 0)
+    fam = {n: {"launches": v[0], "ms": v[1], "gbs": (v[2] / (v[1] * 1e-3) / 1e9) if v[1] else None}
+           for n, v in B.vs_stats_read(e.model).items() if v[0]}
+    rewind()
+    nl = c.n_layers - c.exit_layer
+    kv_row = c.n_kv_heads * c.head_dim * 2 * 2
+    params = nl * layer_bytes(c) // 2 + c.vocab * c.d_model
+    bytes_ = (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * int(sum(ctx)) * kv_row + nl * M * kv_row
+              + M * c.d_model * 4 * 2 + M * c.vocab * 4)
+    flops = 2.0 * M * params
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "verify-step algorithmic HBM GB/s at the 70B ragged batch", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random-init bf16 weights, generator-filled committed KV, random draft rows)",
+        "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": int(sum(ctx)), "exit_layer": c.exit_layer,
+                   "layers": c.n_layers},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "mfma": {"achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0,
+                 "note": "algorithmic flops 2 x rows x weights of the verify layers and head; the split-bf16 "
+                         "activations issue twice as many MFMA operations"},
+        "verify_step_bytes": bytes_, "verify_step_flops": flops, "weights_load_s": t_load,
+        "kernel_families_bracketed": fam,
+    }))
+
+
 def main():
     args = parse()
+    if args.workload == "llama70b_ragged_b32":
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build measures one GPU only"}))
+            sys.exit(2)
+        ragged_verify(args)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return

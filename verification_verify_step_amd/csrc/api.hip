@@ -360,14 +360,15 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   const int P = ctx_bound(kv, rm);
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
   // One 32-key step per wave while that stays under ~2048 waves (all KV loads
-  // in flight at once), else longer splits of at most ~1024 keys; bounded by
-  // the partials buffer and by the combine's capacity (workgroups per unit x
-  // query vectors).
+  // in flight at once), else splits of about 256 keys (a wave's steps run one
+  // after another, so long splits are latency-bound); bounded by the partials
+  // buffer and by the combine's capacity (workgroups per unit x query
+  // vectors).  Splits past a shorter sequence's context run no step.
   int n_split = 0;
   a.kps = 32;
   if (P > 0) {
     const int max_split = (P + 31) / 32;
-    int want = std::max({1, 2048 / std::max(1, units), (P + 1023) / 1024});
+    int want = std::max({1, 2048 / std::max(1, units), (P + 255) / 256});
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
     const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
     const int max_wg = std::min(budget_wg, kAttnCombineSlots / a.qg_size);

@@ -81,10 +81,20 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_parts = a.n_split + 1;
   const int wpb = (n_parts + kWaves - 1) / kWaves;  // workgroups per unit
-  const int i = blockIdx.x / wpb;
-  const int wgi = blockIdx.x % wpb;
+  // The query groups of one (sequence, KV head, key range) read the same
+  // K/V.  Workgroups are handed to the 8 XCDs round-robin by index, so the
+  // index b is decoded as XCD b % 8 and position b / 8 on it, with the query
+  // group varying fastest along that position: the groups of a key range run
+  // back to back on one XCD and the later ones find the K/V in its L2.
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  const int qg = pos % a.n_qg;
+  const int g = (pos / a.n_qg) * 8 + xcd;  // (sequence, workgroup of the unit, KV head)
+  const int X = a.rows.n_seq * wpb;
+  if (g >= X * a.Hkv) return;  // grid padding
+  const int i = (g % X) / wpb;
+  const int wgi = (g % X) % wpb;
   const int split = wgi * kWaves + wave;
-  const int kvh = blockIdx.y, qg = blockIdx.z;
+  const int kvh = g / X;
   const int sq = a.rows.seq[i];
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
@@ -115,7 +125,10 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   // for P.  K of the next step is requested right after this step's S, V of
   // the next step right after this step's P.V.
   const int first = window ? (key_lo / kStep) * kStep : split * a.kps;
-  const int last = !active ? first : window ? key_hi : split * a.kps + a.kps;  // exclusive
+  // exclusive; a committed split stops at the last step holding committed
+  // keys (splits wholly past P run no step: their first loads, issued
+  // before P is known, go unused)
+  const int last = !active ? first : window ? key_hi : min(split * a.kps + a.kps, (P + kStep - 1) / kStep * kStep);
   u32x4 kb[2][KSQ], vb[NDT];
   int nb0 = 0, nb1 = 0;  // blocks of the step being loaded
   auto blocks_of = [&](int base) {
@@ -427,7 +440,8 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
   const int n_parts = a.n_split + 1;
   const int wv = attn_waves(a.qg_size);
   const int wpb = (n_parts + wv - 1) / wv;
-  dim3 grid(a.rows.n_seq * wpb, a.Hkv, a.n_qg);
+  const int groups = a.rows.n_seq * wpb * a.Hkv;
+  dim3 grid(8 * a.n_qg * ((groups + 7) / 8));
   const int mtq = (a.qg_size + 15) / 16;  // at most 2 (query groups hold <= kAttnQG vectors)
 #define VS_ATT(MTQ, HD, WV)                                                                                 \
   do {                                                                                                      \

@@ -83,7 +83,7 @@ struct AttnArgs {
 };
 // One launch: splits, in-workgroup merge, and the last workgroup's combine.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-constexpr int kAttnQG = 32;              // query vectors per query group
+constexpr int kAttnQG = 16;              // query vectors per query group
 constexpr int kAttnCombineSlots = 1024;  // workgroups per unit x query vectors per group, at most
 // splits (waves) per attention workgroup: 8 for query groups of up to 16
 // vectors, 4 for larger ones (more registers and LDS per wave)
