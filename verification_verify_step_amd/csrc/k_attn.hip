@@ -442,7 +442,7 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
   const int wpb = (n_parts + wv - 1) / wv;
   const int groups = a.rows.n_seq * wpb * a.Hkv;
   dim3 grid(8 * a.n_qg * ((groups + 7) / 8));
-  const int mtq = (a.qg_size + 15) / 16;  // at most 2 (query groups hold <= kAttnQG vectors)
+  static_assert(kAttnQG <= 16, "one 16-row query tile per wave");
 #define VS_ATT(MTQ, HD, WV)                                                                                 \
   do {                                                                                                      \
     if (ev0 != nullptr || ev1 != nullptr)                                                                   \
@@ -450,13 +450,8 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
     else                                                                                                    \
       hipLaunchKernelGGL((attn_kernel<MTQ, HD, WV>), grid, dim3(WV * 64), 0, st, a);                        \
   } while (0)
-  if (a.hd == 128) {
-    if (mtq <= 1) VS_ATT(1, 128, 8);
-    else VS_ATT(2, 128, 4);
-  } else {
-    if (mtq <= 1) VS_ATT(1, 64, 8);
-    else VS_ATT(2, 64, 4);
-  }
+  if (a.hd == 128) VS_ATT(1, 128, 8);
+  else VS_ATT(1, 64, 8);
 #undef VS_ATT
 }
 

@@ -85,9 +85,12 @@ struct AttnArgs {
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kAttnQG = 16;              // query vectors per query group
 constexpr int kAttnCombineSlots = 1024;  // workgroups per unit x query vectors per group, at most
-// splits (waves) per attention workgroup: 8 for query groups of up to 16
-// vectors, 4 for larger ones (more registers and LDS per wave)
-inline int attn_waves(int qg_size) { return qg_size <= 16 ? 8 : 4; }
+// splits (waves) per attention workgroup: query groups hold at most 16
+// vectors (one 16-row MFMA tile per wave), and 8 waves fill about one CU
+inline int attn_waves(int qg_size) {
+  (void)qg_size;
+  return 8;
+}
 constexpr int kAttnMaxUnits = 16384;     // arrival counters
 hipError_t attn_init();
 
