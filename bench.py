@@ -287,15 +287,18 @@ def accept_timing(e, B, seq, M, V, k, reps=50):
     return out
 
 
-def ragged_verify(args):
-    """The 70B ragged batch (32 requests, contexts U[512, 8192], drafts
-    U[2, 16]): the verify step (layers 24..79 + head over the drafted rows,
-    greedy accept, commit) timed with HIP events, reported against both
-    roofs: algorithmic HBM bytes (weights of the verify layers and the head
-    once, the committed KV once, in-round KV, hidden and logits) and
-    algorithmic MFMA flops (2 per weight per row).  The committed KV is drawn
-    by the generator (N(0, 1) bf16) rather than prefilled; draft rows are
-    random token ids with random layer-L inputs."""
+def workload_verify(args):
+    """The verify step of a parity workload other than the bench's: the
+    stochastic batch of 8 (llama7b_sample_k4_b8: 8 x 5 rows at context 2048,
+    T = 1), the tree of 63 nodes (llama7b_tree63: 64 rows at context 4096,
+    drafted by vs_draft_tree) and the 70B ragged batch (llama70b_ragged_b32:
+    32 requests, contexts U[512, 8192], drafts U[2, 16]).  Layers L..N-1 +
+    head over the rows, accept, commit, timed with HIP events and reported
+    against both roofs: algorithmic HBM bytes (weights of the verify layers
+    and the head once, the committed KV once, in-round KV, hidden and logits)
+    and algorithmic MFMA flops (2 per weight per row).  The committed KV is
+    drawn by the generator (N(0, 1) bf16) instead of prefilled; chain rows
+    get random token ids and layer-L inputs."""
     import numpy as np
     import torch
 
@@ -307,13 +310,22 @@ def ragged_verify(args):
 
     w = WORKLOADS[args.workload]
     c = w.model
-    ctx, ks, pend = ragged_batch(w)
-    n = len(ctx)
-    rows = [int(k) + 1 for k in ks]
-    M = sum(rows)
-    max_ctx = int(max(ctx)) + 64
+    rng = np.random.default_rng(5)
+    tree = bool(getattr(w, "tree", False))
+    if w.name == "llama70b_ragged_b32":
+        ctx, ks, pend = ragged_batch(w)
+        rows = [int(k) + 1 for k in ks]
+    elif tree:
+        ctx, rows = [w.prompt_len], [1 + w.extra["nodes"]]
+        pend = rng.integers(0, c.vocab, 1)
+    else:
+        ctx, rows = [w.prompt_len] * w.batch, [w.k + 1] * w.batch
+        pend = rng.integers(0, c.vocab, w.batch)
+    ctx = [int(x) for x in ctx]
+    n, M = len(ctx), sum(rows)
+    max_ctx = max(ctx) + 80
     bps = (max_ctx + 15) // 16 + 2
-    e = Engine(c, max_rows=M, max_seqs=n, max_ctx=max_ctx, n_blocks=sum((int(x) + 64 + 15) // 16 for x in ctx) + 16,
+    e = Engine(c, max_rows=M, max_seqs=n, max_ctx=max_ctx, n_blocks=sum((x + 80 + 15) // 16 for x in ctx) + 16,
                max_blocks_per_seq=bps)
     st = e.stream
     t_load = time.time()
@@ -324,26 +336,43 @@ def ragged_verify(args):
         synth.dev_normal_bf16(synth.SEED_KV, synth.stream_kv(layer, 1), V.numel(), V.data_ptr(), st, std=1.0)
     seqs = []
     for i in range(n):
-        s = e.open(int(ctx[i]) + 48)
-        B.vs_seq_assume(e.kv, s, int(ctx[i]), int(pend[i]), st)
+        s = e.open(ctx[i] + 72)
+        B.vs_seq_assume(e.kv, s, ctx[i], int(pend[i]), st)
         seqs.append(s)
     torch.cuda.synchronize()
+    if tree:
+        ex = w.extra
+        toks = torch.empty(M, dtype=torch.int32, device="cuda")
+        depth = torch.empty(M, dtype=torch.int32, device="cuda")
+        mask = torch.empty(M, dtype=torch.int64, device="cuda")
+        parent = torch.empty(M, dtype=torch.int32, device="cuda")
+        hL = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
+        lz = torch.empty((ex["depth"], M, c.vocab), dtype=torch.float32, device="cuda")
+        B.vs_draft_tree(e.model, e.kv, seqs[0], ex["topk"], ex["depth"], ex["nodes"], 1.0, toks.data_ptr(),
+                        depth.data_ptr(), mask.data_ptr(), parent.data_ptr(), hL.data_ptr(), lz.data_ptr(), st)
+        batch = B.make_batch(seqs, rows, depth.data_ptr(), mask.data_ptr())
+    else:
+        hL = torch.from_numpy(rng.standard_normal((M, c.d_model)).astype(np.float32)).cuda()
+        toks = torch.from_numpy(rng.integers(0, c.vocab, M).astype(np.int32)).cuda()
+        batch = B.make_batch(seqs, rows)
+    torch.cuda.synchronize()
     t_load = time.time() - t_load
-    rng = np.random.default_rng(5)
-    hL = torch.from_numpy(rng.standard_normal((M, c.d_model)).astype(np.float32)).cuda()
-    toks = torch.from_numpy(rng.integers(0, c.vocab, M).astype(np.int32)).cuda()
+    sample = w.mode == "sample"
     z = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+    zd = torch.from_numpy(rng.standard_normal((M, c.vocab)).astype(np.float32)).cuda() if sample else None
+    u = torch.from_numpy(rng.random(n * B.VS_N_UNIFORMS)).cuda() if sample else None
     res = torch.zeros((n, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
-    batch = B.make_batch(seqs, rows)
 
     def step():
         B.vs_verify(e.model, e.kv, batch, c.exit_layer, toks.data_ptr(), hL.data_ptr(), z.data_ptr(), st)
-        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, toks.data_ptr(), z.data_ptr(), None, None, res.data_ptr(), st)
+        B.vs_accept(e.model, batch, B.VS_SAMPLE if sample else B.VS_GREEDY, w.temperature, toks.data_ptr(),
+                    z.data_ptr(), zd.data_ptr() if sample else None, u.data_ptr() if sample else None,
+                    res.data_ptr(), st)
         B.vs_commit(e.model, e.kv, batch, res.data_ptr(), st)
 
-    def rewind():
+    def rewind():  # the committed context below P is never written by a round
         for i, s in enumerate(seqs):
-            B.vs_seq_rewind(e.kv, s, int(ctx[i]), int(pend[i]), st)
+            B.vs_seq_rewind(e.kv, s, ctx[i], int(pend[i]), st)
 
     for _ in range(args.warmup):
         step()
@@ -365,24 +394,25 @@ def ragged_verify(args):
     step()
     torch.cuda.synchronize()
     B.vs_stats_enable(e.model, 0)
-    fam = {n: {"launches": v[0], "ms": v[1], "gbs": (v[2] / (v[1] * 1e-3) / 1e9) if v[1] else None}
-           for n, v in B.vs_stats_read(e.model).items() if v[0]}
+    fam = {k: {"launches": v[0], "ms": v[1], "gbs": (v[2] / (v[1] * 1e-3) / 1e9) if v[1] else None}
+           for k, v in B.vs_stats_read(e.model).items() if v[0]}
     rewind()
     nl = c.n_layers - c.exit_layer
     kv_row = c.n_kv_heads * c.head_dim * 2 * 2
     params = nl * layer_bytes(c) // 2 + c.vocab * c.d_model
-    bytes_ = (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * int(sum(ctx)) * kv_row + nl * M * kv_row
+    bytes_ = (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * sum(ctx) * kv_row + nl * M * kv_row
               + M * c.d_model * 4 * 2 + M * c.vocab * 4)
     flops = 2.0 * M * params
     gbs = bytes_ / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     print(json.dumps({
-        "metric": "verify-step algorithmic HBM GB/s at the 70B ragged batch", "value": gbs, "unit": "GB/s",
+        "metric": f"verify-step algorithmic HBM GB/s ({w.name})", "value": gbs, "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (random-init bf16 weights, generator-filled committed KV, random draft rows)",
-        "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": int(sum(ctx)), "exit_layer": c.exit_layer,
-                   "layers": c.n_layers},
+        "data": "synthetic (random-init bf16 weights, generator-filled committed KV"
+                + (", a tree drafted on the GPU)" if tree else ", random draft rows)"),
+        "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": sum(ctx), "exit_layer": c.exit_layer,
+                   "layers": c.n_layers, "mode": w.mode},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
         "mfma": {"achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0,
@@ -395,11 +425,11 @@ def ragged_verify(args):
 
 def main():
     args = parse()
-    if args.workload == "llama70b_ragged_b32":
+    if args.workload != "llama7b_chain_k5":
         if args.gpus != 1:
             print(json.dumps({"error": "this build measures one GPU only"}))
             sys.exit(2)
-        ragged_verify(args)
+        workload_verify(args)
         return
     if args.calibrate_copy:
         calibrate_copy()
