@@ -152,7 +152,7 @@ void launch_copy_rows(const float* src, float* dst, int M, int d, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------
-// Block-level reductions (256 threads) in a fixed order.
+// Workgroup reductions in a fixed order.
 struct Top2 {
   float v1;
   int i1;
@@ -171,75 +171,28 @@ __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
   }
   return r;
 }
-// Per-row statistics of logits: max, argmax (lowest id on ties), second
-// largest value, and S = sum exp((z - max)/T) in fp64 when requested.
-template <int NT>
-__device__ Top2 block_top2_n(Top2 t) {
-  __shared__ Top2 sh[NT];
-  sh[threadIdx.x] = t;
-  __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sh[threadIdx.x] = top2_merge(sh[threadIdx.x], sh[threadIdx.x + o]);
-    __syncthreads();
-  }
-  const Top2 r = sh[0];
-  __syncthreads();
-  return r;
-}
-template <int NT>
-__device__ double block_sum_n(double v) {
-  __shared__ double sh[NT];
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
-    __syncthreads();
-  }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
-}
-
-// One 1024-thread workgroup per row; each thread keeps its contiguous slice of
-// the row in registers (all loads in flight at once).
+// Row kernels: one 1024-thread workgroup per row, the row in registers
+// (up to 32 values per thread, every load in flight at once).
 constexpr int kStatsThreads = 1024;
 constexpr int kStatsPer = 32;  // rows up to 32768 logits
-__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a) {
-  const int m = blockIdx.x;
-  const float* z = a.logits + (size_t)m * a.V;
-  const int j0 = threadIdx.x * kStatsPer;
-  float v[kStatsPer];
+// Workgroup top-2: butterfly over each wave with shuffles, then the wave
+// results merged in wave order.  top2_merge is exact (max / min, no rounding)
+// and its result does not depend on the merge order.
+template <int NT>
+__device__ Top2 block_top2_fast(Top2 t) {
+  __shared__ Top2 sh[NT / 64];
 #pragma unroll
-  for (int q = 0; q < kStatsPer; ++q) v[q] = j0 + q < a.V ? z[j0 + q] : -INFINITY;
-  Top2 t{-INFINITY, INT_MAX, -INFINITY};
-#pragma unroll
-  for (int q = 0; q < kStatsPer; ++q)
-    if (j0 + q < a.V) t = top2_merge(t, Top2{v[q], j0 + q, -INFINITY});
-  t = block_top2_n<kStatsThreads>(t);
-  if (threadIdx.x == 0) {
-    a.mx[m] = t.v1;
-    a.amax[m] = t.i1;
-    if (a.second) a.second[m] = t.v2;
+  for (int o = 32; o > 0; o >>= 1) {
+    const Top2 u{__shfl_xor(t.v1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.v2, o, 64)};
+    t = top2_merge(t, u);
   }
-  if (a.sumexp != nullptr) {
-    const double inv_t = 1.0 / (double)a.temp;
-    double s = 0.0;
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = t;
+  __syncthreads();
+  Top2 r = sh[0];
 #pragma unroll
-    for (int q = 0; q < kStatsPer; ++q)
-      if (j0 + q < a.V) s += exp(((double)v[q] - (double)t.v1) * inv_t);
-    s = block_sum_n<kStatsThreads>(s);
-    if (threadIdx.x == 0) a.sumexp[m] = s;
-  }
-}
-void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
-  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
-}
-
-// Order-preserving 32-bit image of a float: a > b as floats iff key(a) >
-// key(b) as unsigned integers (for non-NaN values).
-__device__ __forceinline__ unsigned ord_key(float z) {
-  const unsigned u = __float_as_uint(z);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  for (int w = 1; w < NT / 64; ++w) r = top2_merge(r, sh[w]);
+  __syncthreads();
+  return r;
 }
 
 // fp64 sum over a workgroup in a fixed order: lane 0 of each wave takes its
@@ -257,6 +210,53 @@ __device__ double block_sum_fixed(double v, double* sh) {
   return s;
 }
 
+// Per-row statistics of logits: max, argmax (lowest id on ties), second
+// largest value, and S = sum exp((z - max)/T) in fp64 when requested.  Thread
+// t takes ids t, t + 1024, ..., so each load instruction of a wave reads 256
+// contiguous bytes.
+__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a) {
+  __shared__ double sh[kStatsThreads / 64];
+  const int m = blockIdx.x;
+  const float* z = a.logits + (size_t)m * a.V;
+  float v[kStatsPer];
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) {
+    const int j = q * kStatsThreads + (int)threadIdx.x;
+    v[q] = j < a.V ? z[j] : -INFINITY;
+  }
+  Top2 t{-INFINITY, INT_MAX, -INFINITY};
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q) {
+    const int j = q * kStatsThreads + (int)threadIdx.x;
+    if (j < a.V) t = top2_merge(t, Top2{v[q], j, -INFINITY});
+  }
+  t = block_top2_fast<kStatsThreads>(t);
+  if (threadIdx.x == 0) {
+    a.mx[m] = t.v1;
+    a.amax[m] = t.i1;
+    if (a.second) a.second[m] = t.v2;
+  }
+  if (a.sumexp != nullptr) {
+    const double inv_t = 1.0 / (double)a.temp;
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kStatsPer; ++q)
+      if (q * kStatsThreads + (int)threadIdx.x < a.V) s += exp(((double)v[q] - (double)t.v1) * inv_t);
+    s = block_sum_fixed<kStatsThreads>(s, sh);
+    if (threadIdx.x == 0) a.sumexp[m] = s;
+  }
+}
+void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
+  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
+}
+
+// Order-preserving 32-bit image of a float: a > b as floats iff key(a) >
+// key(b) as unsigned integers (for non-NaN values).
+__device__ __forceinline__ unsigned ord_key(float z) {
+  const unsigned u = __float_as_uint(z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Top-p (nucleus) truncation of the target on the verify side ("self-
 // speculative" page, §3.4: the draft keeps its full distribution, the verify
 // truncates the target and renormalises on the kept set, then the ratio test
@@ -271,15 +271,15 @@ __global__ __launch_bounds__(kStatsThreads) void top_p_kernel(TopPArgs a) {
   __shared__ double sh[kStatsThreads / 64];
   const int m = blockIdx.x;
   const float* z = a.logits + (size_t)m * a.V;
-  const int j0 = threadIdx.x * kStatsPer;
   const double mx = a.mx[m], inv_t = 1.0 / (double)a.temp;
+  auto id_of = [](int q) { return q * kStatsThreads + (int)threadIdx.x; };  // coalesced
   unsigned key[kStatsPer];
   double e[kStatsPer];
   double part = 0.0;
 #pragma unroll
   for (int q = 0; q < kStatsPer; ++q) {
-    const bool in = j0 + q < a.V;
-    const float zv = in ? z[j0 + q] : -INFINITY;
+    const bool in = id_of(q) < a.V;
+    const float zv = in ? z[id_of(q)] : -INFINITY;
     key[q] = in ? ord_key(zv) : 0u;
     e[q] = in ? exp(((double)zv - mx) * inv_t) : 0.0;
     part += e[q];
@@ -307,13 +307,13 @@ __global__ __launch_bounds__(kStatsThreads) void top_p_kernel(TopPArgs a) {
     const int mid = (ilo + ihi) / 2;
     double s = 0.0;
 #pragma unroll
-    for (int q = 0; q < kStatsPer; ++q) s += (key[q] == kap && j0 + q <= mid) ? e[q] : 0.0;
+    for (int q = 0; q < kStatsPer; ++q) s += (key[q] == kap && id_of(q) <= mid) ? e[q] : 0.0;
     if (above + block_sum_fixed<kStatsThreads>(s, sh) >= thr) ihi = mid;
     else ilo = mid + 1;
   }
   double s_tie = 0.0;
 #pragma unroll
-  for (int q = 0; q < kStatsPer; ++q) s_tie += (key[q] == kap && j0 + q <= ilo) ? e[q] : 0.0;
+  for (int q = 0; q < kStatsPer; ++q) s_tie += (key[q] == kap && id_of(q) <= ilo) ? e[q] : 0.0;
   const double kept = above + block_sum_fixed<kStatsThreads>(s_tie, sh);
   if (threadIdx.x == 0) {
     a.key[m] = kap;
@@ -327,33 +327,43 @@ void launch_top_p(const TopPArgs& a, int M, hipStream_t st) {
 
 // Inverse-CDF draw from weights w_j >= 0 (fp64), ids ascending: the smallest
 // j with u*S < C_j, else the largest j with w_j > 0.  For 1024-thread
-// workgroups with the weights already in registers: thread t holds the
-// weights of ids t*kStatsPer ..
-// (t+1)*kStatsPer - 1 (zero past V), so each weight is computed once.  Chunk
-// sums in id order, an inclusive scan of them over each wave, the wave totals
-// in wave order: C_j = (sum of earlier chunks) + (the chunk's own running
-// sum).  Returns -1 when every weight is zero; *total receives S.
-__device__ int block_sample_reg(const double (&w)[kStatsPer], double u, double* total) {
+// workgroups with the weights already in registers, in the coalesced layout
+// of sample_id(): wave w holds ids [2048 w, 2048 (w + 1)), lane l the ids
+// 2048 w + 64 q + l.  C_j = (sum of earlier waves) + (sum of the wave's
+// earlier 64-id rows) + (scan of the row up to lane l), each in a fixed
+// order.  Only ids with w_j > 0 are candidates: sums of the same weights
+// grouped differently may differ in the last bit, so C_j can step up by a
+// rounding error over a run of zero weights.  Returns -1 when every weight is
+// zero; *total receives S.
+__device__ __forceinline__ int sample_id(int q) {
+  return (int)(threadIdx.x >> 6) * (64 * kStatsPer) + q * 64 + (int)(threadIdx.x & 63);
+}
+__device__ int block_sample_reg(double (&w)[kStatsPer], double u, double* total) {
   __shared__ double wsum[kStatsThreads / 64];
   __shared__ int s_pick, s_last;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int j0 = t * kStatsPer;
-  double s = 0.0;
   int last = -1;
+  unsigned pos = 0;  // bit q: w[q] > 0
+#pragma unroll
+  for (int q = 0; q < kStatsPer; ++q)
+    if (w[q] > 0.0) {
+      last = sample_id(q);
+      pos |= 1u << q;
+    }
+  // w[q] <- carry of the earlier rows + inclusive scan of row q up to this lane
+  double carry = 0.0;
 #pragma unroll
   for (int q = 0; q < kStatsPer; ++q) {
-    s += w[q];
-    if (w[q] > 0.0) last = j0 + q;
-  }
-  double incl = s;
+    double incl = w[q];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    w[q] = carry + incl;
+    carry += __shfl(incl, 63, 64);
   }
-  double excl = __shfl_up(incl, 1, 64);
-  if (lane == 0) excl = 0.0;
-  if (lane == 63) wsum[wave] = incl;
+  if (lane == 0) wsum[wave] = carry;
   if (t == 0) {
     s_pick = INT_MAX;
     s_last = -1;
@@ -367,12 +377,10 @@ __device__ int block_sample_reg(const double (&w)[kStatsPer], double u, double* 
     tot += wsum[i];
   }
   const double target = u * tot;
-  double c = base + excl;
 #pragma unroll
   for (int q = 0; q < kStatsPer; ++q) {
-    c += w[q];
-    if (target < c) {
-      atomicMin(&s_pick, j0 + q);
+    if (((pos >> q) & 1u) && target < base + w[q]) {
+      atomicMin(&s_pick, sample_id(q));
       break;
     }
   }
@@ -396,25 +404,25 @@ __global__ __launch_bounds__(kStatsThreads) void pick_kernel(PickArgs a) {
       const int e = g * a.Mprev + a.src[i];
       t = top2_merge(t, Top2{a.amax_val[e], a.amax_idx[e], -INFINITY});
     }
-    t = block_top2_n<kStatsThreads>(t);
+    t = block_top2_fast<kStatsThreads>(t);
     tok = t.i1;
   } else {
-    // draw from softmax(z / T): the row in registers, its max, the weights
-    // exp((z - max) / T) once, then the inverse-CDF draw
+    // draw from softmax(z / T): the row in registers (coalesced), its max,
+    // the weights exp((z - max) / T) once, then the inverse-CDF draw
     const float* z = a.logits + (size_t)a.lrow[i] * a.V;
-    const int j0 = threadIdx.x * kStatsPer;
     float v[kStatsPer];
     Top2 t{-INFINITY, INT_MAX, -INFINITY};
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {
-      v[q] = j0 + q < a.V ? z[j0 + q] : -INFINITY;
-      if (j0 + q < a.V) t = top2_merge(t, Top2{v[q], j0 + q, -INFINITY});
+      const int j = sample_id(q);
+      v[q] = j < a.V ? z[j] : -INFINITY;
+      if (j < a.V) t = top2_merge(t, Top2{v[q], j, -INFINITY});
     }
-    t = block_top2_n<kStatsThreads>(t);
+    t = block_top2_fast<kStatsThreads>(t);
     const double mx = t.v1, inv_t = 1.0 / (double)a.temp;
     double w[kStatsPer];
 #pragma unroll
-    for (int q = 0; q < kStatsPer; ++q) w[q] = j0 + q < a.V ? exp(((double)v[q] - mx) * inv_t) : 0.0;
+    for (int q = 0; q < kStatsPer; ++q) w[q] = sample_id(q) < a.V ? exp(((double)v[q] - mx) * inv_t) : 0.0;
     double tot;
     tok = block_sample_reg(w, a.u[(size_t)a.uidx[i] * VS_N_UNIFORMS + a.slot], &tot);
   }
@@ -501,8 +509,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
   __syncthreads();
   const int reject = s_reject;
   int y;
-  // weights of the draw in registers: thread t holds ids t*kStatsPer ..
-  const int j0 = threadIdx.x * kStatsPer;
+  // weights of the draw in registers, in the layout of sample_id()
   double w[kStatsPer];
   double tot;
   auto target_weights = [&](int r) {  // exp((z - max)/T) on the (top-p) support
@@ -510,7 +517,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
     const double mt = a.mx[r];
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {
-      const int j = j0 + q;
+      const int j = sample_id(q);
       w[q] = (j < a.V && kept(r, j, zt[j])) ? exp(((double)zt[j] - mt) * inv_t) : 0.0;
     }
   };
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
     const double mt = a.mx[r], md = a.dmx[r], st = tp ? a.tp_mass[r] : a.sumexp[r], sd = a.dsumexp[r];
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {  // residual max(0, p - q)
-      const int j = j0 + q;
+      const int j = sample_id(q);
       if (j < a.V) {
         const double p = kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) / st : 0.0;
         const double qd = exp(((double)zd[j] - md) * inv_t) / sd;
