@@ -89,7 +89,7 @@ constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows *
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -130,6 +130,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.tp_key = take(R * 4);
   w.tp_id = take(R * 4);
   w.tp_mass = take(R * 8);
+  w.rs = take(R * 4);
   w.total = off;
   return w;
 }
@@ -160,7 +161,7 @@ struct vs_model {
   char* ws = nullptr;
   unsigned* attn_cnt;
   TreeArgs tree;          // device pointers of the tree drafting state
-  float *h, *ss, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
+  float *h, *ss, *rs, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
   int* kvrow;
@@ -269,6 +270,7 @@ GemmArgs gemm_base(vs_model* m, const Mat& W, const uint16_t* xa, int M) {
   g.eps = m->c.rms_eps;
   g.d = m->c.d_model;
   g.out_row_identity = 1;
+  g.rs_buf = m->rs;
   return g;
 }
 
@@ -276,16 +278,24 @@ double gemm_bytes(const Mat& W, int M) {
   return (double)W.bytes() + (double)M * W.k_steps * 32 * 4 + (double)M * W.n_tiles * 16 * 4;
 }
 
-// One GEMM of a pass.  A pass of more than kMaxRows rows runs as launches of
-// kMaxRows rows (row offset m0, row stride = the pass's rows) that all use
-// one launch configuration, so the per-workgroup norm sums of an EPI_RESID
-// product keep one layout.  out_rows (optional): destination row of each
-// pass row (h_copy / logits).  Returns the number of workgroups of a launch.
+// One GEMM of a pass.  The row-tiled form takes the whole pass in one launch
+// unless rows are redirected (out_rows).  Otherwise a pass of more than
+// kMaxRows rows runs as launches of kMaxRows rows (row offset m0, row stride
+// = the pass's rows) that all use one launch configuration, so the
+// per-workgroup norm sums of an EPI_RESID product keep one layout (every
+// form writes one sum per 16 columns).  out_rows (optional): destination row
+// of each pass row (h_copy / logits).  Returns the number of norm / argmax
+// groups a launch writes.
 int run_gemm(vs_model* m, GemmArgs g, int epi, int fam, const Mat& W, hipStream_t st, const int* out_rows) {
   const int M = g.M;
   g.m0 = 0;
   g.ld = M;
-  if (M > kMaxRows) g.cfg = gemm_pick(W.n_tiles, W.k_steps, kMaxRows);
+  if (out_rows == nullptr && gemm_uses_tile(W.n_tiles, W.k_steps, M, g.cfg)) {
+    int groups = 0;
+    timed(m, fam, gemm_bytes(W, M), st, [&](hipEvent_t e0, hipEvent_t e1) { groups = launch_gemm(g, epi, st, e0, e1); });
+    return groups;
+  }
+  if (M > kMaxRows && !gemm_uses_tile(W.n_tiles, W.k_steps, kMaxRows, g.cfg)) g.cfg = gemm_pick(W.n_tiles, W.k_steps, kMaxRows);
   int groups = 0;
   for (int m0 = 0; m0 < M; m0 += kMaxRows) {
     GemmArgs c = g;
@@ -578,6 +588,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->xa_o = reinterpret_cast<uint16_t*>(w + m->wsl.xa_o);
   m->xa_act = reinterpret_cast<uint16_t*>(w + m->wsl.xa_act);
   m->ss = reinterpret_cast<float*>(w + m->wsl.ss);
+  m->rs = reinterpret_cast<float*>(w + m->wsl.rs);
   m->q = reinterpret_cast<float*>(w + m->wsl.q);
   m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
   m->kvrow = reinterpret_cast<int*>(w + m->wsl.kvrow);

@@ -1,0 +1,45 @@
+// Device pieces shared by the two GEMM forms (k_gemm.hip, k_gemm_tile.hip).
+//
+// A row's outputs must carry the same bits whichever form computes them and
+// whichever rows share its pass (greedy verify equals plain decoding token
+// for token only if a row's logits do not depend on its neighbours).  Both
+// forms therefore use one MFMA shape with one K order, one grouping of the
+// partial sums, and the arithmetic below; both files are compiled with
+// floating-point contraction off, so no multiply-add is fused differently in
+// one form than in the other.
+#pragma once
+#include "kernels.h"
+
+namespace vs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Number of K chunks whose partial sums a column adds in chunk order: a
+// property of the matrix alone (4 for the wide matrices, >= 512 n-tiles,
+// else 8), never of the rows in the pass.
+__host__ __device__ __forceinline__ int gemm_k_chunks(int n_tiles) { return n_tiles >= 512 ? 4 : 8; }
+// The row-tiled form needs equal K chunks of a multiple of 8 k-steps.
+__host__ __device__ __forceinline__ bool gemm_tile_fits(int n_tiles, int k_steps) {
+  return k_steps % (gemm_k_chunks(n_tiles) * 8) == 0;
+}
+
+// RMSNorm scale from the four strided partial sums S_q (q = group mod 4).
+__device__ __forceinline__ float norm_scale(float s0, float s1, float s2, float s3, float inv_d, float eps) {
+  const float t = (s0 + s1) + (s2 + s3);
+  return 1.0f / sqrtf(t * inv_d + eps);
+}
+
+// RoPE rotation of the pair (y0, y1) = (x_i, x_{i + hd/2}) by (cos, sin).
+__device__ __forceinline__ float rope_first(float y0, float y1, float2 r) { return y0 * r.x - y1 * r.y; }
+__device__ __forceinline__ float rope_second(float y0, float y1, float2 r) { return y1 * r.x + y0 * r.y; }
+
+// SwiGLU: silu(g) * u.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+}  // namespace vs

@@ -16,17 +16,12 @@
 //  * RMSNorm is fused: the producer wrote x*g and per-group sums of x^2; the
 //    1/rms scale is applied to the outputs here.  Epilogues: residual add,
 //    q/k RoPE + KV-cache append, SwiGLU, logits + argmax partials.
-#include "kernels.h"
+//  * Passes of more than 8 rows over the wide matrices run the row-tiled
+//    form in k_gemm_tile.hip, which keeps every row's arithmetic identical.
+#pragma clang fp contract(off)
+#include "gemm_dev.h"
 
 namespace vs {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
-                                                 0, 0);
-}
 
 // MT = 0 is the packed form for M <= 8: one 16-row A operand holds the hi
 // parts of the rows in A rows 0-7 and their lo parts in rows 8-15, so a
@@ -135,10 +130,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   };
   auto finish_rs = [&]() {
     __syncthreads();
-    if (tid < M) {
-      const float t = (sstmp[tid] + sstmp[M + tid]) + (sstmp[2 * M + tid] + sstmp[3 * M + tid]);
-      rs[tid] = 1.0f / sqrtf(t * a.inv_d + a.eps);
-    }
+    if (tid < M) rs[tid] = norm_scale(sstmp[tid], sstmp[M + tid], sstmp[2 * M + tid], sstmp[3 * M + tid], a.inv_d, a.eps);
   };
   if (n_ss > kSS) {  // many sums (large M): reduce straight from memory, before the weight stream starts
     const float s = first_level([&](int g, int m) { return a.ss[(size_t)g * ld + m0 + m]; });
@@ -283,9 +275,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         const int ci = (nn % hd) >> 1;
         float o0 = y0, o1 = y1;
         if (hb < a.H + a.Hkv) {
-          const float2 r = pre_rope[j];
-          o0 = y0 * r.x - y1 * r.y;
-          o1 = y1 * r.x + y0 * r.y;
+          o0 = rope_first(y0, y1, pre_rope[j]);
+          o1 = rope_second(y0, y1, pre_rope[j]);
         }
         if (hb < a.H) {
           float* qo = a.q + ((size_t)(m0 + m) * a.H + hb) * hd;
@@ -314,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const int f = (tile0 * 16) / 2 + pr;  // packed pair (gate f, up f)
       const float g = result(m, 2 * pr) * rs[m];
       const float u = result(m, 2 * pr + 1) * rs[m];
-      const float act = g / (1.0f + expf(-g)) * u;
+      const float act = silu_mul(g, u);
       xa_store(a.xa_act, f, m0 + m, ld, act);
     }
   } else {  // EPI_LOGITS
@@ -394,7 +385,13 @@ static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
   else launch_mt<EPI, 4>(a, cfg, st, ev);
 }
 
+bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg) {
+  if (M <= 8 || !gemm_tile_fits(n_tiles, k_steps)) return false;
+  return cfg >= kGemmCfgTile || (cfg == 0 && n_tiles >= 512);
+}
+
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (gemm_uses_tile(a.n_tiles, a.k_steps, a.M, a.cfg)) return launch_gemm_tile(a, epi, a.cfg - kGemmCfgTile, st, ev0, ev1);
   const Ev ev{ev0, ev1};
   int cfg = (a.cfg > 0 && a.cfg < kGemmCfgs) ? a.cfg : gemm_pick(a.n_tiles, a.k_steps, a.M);
   if (gemm_cfg(cfg).ntw == 2 && a.n_tiles % 2 != 0) cfg -= 2;  // same waves, one n-tile

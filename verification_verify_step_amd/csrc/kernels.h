@@ -47,6 +47,10 @@ struct GemmArgs {
   int out_row_identity;
   int out_row[kMaxRows];
   int cfg;               // launch configuration (0: chosen from the shape), see gemm_cfg()
+  // Row-tiled form: per-row norm scales, computed into rs_buf[m0 .. m0+M)
+  // (a workspace of the pass's rows) before the product when ss is set.
+  float* rs_buf;
+  const float* rs;
 };
 
 // Launch configurations: n-tiles per workgroup (NTW) x waves per workgroup
@@ -59,7 +63,20 @@ constexpr int kGemmCfgs = 5;
 GemmCfg gemm_cfg(int id);
 int gemm_pick(int n_tiles, int k_steps, int M);
 // ev0/ev1 (optional): events timestamped at the kernel's own start and end.
+// Passes of more than 8 rows over matrices of >= 512 n-tiles go to the
+// row-tiled form (cfg 0 or kGemmCfgTile) when its K chunks fit
+// (gemm_tile_fits); cfg 1..4 force the skinny form.
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+constexpr int kGemmCfgTile = 8;  // row-tiled form, n-tiles per wave chosen from the shape (+1, +2, +4: forced)
+bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg);
+
+// Row-tiled form: row blocks of 16*mw rows (n_mblk of them), 4*ntw n-tiles
+// per workgroup.  Returns the number of 16-column groups (= n_tiles).
+struct TileShape {
+  int mw, ntw, n_mblk;
+};
+TileShape gemm_tile_shape(int n_tiles, int M, int ntw);
+int launch_gemm_tile(const GemmArgs& a, int epi, int ntw, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 struct AttnArgs {
   RowMap rows;
