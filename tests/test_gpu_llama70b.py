@@ -114,6 +114,14 @@ def test_head_and_ragged_greedy_accept(ctx):
     dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
     zo = dec.head(Y.cpu().numpy().astype(np.float64)[sample])
     assert np.abs(zg[sample].astype(np.float64) - zo).max() <= G.LOGIT_TOL
+    # the whole pass ran the row-tiled GEMM; launches of 8 rows run the
+    # skinny form: the same bits row for row
+    for c0 in (0, 8, (M // 2) // 8 * 8, (M - 1) // 8 * 8):
+        n = min(8, M - c0)
+        zc = torch.empty((n, CFG.vocab), dtype=torch.float32, device="cuda")
+        B.vs_head(e.model, n, Y[c0:c0 + n].contiguous().data_ptr(), zc.data_ptr(), e.stream)
+        torch.cuda.synchronize()
+        assert np.array_equal(zc.cpu().numpy(), zg[c0:c0 + n]), c0
     toks = ctx["toks"].cpu().numpy().copy()
     want = []
     for i in range(N):

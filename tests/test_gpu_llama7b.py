@@ -88,6 +88,29 @@ def test_head_parity_and_greedy_accept(ctx):
     assert (a, y) == (oa, oy) and path == list(range(1, a + 1))
 
 
+def test_head_rows_identical_across_gemm_forms(ctx):
+    """A row's logits do not depend on the rows that share its pass: 64 rows
+    (row-tiled GEMM, one block of 4 m-tiles), the first 17 of them (tiled,
+    2 m-tiles) and launches of 8 rows (skinny packed form) give the same
+    bits.  Sampled rows against the oracle's head."""
+    e = ctx["e"]
+    rng = np.random.default_rng(0x5EED7711)
+    X = torch.tensor(rng.standard_normal((64, CFG.d_model)), dtype=torch.float32, device="cuda")
+    def head(rows):
+        z = torch.empty((rows.shape[0], CFG.vocab), dtype=torch.float32, device="cuda")
+        B.vs_head(e.model, rows.shape[0], rows.data_ptr(), z.data_ptr(), e.stream)
+        return z
+    z64 = head(X)
+    z17 = head(X[:17].contiguous())
+    z8 = torch.cat([head(X[i:i + 8].contiguous()) for i in range(0, 64, 8)])
+    torch.cuda.synchronize()
+    assert torch.equal(z64, z8)
+    assert torch.equal(z17, z8[:17])
+    dec = Decoder(CFG, SynthWeights(CFG, precision="bf16", cache=True))
+    zo = dec.head(X.cpu().numpy().astype(np.float64)[[0, 63]])
+    assert np.abs(z64.cpu().numpy()[[0, 63]].astype(np.float64) - zo).max() <= G.LOGIT_TOL
+
+
 def test_first_L_kv_identity(ctx):
     """The draft's first-L KV (k+1 sequential one-row passes) equals one batched
     pass over the same k+1 rows, bit for bit."""
