@@ -84,12 +84,13 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
 }
 
 constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
+constexpr int kAmapSlots = 4;                         // attention work maps in rotation
 // tree drafting state: node arrays (4 int + 1 double per node), meta, row arrays
 constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows * 24;
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, amap, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -131,6 +132,7 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.tp_id = take(R * 4);
   w.tp_mass = take(R * 8);
   w.rs = take(R * 4);
+  w.amap = take((size_t)kAmapSlots * kAttnMapMax * 4);
   w.total = off;
   return w;
 }
@@ -162,6 +164,14 @@ struct vs_model {
   unsigned* attn_cnt;
   TreeArgs tree;          // device pointers of the tree drafting state
   float *h, *ss, *rs, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
+  // attention work maps: device slots in the workspace, pinned staging on
+  // the host; ev[slot] follows the last launch that read the slot
+  int* amap_dev[kAmapSlots] = {};
+  int* amap_pin[kAmapSlots] = {};
+  hipEvent_t amap_ev[kAmapSlots] = {};
+  int amap_slot = -1;
+  hipStream_t amap_stream = nullptr;  // stream of the last launch that read the current slot
+  std::vector<int> amap_build, amap_last;
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
   int* kvrow;
@@ -344,6 +354,66 @@ void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const
   m->ss_groups = (m->c.d_model + 255) / 256;
 }
 
+// Attention work map of a pass: sequence i takes ceil(P_i / kps) committed
+// splits (P_i its context bound) plus the in-round window, and only its
+// non-empty query groups, instead of every sequence taking the longest
+// one's splits and every query group.  The (sequence, KV head, key range)
+// groups go to the least-loaded XCD, their query groups back to back there
+// (block b runs on XCD b % 8).  The map is uploaded when it changes, through
+// a rotation of pinned staging and device slots; a slot is rewritten only
+// after the last launch that read it has run.  Returns the slot used, or -1: no map (it would not fit, or
+// would save little over the plain grid).
+int attn_work_map(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, hipStream_t st) {
+  const int wv = attn_waves(a.qg_size);
+  std::vector<int>& mp = m->amap_build;
+  std::vector<int> lists[8];
+  long load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < rm.n_seq; ++i) {
+    const int nr = rm.row_start[i + 1] - rm.row_start[i];
+    const int nqg = (nr * G + a.qg_size - 1) / a.qg_size;
+    const int Pi = kv->P_ub[rm.seq[i]];
+    const int ns = std::min(a.n_split, (Pi + a.kps - 1) / a.kps);
+    a.nsplit[i] = ns;
+    const int wpb = (ns + 1 + wv - 1) / wv;
+    for (int kvh = 0; kvh < a.Hkv; ++kvh)
+      for (int wg = 0; wg < wpb; ++wg) {
+        int x = 0;
+        for (int j = 1; j < 8; ++j)
+          if (load[j] < load[x]) x = j;
+        for (int qg = 0; qg < nqg; ++qg) lists[x].push_back(i | kvh << 6 | qg << 13 | wg << 20);
+        load[x] += nqg;
+      }
+  }
+  size_t n = 0, used = 0;
+  for (int x = 0; x < 8; ++x) {
+    n = std::max(n, lists[x].size());
+    used += lists[x].size();
+  }
+  // The plain grid launches every sequence with the longest one's splits and
+  // every query group; keep it (no upload) unless the map saves a tenth.
+  const size_t wps = (size_t)(a.n_split + wv) / wv;
+  const size_t plain = (size_t)8 * a.n_qg * ((rm.n_seq * wps * a.Hkv + 7) / 8);
+  if (n == 0 || 8 * n > (size_t)kAttnMapMax || 10 * used > 9 * plain) return -1;
+  mp.assign(8 * n, -1);
+  for (int x = 0; x < 8; ++x)
+    for (size_t p = 0; p < lists[x].size(); ++p) mp[8 * p + x] = lists[x][p];
+  if (m->amap_slot < 0 || mp != m->amap_last) {
+    // every launch that read the current slot is on the stream before this
+    // point; a slot is refilled only once its event has passed
+    if (m->amap_slot >= 0) (void)hipEventRecord(m->amap_ev[m->amap_slot], m->amap_stream);
+    const int slot = (m->amap_slot + 1) % kAmapSlots;
+    (void)hipEventSynchronize(m->amap_ev[slot]);
+    memcpy(m->amap_pin[slot], mp.data(), mp.size() * 4);
+    (void)hipMemcpyAsync(m->amap_dev[slot], m->amap_pin[slot], mp.size() * 4, hipMemcpyHostToDevice, st);
+    m->amap_slot = slot;
+    m->amap_last = mp;
+  }
+  a.map = m->amap_dev[m->amap_slot];
+  a.map_n = (int)mp.size();
+  m->amap_stream = st;
+  return m->amap_slot;
+}
+
 int ctx_bound(vs_kv* kv, const RowMap& rm) {
   int p = 0;
   for (int i = 0; i < rm.n_seq; ++i) p = std::max(p, kv->P_ub[rm.seq[i]]);
@@ -396,6 +466,7 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   a.xa_o = m->xa_o;
   a.M = rm.M;
   a.use_mfma = 1;
+  attn_work_map(m, kv, rm, G, a, st);
   double bytes = 0;
   for (int i = 0; i < rm.n_seq; ++i)
     bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
@@ -631,15 +702,20 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   // the attention kernel's arrival counters start at zero and every launch
   // leaves them at zero
   hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
+  for (int i = 0; i < kAmapSlots && ae == hipSuccess; ++i) {
+    m->amap_dev[i] = reinterpret_cast<int*>(w + m->wsl.amap) + (size_t)i * kAttnMapMax;
+    ae = hipHostMalloc(reinterpret_cast<void**>(&m->amap_pin[i]), (size_t)kAttnMapMax * 4, hipHostMallocDefault);
+    if (ae == hipSuccess) ae = hipEventCreateWithFlags(&m->amap_ev[i], hipEventDisableTiming);
+  }
   if (ae == hipSuccess) ae = attn_init();
   if (ae != hipSuccess) {
-    delete m;
+    vs_model_destroy(m);
     (void)hipGetLastError();
     return fail(VS_E_DEVICE, "vs_model_create: attention set-up: %s", hipGetErrorString(ae));
   }
   vs_status rc = check_launch("vs_model_create");
   if (rc != VS_OK) {
-    delete m;
+    vs_model_destroy(m);
     return rc;
   }
   *out = m;
@@ -691,6 +767,13 @@ vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const 
 void vs_model_destroy(vs_model* m) {
   if (!m) return;
   for (auto e : m->ev_pool) hipEventDestroy(e);
+  for (int i = 0; i < kAmapSlots; ++i) {
+    if (m->amap_ev[i] != nullptr) {
+      (void)hipEventSynchronize(m->amap_ev[i]);
+      hipEventDestroy(m->amap_ev[i]);
+    }
+    if (m->amap_pin[i] != nullptr) hipHostFree(m->amap_pin[i]);
+  }
   delete m;
 }
 

@@ -79,22 +79,36 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   __shared__ int last_wg;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_parts = a.n_split + 1;
-  const int wpb = (n_parts + kWaves - 1) / kWaves;  // workgroups per unit
+  const int wps = (a.n_split + 1 + kWaves - 1) / kWaves;  // partial records per unit (layout)
   // The query groups of one (sequence, KV head, key range) read the same
   // K/V.  Workgroups are handed to the 8 XCDs round-robin by index, so the
-  // index b is decoded as XCD b % 8 and position b / 8 on it, with the query
-  // group varying fastest along that position: the groups of a key range run
-  // back to back on one XCD and the later ones find the K/V in its L2.
-  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
-  const int qg = pos % a.n_qg;
-  const int g = (pos / a.n_qg) * 8 + xcd;  // (sequence, workgroup of the unit, KV head)
-  const int X = a.rows.n_seq * wpb;
-  if (g >= X * a.Hkv) return;  // grid padding
-  const int i = (g % X) / wpb;
-  const int wgi = (g % X) % wpb;
+  // index b is read as XCD b % 8 and position b / 8 on it; the host lays the
+  // work out (map) so that the query groups of a key range run back to back
+  // on one XCD and the later ones find the K/V in its L2.  Without a map:
+  // every sequence takes n_split splits and n_qg query groups, the query
+  // group varying fastest along the position.
+  int i, kvh, qg, wgi;
+  if (a.map != nullptr) {
+    const int e = a.map[blockIdx.x];
+    if (e < 0) return;  // grid padding
+    i = e & 63;
+    kvh = (e >> 6) & 127;
+    qg = (e >> 13) & 127;
+    wgi = e >> 20;
+  } else {
+    const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+    qg = pos % a.n_qg;
+    const int g = (pos / a.n_qg) * 8 + xcd;  // (sequence, workgroup of the unit, KV head)
+    const int X = a.rows.n_seq * wps;
+    if (g >= X * a.Hkv) return;  // grid padding
+    i = (g % X) / wps;
+    wgi = (g % X) % wps;
+    kvh = g / X;
+  }
+  const int n_split = a.map != nullptr ? a.nsplit[i] : a.n_split;  // this sequence's committed splits
+  const int n_parts = n_split + 1;
+  const int wpb = (n_parts + kWaves - 1) / kWaves;  // workgroups of this unit
   const int split = wgi * kWaves + wave;
-  const int kvh = g / X;
   const int sq = a.rows.seq[i];
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
@@ -106,7 +120,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const bool active = split < n_parts;
   const int P = a.kv.P[sq];
   const int W = a.rows.idx_off + nr;  // in-round keys present: window indices 0..W-1
-  const bool window = split == a.n_split;
+  const bool window = split == n_split;
   int key_lo, key_hi;  // valid slots of this split
   if (!window) {
     key_lo = split * a.kps;
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const size_t QG = a.qg_size;
   float* po = a.part;                                              // [units][wpb][QG][HD]
   uint64_t* pml = reinterpret_cast<uint64_t*>(a.part + a.ml_off);  // [units][wpb][QG] (max, sum)
-  const size_t rec = (size_t)unit * wpb + wgi;
+  const size_t rec = (size_t)unit * wps + wgi;
   for (int e = lane; e < nq * DS; e += 64) {
     const int row = e / DS, d = wave * DS + e % DS;
     float o = 0.f;
@@ -373,7 +387,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   float2* cml = reinterpret_cast<float2*>(smem);  // [wpb][nq] (max, sum)
   float* cwt = smem + 2 * kAttnCombineSlots;      // [wpb][nq] weights
   float* ctot = cwt + kAttnCombineSlots;          // [nq]
-  const uint64_t* src0 = reinterpret_cast<const uint64_t*>(po) + (size_t)unit * wpb * QG * HP;
+  const uint64_t* src0 = reinterpret_cast<const uint64_t*>(po) + (size_t)unit * wps * QG * HP;
   const int S = (int)QG * HP;  // pairs between consecutive partials
   const int npair = nq * HP;
   uint64_t xc[kCB];
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   if (threadIdx.x < npair) load_batch(threadIdx.x, 0);
   for (int e = threadIdx.x; e < wpb * nq; e += kThreads) {
     const int j = e / nq, r = e - j * nq;
-    const uint64_t b = __hip_atomic_load(pml + ((size_t)unit * wpb + j) * QG + r, __ATOMIC_RELAXED,
+    const uint64_t b = __hip_atomic_load(pml + ((size_t)unit * wps + j) * QG + r, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
     cml[e] = make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
   }
@@ -441,7 +455,7 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEven
   const int wv = attn_waves(a.qg_size);
   const int wpb = (n_parts + wv - 1) / wv;
   const int groups = a.rows.n_seq * wpb * a.Hkv;
-  dim3 grid(8 * a.n_qg * ((groups + 7) / 8));
+  dim3 grid(a.map != nullptr ? a.map_n : 8 * a.n_qg * ((groups + 7) / 8));
   static_assert(kAttnQG <= 16, "one 16-row query tile per wave");
 #define VS_ATT(MTQ, HD, WV)                                                                                 \
   do {                                                                                                      \

@@ -90,14 +90,24 @@ struct AttnArgs {
   int n_qg;
   // Partials of the workgroups of a unit (sequence, kv head, query group):
   // o at part[((unit * wpb + wg) * qg_size + v) * hd + dim], (max, sum) as a
-  // float pair at part[ml_off + 2 * ((unit * wpb + wg) * qg_size + v)].
+  // float pair at part[ml_off + 2 * ((unit * wpb + wg) * qg_size + v)], with
+  // wpb = workgroups per unit at n_split committed splits.
   float* part;
   size_t ml_off;    // floats; even
   unsigned* cnt;    // per-unit arrival counters, zero between launches
   uint16_t* xa_o;
   int M;
   int use_mfma;     // MFMA score/PV path (head_dim 64 or 128)
+  // Work map (optional): one entry per launched workgroup, packed as
+  // i | kvh << 6 | qg << 13 | wg << 20 (sequence index, KV head, query group,
+  // workgroup of the unit), -1 for padding.  With a map, sequence i has its
+  // own committed splits nsplit[i] (<= n_split, which sets the partials'
+  // layout) and only its non-empty query groups are launched.
+  const int* map;
+  int map_n;
+  int nsplit[kMaxSeq];
 };
+constexpr int kAttnMapMax = 1 << 18;     // work-map entries per launch
 // One launch: splits, in-workgroup merge, and the last workgroup's combine.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kAttnQG = 16;              // query vectors per query group
