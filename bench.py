@@ -68,7 +68,7 @@ def pmc_traffic(workload, family):
             k, v = line.rsplit(":", 1)
             kv[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "kernels.h", "common.h"):
+    for f in ("k_gemm.hip", "gemm_dev.h", "kernels.h", "common.h"):
         h.update(open(os.path.join(ROOT, "verification_verify_step_amd", "csrc", f), "rb").read())
     if kv.get("sources_sha256_16") != h.hexdigest()[:16]:
         return None
