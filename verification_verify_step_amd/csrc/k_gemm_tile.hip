@@ -6,8 +6,8 @@
 // batch of rounds multiplies the rows).  The skinny form re-reads the
 // activations from L2 in every wave, which caps it far below the weight
 // stream at these sizes.  Here:
-//  * A workgroup of 4 waves owns a block of BM = 16*MW rows and 4*NWT
-//    n-tiles.  Each k-step's activation fragments of the block (hi and lo
+//  * A workgroup of 4 waves owns a block of BM = 16*MW rows (MW = 1, 2 or 3)
+//    and 4*NWT n-tiles.  Each k-step's activation fragments of the block (hi and lo
 //    parts, 8*BM 16-byte units) are staged once in LDS and read by all four
 //    waves; each wave streams the packed weight fragments of its own NWT
 //    n-tiles straight into registers.
@@ -426,21 +426,23 @@ void go_epi(const GemmArgs& a, const TileShape& sh, hipStream_t st, Ev ev) {
   switch (sh.mw) {
     case 1: go_mw<EPI, 1>(a, sh.n_mblk, sh.ntw, st, ev); break;
     case 2: go_mw<EPI, 2>(a, sh.n_mblk, sh.ntw, st, ev); break;
-    case 3: go_mw<EPI, 3>(a, sh.n_mblk, sh.ntw, st, ev); break;
-    default: go_mw<EPI, 4>(a, sh.n_mblk, sh.ntw, st, ev); break;
+    default: go_mw<EPI, 3>(a, sh.n_mblk, sh.ntw, st, ev); break;
   }
 }
 
 }  // namespace
 
-// Up to 4 m-tiles: one row block.  More: blocks of 3 m-tiles, whose waves
-// take 4 n-tiles each (an LDS fragment then feeds 8 MFMAs).  N-range: the
-// widest (4, 2 or 1 n-tiles per wave; 4 only with up to 3 m-tiles) that
-// still gives >= 200 workgroups.
+// Up to 4 m-tiles (64 rows, bound by the weight stream): blocks of 2
+// m-tiles, which keeps more workgroups and waves in flight (measured at 17,
+// 40 and 64 rows on the 7B QKV, gate/up and head).  More rows (bound by
+// MFMA issue and LDS reads): blocks of 3 m-tiles, whose waves take 4
+// n-tiles each where the grid stays full (an LDS fragment then feeds 8
+// MFMAs).  N-range: the widest (4, 2 or 1 n-tiles per wave; 4 only with up
+// to 3 m-tiles) that still gives >= 200 workgroups.
 TileShape gemm_tile_shape(int n_tiles, int M, int ntw) {
   TileShape sh;
   const int mt = (M + 15) / 16;
-  sh.mw = mt <= 4 ? mt : 3;
+  sh.mw = mt <= 4 ? std::min(mt, 2) : 3;
   sh.n_mblk = (mt + sh.mw - 1) / sh.mw;
   if (ntw == 1 || ntw == 2 || ntw == 4) {
     sh.ntw = ntw;
