@@ -90,7 +90,7 @@ constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows *
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, amap, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, amap, kpart, kcnt, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -133,6 +133,8 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.tp_mass = take(R * 8);
   w.rs = take(R * 4);
   w.amap = take((size_t)kAmapSlots * kAttnMapMax * 4);
+  w.kpart = take(kGemmSplitFloats * 4);
+  w.kcnt = take((size_t)kGemmSplitCells * 4);
   w.total = off;
   return w;
 }
@@ -163,7 +165,8 @@ struct vs_model {
   char* ws = nullptr;
   unsigned* attn_cnt;
   TreeArgs tree;          // device pointers of the tree drafting state
-  float *h, *ss, *rs, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
+  float *h, *ss, *rs, *kpart, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
+  unsigned* kcnt = nullptr;
   // attention work maps: device slots in the workspace, pinned staging on
   // the host; ev[slot] follows the last launch that read the slot
   int* amap_dev[kAmapSlots] = {};
@@ -281,6 +284,8 @@ GemmArgs gemm_base(vs_model* m, const Mat& W, const uint16_t* xa, int M) {
   g.d = m->c.d_model;
   g.out_row_identity = 1;
   g.rs_buf = m->rs;
+  g.kpart = m->kpart;
+  g.kcnt = m->kcnt;
   return g;
 }
 
@@ -660,6 +665,8 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   m->xa_act = reinterpret_cast<uint16_t*>(w + m->wsl.xa_act);
   m->ss = reinterpret_cast<float*>(w + m->wsl.ss);
   m->rs = reinterpret_cast<float*>(w + m->wsl.rs);
+  m->kpart = reinterpret_cast<float*>(w + m->wsl.kpart);
+  m->kcnt = reinterpret_cast<unsigned*>(w + m->wsl.kcnt);
   m->q = reinterpret_cast<float*>(w + m->wsl.q);
   m->rope = reinterpret_cast<float2*>(w + m->wsl.rope);
   m->kvrow = reinterpret_cast<int*>(w + m->wsl.kvrow);
@@ -702,6 +709,8 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   // the attention kernel's arrival counters start at zero and every launch
   // leaves them at zero
   hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
+  // so do the K-split GEMM's arrival counters
+  if (ae == hipSuccess) ae = hipMemset(m->kcnt, 0, kGemmSplitCells * sizeof(unsigned));
   for (int i = 0; i < kAmapSlots && ae == hipSuccess; ++i) {
     m->amap_dev[i] = reinterpret_cast<int*>(w + m->wsl.amap) + (size_t)i * kAttnMapMax;
     ae = hipHostMalloc(reinterpret_cast<void**>(&m->amap_pin[i]), (size_t)kAttnMapMax * 4, hipHostMallocDefault);

@@ -24,8 +24,20 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 // property of the matrix alone (4 for the wide matrices, >= 512 n-tiles,
 // else 8), never of the rows in the pass.
 __host__ __device__ __forceinline__ int gemm_k_chunks(int n_tiles) { return n_tiles >= 512 ? 4 : 8; }
-// The row-tiled form needs equal K chunks of a multiple of 8 k-steps.
-__host__ __device__ __forceinline__ bool gemm_tile_fits(int n_tiles, int k_steps) {
+// The narrow matrices (< 512 n-tiles: too few n-ranges to fill the chip)
+// run the row-tiled form with K split over workgroups, one K chunk each, at
+// up to 64 rows when a chunk is long enough (>= 32 k-steps) to pay for the
+// combine; their chunk sums are added in chunk order by the last workgroup
+// of a tile.  Measured at 40 and 64 rows: the 7B down projection (43
+// k-steps per chunk) gains a quarter to a third; O (16) and the tiny model
+// (1) lose, and keep the skinny form.
+__host__ __device__ __forceinline__ bool gemm_tile_split(int n_tiles, int k_steps, int M) {
+  return n_tiles < 512 && M <= 64 && k_steps % gemm_k_chunks(n_tiles) == 0 && k_steps / gemm_k_chunks(n_tiles) >= 32;
+}
+// Whether the row-tiled form takes the product: the wide matrices with equal
+// K chunks of a multiple of 8 k-steps, the narrow ones with K split.
+__host__ __device__ __forceinline__ bool gemm_tile_fits(int n_tiles, int k_steps, int M) {
+  if (n_tiles < 512) return gemm_tile_split(n_tiles, k_steps, M);
   return k_steps % (gemm_k_chunks(n_tiles) * 8) == 0;
 }
 

@@ -386,8 +386,8 @@ static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
 }
 
 bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg) {
-  if (M <= 8 || !gemm_tile_fits(n_tiles, k_steps)) return false;
-  return cfg >= kGemmCfgTile || (cfg == 0 && n_tiles >= 512);
+  if (M <= 8 || !gemm_tile_fits(n_tiles, k_steps, M)) return false;
+  return cfg >= kGemmCfgTile || cfg == 0;
 }
 
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {

@@ -95,18 +95,23 @@ __global__ __launch_bounds__(4 * kScaleRows) void row_scale_kernel(const float* 
     rs[m0 + m] = norm_scale(part[0][r], part[1][r], part[2][r], part[3][r], inv_d, eps);
 }
 
-template <int MW, int NWT, int PD, int EPI>
+template <int MW, int NWT, int PD, int EPI, bool SK>
 __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs a, const int n_chunks,
                                                                  const int n_mblk, const int n_grp) {
   static_assert(PD % 2 == 0, "the LDS buffer of a k-step is its parity");
   constexpr int NT = kTileThreads, BM = 16 * MW, UA = 8 * BM, UPT = (UA + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // workgroup -> (row block, n-range): XCD = index mod 8; the row blocks of
-  // an n-range are consecutive on that XCD.  Padding workgroups return.
-  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  // workgroup -> (K chunk when split, row block, n-range): XCD = index mod
+  // 8; the row blocks of an n-range are consecutive on that XCD.  Padding
+  // workgroups return.
+  const int xcd = blockIdx.x & 7, pos0 = blockIdx.x >> 3;
+  const int chunk = SK ? pos0 % n_chunks : 0, pos = SK ? pos0 / n_chunks : pos0;
   const int mb = pos % n_mblk, grp = (pos / n_mblk) * 8 + xcd;
   if (grp >= n_grp) return;
   const int M = a.M, m0 = a.m0, ld = a.ld, ks = a.k_steps;
+  const int per = ks / n_chunks;                // k-steps of a K chunk
+  const int c0 = SK ? chunk * per : 0;          // this workgroup's k-steps: c0 .. c0 + ns - 1
+  const int ns = SK ? per : ks;
   const int mrow0 = mb * BM, Mb = min(BM, M - mrow0);  // rows of this block, launch-relative
   const int tile0 = (grp * 4 + wave) * NWT;
   const int mrow = lane & 15, kq = lane >> 4;
@@ -131,7 +136,8 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   }
 
   u32x4 wb[PD][NWT], ar[PD][UPT];
-  auto load = [&](int p, int s) {
+  auto load = [&](int p, int j) {  // ring slot p <- k-step c0 + j (clamped to the workgroup's range)
+    const int s = c0 + min(j, ns - 1);
 #pragma unroll
     for (int t = 0; t < NWT; ++t) wb[p][t] = wbase[t][(size_t)s * 64];
 #pragma unroll
@@ -183,38 +189,90 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
 
   // operand prologue (PD k-steps)
 #pragma unroll
-  for (int p = 0; p < PD; ++p) load(p, min(p, ks - 1));
+  for (int p = 0; p < PD; ++p) load(p, p);
 
   // RMSNorm scales of the block's rows (row_scale_kernel ran just before)
   for (int r = tid; r < BM; r += NT) rs[r] = a.rs != nullptr ? a.rs[m0 + mrow0 + min(r, Mb - 1)] : 1.0f;
 
-  // Main loop.  K-step s: its A operands were fetched from LDS buffer s & 3
-  // during step s - 1; it fetches step s + 1's, runs its MFMAs, stores
-  // A(s + 2) into buffer (s + 2) & 3, refills ring slot s % PD with k-step
-  // s + PD and meets the workgroup at a barrier (so A(s + 2) is visible
-  // when step s + 1 fetches it, and buffer (s + 2) & 3, last read during
-  // step s - 3, is free).  The launcher guarantees equal chunks of a
-  // multiple of 8 k-steps, so the unrolled body has no branch and the chunk
-  // sums close between groups.
+  // Main loop over the workgroup's k-steps j = 0 .. ns - 1 (k-step c0 + j).
+  // Step j: its A operands were fetched from LDS buffer j & 3 during step
+  // j - 1; it fetches step j + 1's, runs its MFMAs, stores A(j + 2) into
+  // buffer (j + 2) & 3, refills ring slot j % PD with step j + PD and meets
+  // the workgroup at a barrier (so A(j + 2) is visible when step j + 1
+  // fetches it, and buffer (j + 2) & 3, last read during step j - 3, is
+  // free).  Steps run in unrolled groups of 8; a whole-K workgroup's chunks
+  // are multiples of 8 steps (gemm_tile_fits) and close between groups, a
+  // K-split workgroup runs one chunk and a guarded tail.
   static_assert(PD == 4 || PD == 8, "ring slots and LDS buffers rotate together");
   put(0, 0);
   put(1, 1);
   __syncthreads();
   fetch(0, 0);
-  const int per = ks / n_chunks;
-  for (int c = 0; c < n_chunks; ++c) {
-    for (int s = c * per; s < (c + 1) * per; s += 8) {
+  auto step = [&](int p, int j0) {
+    fetch((p + 1) & 1, (p + 1) & 3);
+    compute(p & 1, p % PD);
+    put((p + 2) % PD, (p + 2) & 3);
+    load(p % PD, j0 + p + PD);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int j0 = 0;
+  for (; j0 + 8 <= ns; j0 += 8) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        fetch((p + 1) & 1, (p + 1) & 3);
-        compute(p & 1, p % PD);
-        put((p + 2) % PD, (p + 2) & 3);
-        load(p % PD, min(s + p + PD, ks - 1));
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
+    for (int p = 0; p < 8; ++p) step(p, j0);
+    if (!SK && (j0 + 8) % per == 0) close_chunk();
+  }
+  if (SK && j0 < ns) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      if (j0 + p < ns) step(p, j0);
+  }
+
+  if constexpr (SK) {
+    // Publish this chunk's sum (hi + lo) with device-coherent stores, count
+    // the workgroup in, and let the last of the tile's n_chunks workgroups
+    // add the chunk sums in chunk order -- the skinny form's order -- before
+    // the epilogue.
+    __shared__ int s_last;
+    const size_t tile_rec = (size_t)MW * NWT * 64 * 2;  // uint64 pairs per wave
+    const size_t cell = (size_t)grp * n_mblk + mb;
+    uint64_t* pw = reinterpret_cast<uint64_t*>(a.kpart) + ((cell * n_chunks + chunk) * 4 + wave) * tile_rec;
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+      for (int t = 0; t < NWT; ++t) {
+        const f32x4 v = hi[mt][t] + lo[mt][t];
+        const size_t e = ((size_t)(mt * NWT + t) * 64 + lane) * 2;
+        __hip_atomic_store(pw + e, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pw + e + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+    // the stores must have completed before the count (a workgroup-scope
+    // fence does not wait for stores on this target)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.kcnt + cell, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (unsigned)(n_chunks - 1);
+      if (s_last) __hip_atomic_store(a.kcnt + cell, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    close_chunk();
+    __syncthreads();
+    if (!s_last) return;
+    const uint64_t* pr = reinterpret_cast<const uint64_t*>(a.kpart) + (cell * n_chunks * 4 + wave) * tile_rec;
+    for (int c = 0; c < n_chunks; ++c) {
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int t = 0; t < NWT; ++t) {
+          const size_t e = (size_t)c * 4 * tile_rec + ((size_t)(mt * NWT + t) * 64 + lane) * 2;
+          const uint64_t u0 = __hip_atomic_load(pr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t u1 = __hip_atomic_load(pr + e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const f32x4 v = {__uint_as_float((uint32_t)u0), __uint_as_float((uint32_t)(u0 >> 32)),
+                           __uint_as_float((uint32_t)u1), __uint_as_float((uint32_t)(u1 >> 32))};
+          y[mt][t] += v;
+        }
+    }
   }
   __syncthreads();  // the epilogues reuse the operand buffers
 
@@ -386,12 +444,12 @@ struct Ev {
   hipEvent_t a, b;
 };
 
-template <int EPI, int MW, int NWT>
+template <int EPI, int MW, int NWT, bool SK>
 void go_tile(const GemmArgs& a, int n_mblk, hipStream_t st, Ev ev) {
   constexpr int PD = MW * NWT >= 12 ? 4 : 8;  // fewer registers for the rings where the k-step is long
   const int n_grp = (a.n_tiles + 4 * NWT - 1) / (4 * NWT);
-  const dim3 grid(8 * n_mblk * ((n_grp + 7) / 8));
   const int nc = gemm_k_chunks(a.n_tiles);
+  const dim3 grid(8 * (SK ? nc : 1) * n_mblk * ((n_grp + 7) / 8));
   GemmArgs g = a;
   hipEvent_t start = ev.a;
   if (a.ss != nullptr) {
@@ -406,27 +464,33 @@ void go_tile(const GemmArgs& a, int n_mblk, hipStream_t st, Ev ev) {
     g.rs = a.rs_buf;
   }
   if (start != nullptr || ev.b != nullptr)
-    hipExtLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI>), grid, dim3(kTileThreads), 0, st, start, ev.b, 0, g, nc,
-                          n_mblk, n_grp);
+    hipExtLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK>), grid, dim3(kTileThreads), 0, st, start, ev.b, 0, g,
+                          nc, n_mblk, n_grp);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI>), grid, dim3(kTileThreads), 0, st, g, nc, n_mblk, n_grp);
+    hipLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK>), grid, dim3(kTileThreads), 0, st, g, nc, n_mblk, n_grp);
 }
 
 // Four n-tiles per wave only with up to three m-tiles: beyond that the
-// accumulators and the operand rings do not fit the registers.
-template <int EPI, int MW>
-void go_mw(const GemmArgs& a, int n_mblk, int ntw, hipStream_t st, Ev ev) {
-  if (ntw == 1) go_tile<EPI, MW, 1>(a, n_mblk, st, ev);
-  else if (ntw == 2 || MW > 3) go_tile<EPI, MW, 2>(a, n_mblk, st, ev);
-  else go_tile<EPI, MW, (MW > 3 ? 2 : 4)>(a, n_mblk, st, ev);
+// accumulators and the operand rings do not fit the registers.  The K split
+// is only used with blocks of up to 2 m-tiles (passes of up to 64 rows).
+template <int EPI, int MW, bool SK>
+void go_ntw(const GemmArgs& a, int n_mblk, int ntw, hipStream_t st, Ev ev) {
+  if (ntw == 1) go_tile<EPI, MW, 1, SK>(a, n_mblk, st, ev);
+  else if (ntw == 2 || MW > 3) go_tile<EPI, MW, 2, SK>(a, n_mblk, st, ev);
+  else go_tile<EPI, MW, (MW > 3 ? 2 : 4), SK>(a, n_mblk, st, ev);
 }
 
 template <int EPI>
 void go_epi(const GemmArgs& a, const TileShape& sh, hipStream_t st, Ev ev) {
+  if (sh.split) {
+    if (sh.mw == 1) go_ntw<EPI, 1, true>(a, sh.n_mblk, sh.ntw, st, ev);
+    else go_ntw<EPI, 2, true>(a, sh.n_mblk, sh.ntw, st, ev);
+    return;
+  }
   switch (sh.mw) {
-    case 1: go_mw<EPI, 1>(a, sh.n_mblk, sh.ntw, st, ev); break;
-    case 2: go_mw<EPI, 2>(a, sh.n_mblk, sh.ntw, st, ev); break;
-    default: go_mw<EPI, 3>(a, sh.n_mblk, sh.ntw, st, ev); break;
+    case 1: go_ntw<EPI, 1, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
+    case 2: go_ntw<EPI, 2, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
+    default: go_ntw<EPI, 3, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
   }
 }
 
@@ -434,22 +498,26 @@ void go_epi(const GemmArgs& a, const TileShape& sh, hipStream_t st, Ev ev) {
 
 // Up to 4 m-tiles (64 rows, bound by the weight stream): blocks of 2
 // m-tiles, which keeps more workgroups and waves in flight (measured at 17,
-// 40 and 64 rows on the 7B QKV, gate/up and head).  More rows (bound by
+// 40 and 64 rows on the 7B QKV, gate/up and head); the narrow matrices
+// split K over workgroups as well (gemm_tile_split).  More rows (bound by
 // MFMA issue and LDS reads): blocks of 3 m-tiles, whose waves take 4
 // n-tiles each where the grid stays full (an LDS fragment then feeds 8
 // MFMAs).  N-range: the widest (4, 2 or 1 n-tiles per wave; 4 only with up
-// to 3 m-tiles) that still gives >= 200 workgroups.
+// to 3 m-tiles) that still gives >= 200 workgroups (>= 400 with K split).
 TileShape gemm_tile_shape(int n_tiles, int M, int ntw) {
   TileShape sh;
   const int mt = (M + 15) / 16;
+  sh.split = n_tiles < 512;  // the launcher only sends narrow matrices that split K (gemm_tile_fits)
   sh.mw = mt <= 4 ? std::min(mt, 2) : 3;
   sh.n_mblk = (mt + sh.mw - 1) / sh.mw;
+  const long per_grp = (long)sh.n_mblk * (sh.split ? gemm_k_chunks(n_tiles) : 1);
+  const long want = sh.split ? 400 : 200;  // split: measured best at about two workgroups per CU
   if (ntw == 1 || ntw == 2 || ntw == 4) {
     sh.ntw = ntw;
   } else {
     sh.ntw = 1;
     for (int w : {4, 2})
-      if ((long)((n_tiles + 4 * w - 1) / (4 * w)) * sh.n_mblk >= 200) {
+      if ((n_tiles + 4 * w - 1) / (4 * w) * per_grp >= want) {
         sh.ntw = w;
         break;
       }

@@ -51,6 +51,10 @@ struct GemmArgs {
   // (a workspace of the pass's rows) before the product when ss is set.
   float* rs_buf;
   const float* rs;
+  // Row-tiled form with K split: chunk sums [cell][chunk][wave][...] and one
+  // arrival counter per (n-range, row block) cell, zero between launches.
+  float* kpart;
+  unsigned* kcnt;
 };
 
 // Launch configurations: n-tiles per workgroup (NTW) x waves per workgroup
@@ -63,9 +67,11 @@ constexpr int kGemmCfgs = 5;
 GemmCfg gemm_cfg(int id);
 int gemm_pick(int n_tiles, int k_steps, int M);
 // ev0/ev1 (optional): events timestamped at the kernel's own start and end.
-// Passes of more than 8 rows over matrices of >= 512 n-tiles go to the
-// row-tiled form (cfg 0 or kGemmCfgTile) when its K chunks fit
-// (gemm_tile_fits); cfg 1..4 force the skinny form.
+// Passes of more than 8 rows go to the row-tiled form (cfg 0 or
+// kGemmCfgTile) when its K chunks fit (gemm_tile_fits): the wide matrices
+// (>= 512 n-tiles) at any row count, the narrow ones with long K chunks at
+// up to 64 rows with K split over workgroups; cfg 1..4 force the skinny
+// form.
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kGemmCfgTile = 8;  // row-tiled form, n-tiles per wave chosen from the shape (+1, +2, +4: forced)
 bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg);
@@ -74,6 +80,7 @@ bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg);
 // per workgroup.  Returns the number of 16-column groups (= n_tiles).
 struct TileShape {
   int mw, ntw, n_mblk;
+  bool split;  // K split over workgroups (gemm_tile_split)
 };
 TileShape gemm_tile_shape(int n_tiles, int M, int ntw);
 int launch_gemm_tile(const GemmArgs& a, int epi, int ntw, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
@@ -108,6 +115,8 @@ struct AttnArgs {
   int nsplit[kMaxSeq];
 };
 constexpr int kAttnMapMax = 1 << 18;     // work-map entries per launch
+constexpr int kGemmSplitCells = 4096;    // K-split arrival counters
+constexpr size_t kGemmSplitFloats = size_t(8) * 8192 * 64;  // K-split chunk sums: 8 chunks x 8192 columns x 64 rows
 // One launch: splits, in-workgroup merge, and the last workgroup's combine.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kAttnQG = 16;              // query vectors per query group
