@@ -169,6 +169,7 @@ struct vs_model {
   unsigned* kcnt = nullptr;
   // attention work maps: device slots in the workspace, pinned staging on
   // the host; ev[slot] follows the last launch that read the slot
+  int n_cu = 256;  // compute units of the device
   int* amap_dev[kAmapSlots] = {};
   int* amap_pin[kAmapSlots] = {};
   hipEvent_t amap_ev[kAmapSlots] = {};
@@ -444,23 +445,44 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
   const int P = ctx_bound(kv, rm);
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
-  // One 32-key step per wave while that stays under ~2048 waves (all KV loads
-  // in flight at once), else splits of about 256 keys (a wave's steps run one
-  // after another, so long splits are latency-bound); bounded by the partials
-  // buffer and by the combine's capacity (workgroups per unit x query
-  // vectors).  Splits past a shorter sequence's context run no step.
+  // Splits: a wave's 32-key steps run one after another (about 2.5 us each,
+  // latency-bound), a workgroup of W waves takes W splits of a unit, and
+  // units of more than one workgroup pay the cross-workgroup combine.  With
+  // one workgroup per CU (the kernel's registers), the launch takes about
+  // ceil(workgroups / CUs) x (start + steps x step + combine); the split
+  // count is chosen to minimise that, with full workgroups (W·w − 1
+  // committed splits and the in-round window), bounded by the partials
+  // buffer and the combine's capacity.  Measured on MI355X against the
+  // earlier rule (~256-key splits): 8 sequences x 2048 keys 91 -> 53 us,
+  // one sequence x 4096 keys x 64 rows 65 -> 46 us, the 7B chain unchanged.
+  // Splits past a shorter sequence's context run no step.
+  int units_eff = 0;  // units with work: every sequence's non-empty query groups
+  for (int i = 0; i < rm.n_seq; ++i)
+    units_eff += c.n_kv_heads * (((rm.row_start[i + 1] - rm.row_start[i]) * G + a.qg_size - 1) / a.qg_size);
   int n_split = 0;
   a.kps = 32;
   if (P > 0) {
+    const int wv = attn_waves(a.qg_size);
     const int max_split = (P + 31) / 32;
-    int want = std::max({1, 2048 / std::max(1, units), (P + 255) / 256});
     const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
     const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
-    const int max_wg = std::min(budget_wg, kAttnCombineSlots / a.qg_size);
-    want = std::min(want, max_wg * attn_waves(a.qg_size) - 1);
-    n_split = std::min(max_split, std::max(1, want));
-    a.kps = ((P + n_split - 1) / n_split + 31) / 32 * 32;
-    n_split = (P + a.kps - 1) / a.kps;
+    const int max_wg = std::max(1, std::min(budget_wg, kAttnCombineSlots / a.qg_size));
+    constexpr double kStart = 5.0, kPerStep = 2.5, kCombine = 6.0;  // us, measured
+    double best = 1e30;
+    for (int w = 1; w <= max_wg; ++w) {
+      const int ns0 = std::min(max_split, wv * w - 1 > 0 ? wv * w - 1 : 1);
+      const int kps = ((P + ns0 - 1) / ns0 + 31) / 32 * 32;
+      const int ns = (P + kps - 1) / kps;
+      const int wpb = (ns + 1 + wv - 1) / wv;
+      const double rounds = std::ceil((double)units_eff * wpb / std::max(1, m->n_cu));
+      const double t = rounds * (kStart + kPerStep * (kps / 32) + (wpb > 1 ? kCombine : 0.0));
+      if (t < best) {
+        best = t;
+        n_split = ns;
+        a.kps = kps;
+      }
+      if (ns0 == max_split) break;
+    }
   }
   a.n_split = n_split;
   const int wpb = (n_split + 1 + attn_waves(a.qg_size) - 1) / attn_waves(a.qg_size);
@@ -711,6 +733,12 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
   hipError_t ae = hipMemset(m->attn_cnt, 0, kAttnMaxUnits * sizeof(unsigned));
   // so do the K-split GEMM's arrival counters
   if (ae == hipSuccess) ae = hipMemset(m->kcnt, 0, kGemmSplitCells * sizeof(unsigned));
+  if (ae == hipSuccess) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
+      m->n_cu = n_cu;
+  }
   for (int i = 0; i < kAmapSlots && ae == hipSuccess; ++i) {
     m->amap_dev[i] = reinterpret_cast<int*>(w + m->wsl.amap) + (size_t)i * kAttnMapMax;
     ae = hipHostMalloc(reinterpret_cast<void**>(&m->amap_pin[i]), (size_t)kAttnMapMax * 4, hipHostMallocDefault);
