@@ -16,8 +16,9 @@
 //  * RMSNorm is fused: the producer wrote x*g and per-group sums of x^2; the
 //    1/rms scale is applied to the outputs here.  Epilogues: residual add,
 //    q/k RoPE + KV-cache append, SwiGLU, logits + argmax partials.
-//  * Passes of more than 8 rows over the wide matrices run the row-tiled
-//    form in k_gemm_tile.hip, which keeps every row's arithmetic identical.
+//  * Passes of more than 8 rows run the row-tiled form in k_gemm_tile.hip
+//    where its K chunks fit (every wide matrix; narrow ones with long K
+//    chunks), which keeps every row's arithmetic identical.
 #pragma clang fp contract(off)
 #include "gemm_dev.h"
 

@@ -7,16 +7,17 @@
 // activations from L2 in every wave, which caps it far below the weight
 // stream at these sizes.  Here:
 //  * A workgroup of 4 waves owns a block of BM = 16*MW rows (MW = 1, 2 or 3)
-//    and 4*NWT n-tiles.  Each k-step's activation fragments of the block (hi and lo
-//    parts, 8*BM 16-byte units) are staged once in LDS and read by all four
-//    waves; each wave streams the packed weight fragments of its own NWT
-//    n-tiles straight into registers.
+//    and 4*NWT n-tiles.  Each k-step's activation fragments of the block (hi
+//    and lo parts, 8*BM 16-byte units) are staged once in LDS and read by
+//    all four waves; each wave streams the packed weight fragments of its
+//    own NWT n-tiles straight into registers.
 //  * Per k-step a wave issues 2*MW*NWT MFMAs from 2*MW LDS fragments and
 //    NWT weight fragments.  Global loads run PD k-steps ahead (a register
 //    ring for both operands); the staged activations rotate through four
 //    LDS buffers, and the A operands of the next k-step are read from LDS
-//    during the current one.  The K chunks must be equal and a multiple of
-//    8 k-steps (gemm_tile_fits).
+//    during the current one.  A workgroup runs all K chunks (equal, a
+//    multiple of 8 k-steps), or, for the narrow matrices, one chunk with K
+//    split over workgroups (gemm_tile_fits).
 //  * Rows stay bit-identical to the skinny form: the same 16x16x32 MFMA over
 //    the same k-steps in increasing order, hi and lo accumulated apart and
 //    added at the end of each K chunk (the chunks the skinny form gives to
