@@ -7,6 +7,7 @@
 #include <string>
 #include <vector>
 
+#include "attn_group.h"
 #include "kernels.h"
 #include "misc.h"
 
@@ -360,15 +361,15 @@ void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const
   m->ss_groups = (m->c.d_model + 255) / 256;
 }
 
+int upload_work_map(vs_model* m, AttnArgs& a, hipStream_t st);
+
 // Attention work map of a pass: sequence i takes ceil(P_i / kps) committed
 // splits (P_i its context bound) plus the in-round window, and only its
 // non-empty query groups, instead of every sequence taking the longest
 // one's splits and every query group.  The (sequence, KV head, key range)
 // groups go to the least-loaded XCD, their query groups back to back there
-// (block b runs on XCD b % 8).  The map is uploaded when it changes, through
-// a rotation of pinned staging and device slots; a slot is rewritten only
-// after the last launch that read it has run.  Returns the slot used, or -1: no map (it would not fit, or
-// would save little over the plain grid).
+// (block b runs on XCD b % 8).  Returns the slot used, or -1: no map (it
+// would not fit, or would save little over the plain grid).
 int attn_work_map(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, hipStream_t st) {
   const int wv = attn_waves(a.qg_size);
   std::vector<int>& mp = m->amap_build;
@@ -403,6 +404,15 @@ int attn_work_map(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, 
   mp.assign(8 * n, -1);
   for (int x = 0; x < 8; ++x)
     for (size_t p = 0; p < lists[x].size(); ++p) mp[8 * p + x] = lists[x][p];
+  return upload_work_map(m, a, st);
+}
+
+// Makes m->amap_build the launch's work map (a.map, a.map_n): uploaded when
+// it differs from the current slot's, through a rotation of pinned staging
+// and device slots; a slot is rewritten only after the last launch that read
+// it has run.  Returns the slot used.
+int upload_work_map(vs_model* m, AttnArgs& a, hipStream_t st) {
+  const std::vector<int>& mp = m->amap_build;
   if (m->amap_slot < 0 || mp != m->amap_last) {
     // every launch that read the current slot is on the stream before this
     // point; a slot is refilled only once its event has passed
@@ -426,6 +436,77 @@ int ctx_bound(vs_kv* kv, const RowMap& rm) {
   return p;
 }
 
+// Grouped attention (attn_group.h) for passes whose KV heads carry two or
+// more query groups: the K/V of a step are read once for all of them.  The
+// split length kps (a multiple of 32 keys) minimises a launch-time model:
+// ceil(workgroups / slots) x (start + steps x step) + the combine launch when
+// a sequence has more than one split, with one workgroup of 8 waves (two of
+// 4) per CU.  A split holds at most kAttnGroupSteps steps including the
+// in-round keys.  Returns false when the pass does not fit this form.
+bool attention_group(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, double bytes, hipStream_t st) {
+  const vs_model_cfg& c = m->c;
+  if (a.n_qg < 2 || (c.head_dim != 64 && c.head_dim != 128)) return false;
+  int max_qg = 0, span = 0;
+  for (int i = 0; i < rm.n_seq; ++i) {
+    const int nr = rm.row_start[i + 1] - rm.row_start[i];
+    max_qg = std::max(max_qg, (nr * G + a.qg_size - 1) / a.qg_size);
+    span = std::max(span, rm.win + rm.idx_off + nr);
+  }
+  const int wv = max_qg <= 4 ? 4 : 8;
+  const int kps_cap = (kAttnGroupSteps * kAttnStepKeys - span - kAttnStepKeys) / kAttnStepKeys * kAttnStepKeys;
+  if (kps_cap < kAttnStepKeys) return false;
+  const int slots = std::max(1, m->n_cu) * (wv == 4 ? 2 : 1);
+  const size_t units = (size_t)rm.n_seq * c.n_kv_heads * a.n_qg;
+  const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
+  const double kStart = 4.0, kStepUs = wv == 8 ? 0.45 : 0.3, kCombine = 4.0;  // us
+  double best = 1e30;
+  int best_kps = 0;
+  for (int kps = kAttnStepKeys; kps <= kps_cap; kps += kAttnStepKeys) {
+    long wgs = 0;
+    int max_ns = 1;
+    for (int i = 0; i < rm.n_seq; ++i) {
+      const int nr = rm.row_start[i + 1] - rm.row_start[i];
+      const int nqb = ((nr * G + a.qg_size - 1) / a.qg_size + wv - 1) / wv;
+      const int ns = std::max(1, (kv->P_ub[rm.seq[i]] + kps - 1) / kps);
+      max_ns = std::max(max_ns, ns);
+      wgs += (long)c.n_kv_heads * nqb * ns;
+    }
+    if (max_ns > kAttnGroupMaxSplits || (max_ns > 1 && units * max_ns * rec > kAttnPartFloats) ||
+        wgs > kAttnMapMax)
+      continue;
+    const double t = std::ceil((double)wgs / slots) * (kStart + kStepUs * (kps / kAttnStepKeys)) +
+                     (max_ns > 1 ? kCombine : 0.0);
+    if (t < best) {
+      best = t;
+      best_kps = kps;
+    }
+  }
+  if (best_kps == 0) return false;
+  a.kps = best_kps;
+  a.n_split = 1;
+  std::vector<int>& mp = m->amap_build;
+  mp.clear();
+  for (int i = 0; i < rm.n_seq; ++i) {
+    const int nr = rm.row_start[i + 1] - rm.row_start[i];
+    const int nqb = ((nr * G + a.qg_size - 1) / a.qg_size + wv - 1) / wv;
+    const int ns = std::max(1, (kv->P_ub[rm.seq[i]] + a.kps - 1) / a.kps);
+    a.nsplit[i] = ns;
+    a.n_split = std::max(a.n_split, ns);
+    for (int kvh = 0; kvh < c.n_kv_heads; ++kvh)
+      for (int qb = 0; qb < nqb; ++qb)
+        for (int sp = 0; sp < ns; ++sp) mp.push_back(i | kvh << 6 | qb << 13 | sp << 20);
+  }
+  a.part = m->part;
+  a.ml_off = units * a.n_split * a.qg_size * c.head_dim;
+  a.ml_off += a.ml_off & 1;
+  a.xa_o = m->xa_o;
+  a.M = rm.M;
+  a.use_mfma = 1;
+  upload_work_map(m, a, st);
+  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention_group(a, wv, st, e0, e1); });
+  return true;
+}
+
 void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t st) {
   const vs_model_cfg& c = m->c;
   AttnArgs a;
@@ -444,6 +525,11 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   a.n_qg = (nq + kAttnQG - 1) / kAttnQG;
   a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
   const int P = ctx_bound(kv, rm);
+  double bytes = 0;
+  for (int i = 0; i < rm.n_seq; ++i)
+    bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
+             c.head_dim * 4;
+  if (attention_group(m, kv, rm, G, a, bytes, st)) return;
   const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
   // Splits: a wave's 32-key steps run one after another (about 2.5 us each,
   // latency-bound), a workgroup of W waves takes W splits of a unit, and
@@ -494,10 +580,6 @@ void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t 
   a.M = rm.M;
   a.use_mfma = 1;
   attn_work_map(m, kv, rm, G, a, st);
-  double bytes = 0;
-  for (int i = 0; i < rm.n_seq; ++i)
-    bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
-             c.head_dim * 4;
   timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention(a, st, e0, e1); });
 }
 

@@ -34,33 +34,9 @@
 // fence would write back or invalidate the whole L2.  Ordering comes from
 // waiting on the vector memory counter before the count, so the
 // device-coherent stores have completed.
-#include "kernels.h"
+#include "attn_dev.h"
 
 namespace vs {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kStep = 32;           // keys per step
-
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
-// 8 floats -> bf16 hi and lo parts, packed as two MFMA operand registers.
-__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint16_t h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
-    const uint16_t l0 = f2bf(x[2 * e] - bf2f(h0)), l1 = f2bf(x[2 * e + 1] - bf2f(h1));
-    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
-}
 
 // Query vectors of a unit: vector gq of the query group maps to row
 // r0 + gq % nr and head kvh*G + gq / nr.
@@ -243,7 +219,12 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
         sacc[mt][t] = c;
       }
     if (more) load_k();
-    // mask, online softmax update, P into the scratch (row, key) layout
+    // mask, online softmax update, P into the scratch (row, key) layout; a
+    // step of committed keys inside the split needs no mask, and the
+    // accumulators are rescaled only when some factor is not exactly 1
+    const bool full = !window && base >= key_lo && base + kStep <= key_hi;
+    float corr[MTQ][4];
+    bool same = true;
 #pragma unroll
     for (int mt = 0; mt < MTQ; ++mt)
 #pragma unroll
@@ -252,16 +233,19 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
         float v[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int slot = base + 16 * t + mrow;
-          bool vis = slot >= key_lo && slot < key_hi;
-          if (vis && window) vis = (qmask[mt][r] >> (slot - key_lo)) & 1ull;
-          v[t] = vis ? sacc[mt][t][r] : -INFINITY;
+          if (full) {
+            v[t] = sacc[mt][t][r];
+          } else {
+            const int slot = base + 16 * t + mrow;
+            bool vis = slot >= key_lo && slot < key_hi;
+            if (vis && window) vis = (qmask[mt][r] >> ((slot - key_lo) & 63)) & 1ull;  // count kept in 0..63
+            v[t] = vis ? sacc[mt][t][r] : -INFINITY;
+          }
         }
-        float mx = fmaxf(v[0], v[1]);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const float mx = row16_max(fmaxf(v[0], v[1]));
         const float mnew = fmaxf(mrun[mt][r], mx);
-        const float corr = (mrun[mt][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[mt][r] - mnew);
+        corr[mt][r] = (mrun[mt][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[mt][r] - mnew);
+        same &= corr[mt][r] == 1.f;
         float ps = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -269,13 +253,18 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
           pw[row * PS + 16 * t + mrow] = p;
           ps += p;
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
-        lrun[mt][r] = lrun[mt][r] * corr + ps;
+        ps = row16_sum(ps);
+        lrun[mt][r] = lrun[mt][r] * corr[mt][r] + ps;
         mrun[mt][r] = mnew;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) oacc[mt][t][r] *= corr;
       }
+    if (!__all(same)) {
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) oacc[mt][t][r] *= corr[mt][r];
+    }
     // O += P.V (P rows in A-operand order: row = lane%16, keys 8*(lane/16) .. +8)
 #pragma unroll
     for (int mt = 0; mt < MTQ; ++mt) {

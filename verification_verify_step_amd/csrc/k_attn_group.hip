@@ -1,0 +1,370 @@
+// Masked multi-query attention with the K/V of a step shared by the query
+// groups of a KV head (gfx950).
+//
+// What is computed is the same as in k_attn.hip ("FlashSpec" page,
+// lnrk.cn/news/47842, §2.2: every row attends to the committed keys of its
+// sequence and to the in-round keys its ancestor mask selects; §5.2: nothing
+// outside the mask may leak).  The work is cut differently.  k_attn.hip gives
+// each wave its own key range of one query group, so when a KV head has many
+// query vectors (GQA heads, or the 64 rows of a token tree) every group reads
+// the same K/V again.  Here a workgroup owns one key range (split) of one KV
+// head and up to WV query groups, one per wave:
+//
+//  * the workgroup's threads load each 32-key step (two 16-key blocks of K
+//    and of V, 16 KB at head_dim 128) in 16-byte pieces, kDepth steps ahead
+//    in registers, and put a step into one of two LDS stages (K rows padded
+//    by 16 bytes so the fragment reads of one MFMA do not collide in a bank);
+//  * every wave then reads the S = Q.K^T and P.V operands of its query group
+//    from that stage: the same 16x16x32 bf16 MFMA products, hi/lo query and P
+//    splits, masking and base-2 online softmax as k_attn.hip;
+//  * one barrier per step (LDS counter only: loads stay in flight across it).
+//
+// A sequence's committed keys are cut into splits of kps keys; its last split
+// also takes the in-round keys, so a sequence with one split needs no merge
+// and its workgroups write the result.  Otherwise each wave writes its (max,
+// sum, o) partial and attn_group_combine merges the splits of each query
+// group in split order.
+#include "attn_dev.h"
+#include "attn_group.h"
+
+namespace vs {
+
+namespace {
+
+constexpr int kDepth = 4;  // steps loaded ahead of the one in LDS
+
+// This wave's LDS writes are done, then the workgroup barrier.  Unlike
+// __syncthreads() it does not wait for global loads, so the steps loaded
+// ahead stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+}  // namespace
+
+template <int HD, int WV>
+__global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
+  constexpr int kThreads = WV * 64;
+  constexpr int KSQ = HD / 32;        // k-steps of S over head dims
+  constexpr int NDT = HD / 16;        // 16-dim output tiles
+  constexpr int KROW = HD + 8;        // padded K row in LDS (elements)
+  constexpr int KPART = 2 * kBlock * KROW;
+  constexpr int STAGE = KPART + 2 * kBlock * HD;  // one step: K (padded rows), then V as in HBM
+  constexpr int PIECES = 8 * HD;                  // 16-byte pieces of one step's K and V
+  constexpr int PPT = PIECES / kThreads;
+  static_assert(PPT >= 1 && PPT * kThreads == PIECES, "pieces per thread");
+  constexpr int PS = kStep + 4;  // P scratch row stride (floats)
+  __shared__ __attribute__((aligned(16))) uint16_t stg[2 * STAGE];
+  __shared__ float pscr[WV * 16 * PS];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = a.map[blockIdx.x];
+  if (e < 0) return;  // grid padding
+  const int i = e & 63, kvh = (e >> 6) & 127, qb = (e >> 13) & 127, s = e >> 20;
+  const int ns = a.nsplit[i];
+  const bool last_split = s == ns - 1;
+  const int sq = a.rows.seq[i];
+  const int r0 = a.rows.row_start[i];
+  const int nr = a.rows.row_start[i + 1] - r0;
+  const int G = a.H / a.Hkv;
+  const int qg = qb * WV + wave;
+  const int q0 = qg * a.qg_size;
+  const int nq = qg < a.n_qg ? max(0, min(a.qg_size, nr * G - q0)) : 0;  // this wave's query vectors
+  const int P = a.kv.P[sq];
+  const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
+  const int clo = s * a.kps, chi = min(P, clo + a.kps);            // committed keys of this split
+  int first = clo, last = min(clo + a.kps, (P + kStep - 1) / kStep * kStep);
+  if (last_split) {
+    first = min(first, wlo / kStep * kStep);
+    last = (whi + kStep - 1) / kStep * kStep;
+  }
+  // both ends are step-aligned; the host keeps a split within kAttnGroupSteps
+  const int n_steps = min(last > first ? (last - first) / kStep : 0, kAttnGroupSteps);
+
+  // Block-table entries of the split, one per lane (two per step).
+  const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
+  const int btreg = bt[min(first / kBlock + lane, a.kv.bps - 1)];
+  const size_t head_stride = (size_t)kBlock * HD;  // elements per (block, kv head)
+  const uint16_t* const kpool = a.kv.k;
+  const uint16_t* const vpool = a.kv.v;
+  __builtin_assume(threadIdx.x < kThreads);
+
+  // piece x of a step: K (x < 4 HD) or V, block (x / 2 HD) % 2, 16-byte
+  // offset x % 2 HD inside that block's [16][HD] tile (V: [HD][16])
+  auto load_step = [&](int t, u32x4(&r)[PPT]) {
+    const int nb0 = __builtin_amdgcn_readlane(btreg, 2 * t);
+    const int nb1 = __builtin_amdgcn_readlane(btreg, 2 * t + 1);
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int x = threadIdx.x + j * kThreads;
+      const int isv = x / (4 * HD), blk = (x / (2 * HD)) & 1, off = x % (2 * HD);
+      const uint16_t* src = (isv ? vpool : kpool) + ((size_t)(blk ? nb1 : nb0) * a.Hkv + kvh) * head_stride;
+      r[j] = reinterpret_cast<const u32x4*>(src)[off];
+    }
+  };
+  auto put_step = [&](const u32x4(&r)[PPT], int sb) {
+    uint16_t* d = stg + sb * STAGE;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int x = threadIdx.x + j * kThreads;
+      const int isv = x / (4 * HD), blk = (x / (2 * HD)) & 1, off = x % (2 * HD);
+      uint16_t* dst = isv ? d + KPART + blk * kBlock * HD + off * 8
+                          : d + (blk * kBlock + off / (HD / 8)) * KROW + (off % (HD / 8)) * 8;
+      *reinterpret_cast<u32x4*>(dst) = r[j];
+    }
+  };
+
+  // Every thread issues the same loads on every path (steps past the
+  // split's end re-read its last step, a wave without queries reads a valid
+  // query row), so that the compiler's wait counts stay exact and the ring's
+  // steps remain in flight across iterations.
+  const int t_end = max(n_steps - 1, 0);
+  u32x4 ring[kDepth][PPT];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load_step(min(d, t_end), ring[d]);
+
+  // Query vectors and visibility masks of this wave's group: vector gq maps
+  // to row r0 + gq % nr and head kvh*G + gq / nr.
+  const int mrow = lane & 15, kq = lane >> 4;
+  float4 qraw[KSQ][2];
+  uint64_t qmask[4];  // rows this lane holds in S
+  {
+    const int gq = min(q0 + min(mrow, max(nq, 1) - 1), nr * G - 1);
+    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
+#pragma unroll
+    for (int s2 = 0; s2 < KSQ; ++s2) {
+      qraw[s2][0] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq);
+      qraw[s2][1] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * kq + r;
+      const int rl = min(q0 + min(row, max(nq, 1) - 1), nr * G - 1) % nr;
+      const int idx = a.rows.idx_off + rl;
+      const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + rl] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+      qmask[r] = row < nq ? mk : 0ull;
+    }
+  }
+
+  // query fragments, pre-scaled into base-2 units and split hi/lo
+  const float qscale = a.scale * 1.4426950408889634f;
+  u32x4 qh[KSQ], ql[KSQ];
+#pragma unroll
+  for (int s2 = 0; s2 < KSQ; ++s2) {
+    const bool qok = mrow < nq;
+    const float4 u = qraw[s2][0], v = qraw[s2][1];
+    const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = qok ? x[k] * qscale : 0.f;
+    split8(y, qh[s2], ql[s2]);
+  }
+
+  float mrun[4], lrun[4];
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrun[r] = -INFINITY;
+    lrun[r] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* pw = pscr + wave * 16 * PS;
+
+  auto compute = [&](int t, int sb) {
+    const int base = first + t * kStep;
+    const uint16_t* kst = stg + sb * STAGE;
+    const uint16_t* vst = kst + KPART;
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KSQ; ++s2) {
+        const u32x4 kb = *reinterpret_cast<const u32x4*>(kst + (t2 * kBlock + mrow) * KROW + 32 * s2 + 8 * kq);
+        c = mfma16(qh[s2], kb, c);
+        c = mfma16(ql[s2], kb, c);
+      }
+      sacc[t2] = c;
+    }
+    // a step of committed keys only, all inside this split: no masking
+    const bool full = base >= clo && base + kStep <= chi;
+    float corr[4];
+    bool same = true;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * kq + r;
+      float v[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        if (full) {
+          v[t2] = sacc[t2][r];
+        } else {
+          // branch-free, and the shift count kept in 0..63: a count outside
+          // it is undefined and lets the compiler drop the whole term
+          const int slot = base + 16 * t2 + mrow, wo = slot - wlo;
+          const bool inwin = last_split & (wo >= 0) & (slot < whi);
+          const bool vis = ((slot >= clo) & (slot < chi)) | (inwin & (((qmask[r] >> (wo & 63)) & 1ull) != 0));
+          v[t2] = vis ? sacc[t2][r] : -INFINITY;
+        }
+      }
+      const float mx = row16_max(fmaxf(v[0], v[1]));
+      const float mnew = fmaxf(mrun[r], mx);
+      corr[r] = (mrun[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mnew);
+      same &= corr[r] == 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float p = v[t2] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[t2] - mnew);
+        pw[row * PS + 16 * t2 + mrow] = p;
+        ps += p;
+      }
+      ps = row16_sum(ps);
+      lrun[r] = lrun[r] * corr[r] + ps;
+      mrun[r] = mnew;
+    }
+    // rescale the accumulators unless every factor is exactly 1 (no new max)
+    if (!__all(same)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t3 = 0; t3 < NDT; ++t3) oacc[t3][r] *= corr[r];
+    }
+    u32x4 ph, pl;
+    split8(pw + mrow * PS + 8 * kq, ph, pl);
+#pragma unroll
+    for (int t3 = 0; t3 < NDT; ++t3) {
+      const u32x4 vb =
+          *reinterpret_cast<const u32x4*>(vst + (kq >> 1) * kBlock * HD + (16 * t3 + mrow) * kBlock + 8 * (kq & 1));
+      oacc[t3] = mfma16(ph, vb, oacc[t3]);
+      oacc[t3] = mfma16(pl, vb, oacc[t3]);
+    }
+  };
+
+  // Step t is computed from LDS stage t % 2 while the ring holds steps
+  // t+1 .. t+kDepth; after it, step t+1 moves into the other stage and its
+  // ring slot takes step t+1+kDepth.  The loop is unrolled by kDepth so that
+  // ring slots are registers.
+  put_step(ring[0], 0);
+  load_step(min(kDepth, t_end), ring[0]);
+  lds_barrier();
+  for (int t0 = 0; t0 < n_steps; t0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int t = t0 + u;
+      if (t < n_steps && nq > 0) compute(t, u & 1);
+      put_step(ring[(u + 1) % kDepth], (u + 1) & 1);
+      load_step(min(t + 1 + kDepth, t_end), ring[(u + 1) % kDepth]);
+      lds_barrier();
+    }
+  }
+  if (nq == 0) return;
+
+  const int unit = (i * a.Hkv + kvh) * a.n_qg + qg;
+  if (ns == 1) {  // the only split: write the result
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * kq + r;
+      if (row < nq) {
+        const int gq = q0 + row;
+        const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+#pragma unroll
+        for (int t3 = 0; t3 < NDT; ++t3) xa_store(a.xa_o, h * HD + 16 * t3 + mrow, m, a.M, oacc[t3][r] / lrun[r]);
+      }
+    }
+    return;
+  }
+  const size_t QG = a.qg_size;
+  const size_t rec = (size_t)unit * a.n_split + s;
+  float2* pml = reinterpret_cast<float2*>(a.part + a.ml_off);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * kq + r;
+    if (row < nq) {
+#pragma unroll
+      for (int t3 = 0; t3 < NDT; ++t3) a.part[(rec * QG + row) * HD + 16 * t3 + mrow] = oacc[t3][r];
+      if (mrow == 0) pml[rec * QG + row] = make_float2(mrun[r], lrun[r]);
+    }
+  }
+}
+
+// One workgroup per (sequence, KV head, query group) with more than one
+// split: weights exp2(m_j - max) per row, then o = sum_j w_j o_j / sum_j w_j
+// l_j in split order.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
+  __shared__ float wts[kAttnGroupMaxSplits * kAttnQG];
+  __shared__ float tot[kAttnQG];
+  const int unit = blockIdx.x;
+  const int qg = unit % a.n_qg, ik = unit / a.n_qg, kvh = ik % a.Hkv, i = ik / a.Hkv;
+  const int ns = a.nsplit[i];
+  if (ns <= 1) return;  // written by the main kernel
+  const int r0 = a.rows.row_start[i];
+  const int nr = a.rows.row_start[i + 1] - r0;
+  const int G = a.H / a.Hkv;
+  const int q0 = qg * a.qg_size;
+  const int nq = max(0, min(a.qg_size, nr * G - q0));
+  if (nq == 0) return;
+  const size_t QG = a.qg_size, rec0 = (size_t)unit * a.n_split;
+  const float2* pml = reinterpret_cast<const float2*>(a.part + a.ml_off);
+  if (threadIdx.x < nq) {
+    const int r = threadIdx.x;
+    float mx = -INFINITY;
+    for (int j = 0; j < ns; ++j) {
+      const float2 v = pml[(rec0 + j) * QG + r];
+      if (v.y > 0.f) mx = fmaxf(mx, v.x);  // a split that saw no key has sum 0
+    }
+    float t = 0.f;
+    for (int j = 0; j < ns; ++j) {
+      const float2 v = pml[(rec0 + j) * QG + r];
+      const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
+      wts[j * kAttnQG + r] = w;
+      t += w * v.y;
+    }
+    tot[r] = t;
+  }
+  __syncthreads();
+  constexpr int HP = HD / 2;
+  for (int p = threadIdx.x; p < nq * HP; p += 256) {
+    const int r = p / HP, c = p - r * HP;
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < ns; ++j) {
+      const float2 x = *reinterpret_cast<const float2*>(a.part + ((rec0 + j) * QG + r) * HD + 2 * c);
+      const float w = wts[j * kAttnQG + r];
+      o0 += w * x.x;
+      o1 += w * x.y;
+    }
+    const int gq = q0 + r;
+    const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+    xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / tot[r]);
+    xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot[r]);
+  }
+}
+
+void launch_attention_group(const AttnArgs& a, int wv, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const bool combine = a.n_split > 1;
+  const dim3 grid(a.map_n), cgrid(a.rows.n_seq * a.Hkv * a.n_qg);
+  hipEvent_t e1 = combine ? nullptr : ev1;
+#define VS_GRP(HD, WV)                                                                                         \
+  do {                                                                                                         \
+    if (ev0 != nullptr || e1 != nullptr)                                                                       \
+      hipExtLaunchKernelGGL((attn_group_kernel<HD, WV>), grid, dim3(WV * 64), 0, st, ev0, e1, 0, a);           \
+    else                                                                                                       \
+      hipLaunchKernelGGL((attn_group_kernel<HD, WV>), grid, dim3(WV * 64), 0, st, a);                          \
+    if (combine) {                                                                                             \
+      if (ev1 != nullptr)                                                                                      \
+        hipExtLaunchKernelGGL((attn_group_combine<HD>), cgrid, dim3(256), 0, st, nullptr, ev1, 0, a);          \
+      else                                                                                                     \
+        hipLaunchKernelGGL((attn_group_combine<HD>), cgrid, dim3(256), 0, st, a);                              \
+    }                                                                                                          \
+  } while (0)
+  if (a.hd == 128) {
+    if (wv == 4) VS_GRP(128, 4);
+    else VS_GRP(128, 8);
+  } else {
+    if (wv == 4) VS_GRP(64, 4);
+    else VS_GRP(64, 8);
+  }
+#undef VS_GRP
+}
+
+}  // namespace vs
