@@ -14,9 +14,12 @@
 //    and of V, 16 KB at head_dim 128) in 16-byte pieces, kDepth steps ahead
 //    in registers, and put a step into one of two LDS stages (K rows padded
 //    by 16 bytes so the fragment reads of one MFMA do not collide in a bank);
-//  * every wave then reads the S = Q.K^T and P.V operands of its query group
-//    from that stage: the same 16x16x32 bf16 MFMA products, hi/lo query and P
-//    splits, masking and base-2 online softmax as k_attn.hip;
+//  * every wave then computes its group's step transposed, S^T = K.Q^T on
+//    the bf16 16x16x32 MFMA (query split hi/lo), so that a lane holds eight
+//    scores of one query: masking and the base-2 online softmax reduce them
+//    in the lane and then across the four lane groups, and the
+//    probabilities (split hi/lo) are directly the B operand of
+//    O^T += V^T.P^T, with no trip through LDS;
 //  * one barrier per step (LDS counter only: loads stay in flight across it).
 //
 // A sequence's committed keys are cut into splits of kps keys; its last split
@@ -31,7 +34,6 @@ namespace vs {
 
 namespace {
 
-constexpr int kDepth = 4;  // steps loaded ahead of the one in LDS
 
 // This wave's LDS writes are done, then the workgroup barrier.  Unlike
 // __syncthreads() it does not wait for global loads, so the steps loaded
@@ -51,9 +53,8 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   constexpr int PIECES = 8 * HD;                  // 16-byte pieces of one step's K and V
   constexpr int PPT = PIECES / kThreads;
   static_assert(PPT >= 1 && PPT * kThreads == PIECES, "pieces per thread");
-  constexpr int PS = kStep + 4;  // P scratch row stride (floats)
+  constexpr int kDepth = 4;  // steps loaded ahead of the one in LDS (even; 8 measured no faster)
   __shared__ __attribute__((aligned(16))) uint16_t stg[2 * STAGE];
-  __shared__ float pscr[WV * 16 * PS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = a.map[blockIdx.x];
@@ -121,35 +122,32 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load_step(min(d, t_end), ring[d]);
 
-  // Query vectors and visibility masks of this wave's group: vector gq maps
-  // to row r0 + gq % nr and head kvh*G + gq / nr.
+  // This lane's query vector (query mrow of the wave's group) and its
+  // visibility mask; vector gq maps to row r0 + gq % nr and head
+  // kvh*G + gq / nr.
   const int mrow = lane & 15, kq = lane >> 4;
+  const bool qok = mrow < nq;
+  const int gq = min(q0 + min(mrow, max(nq, 1) - 1), nr * G - 1);
   float4 qraw[KSQ][2];
-  uint64_t qmask[4];  // rows this lane holds in S
+  uint64_t qmask;
   {
-    const int gq = min(q0 + min(mrow, max(nq, 1) - 1), nr * G - 1);
     const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
 #pragma unroll
     for (int s2 = 0; s2 < KSQ; ++s2) {
       qraw[s2][0] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq);
       qraw[s2][1] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq + 4);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * kq + r;
-      const int rl = min(q0 + min(row, max(nq, 1) - 1), nr * G - 1) % nr;
-      const int idx = a.rows.idx_off + rl;
-      const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + rl] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
-      qmask[r] = row < nq ? mk : 0ull;
-    }
+    const int idx = a.rows.idx_off + gq % nr;
+    const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + gq % nr] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+    qmask = qok ? mk : 0ull;
   }
 
-  // query fragments, pre-scaled into base-2 units and split hi/lo
+  // query fragments (the B operand of S^T), pre-scaled into base-2 units and
+  // split hi/lo
   const float qscale = a.scale * 1.4426950408889634f;
   u32x4 qh[KSQ], ql[KSQ];
 #pragma unroll
   for (int s2 = 0; s2 < KSQ; ++s2) {
-    const bool qok = mrow < nq;
     const float4 u = qraw[s2][0], v = qraw[s2][1];
     const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
     float y[8];
@@ -158,17 +156,19 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
     split8(y, qh[s2], ql[s2]);
   }
 
-  float mrun[4], lrun[4];
+  // Online softmax of this lane's query; O^T tile t3 holds dims
+  // 16 t3 + 4 kq + r of it.
+  float mrun = -INFINITY, lrun = 0.f;
   f32x4 oacc[NDT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mrun[r] = -INFINITY;
-    lrun[r] = 0.f;
-  }
-#pragma unroll
   for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* pw = pscr + wave * 16 * PS;
 
+  // One step, computed transposed: S^T = K.Q^T puts keys 4 kq + r of block
+  // t2 of the lane's query in its registers, so that the softmax reduces
+  // eight values in the lane and then across the four lane groups, and the
+  // probabilities are already the B operand of O^T += V^T.P^T (their k order
+  // is block-major by lane group: k = 8 kq + j is key 4 kq + j % 4 of block
+  // j / 4; V^T is read from LDS in the same order).
   auto compute = [&](int t, int sb) {
     const int base = first + t * kStep;
     const uint16_t* kst = stg + sb * STAGE;
@@ -180,62 +180,57 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < KSQ; ++s2) {
         const u32x4 kb = *reinterpret_cast<const u32x4*>(kst + (t2 * kBlock + mrow) * KROW + 32 * s2 + 8 * kq);
-        c = mfma16(qh[s2], kb, c);
-        c = mfma16(ql[s2], kb, c);
+        c = mfma16(kb, qh[s2], c);
+        c = mfma16(kb, ql[s2], c);
       }
       sacc[t2] = c;
     }
     // a step of committed keys only, all inside this split: no masking
     const bool full = base >= clo && base + kStep <= chi;
-    float corr[4];
-    bool same = true;
+    float v[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * kq + r;
-      float v[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        if (full) {
-          v[t2] = sacc[t2][r];
-        } else {
-          // branch-free, and the shift count kept in 0..63: a count outside
-          // it is undefined and lets the compiler drop the whole term
-          const int slot = base + 16 * t2 + mrow, wo = slot - wlo;
-          const bool inwin = last_split & (wo >= 0) & (slot < whi);
-          const bool vis = ((slot >= clo) & (slot < chi)) | (inwin & (((qmask[r] >> (wo & 63)) & 1ull) != 0));
-          v[t2] = vis ? sacc[t2][r] : -INFINITY;
-        }
+    for (int j = 0; j < 8; ++j) {
+      const int t2 = j >> 2, r = j & 3;
+      if (full) {
+        v[j] = sacc[t2][r];
+      } else {
+        // branch-free, and the shift count kept in 0..63: a count outside
+        // it is undefined and lets the compiler drop the whole term
+        const int slot = base + 16 * t2 + 4 * kq + r, wo = slot - wlo;
+        const bool inwin = last_split & (wo >= 0) & (slot < whi);
+        const bool vis = ((slot >= clo) & (slot < chi)) | (inwin & (((qmask >> (wo & 63)) & 1ull) != 0));
+        v[j] = vis ? sacc[t2][r] : -INFINITY;
       }
-      const float mx = row16_max(fmaxf(v[0], v[1]));
-      const float mnew = fmaxf(mrun[r], mx);
-      corr[r] = (mrun[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mnew);
-      same &= corr[r] == 1.f;
-      float ps = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const float p = v[t2] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[t2] - mnew);
-        pw[row * PS + 16 * t2 + mrow] = p;
-        ps += p;
-      }
-      ps = row16_sum(ps);
-      lrun[r] = lrun[r] * corr[r] + ps;
-      mrun[r] = mnew;
     }
+    float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float corr = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = v[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[j] - mnew);
+    // the four lanes of a query add the same values in the same pairs
+    float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lrun = lrun * corr + ps;
+    mrun = mnew;
     // rescale the accumulators unless every factor is exactly 1 (no new max)
-    if (!__all(same)) {
+    if (!__all(corr == 1.f)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t3 = 0; t3 < NDT; ++t3) oacc[t3][r] *= corr[r];
+      for (int t3 = 0; t3 < NDT; ++t3) oacc[t3] *= corr;
     }
     u32x4 ph, pl;
-    split8(pw + mrow * PS + 8 * kq, ph, pl);
+    split8(p, ph, pl);
 #pragma unroll
     for (int t3 = 0; t3 < NDT; ++t3) {
-      const u32x4 vb =
-          *reinterpret_cast<const u32x4*>(vst + (kq >> 1) * kBlock * HD + (16 * t3 + mrow) * kBlock + 8 * (kq & 1));
-      oacc[t3] = mfma16(ph, vb, oacc[t3]);
-      oacc[t3] = mfma16(pl, vb, oacc[t3]);
+      const uint16_t* vr = vst + (16 * t3 + mrow) * kBlock + 4 * kq;
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vr);                   // block 0
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + kBlock * HD);     // block 1
+      const u32x4 va = u32x4{v0.x, v0.y, v1.x, v1.y};
+      oacc[t3] = mfma16(va, ph, oacc[t3]);
+      oacc[t3] = mfma16(va, pl, oacc[t3]);
     }
   };
 
@@ -256,34 +251,23 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
       lds_barrier();
     }
   }
-  if (nq == 0) return;
+  if (!qok) return;
 
   const int unit = (i * a.Hkv + kvh) * a.n_qg + qg;
   if (ns == 1) {  // the only split: write the result
+    const int m = r0 + gq % nr, h = kvh * G + gq / nr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * kq + r;
-      if (row < nq) {
-        const int gq = q0 + row;
-        const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+    for (int t3 = 0; t3 < NDT; ++t3)
 #pragma unroll
-        for (int t3 = 0; t3 < NDT; ++t3) xa_store(a.xa_o, h * HD + 16 * t3 + mrow, m, a.M, oacc[t3][r] / lrun[r]);
-      }
-    }
+      for (int r = 0; r < 4; ++r) xa_store(a.xa_o, h * HD + 16 * t3 + 4 * kq + r, m, a.M, oacc[t3][r] / lrun);
     return;
   }
   const size_t QG = a.qg_size;
   const size_t rec = (size_t)unit * a.n_split + s;
-  float2* pml = reinterpret_cast<float2*>(a.part + a.ml_off);
+  float* po = a.part + (rec * QG + mrow) * HD + 4 * kq;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * kq + r;
-    if (row < nq) {
-#pragma unroll
-      for (int t3 = 0; t3 < NDT; ++t3) a.part[(rec * QG + row) * HD + 16 * t3 + mrow] = oacc[t3][r];
-      if (mrow == 0) pml[rec * QG + row] = make_float2(mrun[r], lrun[r]);
-    }
-  }
+  for (int t3 = 0; t3 < NDT; ++t3) *reinterpret_cast<float4*>(po + 16 * t3) = make_float4(oacc[t3][0], oacc[t3][1], oacc[t3][2], oacc[t3][3]);
+  if (kq == 0) reinterpret_cast<float2*>(a.part + a.ml_off)[rec * QG + mrow] = make_float2(mrun, lrun);
 }
 
 // One workgroup per (sequence, KV head, query group) with more than one
