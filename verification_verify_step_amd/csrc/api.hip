@@ -84,7 +84,7 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
   return L;
 }
 
-constexpr size_t kAttnPartFloats = size_t(32) << 20;  // 128 MB of attention partials
+constexpr size_t kAttnPartFloats = size_t(128) << 20;  // 512 MB of attention partials
 constexpr int kAmapSlots = 4;                         // attention work maps in rotation
 // tree drafting state: node arrays (4 int + 1 double per node), meta, row arrays
 constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows * 24;

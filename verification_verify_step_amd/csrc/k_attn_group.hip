@@ -270,14 +270,19 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   if (kq == 0) reinterpret_cast<float2*>(a.part + a.ml_off)[rec * QG + mrow] = make_float2(mrun, lrun);
 }
 
-// One workgroup per (sequence, KV head, query group) with more than one
-// split: weights exp2(m_j - max) per row, then o = sum_j w_j o_j / sum_j w_j
-// l_j in split order.
+// Merge of the splits, for sequences with more than one.  A workgroup of 4
+// waves takes 4 query vectors of one (sequence, KV head, query group): wave
+// w reads the (max, sum) of vector w of every split in one load per lane
+// (split j in lane j) and puts the weights exp2(m_j - max) and their total
+// in LDS; then each thread sums one pair of dims over the splits in split
+// order, with the loads of 16 splits in flight at a time.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
-  __shared__ float wts[kAttnGroupMaxSplits * kAttnQG];
-  __shared__ float tot[kAttnQG];
-  const int unit = blockIdx.x;
+  static_assert(kAttnGroupMaxSplits <= 64, "one split per lane");
+  __shared__ float wts[4][kAttnGroupMaxSplits];
+  __shared__ float tot[4];
+  const int quarters = (a.qg_size + 3) / 4;
+  const int unit = blockIdx.x / quarters, v0 = (blockIdx.x % quarters) * 4;
   const int qg = unit % a.n_qg, ik = unit / a.n_qg, kvh = ik % a.Hkv, i = ik / a.Hkv;
   const int ns = a.nsplit[i];
   if (ns <= 1) return;  // written by the main kernel
@@ -286,47 +291,48 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   const int G = a.H / a.Hkv;
   const int q0 = qg * a.qg_size;
   const int nq = max(0, min(a.qg_size, nr * G - q0));
-  if (nq == 0) return;
+  if (v0 >= nq) return;
   const size_t QG = a.qg_size, rec0 = (size_t)unit * a.n_split;
-  const float2* pml = reinterpret_cast<const float2*>(a.part + a.ml_off);
-  if (threadIdx.x < nq) {
-    const int r = threadIdx.x;
-    float mx = -INFINITY;
-    for (int j = 0; j < ns; ++j) {
-      const float2 v = pml[(rec0 + j) * QG + r];
-      if (v.y > 0.f) mx = fmaxf(mx, v.x);  // a split that saw no key has sum 0
-    }
-    float t = 0.f;
-    for (int j = 0; j < ns; ++j) {
-      const float2 v = pml[(rec0 + j) * QG + r];
-      const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
-      wts[j * kAttnQG + r] = w;
-      t += w * v.y;
-    }
-    tot[r] = t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {
+    const int v = v0 + wave;
+    const float2 ml = (v < nq && lane < ns) ? reinterpret_cast<const float2*>(a.part + a.ml_off)[(rec0 + lane) * QG + v]
+                                            : make_float2(-INFINITY, 0.f);
+    const float mx = wave_max(ml.y > 0.f ? ml.x : -INFINITY);  // a split that saw no key has sum 0
+    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+    const float t = wave_sum(w * ml.y);
+    if (lane < kAttnGroupMaxSplits) wts[wave][lane] = w;
+    if (lane == 0) tot[wave] = t;
   }
   __syncthreads();
-  constexpr int HP = HD / 2;
-  for (int p = threadIdx.x; p < nq * HP; p += 256) {
-    const int r = p / HP, c = p - r * HP;
-    float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < ns; ++j) {
-      const float2 x = *reinterpret_cast<const float2*>(a.part + ((rec0 + j) * QG + r) * HD + 2 * c);
-      const float w = wts[j * kAttnQG + r];
-      o0 += w * x.x;
-      o1 += w * x.y;
+  constexpr int HP = HD / 2;  // dim pairs
+  static_assert(HP <= 64, "one pair per lane");
+  const int v = v0 + wave, c = lane;
+  if (v >= nq || c >= HP) return;
+  const float* src = a.part + (rec0 * QG + v) * HD + 2 * c;
+  const size_t stride = QG * HD;  // floats between consecutive splits
+  float o0 = 0.f, o1 = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += 16) {
+    float2 x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      x[e] = *reinterpret_cast<const float2*>(src + (size_t)min(j0 + e, ns - 1) * stride);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float w = j0 + e < ns ? wts[wave][j0 + e] : 0.f;
+      o0 += w * x[e].x;
+      o1 += w * x[e].y;
     }
-    const int gq = q0 + r;
-    const int m = r0 + gq % nr, h = kvh * G + gq / nr;
-    xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / tot[r]);
-    xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot[r]);
   }
+  const int gq = q0 + v;
+  const int m = r0 + gq % nr, h = kvh * G + gq / nr;
+  xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / tot[wave]);
+  xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot[wave]);
 }
 
 void launch_attention_group(const AttnArgs& a, int wv, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const bool combine = a.n_split > 1;
-  const dim3 grid(a.map_n), cgrid(a.rows.n_seq * a.Hkv * a.n_qg);
+  const dim3 grid(a.map_n), cgrid(a.rows.n_seq * a.Hkv * a.n_qg * ((a.qg_size + 3) / 4));
   hipEvent_t e1 = combine ? nullptr : ev1;
 #define VS_GRP(HD, WV)                                                                                         \
   do {                                                                                                         \
