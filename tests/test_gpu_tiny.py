@@ -68,6 +68,36 @@ def test_prefill_logits_and_kv(eng, dec):
     B.vs_seq_close(eng.kv, seq)
 
 
+def test_long_prefill_split_attention(dec):
+    """A 960-token prefill in 64-row chunks: from the second chunk on, every
+    KV head carries four query groups over up to 896 committed keys, so the
+    grouped attention kernel runs with the committed keys cut into several
+    splits (head_dim 64) and merges them.  Logits and the last chunk's KV
+    against the oracle."""
+    e = G.engine(CFG, force_host=True, max_rows=64, max_seqs=2, max_ctx=1100)
+    n = 960
+    p = G.prompt(CFG, n, req=7)
+    seq = e.open(1000)
+    z = torch.empty(CFG.vocab, dtype=torch.float32, device="cuda")
+    B.vs_prefill(e.model, e.kv, seq, G.i32(p).data_ptr(), n, B.VS_GREEDY, 1.0, None, z.data_ptr(), e.stream)
+    torch.cuda.synchronize()
+    cache = KVCache(CFG, 1024)
+    st, zo = spec.prefill(dec, cache, 0, p)
+    zg = z.cpu().numpy().astype(np.float64)
+    assert np.abs(zg - zo).max() <= G.LOGIT_TOL, np.abs(zg - zo).max()
+    P, pending, committed = e.state()
+    assert P[seq] == n and committed[seq] == n + 1
+    if not G.near_tie(zo):
+        assert pending[seq] == st.pending
+    last = np.arange(n - 64, n)
+    for l in range(CFG.n_layers):
+        k, v = G.kv_slots(e, seq, l, last)
+        Ko, Vo = cache.get(0, l)
+        assert np.abs(k - Ko[:, last]).max() <= 0.05 * max(1.0, np.abs(Ko[:, last]).max())
+        assert np.abs(v - Vo[:, last]).max() <= 0.05 * max(1.0, np.abs(Vo[:, last]).max())
+    B.vs_seq_close(e.kv, seq)
+
+
 @pytest.mark.parametrize("eps", [None, 0.0, 0.5])
 def test_spec_equals_ar_and_oracle(eng, eps):
     """GPU speculative tokens == GPU greedy AR tokens == oracle greedy tokens
