@@ -34,7 +34,6 @@ namespace vs {
 
 namespace {
 
-
 // This wave's LDS writes are done, then the workgroup barrier.  Unlike
 // __syncthreads() it does not wait for global loads, so the steps loaded
 // ahead stay in flight.
