@@ -440,25 +440,23 @@ int ctx_bound(vs_kv* kv, const RowMap& rm) {
 // more query groups: the K/V of a step are read once for all of them.  The
 // split length kps (a multiple of 32 keys) minimises a launch-time model:
 // ceil(workgroups / slots) x (start + steps x step) + the combine launch when
-// a sequence has more than one split, with one workgroup of 8 waves (two of
-// 4) per CU.  A split holds at most kAttnGroupSteps steps including the
+// a sequence has more than one split, with two workgroups of 4 waves per CU.  A split holds at most kAttnGroupSteps steps including the
 // in-round keys.  Returns false when the pass does not fit this form.
 bool attention_group(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, double bytes, hipStream_t st) {
   const vs_model_cfg& c = m->c;
   if (a.n_qg < 2 || (c.head_dim != 64 && c.head_dim != 128)) return false;
-  int max_qg = 0, span = 0;
-  for (int i = 0; i < rm.n_seq; ++i) {
-    const int nr = rm.row_start[i + 1] - rm.row_start[i];
-    max_qg = std::max(max_qg, (nr * G + a.qg_size - 1) / a.qg_size);
-    span = std::max(span, rm.win + rm.idx_off + nr);
-  }
-  const int wv = max_qg <= 4 ? 4 : 8;
+  int span = 0;
+  for (int i = 0; i < rm.n_seq; ++i) span = std::max(span, rm.win + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]);
+  // 4-wave workgroups, two per CU: measured faster than 8-wave ones also
+  // where a KV head has more than four query groups (70B-shaped: 326 against
+  // 347 us), the second workgroup covering the first one's pipeline start
+  const int wv = kAttnGroupWaves;
   const int kps_cap = (kAttnGroupSteps * kAttnStepKeys - span - kAttnStepKeys) / kAttnStepKeys * kAttnStepKeys;
   if (kps_cap < kAttnStepKeys) return false;
-  const int slots = std::max(1, m->n_cu) * (wv == 4 ? 2 : 1);
+  const int slots = std::max(1, m->n_cu) * 2;
   const size_t units = (size_t)rm.n_seq * c.n_kv_heads * a.n_qg;
   const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
-  const double kStart = 4.0, kStepUs = wv == 8 ? 0.45 : 0.3, kCombine = 4.0;  // us
+  const double kStart = 4.0, kStepUs = 0.3, kCombine = 4.0;  // us
   double best = 1e30;
   int best_kps = 0;
   for (int kps = kAttnStepKeys; kps <= kps_cap; kps += kAttnStepKeys) {
@@ -503,7 +501,7 @@ bool attention_group(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& 
   a.M = rm.M;
   a.use_mfma = 1;
   upload_work_map(m, a, st);
-  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention_group(a, wv, st, e0, e1); });
+  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention_group(a, st, e0, e1); });
   return true;
 }
 

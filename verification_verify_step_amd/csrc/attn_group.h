@@ -2,7 +2,7 @@
 //
 // For passes whose KV heads carry more than one query group (GQA heads, or
 // many rows per sequence: a token tree), one workgroup takes one
-// (sequence, KV head, block of up to WV query groups, key split): its threads
+// (sequence, KV head, block of up to four query groups, key split): its threads
 // bring each 32-key step of K and V into LDS once, and each wave runs the
 // online softmax of one query group over it.  The splits of a sequence are
 // merged by a second, small kernel.
@@ -20,6 +20,7 @@ namespace vs {
 constexpr int kAttnStepKeys = 32;       // keys per step
 constexpr int kAttnGroupSteps = 32;     // steps per split at most (two block-table entries per step, one per lane)
 constexpr int kAttnGroupMaxSplits = 64;
-void launch_attention_group(const AttnArgs& a, int wv, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+constexpr int kAttnGroupWaves = 4;      // waves (query groups) per workgroup
+void launch_attention_group(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace vs

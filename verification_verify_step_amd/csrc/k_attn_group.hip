@@ -8,7 +8,8 @@
 // each wave its own key range of one query group, so when a KV head has many
 // query vectors (GQA heads, or the 64 rows of a token tree) every group reads
 // the same K/V again.  Here a workgroup owns one key range (split) of one KV
-// head and up to WV query groups, one per wave:
+// head and up to WV query groups, one per wave (WV = 4: two workgroups per
+// CU, so that one's pipeline start overlaps the other's steps):
 //
 //  * the workgroup's threads load each 32-key step (two 16-key blocks of K
 //    and of V, 16 KB at head_dim 128) in 16-byte pieces, kDepth steps ahead
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot[wave]);
 }
 
-void launch_attention_group(const AttnArgs& a, int wv, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+void launch_attention_group(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const bool combine = a.n_split > 1;
   const dim3 grid(a.map_n), cgrid(a.rows.n_seq * a.Hkv * a.n_qg * ((a.qg_size + 3) / 4));
   hipEvent_t e1 = combine ? nullptr : ev1;
@@ -346,13 +347,8 @@ void launch_attention_group(const AttnArgs& a, int wv, hipStream_t st, hipEvent_
         hipLaunchKernelGGL((attn_group_combine<HD>), cgrid, dim3(256), 0, st, a);                              \
     }                                                                                                          \
   } while (0)
-  if (a.hd == 128) {
-    if (wv == 4) VS_GRP(128, 4);
-    else VS_GRP(128, 8);
-  } else {
-    if (wv == 4) VS_GRP(64, 4);
-    else VS_GRP(64, 8);
-  }
+  if (a.hd == 128) VS_GRP(128, kAttnGroupWaves);
+  else VS_GRP(64, kAttnGroupWaves);
 #undef VS_GRP
 }
 
