@@ -119,6 +119,18 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
  * FINAL_NORM and HEAD. */
 vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const void* d_src, void* stream);
 void vs_model_destroy(vs_model* m);
+/* Split length of the grouped attention kernel, the one that takes passes
+ * whose KV heads carry more than one query group (GQA models, or more than
+ * 16 rows of a sequence).  A sequence's committed keys are cut into splits
+ * of `keys` keys at fixed absolute positions ("FlashSpec" page, §2.2: every
+ * row attends to all committed keys and its in-round ancestors), so a row's
+ * result does not depend on the other sequences of its pass; the setting
+ * changes rounding only.  keys: a multiple of 32 in [32, 928]; the default
+ * cuts about 4 MiB of K/V (all KV heads of a sequence) per split.  A context
+ * may span at most 64 splits.  Errors: VS_E_INVAL (null model, bad keys).
+ * vs_model_attn_split returns the current setting (0 for a null model). */
+vs_status vs_model_set_attn_split(vs_model* m, int32_t keys);
+int32_t vs_model_attn_split(const vs_model* m);
 
 /* ---- KV cache ---- */
 vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq,

@@ -166,29 +166,31 @@ def accept_greedy_chain(toks, logits):
 
 
 def accept_stochastic_chain(toks, p_rows, q_rows, u):
-    """The page's accept_or_reject, left to right with shared uniforms.
+    """Stochastic verification of a chain under shared uniforms
+    (self-speculative decoding page, m.lqnn.cn/news/278124, §2.4; "推测解码"
+    page, §2.2).
 
-    p_rows[i], q_rows[i]: target and draft distributions at row i (the
-    distribution that judges toks[i+1]); p_rows has k+1 rows.  Uses uniform
-    slots 16+i for the tests and slot 32 for the residual or bonus draw.
-    Returns (a, y, flags) with flags = rows whose |p/q - u| < 1e-3.
+    Draft d_{i+1} = toks[i+1] is kept when u[16+i] < min(1, p_i(d)/q_i(d)),
+    the ratio being 0 where q_i(d) = 0; a is the number of leading drafts
+    kept.  After a rejection at row a the emitted token is drawn with u[32]
+    from normalize(max(0, p_a - q_a)), or from p_a when that has no mass;
+    when every draft is kept it is drawn from p_k (the bonus row).
+    p_rows has k+1 rows, q_rows at least k.  Returns (a, y, flags), flags
+    listing the tested rows (0..min(a, k-1)) whose |ratio - u| < 1e-3.
     """
     k = len(toks) - 1
-    flags = []
-    for i in range(k):
-        tok = toks[i + 1]
-        p, q = p_rows[i], q_rows[i]
-        ratio = p[tok] / q[tok] if q[tok] > 0 else 0.0
-        ui = u[SLOT_ACCEPT + i]
-        if abs(ratio - ui) < FLAG_BAND:
-            flags.append(i)
-        if ui < min(1.0, ratio):
-            continue
-        w = np.maximum(p - q, 0.0)
-        if w.sum() <= 0:
-            w = p
-        return i, sample_index(w, u[SLOT_RESAMPLE]), flags
-    return k, sample_index(p_rows[k], u[SLOT_RESAMPLE]), flags
+    d = [int(t) for t in toks[1:]]
+    ratio = np.array([p_rows[i][d[i]] / q_rows[i][d[i]] if q_rows[i][d[i]] > 0 else 0.0 for i in range(k)],
+                     dtype=np.float64)
+    ut = np.asarray(u[SLOT_ACCEPT:SLOT_ACCEPT + k], dtype=np.float64)
+    kept = ut < np.minimum(1.0, ratio)
+    a = k if bool(kept.all()) else int(np.argmin(kept))  # the first rejected row
+    flags = [i for i in range(min(a + 1, k)) if abs(ratio[i] - ut[i]) < FLAG_BAND]
+    if a == k:
+        return k, sample_index(p_rows[k], u[SLOT_RESAMPLE]), flags
+    p_a, q_a = np.asarray(p_rows[a], dtype=np.float64), np.asarray(q_rows[a], dtype=np.float64)
+    resid = np.maximum(p_a - q_a, 0.0)
+    return a, sample_index(resid if resid.sum() > 0 else p_a, u[SLOT_RESAMPLE]), flags
 
 
 def commit_chain(cache, st, toks, a, y):

@@ -5,7 +5,7 @@ import torch
 
 import synth
 from synth import gpu_weights
-from synth.model_weights import SynthWeights
+from synth.model_weights import LAYER_TENSORS, SynthWeights
 from oracle.decoder import Decoder
 from verification_verify_step_amd import binding as B
 from verification_verify_step_amd.runtime import Engine
@@ -65,3 +65,24 @@ def near_tie(z, scale=1.0):
     logits and their rounding errors alike)."""
     s = np.sort(np.asarray(z, dtype=np.float64))
     return s[-1] - s[-2] < NEAR_TIE * scale
+
+
+class LayerWeights:
+    """The oracle's weights one layer at a time: each tensor is drawn once
+    per layer and kept until another layer is asked for (a float64 copy of
+    all verify layers of the 7B or 70B shape would not fit in host memory)."""
+
+    def __init__(self, cfg):
+        self.base = SynthWeights(cfg, precision="bf16", cache=False)
+        self.layer, self.cur, self.glob = None, {}, {}
+
+    def get(self, t, layer=0):
+        if t in LAYER_TENSORS:
+            if layer != self.layer:
+                self.layer, self.cur = layer, {}
+            if t not in self.cur:
+                self.cur[t] = self.base.get(t, layer)
+            return self.cur[t]
+        if t not in self.glob:
+            self.glob[t] = self.base.get(t, layer)
+        return self.glob[t]

@@ -126,6 +126,7 @@ def test_head_and_stochastic_accept(ctx):
         pr = [spec.probs(r, T) for r in zg[rs]]
         qr = [spec.probs(r, T) for r in zd[rs]]
         a, y, flags = spec.accept_stochastic_chain(list(toks[rs]), pr, qr, ctx["U"][i])
+        assert bool(got[i][2] & 1) == bool(flags), (i, got[i][2], flags)  # the same near-ties are flagged
         if flags:
             flagged += 1
             continue
@@ -164,6 +165,7 @@ def test_top_p_accept(ctx):
         pr = [spec.top_p_filter(p, top_p) for p in pr_full]
         qr = [spec.probs(r, T) for r in zd[rs]]
         a, y, flags = spec.accept_stochastic_chain(list(toks[rs]), pr, qr, ctx["U"][i])
+        assert bool(got[i][2] & 1) == bool(flags), (i, got[i][2], flags)  # the same near-ties are flagged
         if flags:
             flagged += 1
             continue

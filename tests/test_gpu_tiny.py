@@ -71,10 +71,12 @@ def test_prefill_logits_and_kv(eng, dec):
 def test_long_prefill_split_attention(dec):
     """A 960-token prefill in 64-row chunks: from the second chunk on, every
     KV head carries four query groups over up to 896 committed keys, so the
-    grouped attention kernel runs with the committed keys cut into several
-    splits (head_dim 64) and merges them.  Logits and the last chunk's KV
-    against the oracle."""
+    grouped attention kernel runs; with its split length set to 32 keys the
+    committed keys are cut into up to 28 splits (head_dim 64) that the
+    combine merges.  Logits and the last chunk's KV against the oracle."""
     e = G.engine(CFG, force_host=True, max_rows=64, max_seqs=2, max_ctx=1100)
+    B.vs_model_set_attn_split(e.model, 32)
+    assert B.vs_model_attn_split(e.model) == 32
     n = 960
     p = G.prompt(CFG, n, req=7)
     seq = e.open(1000)
@@ -175,15 +177,23 @@ def test_draft_verify_parity(eng, dec):
         assert np.abs(gz[s] - oz[s]).max() <= G.LOGIT_TOL
         if not G.near_tie(oz[s]):
             assert gt[s + 1] == ot[s + 1]
+    # the drafts may part only at a near-tie of the oracle (asserted above)
     if gt == ot:
         gh = hL.cpu().numpy().astype(np.float64)
         assert np.abs(gh - oh).max() <= 1e-2 * max(1.0, np.abs(oh).max())
-        # verify over the GPU's own hidden rows vs the oracle's verify
-        z = torch.empty((k + 1, CFG.vocab), dtype=torch.float32, device="cuda")
-        B.vs_verify(eng.model, eng.kv, B.make_batch([seq], [k + 1]), CFG.exit_layer, toks.data_ptr(), hL.data_ptr(),
-                    z.data_ptr(), eng.stream)
-        zo = spec.verify_chain(dec, cache, st, ot, oh)
-        assert np.abs(z.cpu().numpy() - zo).max() <= G.LOGIT_TOL
+    # verify parity on the oracle's own draft tokens: the GPU's first-L pass
+    # over them (writing the same in-round slots), then the verify layers
+    # and the head, against the oracle's verify of the same rows
+    ot_d = G.i32(ot)
+    hL2 = torch.empty((k + 1, CFG.d_model), dtype=torch.float32, device="cuda")
+    batch = B.make_batch([seq], [k + 1])
+    B.vs_forward_layers(eng.model, eng.kv, batch, 0, CFG.exit_layer, ot_d.data_ptr(), None, hL2.data_ptr(), eng.stream)
+    z = torch.empty((k + 1, CFG.vocab), dtype=torch.float32, device="cuda")
+    B.vs_verify(eng.model, eng.kv, batch, CFG.exit_layer, ot_d.data_ptr(), hL2.data_ptr(), z.data_ptr(), eng.stream)
+    gh2 = hL2.cpu().numpy().astype(np.float64)
+    assert np.abs(gh2 - oh).max() <= 1e-2 * max(1.0, np.abs(oh).max())
+    zo = spec.verify_chain(dec, cache, st, ot, oh)
+    assert np.abs(z.cpu().numpy() - zo).max() <= G.LOGIT_TOL
     B.vs_seq_close(eng.kv, seq)
 
 
@@ -253,7 +263,8 @@ def test_tree_verify_accept_commit(eng, dec):
 
 def test_stochastic_accept_parity(eng):
     """Accept decisions on identical logits with shared uniforms equal the
-    oracle's accept_or_reject, except decisions flagged as near-ties."""
+    oracle's stochastic acceptance, except decisions flagged as near-ties;
+    the GPU's flag bit equals the oracle's flags for every sequence."""
     rng = np.random.default_rng(7)
     n_seq, k, V = 8, 4, CFG.vocab
     M = n_seq * (k + 1)
@@ -279,6 +290,7 @@ def test_stochastic_accept_parity(eng):
         pr = [spec.probs(z, T) for z in zt[rs].astype(np.float64)]
         qr = [spec.probs(z, T) for z in zd[rs].astype(np.float64)]
         a, y, flags = spec.accept_stochastic_chain(list(toks[rs]), pr, qr, U[i])
+        assert bool(got[i][2] & 1) == bool(flags), (i, got[i][2], flags)  # the same near-ties are flagged
         if flags:
             continue
         assert (got[i][0], got[i][1]) == (a, y), (i, got[i], a, y)

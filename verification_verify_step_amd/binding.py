@@ -19,7 +19,7 @@ VS_DYNK_MAX_WINDOW = 256
 
 EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
-    "vs_model_destroy", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
+    "vs_model_destroy", "vs_model_set_attn_split", "vs_model_attn_split", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_accept_top_p", "vs_commit",
     "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_dynk_init",
     "vs_dynk_update", "vs_ngram_propose", "vs_step_ngram", "vs_stats_enable", "vs_stats_read",
@@ -96,6 +96,8 @@ def lib():
             "vs_model_create": (I32, [pcfg, VP, VP, I32, I32, I32, VP, P(VP)]),
             "vs_model_set_tensor": (I32, [VP, I32, I32, VP, VP]),
             "vs_model_destroy": (None, [VP]),
+            "vs_model_set_attn_split": (I32, [VP, I32]),
+            "vs_model_attn_split": (I32, [VP]),
             "vs_kv_create": (I32, [VP, VP, I32, I32, I32, VP, P(VP)]),
             "vs_kv_destroy": (None, [VP]),
             "vs_seq_open": (I32, [VP, I32, VP, pI]),
@@ -173,6 +175,14 @@ def vs_model_set_tensor(model, tensor, layer, d_src, stream):
 
 def vs_model_destroy(model):
     lib().vs_model_destroy(model)
+
+
+def vs_model_set_attn_split(model, keys):
+    _check("vs_model_set_attn_split", lib().vs_model_set_attn_split(model, keys))
+
+
+def vs_model_attn_split(model):
+    return lib().vs_model_attn_split(model)
 
 
 def vs_kv_create(model, d_kv, n_blocks, max_seqs, max_blocks_per_seq, stream):

@@ -52,7 +52,7 @@ bool shape_ok(const vs_model_cfg* c, std::string* why) {
   if (c->exit_layer < 0 || c->exit_layer > c->n_layers) return bad("exit_layer must lie in [0, n_layers]");
   if (c->d_model % 256 != 0) return bad("d_model must be a multiple of 256");
   if (c->d_ffn % 32 != 0) return bad("d_ffn must be a multiple of 32");
-  if (c->head_dim % 16 != 0 || c->head_dim > 128) return bad("head_dim must be a multiple of 16, at most 128");
+  if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (c->n_heads % c->n_kv_heads != 0) return bad("n_heads must be a multiple of n_kv_heads");
   if ((c->n_heads * c->head_dim) % 32 != 0) return bad("n_heads*head_dim must be a multiple of 32");
   if (c->vocab % 16 != 0 || c->vocab > 32768) return bad("vocab must be a multiple of 16, at most 32768");
@@ -85,13 +85,12 @@ WeightLayout weight_layout(const vs_model_cfg* c) {
 }
 
 constexpr size_t kAttnPartFloats = size_t(128) << 20;  // 512 MB of attention partials
-constexpr int kAmapSlots = 4;                         // attention work maps in rotation
 // tree drafting state: node arrays (4 int + 1 double per node), meta, row arrays
 constexpr size_t kTreeBytes = (size_t)kTreeNodes * 24 + 256 + (size_t)kMaxRows * 24;
 
 struct WsLayout {
   size_t h, xa_h, xa_o, xa_act, ss, q, rope, kvrow, part, attn_cnt, tree, amax_val, amax_idx, logits, dlogits, hidden, tokens, st_mx, st_amax,
-      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, amap, kpart, kcnt, total;
+      st_second, st_sum, dst_mx, dst_amax, dst_sum, result, conf, tp_key, tp_id, tp_mass, rs, kpart, kcnt, total;
 };
 
 WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
@@ -133,11 +132,24 @@ WsLayout ws_layout(const vs_model_cfg* c, int R, int S) {
   w.tp_id = take(R * 4);
   w.tp_mass = take(R * 8);
   w.rs = take(R * 4);
-  w.amap = take((size_t)kAmapSlots * kAttnMapMax * 4);
   w.kpart = take(kGemmSplitFloats * 4);
   w.kcnt = take((size_t)kGemmSplitCells * 4);
   w.total = off;
   return w;
+}
+
+// Longest committed split of the grouped attention kernel: 29 steps, so that
+// with up to 64 in-round keys a split stays within kAttnGroupSteps steps.
+constexpr int kAttnGroupMaxKps = (kAttnGroupSteps - 3) * kAttnStepKeys;
+
+// Default split length of the grouped kernel for a model: the splits of one
+// sequence cut about 4 MiB of K/V (all its KV heads) each, within
+// [32, kAttnGroupMaxKps] keys: 256 keys at the 7B shape (32 KV heads x 128),
+// the longest split at the 70B shape (8 x 128).
+int default_attn_split(const vs_model_cfg& c) {
+  const long per_key = (long)c.n_kv_heads * c.head_dim * 4;
+  const long keys = (4L << 20) / per_key / kAttnStepKeys * kAttnStepKeys;
+  return (int)std::min<long>(kAttnGroupMaxKps, std::max<long>(kAttnStepKeys, keys));
 }
 
 enum Family { F_QKV = 0, F_O, F_GU, F_DOWN, F_HEAD, F_ATTN, F_SMALL, F_COUNT };
@@ -168,15 +180,8 @@ struct vs_model {
   TreeArgs tree;          // device pointers of the tree drafting state
   float *h, *ss, *rs, *kpart, *q, *part, *logits, *dlogits, *hidden, *st_mx, *st_second, *dst_mx, *amax_val;
   unsigned* kcnt = nullptr;
-  // attention work maps: device slots in the workspace, pinned staging on
-  // the host; ev[slot] follows the last launch that read the slot
-  int n_cu = 256;  // compute units of the device
-  int* amap_dev[kAmapSlots] = {};
-  int* amap_pin[kAmapSlots] = {};
-  hipEvent_t amap_ev[kAmapSlots] = {};
-  int amap_slot = -1;
-  hipStream_t amap_stream = nullptr;  // stream of the last launch that read the current slot
-  std::vector<int> amap_build, amap_last;
+  int n_cu = 256;        // compute units of the device
+  int attn_split = 256;  // keys per committed split of the grouped attention kernel
   uint16_t *xa_h, *xa_o, *xa_act;
   float2* rope;
   int* kvrow;
@@ -361,224 +366,175 @@ void load_rows(vs_model* m, int M, const int* tokens, const float* hidden, const
   m->ss_groups = (m->c.d_model + 255) / 256;
 }
 
-int upload_work_map(vs_model* m, AttnArgs& a, hipStream_t st);
+// Split plan of a pass's attention (the same for every layer of the pass).
+// The split structure itself is fixed (see AttnArgs): the plan lays out the
+// workgroups from the host's upper bound P_ub of each sequence's KV length,
+// and the kernels skip what the device's P does not need.  The kernel class
+// is a property of the sequence alone: a sequence whose KV heads carry more
+// than one query group (a GQA model, or more than 16 rows of an MHA model)
+// takes the grouped kernel, which reads each K/V step once for all of a
+// head's query groups; the others take the one-group kernel.  A pass that
+// holds both runs both launches, each over its own sequences (the other
+// sequences get no workgroups and nsplit 0).  Fails when a launch does not
+// fit the partials workspace, the counters or the combine.
+struct AttnPlan {
+  AttnArgs one, grp;  // split fields, workgroup layout, query groups
+  bool has_one = false, has_grp = false;
+  double bytes_one = 0, bytes_grp = 0;  // algorithmic K/V bytes of one layer
+};
 
-// Attention work map of a pass: sequence i takes ceil(P_i / kps) committed
-// splits (P_i its context bound) plus the in-round window, and only its
-// non-empty query groups, instead of every sequence taking the longest
-// one's splits and every query group.  The (sequence, KV head, key range)
-// groups go to the least-loaded XCD, their query groups back to back there
-// (block b runs on XCD b % 8).  Returns the slot used, or -1: no map (it
-// would not fit, or would save little over the plain grid).
-int attn_work_map(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, hipStream_t st) {
-  const int wv = attn_waves(a.qg_size);
-  std::vector<int>& mp = m->amap_build;
-  std::vector<int> lists[8];
-  long load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+bool attn_seq_grouped(const vs_model_cfg& c, int nr) {
+  const int G = c.n_heads / c.n_kv_heads;
+  return G > 1 || nr * G > kAttnQG;
+}
+
+vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
+  const vs_model_cfg& c = m->c;
+  const int G = c.n_heads / c.n_kv_heads;
+  auto base = [&](AttnArgs& a) {
+    memset(&a, 0, sizeof(a));
+    a.rows = rm;
+    a.H = c.n_heads;
+    a.Hkv = c.n_kv_heads;
+    a.hd = c.head_dim;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    a.part = m->part;
+    a.cnt = m->attn_cnt;
+    a.xa_o = m->xa_o;
+    a.M = rm.M;
+  };
+  base(pl->one);
+  base(pl->grp);
+  pl->has_one = pl->has_grp = false;
+  pl->bytes_one = pl->bytes_grp = 0;
+  int nr_one = 0, nr_grp = 0;
+  bool grp[kMaxSeq];
   for (int i = 0; i < rm.n_seq; ++i) {
     const int nr = rm.row_start[i + 1] - rm.row_start[i];
-    const int nqg = (nr * G + a.qg_size - 1) / a.qg_size;
-    const int Pi = kv->P_ub[rm.seq[i]];
-    const int ns = std::min(a.n_split, (Pi + a.kps - 1) / a.kps);
-    a.nsplit[i] = ns;
-    const int wpb = (ns + 1 + wv - 1) / wv;
-    for (int kvh = 0; kvh < a.Hkv; ++kvh)
-      for (int wg = 0; wg < wpb; ++wg) {
-        int x = 0;
-        for (int j = 1; j < 8; ++j)
-          if (load[j] < load[x]) x = j;
-        for (int qg = 0; qg < nqg; ++qg) lists[x].push_back(i | kvh << 6 | qg << 13 | wg << 20);
-        load[x] += nqg;
-      }
+    grp[i] = attn_seq_grouped(c, nr);
+    const double b = (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + nr) * c.n_kv_heads * c.head_dim * 4;
+    if (grp[i]) {
+      nr_grp = std::max(nr_grp, nr);
+      pl->bytes_grp += b;
+    } else {
+      nr_one = std::max(nr_one, nr);
+      pl->bytes_one += b;
+    }
   }
-  size_t n = 0, used = 0;
-  for (int x = 0; x < 8; ++x) {
-    n = std::max(n, lists[x].size());
-    used += lists[x].size();
-  }
-  // The plain grid launches every sequence with the longest one's splits and
-  // every query group; keep it (no upload) unless the map saves a tenth.
-  const size_t wps = (size_t)(a.n_split + wv) / wv;
-  const size_t plain = (size_t)8 * a.n_qg * ((rm.n_seq * wps * a.Hkv + 7) / 8);
-  if (n == 0 || 8 * n > (size_t)kAttnMapMax || 10 * used > 9 * plain) return -1;
-  mp.assign(8 * n, -1);
-  for (int x = 0; x < 8; ++x)
-    for (size_t p = 0; p < lists[x].size(); ++p) mp[8 * p + x] = lists[x][p];
-  return upload_work_map(m, a, st);
-}
-
-// Makes m->amap_build the launch's work map (a.map, a.map_n): uploaded when
-// it differs from the current slot's, through a rotation of pinned staging
-// and device slots; a slot is rewritten only after the last launch that read
-// it has run.  Returns the slot used.
-int upload_work_map(vs_model* m, AttnArgs& a, hipStream_t st) {
-  const std::vector<int>& mp = m->amap_build;
-  if (m->amap_slot < 0 || mp != m->amap_last) {
-    // every launch that read the current slot is on the stream before this
-    // point; a slot is refilled only once its event has passed
-    if (m->amap_slot >= 0) (void)hipEventRecord(m->amap_ev[m->amap_slot], m->amap_stream);
-    const int slot = (m->amap_slot + 1) % kAmapSlots;
-    (void)hipEventSynchronize(m->amap_ev[slot]);
-    memcpy(m->amap_pin[slot], mp.data(), mp.size() * 4);
-    (void)hipMemcpyAsync(m->amap_dev[slot], m->amap_pin[slot], mp.size() * 4, hipMemcpyHostToDevice, st);
-    m->amap_slot = slot;
-    m->amap_last = mp;
-  }
-  a.map = m->amap_dev[m->amap_slot];
-  a.map_n = (int)mp.size();
-  m->amap_stream = st;
-  return m->amap_slot;
-}
-
-int ctx_bound(vs_kv* kv, const RowMap& rm) {
-  int p = 0;
-  for (int i = 0; i < rm.n_seq; ++i) p = std::max(p, kv->P_ub[rm.seq[i]]);
-  return p;
-}
-
-// Grouped attention (attn_group.h) for passes whose KV heads carry two or
-// more query groups: the K/V of a step are read once for all of them.  The
-// split length kps (a multiple of 32 keys) minimises a launch-time model:
-// ceil(workgroups / slots) x (start + steps x step) + the combine launch when
-// a sequence has more than one split, with two workgroups of 4 waves per CU.  A split holds at most kAttnGroupSteps steps including the
-// in-round keys.  Returns false when the pass does not fit this form.
-bool attention_group(vs_model* m, vs_kv* kv, const RowMap& rm, int G, AttnArgs& a, double bytes, hipStream_t st) {
-  const vs_model_cfg& c = m->c;
-  if (a.n_qg < 2 || (c.head_dim != 64 && c.head_dim != 128)) return false;
-  int span = 0;
-  for (int i = 0; i < rm.n_seq; ++i) span = std::max(span, rm.win + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]);
-  // 4-wave workgroups, two per CU: measured faster than 8-wave ones also
-  // where a KV head has more than four query groups (70B-shaped: 326 against
-  // 347 us), the second workgroup covering the first one's pipeline start
-  const int wv = kAttnGroupWaves;
-  const int kps_cap = (kAttnGroupSteps * kAttnStepKeys - span - kAttnStepKeys) / kAttnStepKeys * kAttnStepKeys;
-  if (kps_cap < kAttnStepKeys) return false;
-  const int slots = std::max(1, m->n_cu) * 2;
-  const size_t units = (size_t)rm.n_seq * c.n_kv_heads * a.n_qg;
-  const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
-  const double kStart = 4.0, kStepUs = 0.3, kCombine = 4.0;  // us
-  double best = 1e30;
-  int best_kps = 0;
-  for (int kps = kAttnStepKeys; kps <= kps_cap; kps += kAttnStepKeys) {
+  const size_t rec_floats = (size_t)c.head_dim + 2;
+  auto finish = [&](AttnArgs& a, size_t units) -> vs_status {
+    if (units > (size_t)kAttnMaxUnits)
+      return fail(VS_E_SHAPE, "attention: %zu units exceed the %d counters", units, kAttnMaxUnits);
+    if (units * a.n_split * a.qg_size * rec_floats > kAttnPartFloats)
+      return fail(VS_E_SHAPE, "attention: pass too wide for the partials workspace");
+    a.ml_off = units * a.n_split * a.qg_size * c.head_dim;
+    a.ml_off += a.ml_off & 1;
+    return VS_OK;
+  };
+  if (nr_grp > 0) {
+    AttnArgs& a = pl->grp;
+    pl->has_grp = true;
+    const int nq = nr_grp * G;
+    a.n_qg = (nq + kAttnQG - 1) / kAttnQG;
+    a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
+    const int wv = kAttnGroupWaves;
+    a.kps = m->attn_split;
     long wgs = 0;
-    int max_ns = 1;
+    int nmax = 1;
     for (int i = 0; i < rm.n_seq; ++i) {
+      a.wg_start[i] = (int)wgs;
+      a.nsplit[i] = 0;
+      if (!grp[i]) continue;
       const int nr = rm.row_start[i + 1] - rm.row_start[i];
       const int nqb = ((nr * G + a.qg_size - 1) / a.qg_size + wv - 1) / wv;
-      const int ns = std::max(1, (kv->P_ub[rm.seq[i]] + kps - 1) / kps);
-      max_ns = std::max(max_ns, ns);
-      wgs += (long)c.n_kv_heads * nqb * ns;
+      const int ns = std::max(1, (kv->P_ub[rm.seq[i]] + a.kps - 1) / a.kps);
+      if (ns > kAttnGroupMaxSplits)
+        return fail(VS_E_SHAPE, "attention: a context of %d keys needs more than %d splits of %d keys",
+                    kv->P_ub[rm.seq[i]], kAttnGroupMaxSplits, a.kps);
+      const long groups = ((long)c.n_kv_heads * ns + kAttnXcds - 1) / kAttnXcds * kAttnXcds;
+      a.nsplit[i] = ns;
+      wgs += groups * nqb;
+      nmax = std::max(nmax, ns);
+      if (wgs > (1L << 30)) return fail(VS_E_SHAPE, "attention: pass too large");
     }
-    if (max_ns > kAttnGroupMaxSplits || (max_ns > 1 && units * max_ns * rec > kAttnPartFloats) ||
-        wgs > kAttnMapMax)
-      continue;
-    const double t = std::ceil((double)wgs / slots) * (kStart + kStepUs * (kps / kAttnStepKeys)) +
-                     (max_ns > 1 ? kCombine : 0.0);
-    if (t < best) {
-      best = t;
-      best_kps = kps;
+    a.wg_start[rm.n_seq] = (int)wgs;
+    a.n_split = nmax;
+    vs_status rc = finish(a, (size_t)rm.n_seq * c.n_kv_heads * a.n_qg);
+    if (rc != VS_OK) return rc;
+  }
+  if (nr_one > 0) {
+    AttnArgs& a = pl->one;
+    pl->has_one = true;
+    a.n_qg = 1;
+    a.qg_size = nr_one * G;
+    // Chunks of each sequence (8 one-step splits and the window), then the
+    // chunks per workgroup (cpw) that minimise a launch-time model: a
+    // workgroup starts in about kStart, runs its chunks one after another at
+    // about kChunk each (one step, the merge; the next chunk's loads in
+    // flight meanwhile), with about ceil(workgroups / CUs) workgroups per
+    // CU, plus the cross-workgroup combine when a unit has several
+    // workgroups.  One sequence at a short context takes one chunk per
+    // workgroup (parallel over the chip); many sequences or long contexts
+    // take several (fewer starts and combines).
+    int chunks[kMaxSeq];
+    int cmax = 1;
+    for (int i = 0; i < rm.n_seq; ++i) {
+      chunks[i] = 0;
+      if (grp[i]) continue;
+      const int ns = (kv->P_ub[rm.seq[i]] + kAttnStepKeys - 1) / kAttnStepKeys;
+      chunks[i] = (ns + 1 + kAttnWaves - 1) / kAttnWaves;
+      cmax = std::max(cmax, chunks[i]);
     }
-  }
-  if (best_kps == 0) return false;
-  a.kps = best_kps;
-  a.n_split = 1;
-  std::vector<int>& mp = m->amap_build;
-  mp.clear();
-  for (int i = 0; i < rm.n_seq; ++i) {
-    const int nr = rm.row_start[i + 1] - rm.row_start[i];
-    const int nqb = ((nr * G + a.qg_size - 1) / a.qg_size + wv - 1) / wv;
-    const int ns = std::max(1, (kv->P_ub[rm.seq[i]] + a.kps - 1) / a.kps);
-    a.nsplit[i] = ns;
-    a.n_split = std::max(a.n_split, ns);
-    for (int kvh = 0; kvh < c.n_kv_heads; ++kvh)
-      for (int qb = 0; qb < nqb; ++qb)
-        for (int sp = 0; sp < ns; ++sp) mp.push_back(i | kvh << 6 | qb << 13 | sp << 20);
-  }
-  a.part = m->part;
-  a.ml_off = units * a.n_split * a.qg_size * c.head_dim;
-  a.ml_off += a.ml_off & 1;
-  a.xa_o = m->xa_o;
-  a.M = rm.M;
-  a.use_mfma = 1;
-  upload_work_map(m, a, st);
-  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention_group(a, st, e0, e1); });
-  return true;
-}
-
-void attention(vs_model* m, vs_kv* kv, const RowMap& rm, int layer, hipStream_t st) {
-  const vs_model_cfg& c = m->c;
-  AttnArgs a;
-  memset(&a, 0, sizeof(a));
-  a.rows = rm;
-  a.kv = kv_view(kv, layer);
-  a.q = m->q;
-  a.H = c.n_heads;
-  a.Hkv = c.n_kv_heads;
-  a.hd = c.head_dim;
-  a.scale = 1.0f / std::sqrt((float)c.head_dim);
-  int max_nr = 0;
-  for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
-  const int G = c.n_heads / c.n_kv_heads;
-  const int nq = max_nr * G;
-  a.n_qg = (nq + kAttnQG - 1) / kAttnQG;
-  a.qg_size = (nq + a.n_qg - 1) / a.n_qg;
-  const int P = ctx_bound(kv, rm);
-  double bytes = 0;
-  for (int i = 0; i < rm.n_seq; ++i)
-    bytes += (double)(kv->P_ub[rm.seq[i]] + rm.idx_off + rm.row_start[i + 1] - rm.row_start[i]) * c.n_kv_heads *
-             c.head_dim * 4;
-  if (attention_group(m, kv, rm, G, a, bytes, st)) return;
-  const int units = rm.n_seq * c.n_kv_heads * a.n_qg;
-  // Splits: a wave's 32-key steps run one after another (about 2.5 us each,
-  // latency-bound), a workgroup of W waves takes W splits of a unit, and
-  // units of more than one workgroup pay the cross-workgroup combine.  With
-  // one workgroup per CU (the kernel's registers), the launch takes about
-  // ceil(workgroups / CUs) x (start + steps x step + combine); the split
-  // count is chosen to minimise that, with full workgroups (W·w − 1
-  // committed splits and the in-round window), bounded by the partials
-  // buffer and the combine's capacity.  Measured on MI355X against the
-  // earlier rule (~256-key splits): 8 sequences x 2048 keys 91 -> 53 us,
-  // one sequence x 4096 keys x 64 rows 65 -> 46 us, the 7B chain unchanged.
-  // Splits past a shorter sequence's context run no step.
-  int units_eff = 0;  // units with work: every sequence's non-empty query groups
-  for (int i = 0; i < rm.n_seq; ++i)
-    units_eff += c.n_kv_heads * (((rm.row_start[i + 1] - rm.row_start[i]) * G + a.qg_size - 1) / a.qg_size);
-  int n_split = 0;
-  a.kps = 32;
-  if (P > 0) {
-    const int wv = attn_waves(a.qg_size);
-    const int max_split = (P + 31) / 32;
-    const size_t rec = (size_t)a.qg_size * (c.head_dim + 2);
-    const int budget_wg = (int)std::max<size_t>(1, kAttnPartFloats / (rec * units));
-    const int max_wg = std::max(1, std::min(budget_wg, kAttnCombineSlots / a.qg_size));
-    constexpr double kStart = 5.0, kPerStep = 2.5, kCombine = 6.0;  // us, measured
+    if ((size_t)cmax * a.qg_size > (size_t)kAttnCombineSlots)
+      return fail(VS_E_SHAPE, "attention: a context needs %d chunks of %d keys, beyond the combine's %d slots", cmax,
+                  kAttnWaves * kAttnStepKeys, kAttnCombineSlots / a.qg_size);
+    constexpr double kStart = 5.0, kChunk = 3.0, kCombine = 5.0;  // us
+    const int ncu = std::max(1, m->n_cu);
     double best = 1e30;
-    for (int w = 1; w <= max_wg; ++w) {
-      const int ns0 = std::min(max_split, wv * w - 1 > 0 ? wv * w - 1 : 1);
-      const int kps = ((P + ns0 - 1) / ns0 + 31) / 32 * 32;
-      const int ns = (P + kps - 1) / kps;
-      const int wpb = (ns + 1 + wv - 1) / wv;
-      const double rounds = std::ceil((double)units_eff * wpb / std::max(1, m->n_cu));
-      const double t = rounds * (kStart + kPerStep * (kps / 32) + (wpb > 1 ? kCombine : 0.0));
+    int best_cpw = 1;
+    for (int cpw = 1; cpw <= cmax; ++cpw) {
+      if (cpw > 1 && (cmax + cpw - 1) / cpw == (cmax + cpw - 2) / (cpw - 1)) continue;  // same split of the longest
+      long wgs = 0;
+      bool multi = false;
+      for (int i = 0; i < rm.n_seq; ++i) {
+        wgs += (long)c.n_kv_heads * ((chunks[i] + cpw - 1) / cpw);
+        multi |= chunks[i] > cpw;
+      }
+      const double t = std::ceil((double)wgs / ncu) * (kStart + cpw * kChunk) + (multi ? kCombine : 0.0);
       if (t < best) {
         best = t;
-        n_split = ns;
-        a.kps = kps;
+        best_cpw = cpw;
       }
-      if (ns0 == max_split) break;
     }
+    a.cpw = best_cpw;
+    a.kps = kAttnStepKeys;
+    long wgs = 0;
+    for (int i = 0; i < rm.n_seq; ++i) {
+      a.wg_start[i] = (int)wgs;
+      a.nsplit[i] = chunks[i];
+      wgs += (long)c.n_kv_heads * ((chunks[i] + a.cpw - 1) / a.cpw);
+    }
+    a.wg_start[rm.n_seq] = (int)wgs;
+    a.n_split = cmax;
+    vs_status rc = finish(a, (size_t)rm.n_seq * c.n_kv_heads);
+    if (rc != VS_OK) return rc;
   }
-  a.n_split = n_split;
-  const int wpb = (n_split + 1 + attn_waves(a.qg_size) - 1) / attn_waves(a.qg_size);
-  a.part = m->part;
-  a.ml_off = (size_t)units * wpb * a.qg_size * c.head_dim;
-  a.ml_off += a.ml_off & 1;
-  a.cnt = m->attn_cnt;
-  a.xa_o = m->xa_o;
-  a.M = rm.M;
-  a.use_mfma = 1;
-  attn_work_map(m, kv, rm, G, a, st);
-  timed(m, F_ATTN, bytes, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention(a, st, e0, e1); });
+  return VS_OK;
+}
+
+void attention(vs_model* m, vs_kv* kv, const AttnPlan& pl, int layer, hipStream_t st) {
+  if (pl.has_one) {
+    AttnArgs a = pl.one;
+    a.kv = kv_view(kv, layer);
+    a.q = m->q;
+    timed(m, F_ATTN, pl.bytes_one, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention(a, st, e0, e1); });
+  }
+  if (pl.has_grp) {
+    AttnArgs a = pl.grp;
+    a.kv = kv_view(kv, layer);
+    a.q = m->q;
+    timed(m, F_ATTN, pl.bytes_grp, st, [&](hipEvent_t e0, hipEvent_t e1) { launch_attention_group(a, st, e0, e1); });
+  }
 }
 
 // Layers [start, end) over rows already loaded into h / xa_h / ss.
@@ -586,6 +542,8 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
                 const int* copy_rows) {
   const vs_model_cfg& c = m->c;
   const int M = rm.M;
+  AttnPlan plan;
+  if (start < end) (void)attn_plan(m, kv, rm, &plan);  // checked before the pass was enqueued
   for (int l = start; l < end; ++l) {
     {
       GemmArgs g = gemm_base(m, m->qkv[l], m->xa_h, M);
@@ -601,7 +559,7 @@ void run_layers(vs_model* m, vs_kv* kv, const RowMap& rm, int start, int end, hi
       g.kvrow = m->kvrow;
       run_gemm(m, g, EPI_QKV, F_QKV, m->qkv[l], st, nullptr);
     }
-    attention(m, kv, rm, l, st);
+    attention(m, kv, plan, l, st);
     {
       GemmArgs g = gemm_base(m, m->o[l], m->xa_o, M);
       g.h = m->h;
@@ -674,22 +632,14 @@ vs_status batch_rowmap(vs_kv* kv, const vs_batch* b, RowMap* rm) {
   return VS_OK;
 }
 
-// Attention partials need (splits + 1) records per (sequence, KV head, query
-// group); at least two splits must fit.
-vs_status check_attn_budget(vs_model* m, const RowMap& rm) {
-  int max_nr = 0;
-  for (int i = 0; i < rm.n_seq; ++i) max_nr = std::max(max_nr, rm.row_start[i + 1] - rm.row_start[i]);
-  const int G = m->c.n_heads / m->c.n_kv_heads;
-  const int nq = max_nr * G, n_qg = (nq + kAttnQG - 1) / kAttnQG, qg = (nq + n_qg - 1) / n_qg;
-  const size_t need = (size_t)rm.n_seq * m->c.n_kv_heads * n_qg * qg * (m->c.head_dim + 2) * 2;
-  if (need > kAttnPartFloats) return fail(VS_E_SHAPE, "pass too wide for the attention workspace");
-  if ((size_t)rm.n_seq * m->c.n_kv_heads * n_qg > (size_t)kAttnMaxUnits)
-    return fail(VS_E_SHAPE, "pass has more attention units than the %d counters", kAttnMaxUnits);
-  return VS_OK;
+// The pass's attention plan must fit the workspace (attn_plan).
+vs_status check_attn_budget(vs_model* m, vs_kv* kv, const RowMap& rm) {
+  AttnPlan pl;
+  return attn_plan(m, kv, rm, &pl);
 }
 
 vs_status check_capacity(vs_kv* kv, const RowMap& rm) {
-  vs_status rc = check_attn_budget(kv->m, rm);
+  vs_status rc = check_attn_budget(kv->m, kv, rm);
   if (rc != VS_OK) return rc;
   for (int i = 0; i < rm.n_seq; ++i) {
     const int s = rm.seq[i];
@@ -819,11 +769,7 @@ vs_status vs_model_create(const vs_model_cfg* cfg, void* d_weights, void* d_work
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
       m->n_cu = n_cu;
   }
-  for (int i = 0; i < kAmapSlots && ae == hipSuccess; ++i) {
-    m->amap_dev[i] = reinterpret_cast<int*>(w + m->wsl.amap) + (size_t)i * kAttnMapMax;
-    ae = hipHostMalloc(reinterpret_cast<void**>(&m->amap_pin[i]), (size_t)kAttnMapMax * 4, hipHostMallocDefault);
-    if (ae == hipSuccess) ae = hipEventCreateWithFlags(&m->amap_ev[i], hipEventDisableTiming);
-  }
+  m->attn_split = default_attn_split(*cfg);
   if (ae == hipSuccess) ae = attn_init();
   if (ae != hipSuccess) {
     vs_model_destroy(m);
@@ -884,15 +830,19 @@ vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const 
 void vs_model_destroy(vs_model* m) {
   if (!m) return;
   for (auto e : m->ev_pool) hipEventDestroy(e);
-  for (int i = 0; i < kAmapSlots; ++i) {
-    if (m->amap_ev[i] != nullptr) {
-      (void)hipEventSynchronize(m->amap_ev[i]);
-      hipEventDestroy(m->amap_ev[i]);
-    }
-    if (m->amap_pin[i] != nullptr) hipHostFree(m->amap_pin[i]);
-  }
   delete m;
 }
+
+vs_status vs_model_set_attn_split(vs_model* m, int32_t keys) {
+  if (m == nullptr) return fail(VS_E_INVAL, "vs_model_set_attn_split: null model");
+  if (keys < kAttnStepKeys || keys > kAttnGroupMaxKps || keys % kAttnStepKeys != 0)
+    return fail(VS_E_INVAL, "vs_model_set_attn_split: %d keys (a multiple of %d in [%d, %d])", keys, kAttnStepKeys,
+                kAttnStepKeys, kAttnGroupMaxKps);
+  m->attn_split = keys;
+  return VS_OK;
+}
+
+int32_t vs_model_attn_split(const vs_model* m) { return m == nullptr ? 0 : m->attn_split; }
 
 vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq,
                        void* stream, vs_kv** out) {
@@ -1018,10 +968,15 @@ vs_status vs_seq_rewind(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void
   if (kv == nullptr) return fail(VS_E_INVAL, "vs_seq_rewind: null argument");
   if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_seq_rewind: sequence %d is not open", seq);
   if (!kv->prefilled[seq]) return fail(VS_E_STATE, "vs_seq_rewind: sequence %d holds no context", seq);
-  if (P < 0 || P > kv->P_ub[seq])
-    return fail(VS_E_NOKV, "vs_seq_rewind: length %d beyond the sequence's %d", P, kv->P_ub[seq]);
   if (pending < 0 || pending >= kv->m->c.vocab) return fail(VS_E_INVAL, "vs_seq_rewind: pending token %d", pending);
-  launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, S(stream));
+  // the KV length lives on the device: read it back to check P exactly
+  hipStream_t st = S(stream);
+  int P_now = 0;
+  hipError_t e = hipMemcpyAsync(&P_now, kv->P + seq, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_seq_rewind: %s", hipGetErrorString(e));
+  if (P < 0 || P > P_now) return fail(VS_E_NOKV, "vs_seq_rewind: length %d beyond the sequence's %d", P, P_now);
+  launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, st);
   vs_status rc = check_launch("vs_seq_rewind");
   if (rc != VS_OK) return rc;
   kv->P_ub[seq] = P;
@@ -1102,8 +1057,22 @@ vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_token
   if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "vs_prefill: mode %d", mode);
   if (mode == VS_SAMPLE && (d_u == nullptr || !(temp > 0.f))) return fail(VS_E_INVAL, "vs_prefill: sampling needs u, T>0");
   if (n + 1 > kv->cap[seq]) return fail(VS_E_NOKV, "vs_prefill: %d tokens exceed capacity %d", n, kv->cap[seq]);
-  hipStream_t st = S(stream);
   const int chunk = std::min(kMaxRows, m->max_rows);
+  {  // the last chunk's attention plan bounds the others' (same rows or fewer, shorter contexts)
+    const int nc = n - (n - 1) / chunk * chunk;
+    RowMap rm;
+    memset(&rm, 0, sizeof(rm));
+    rm.n_seq = 1;
+    rm.M = chunk;
+    rm.seq[0] = seq;
+    rm.row_start[1] = chunk;
+    const int saved = kv->P_ub[seq];
+    kv->P_ub[seq] = n - nc;
+    vs_status rc = check_attn_budget(m, kv, rm);
+    kv->P_ub[seq] = saved;
+    if (rc != VS_OK) return rc;
+  }
+  hipStream_t st = S(stream);
   for (int c0 = 0; c0 < n; c0 += chunk) {
     const int nc = std::min(chunk, n - c0);
     RowMap rm;
@@ -1171,6 +1140,18 @@ vs_status validate_chain(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, 
     M += k[i] + 1;
   }
   if (M > m->max_rows || M > kMaxPassRows) return fail(VS_E_SHAPE, "%d verify rows exceed max_rows %d", M, m->max_rows);
+  // the verify pass's attention plan bounds the draft steps' (fewer rows,
+  // the same contexts)
+  RowMap rm;
+  memset(&rm, 0, sizeof(rm));
+  rm.n_seq = n_seq;
+  for (int i = 0; i < n_seq; ++i) {
+    rm.seq[i] = seq[i];
+    rm.row_start[i + 1] = rm.row_start[i] + k[i] + 1;
+  }
+  rm.M = M;
+  vs_status rc = check_attn_budget(m, kv, rm);
+  if (rc != VS_OK) return rc;
   *M_out = M;
   return VS_OK;
 }
@@ -1710,6 +1691,8 @@ vs_status vs_step_ngram(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* h_hi
   e = hipMemcpyAsync(h_result, d_result, VS_RESULT_INTS * sizeof(int32_t), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_ngram: %s", hipGetErrorString(e));
+  // the commit counted all k+1 rows into the host's bound of P; a + 1 were kept
+  kv->P_ub[seq] -= n_rows - (h_result[0] + 1);
   *k_out = k;
   return VS_OK;
 }
@@ -1739,6 +1722,8 @@ vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* se
   if (e == hipSuccess) e = hipMemcpyAsync(conf.data(), m->conf, conf.size() * 8, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_sched: %s", hipGetErrorString(e));
+  // the commit counted all k+1 rows into the host's bound of P; a + 1 were kept
+  for (int i = 0; i < n_seq; ++i) kv->P_ub[seq[i]] -= rows[i] - (h_result[i * VS_RESULT_INTS] + 1);
   for (int i = 0; i < n_seq; ++i) {
     if ((rc = vs_sched_update(c, &states[i], h_result[i * VS_RESULT_INTS], conf[2 * i], conf[2 * i + 1])) != VS_OK)
       return rc;

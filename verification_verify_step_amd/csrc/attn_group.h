@@ -11,12 +11,16 @@
 
 namespace vs {
 
-// Map entries: i | kvh << 6 | qb << 13 | s << 20 (sequence index, KV head,
-// query-group block, split), -1 for padding.  Sequence i has a.nsplit[i]
-// splits of a.kps committed keys; its last split also takes the in-round
-// keys.  With more than one split a workgroup writes, per query group, a
-// partial record at split s of the layout of AttnArgs with wpb = a.n_split
-// (the largest nsplit); the combine kernel then writes the result.
+// Workgroup layout of sequence i (AttnArgs.wg_start, 8-aligned): its
+// groups g = kvh * nsplit[i] + s (KV head, split of the host's bound; the
+// count padded to a multiple of 8) times its blocks of query groups, laid
+// out so that the blocks of one group sit on one XCD back to back: local
+// index ((g / 8) * nqb + qb) * 8 + g % 8 (block b runs on XCD b % 8).  The
+// device's own split count max(1, ceil(P / kps)) decides which splits run;
+// its last split also takes the in-round keys.  With more than one split a
+// wave writes its query group's partial record at split s; the combine
+// kernel then writes the result.
+constexpr int kAttnXcds = 8;            // workgroup b runs on XCD b % 8
 constexpr int kAttnStepKeys = 32;       // keys per step
 constexpr int kAttnGroupSteps = 32;     // steps per split at most (two block-table entries per step, one per lane)
 constexpr int kAttnGroupMaxSplits = 64;

@@ -57,10 +57,27 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stg[2 * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = a.map[blockIdx.x];
-  if (e < 0) return;  // grid padding
-  const int i = e & 63, kvh = (e >> 6) & 127, qb = (e >> 13) & 127, s = e >> 20;
-  const int ns = a.nsplit[i];
+  const int b = blockIdx.x;
+  if (b >= a.wg_start[a.rows.n_seq]) return;
+  int i = 0;
+  {  // the last sequence with wg_start[i] <= b
+    int hi = a.rows.n_seq - 1;
+    while (i < hi) {
+      const int mid = (i + hi + 1) >> 1;
+      if (a.wg_start[mid] <= b) i = mid;
+      else hi = mid - 1;
+    }
+  }
+  const int nr_i = a.rows.row_start[i + 1] - a.rows.row_start[i];
+  const int nqb = ((nr_i * (a.H / a.Hkv) + a.qg_size - 1) / a.qg_size + WV - 1) / WV;
+  const int l = b - a.wg_start[i], t8 = l / kAttnXcds;
+  const int g = (t8 / nqb) * kAttnXcds + l % kAttnXcds, qb = t8 % nqb;
+  const int ns_ub = a.nsplit[i];
+  if (g >= a.Hkv * ns_ub) return;  // padding of the group count to the XCDs
+  const int kvh = g / ns_ub, s = g % ns_ub;
+  const int P = a.kv.P[a.rows.seq[i]];
+  const int ns = min(max(1, (P + a.kps - 1) / a.kps), ns_ub);  // this sequence's splits (P <= the host's bound)
+  if (s >= ns) return;  // past what its context needs
   const bool last_split = s == ns - 1;
   const int sq = a.rows.seq[i];
   const int r0 = a.rows.row_start[i];
@@ -69,7 +86,6 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   const int qg = qb * WV + wave;
   const int q0 = qg * a.qg_size;
   const int nq = qg < a.n_qg ? max(0, min(a.qg_size, nr * G - q0)) : 0;  // this wave's query vectors
-  const int P = a.kv.P[sq];
   const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
   const int clo = s * a.kps, chi = min(P, clo + a.kps);            // committed keys of this split
   int first = clo, last = min(clo + a.kps, (P + kStep - 1) / kStep * kStep);
@@ -284,7 +300,7 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   const int quarters = (a.qg_size + 3) / 4;
   const int unit = blockIdx.x / quarters, v0 = (blockIdx.x % quarters) * 4;
   const int qg = unit % a.n_qg, ik = unit / a.n_qg, kvh = ik % a.Hkv, i = ik / a.Hkv;
-  const int ns = a.nsplit[i];
+  const int ns = min(max(1, (a.kv.P[a.rows.seq[i]] + a.kps - 1) / a.kps), a.nsplit[i]);
   if (ns <= 1) return;  // written by the main kernel
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
 
 void launch_attention_group(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const bool combine = a.n_split > 1;
-  const dim3 grid(a.map_n), cgrid(a.rows.n_seq * a.Hkv * a.n_qg * ((a.qg_size + 3) / 4));
+  const dim3 grid(a.wg_start[a.rows.n_seq]), cgrid(a.rows.n_seq * a.Hkv * a.n_qg * ((a.qg_size + 3) / 4));
   hipEvent_t e1 = combine ? nullptr : ev1;
 #define VS_GRP(HD, WV)                                                                                         \
   do {                                                                                                         \

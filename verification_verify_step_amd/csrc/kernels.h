@@ -91,42 +91,44 @@ struct AttnArgs {
   const float* q;   // [M][H][hd]
   int H, Hkv, hd;
   float scale;
-  int n_split;      // committed-key splits; split n_split is the in-round window
-  int kps;          // keys per committed split (multiple of 32)
-  int qg_size;      // query vectors per workgroup
-  int n_qg;
-  // Partials of the workgroups of a unit (sequence, kv head, query group):
-  // o at part[((unit * wpb + wg) * qg_size + v) * hd + dim], (max, sum) as a
-  // float pair at part[ml_off + 2 * ((unit * wpb + wg) * qg_size + v)], with
-  // wpb = workgroups per unit at n_split committed splits.
+  int qg_size;      // query vectors per query group (<= 16)
+  int n_qg;         // query groups per (sequence, KV head) at the pass's longest sequence
+  // Split structure.  Keys are cut at fixed absolute indices, and every
+  // count a kernel acts on follows from the sequence's own KV length P (read
+  // on the device), so a row's result depends neither on the other
+  // sequences of the pass nor on the host's bound of P.
+  //  * one-group kernel: committed splits of one 32-key step, the in-round
+  //    window as one more split, chunks of WV consecutive splits (one per
+  //    wave); a workgroup runs cpw consecutive chunks of its unit;
+  //  * grouped kernel: committed splits of kps keys (a multiple of 32), the
+  //    last one also taking the in-round window.
+  int kps;
+  int cpw;
+  // Workgroups of sequence i: [wg_start[i], wg_start[i+1]), laid out from
+  // the host's upper bound of P; workgroups the device's P does not need
+  // exit at once.  nsplit[i]: the bound's split (grouped) or chunk
+  // (one-group) count of sequence i.
+  int wg_start[kMaxSeq + 1];
+  int nsplit[kMaxSeq];
+  int n_split;      // largest nsplit: the partials' records per unit
+  // Partials of a unit (sequence, KV head, query group), record j (split or
+  // chunk): o at part[((unit * n_split + j) * qg_size + v) * hd + dim],
+  // (max, sum) as a float pair at part[ml_off + 2 * ((unit * n_split + j) *
+  // qg_size + v)].
   float* part;
   size_t ml_off;    // floats; even
   unsigned* cnt;    // per-unit arrival counters, zero between launches
   uint16_t* xa_o;
   int M;
-  int use_mfma;     // MFMA score/PV path (head_dim 64 or 128)
-  // Work map (optional): one entry per launched workgroup, packed as
-  // i | kvh << 6 | qg << 13 | wg << 20 (sequence index, KV head, query group,
-  // workgroup of the unit), -1 for padding.  With a map, sequence i has its
-  // own committed splits nsplit[i] (<= n_split, which sets the partials'
-  // layout) and only its non-empty query groups are launched.
-  const int* map;
-  int map_n;
-  int nsplit[kMaxSeq];
 };
-constexpr int kAttnMapMax = 1 << 18;     // work-map entries per launch
 constexpr int kGemmSplitCells = 4096;    // K-split arrival counters
 constexpr size_t kGemmSplitFloats = size_t(8) * 8192 * 64;  // K-split chunk sums: 8 chunks x 8192 columns x 64 rows
-// One launch: splits, in-workgroup merge, and the last workgroup's combine.
+// One launch: splits, in-workgroup merge per chunk, and the last
+// workgroup's combine over the chunks of its unit.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kAttnQG = 16;              // query vectors per query group
-constexpr int kAttnCombineSlots = 1024;  // workgroups per unit x query vectors per group, at most
-// splits (waves) per attention workgroup: query groups hold at most 16
-// vectors (one 16-row MFMA tile per wave), and 8 waves fill about one CU
-inline int attn_waves(int qg_size) {
-  (void)qg_size;
-  return 8;
-}
+constexpr int kAttnWaves = 8;            // one-group kernel: waves (splits) per chunk
+constexpr int kAttnCombineSlots = 4096;  // one-group kernel: chunks per unit x query vectors, at most
 constexpr int kAttnMaxUnits = 16384;     // arrival counters
 hipError_t attn_init();
 
