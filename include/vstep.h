@@ -243,6 +243,21 @@ vs_status vs_accept_top_p(vs_model* m, const vs_batch* b, float temp, double top
                           const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
                           void* stream);
 
+/* vs_accept without a model or workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, rules and results as
+ * vs_accept (VS_GREEDY any mask shape, VS_SAMPLE chains), with the model
+ * handle replaced by the vocabulary size (a multiple of 16 in [16, 32768]).
+ * The per-row statistics live in a fixed device array inside the library
+ * (about 60 KB per GPU, held until the process ends): at most
+ * VS_MAX_PASS_ROWS rows per call, VS_E_SHAPE beyond.  Calls no allocating
+ * routine.  Calls on one GPU share that array: calls that overlap on one GPU
+ * (different streams, or host threads) race and must be ordered by the
+ * caller.  The stream must belong to the current device. */
+vs_status vs_accept_noalloc(int32_t vocab, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
+                            const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                            void* stream);
+
 /* Commit: P += a + 1, pending = y, committed += a + 1.  For masks that are not
  * chains, first copies the K/V (all layers) of the accepted path rows
  * P + path[i] to slots P + 1 + i. */

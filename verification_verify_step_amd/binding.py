@@ -20,7 +20,7 @@ VS_DYNK_MAX_WINDOW = 256
 EXPORTS = [
     "vs_last_error", "vs_weight_bytes", "vs_workspace_bytes", "vs_kv_bytes", "vs_model_create", "vs_model_set_tensor",
     "vs_model_destroy", "vs_model_set_attn_split", "vs_model_attn_split", "vs_kv_create", "vs_kv_destroy", "vs_seq_open", "vs_seq_assume", "vs_seq_rewind", "vs_seq_close", "vs_kv_state", "vs_kv_layer",
-    "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_accept_top_p", "vs_commit",
+    "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_accept_top_p", "vs_accept_noalloc", "vs_commit",
     "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_dynk_init",
     "vs_dynk_update", "vs_ngram_propose", "vs_step_ngram", "vs_stats_enable", "vs_stats_read",
     "vs_stats_reset",
@@ -115,6 +115,7 @@ def lib():
             "vs_verify": (I32, [VP, VP, P(vs_batch), I32, VP, VP, VP, VP]),
             "vs_accept": (I32, [VP, P(vs_batch), I32, F, VP, VP, VP, VP, VP, VP]),
             "vs_accept_top_p": (I32, [VP, P(vs_batch), F, D, VP, VP, VP, VP, VP, VP]),
+            "vs_accept_noalloc": (I32, [I32, P(vs_batch), I32, F, VP, VP, VP, VP, VP, VP]),
             "vs_commit": (I32, [VP, VP, P(vs_batch), VP, VP]),
             "vs_step": (I32, [VP, VP, I32, pI, pI, I32, F, VP, VP, VP, VP]),
             "vs_confidence": (I32, [VP, P(vs_batch), F, VP, VP, VP]),
@@ -279,6 +280,11 @@ def vs_accept(model, batch, mode, temp, d_tokens, d_logits, d_draft_logits, d_u,
 def vs_accept_top_p(model, batch, temp, top_p, d_tokens, d_logits, d_draft_logits, d_u, d_result, stream):
     _check("vs_accept_top_p", lib().vs_accept_top_p(model, ctypes.byref(batch), temp, top_p, d_tokens, d_logits,
                                                     d_draft_logits, d_u, d_result, stream))
+
+
+def vs_accept_noalloc(vocab, batch, mode, temp, d_tokens, d_logits, d_draft_logits, d_u, d_result, stream):
+    _check("vs_accept_noalloc", lib().vs_accept_noalloc(vocab, ctypes.byref(batch), mode, temp, d_tokens, d_logits,
+                                                        d_draft_logits, d_u, d_result, stream))
 
 
 def vs_commit(model, kv, batch, d_result, stream):

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1353,25 +1354,41 @@ vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_lay
   return check_launch("vs_verify");
 }
 
-static vs_status accept_impl(vs_model* m, const vs_batch* b, int32_t mode, float temp, double top_p,
-                             const int32_t* d_tokens, const float* d_logits, const float* d_draft_logits,
-                             const double* d_u, int32_t* d_result, void* stream) {
-  if (m == nullptr || d_tokens == nullptr || d_logits == nullptr || d_result == nullptr || b == nullptr ||
-      b->seq == nullptr || b->n_rows == nullptr)
-    return fail(VS_E_INVAL, "vs_accept: null argument");
-  if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "vs_accept: mode %d", mode);
-  if (b->n_seq < 1 || b->n_seq > kMaxSeq) return fail(VS_E_SHAPE, "vs_accept: n_seq %d", b->n_seq);
+}  // extern "C"
+
+namespace {
+
+// Per-row statistics the accept kernels use (target, draft, top-p set).
+struct AcceptBufs {
+  float *mx, *second, *dmx;
+  int *amax, *damax;
+  double *sum, *dsum, *tp_mass;
+  unsigned* tp_key;
+  int* tp_id;
+};
+
+// The accept step over a batch's rows: vocabulary statistics of the target
+// (and of the draft when sampling), the top-p set when top_p < 1, then the
+// acceptance kernel.  m (optional) times the launches.
+vs_status accept_core(vs_model* m, const AcceptBufs& bf, int V, int max_rows, const char* name, const vs_batch* b,
+                      int32_t mode, float temp, double top_p, const int32_t* d_tokens, const float* d_logits,
+                      const float* d_draft_logits, const double* d_u, int32_t* d_result, hipStream_t st) {
+  if (d_tokens == nullptr || d_logits == nullptr || d_result == nullptr || b == nullptr || b->seq == nullptr ||
+      b->n_rows == nullptr)
+    return fail(VS_E_INVAL, "%s: null argument", name);
+  if (mode != VS_GREEDY && mode != VS_SAMPLE) return fail(VS_E_INVAL, "%s: mode %d", name, mode);
+  if (b->n_seq < 1 || b->n_seq > kMaxSeq) return fail(VS_E_SHAPE, "%s: n_seq %d", name, b->n_seq);
   if (mode == VS_SAMPLE) {
     if (d_draft_logits == nullptr || d_u == nullptr || !(temp > 0.f))
-      return fail(VS_E_INVAL, "vs_accept: sampling needs draft logits, u and T > 0");
-    if (b->d_mask != nullptr || b->d_depth != nullptr) return fail(VS_E_INVAL, "vs_accept: sampling is chain-only");
+      return fail(VS_E_INVAL, "%s: sampling needs draft logits, u and T > 0", name);
+    if (b->d_mask != nullptr || b->d_depth != nullptr) return fail(VS_E_INVAL, "%s: sampling is chain-only", name);
   }
   RowMap rm;
   memset(&rm, 0, sizeof(rm));
   rm.n_seq = b->n_seq;
   int M = 0;
   for (int i = 0; i < b->n_seq; ++i) {
-    if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows) return fail(VS_E_SHAPE, "vs_accept: rows %d", b->n_rows[i]);
+    if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows) return fail(VS_E_SHAPE, "%s: rows %d", name, b->n_rows[i]);
     rm.seq[i] = b->seq[i];
     rm.row_start[i] = M;
     M += b->n_rows[i];
@@ -1380,46 +1397,49 @@ static vs_status accept_impl(vs_model* m, const vs_batch* b, int32_t mode, float
   rm.M = M;
   rm.mask = b->d_mask;
   rm.depth = b->d_depth;
-  if (M > m->max_rows) return fail(VS_E_SHAPE, "vs_accept: %d rows exceed max_rows", M);
-  hipStream_t st = S(stream);
+  if (M > max_rows) return fail(VS_E_SHAPE, "%s: %d rows exceed the limit of %d", name, M, max_rows);
+  auto run = [&](double bytes, auto launch) {
+    if (m != nullptr) timed(m, F_SMALL, bytes, st, [&](hipEvent_t, hipEvent_t) { launch(); });
+    else launch();
+  };
   StatsArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.logits = d_logits;
-  sa.V = m->c.vocab;
+  sa.V = V;
   sa.temp = mode == VS_SAMPLE ? temp : 1.0f;
-  sa.mx = m->st_mx;
-  sa.amax = m->st_amax;
-  sa.second = m->st_second;
-  sa.sumexp = mode == VS_SAMPLE ? m->st_sum : nullptr;
-  timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(sa, M, st); });
+  sa.mx = bf.mx;
+  sa.amax = bf.amax;
+  sa.second = bf.second;
+  sa.sumexp = mode == VS_SAMPLE ? bf.sum : nullptr;
+  run((double)M * V * 4, [&]() { launch_row_stats(sa, M, st); });
   if (mode == VS_SAMPLE) {
     StatsArgs da = sa;
     da.logits = d_draft_logits;
-    da.mx = m->dst_mx;
-    da.amax = m->dst_amax;
+    da.mx = bf.dmx;
+    da.amax = bf.damax;
     da.second = nullptr;
-    da.sumexp = m->dst_sum;
-    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_row_stats(da, M, st); });
+    da.sumexp = bf.dsum;
+    run((double)M * V * 4, [&]() { launch_row_stats(da, M, st); });
   }
   const bool tp = top_p < 1.0;
   if (tp) {
     TopPArgs ta;
     ta.logits = d_logits;
-    ta.V = m->c.vocab;
+    ta.V = V;
     ta.temp = temp;
     ta.top_p = top_p;
-    ta.mx = m->st_mx;
-    ta.key = m->tp_key;
-    ta.id = m->tp_id;
-    ta.mass = m->tp_mass;
-    timed(m, F_SMALL, (double)M * m->c.vocab * 4, st, [&](hipEvent_t, hipEvent_t) { launch_top_p(ta, M, st); });
+    ta.mx = bf.mx;
+    ta.key = bf.tp_key;
+    ta.id = bf.tp_id;
+    ta.mass = bf.tp_mass;
+    run((double)M * V * 4, [&]() { launch_top_p(ta, M, st); });
   }
   AcceptArgs a;
   memset(&a, 0, sizeof(a));
   if (tp) {
-    a.tp_key = m->tp_key;
-    a.tp_id = m->tp_id;
-    a.tp_mass = m->tp_mass;
+    a.tp_key = bf.tp_key;
+    a.tp_id = bf.tp_id;
+    a.tp_mass = bf.tp_mass;
   }
   a.rows = rm;
   a.mode = mode;
@@ -1427,17 +1447,128 @@ static vs_status accept_impl(vs_model* m, const vs_batch* b, int32_t mode, float
   a.tokens = d_tokens;
   a.logits = d_logits;
   a.dlogits = d_draft_logits;
-  a.mx = m->st_mx;
-  a.amax = m->st_amax;
-  a.second = m->st_second;
-  a.sumexp = m->st_sum;
-  a.dmx = m->dst_mx;
-  a.dsumexp = m->dst_sum;
-  a.V = m->c.vocab;
+  a.mx = bf.mx;
+  a.amax = bf.amax;
+  a.second = bf.second;
+  a.sumexp = bf.sum;
+  a.dmx = bf.dmx;
+  a.dsumexp = bf.dsum;
+  a.V = V;
   a.u = d_u;
   a.result = d_result;
-  timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_accept(a, st); });
-  return check_launch(tp ? "vs_accept_top_p" : "vs_accept");
+  run(0, [&]() { launch_accept(a, st); });
+  return check_launch(name);
+}
+
+AcceptBufs model_accept_bufs(vs_model* m) {
+  AcceptBufs bf;
+  bf.mx = m->st_mx;
+  bf.amax = m->st_amax;
+  bf.second = m->st_second;
+  bf.sum = m->st_sum;
+  bf.dmx = m->dst_mx;
+  bf.damax = m->dst_amax;
+  bf.dsum = m->dst_sum;
+  bf.tp_key = m->tp_key;
+  bf.tp_id = m->tp_id;
+  bf.tp_mass = m->tp_mass;
+  return bf;
+}
+
+vs_status accept_impl(vs_model* m, const vs_batch* b, int32_t mode, float temp, double top_p, const int32_t* d_tokens,
+                      const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                      void* stream) {
+  const char* name = top_p < 1.0 ? "vs_accept_top_p" : "vs_accept";
+  if (m == nullptr) return fail(VS_E_INVAL, "%s: null model", name);
+  return accept_core(m, model_accept_bufs(m), m->c.vocab, m->max_rows, name, b, mode, temp, top_p, d_tokens, d_logits,
+                     d_draft_logits, d_u, d_result, S(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+}  // extern "C"
+
+// ---- allocation-free accept ----------------------------------------------
+// vs_accept_noalloc keeps the per-row statistics of the accept kernels in a
+// file-scope device array instead of a model workspace, for up to
+// kNoAllocRows rows.  In host code the array's name is only a stand-in: its
+// device address, one per GPU, comes from hipGetSymbolAddress on the first
+// call on that GPU, and only that address is handed to kernels.  Every
+// field is written by the statistics kernels before it is read, so nothing
+// needs clearing; calls that overlap on one GPU share the array and race.
+namespace {
+
+constexpr int kNoAllocRows = VS_MAX_PASS_ROWS;
+constexpr size_t kNaSlot4 = (size_t(kNoAllocRows) * 4 + 255) / 256 * 256;  // one 4-byte field per row
+constexpr size_t kNaSlot8 = (size_t(kNoAllocRows) * 8 + 255) / 256 * 256;  // one 8-byte field per row
+constexpr size_t kNoAllocBytes = 7 * kNaSlot4 + 3 * kNaSlot8;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per GPU
+
+// Device address of `scratch` on the current GPU, looked up once per GPU.
+vs_status scratch_address(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_accept_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(VS_E_DEVICE, "vs_accept_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(VS_E_DEVICE, "vs_accept_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return VS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vs_status vs_accept_noalloc(int32_t vocab, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
+                            const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
+                            void* stream) {
+  if (vocab < 16 || vocab > 32768 || vocab % 16 != 0)
+    return fail(VS_E_SHAPE, "vs_accept_noalloc: vocab %d (a multiple of 16 in [16, 32768])", vocab);
+  unsigned char* base = nullptr;
+  vs_status rc = scratch_address(&base);
+  if (rc != VS_OK) return rc;
+  AcceptBufs bf;
+  unsigned char* p = base;
+  auto take4 = [&]() {
+    unsigned char* q = p;
+    p += kNaSlot4;
+    return q;
+  };
+  auto take8 = [&]() {
+    unsigned char* q = p;
+    p += kNaSlot8;
+    return q;
+  };
+  bf.mx = reinterpret_cast<float*>(take4());
+  bf.amax = reinterpret_cast<int*>(take4());
+  bf.second = reinterpret_cast<float*>(take4());
+  bf.dmx = reinterpret_cast<float*>(take4());
+  bf.damax = reinterpret_cast<int*>(take4());
+  bf.tp_key = reinterpret_cast<unsigned*>(take4());
+  bf.tp_id = reinterpret_cast<int*>(take4());
+  bf.sum = reinterpret_cast<double*>(take8());
+  bf.dsum = reinterpret_cast<double*>(take8());
+  bf.tp_mass = reinterpret_cast<double*>(take8());
+  return accept_core(nullptr, bf, vocab, kNoAllocRows, "vs_accept_noalloc", b, mode, temp, 1.0, d_tokens, d_logits,
+                     d_draft_logits, d_u, d_result, S(stream));
 }
 
 vs_status vs_accept(vs_model* m, const vs_batch* b, int32_t mode, float temp, const int32_t* d_tokens,
