@@ -4,15 +4,21 @@ Workload (default): the 7B Llama-shape chain round: 32 layers, d 4096, 32x128
 MHA, FFN 11008, V 32000, bf16 weights N(0, 0.02) from seed, prompt of 1024
 uniform-random ids, draft = first 12 layers + head with KV reuse, chain k = 5,
 greedy, batch 1.  One step = one round: draft (5 steps + finishing pass),
-verify (layers 12..31 + head over 6 rows), accept, commit.
+verify (layers 12..31 + head over 6 rows), accept, commit.  The default 244
+rounds commit about 256 tokens (context 1024 -> ~1280) at this model's
+acceptance.
 
 Printed JSON line:
   value          verified tokens/s (committed tokens of the timed rounds / time)
   roofline       the dominant kernel family (by time) against HBM peak, from
                  HIP events around every launch on the library's stream
   verify_step_*  verify + accept + commit per round: ms, algorithmic GB/s,
-                 fraction of the 8 TB/s peak
+                 fraction of the 8 TB/s peak and of the measured read ceiling
+  achievable_read  the library's streaming-read probe over 2 GiB
   cpu_baseline   the CPU oracle on a bounded sample of the same round
+  configs        the other workloads' verify steps (stochastic batch of 8,
+                 63-node tree, 70B ragged batch) and the tiny decoder's
+                 tokens/s, each with its roofline and oracle baseline
 """
 import argparse
 import json
@@ -29,11 +35,13 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=244)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_chain_k5")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the AR and calibrated-acceptance runs")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' lines")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed verify steps per other workload")
     ap.add_argument("--cpu-layers", type=int, default=2, help="layers timed per kind in the CPU sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (to scale the HBM byte counters)")
@@ -89,70 +97,6 @@ def verify_step_bytes(c, P, M):
     kv_row = c.n_kv_heads * c.head_dim * 2 * 2  # K and V, bf16
     return (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * (P + M) * kv_row + nl * M * kv_row
             + M * c.d_model * 4 * 2 + M * c.vocab * 4)
-
-
-def cpu_baseline(w, P, n_layers_sample):
-    """The oracle as it stands on a bounded sample of one round: n verify
-    layers (k+1 rows at context P), n draft layers (1 row), the head on k+1
-    rows and on 1 row; the round time is extrapolated by layer count."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
-    from oracle.decoder import Decoder, KVCache, Row
-    from synth.model_weights import SynthWeights
-
-    c = w.model
-    k = w.k
-    weights = SynthWeights(c, precision="bf16", cache=True)
-    dec = Decoder(c, weights)
-    rng = np.random.default_rng(0)
-    cache = KVCache(c, P + k + 2, kv_round="bf16")
-    draft_layers = list(range(n_layers_sample))
-    verify_layers = list(range(c.exit_layer, c.exit_layer + n_layers_sample))
-    for l in draft_layers + verify_layers:  # stand-in committed context
-        K, V = cache.get(0, l)
-        K[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
-        V[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
-    for l in draft_layers + verify_layers:  # generate weights before timing
-        for t in range(1, 10):
-            weights.get(t, l)
-    weights.get(10), weights.get(11)
-    rows6 = [Row(0, P + i, P + i, np.arange(P + i + 1)) for i in range(k + 1)]
-    rows1 = [Row(0, P, P, np.arange(P + 1))]
-    h6 = rng.standard_normal((k + 1, c.d_model))
-    h1 = h6[:1].copy()
-    # repeat the sample until about 10 s of oracle work have been timed
-    tv, td, th6, th1 = [], [], [], []
-    spent, reps = 0.0, 0
-    while spent < 10.0 and reps < 400:
-        for l in verify_layers:
-            t0 = time.perf_counter()
-            dec.layer(l, cache, rows6, h6)
-            tv.append(time.perf_counter() - t0)
-        for l in draft_layers:
-            t0 = time.perf_counter()
-            dec.layer(l, cache, rows1, h1)
-            td.append(time.perf_counter() - t0)
-        t0 = time.perf_counter()
-        dec.head(h6)
-        th6.append(time.perf_counter() - t0)
-        t0 = time.perf_counter()
-        dec.head(h1)
-        th1.append(time.perf_counter() - t0)
-        spent = sum(tv) + sum(td) + sum(th6) + sum(th1)
-        reps += 1
-    t_v, t_d = sum(tv) / len(tv), sum(td) / len(td)
-    t_h6, t_h1 = sum(th6) / len(th6), sum(th1) / len(th1)
-    nv = c.n_layers - c.exit_layer
-    round_s = (k + 1) * c.exit_layer * t_d + k * t_h1 + nv * t_v + t_h6
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": 1.0 / round_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 numpy oracle, {spent:.1f} s timed: {reps} repetitions of {len(verify_layers)} verify "
-                       f"layers ({k + 1} rows, context {P}, "
-                       f"random committed KV), {len(draft_layers)} draft layers (1 row), head on {k + 1} and 1 rows; "
-                       f"round = {k + 1}x{c.exit_layer} draft layers + {k} draft heads + {nv} verify layers + "
-                       f"1 verify head, one committed token per round as on the GPU (acceptance ~0)"),
-            "round_s": round_s, "verify_step_s": nv * t_v + t_h6, "timed_s": spent}
 
 
 def scheduled_rounds(e, B, open_prefilled, k0, steps, warmup):
@@ -287,46 +231,342 @@ def accept_timing(e, B, seq, M, V, k, reps=50):
     return out
 
 
-def workload_verify(args):
-    """The verify step of a parity workload other than the bench's: the
-    stochastic batch of 8 (llama7b_sample_k4_b8: 8 x 5 rows at context 2048,
-    T = 1), the tree of 63 nodes (llama7b_tree63: 64 rows at context 4096,
-    drafted by vs_draft_tree) and the 70B ragged batch (llama70b_ragged_b32:
-    32 requests, contexts U[512, 8192], drafts U[2, 16]).  Layers L..N-1 +
-    head over the rows, accept, commit, timed with HIP events and reported
-    against both roofs: algorithmic HBM bytes (weights of the verify layers
-    and the head once, the committed KV once, in-round KV, hidden and logits)
-    and algorithmic MFMA flops (2 per weight per row).  The committed KV is
-    drawn by the generator (N(0, 1) bf16) instead of prefilled; chain rows
-    get random token ids and layer-L inputs."""
+def host_info():
+    """CPU model and the cores this process may use (the oracle's host)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "cpus_available": avail}
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def cpu_baseline(w, P, n_layers_sample):
+    """The oracle as it stands on a bounded sample of one round: n verify
+    layers (k+1 rows at context P), n draft layers (1 row), the head on k+1
+    rows and on 1 row; the round time is extrapolated by layer count."""
+    import numpy as np
+
+    from oracle.decoder import Decoder, KVCache, Row
+    from synth.model_weights import SynthWeights
+
+    c = w.model
+    k = w.k
+    weights = SynthWeights(c, precision="bf16", cache=True)
+    dec = Decoder(c, weights)
+    rng = np.random.default_rng(0)
+    cache = KVCache(c, P + k + 2, kv_round="bf16")
+    draft_layers = list(range(n_layers_sample))
+    verify_layers = list(range(c.exit_layer, c.exit_layer + n_layers_sample))
+    for l in draft_layers + verify_layers:  # stand-in committed context
+        K, V = cache.get(0, l)
+        K[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+        V[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+    for l in draft_layers + verify_layers:  # generate weights before timing
+        for t in range(1, 10):
+            weights.get(t, l)
+    weights.get(10), weights.get(11)
+    rows6 = [Row(0, P + i, P + i, np.arange(P + i + 1)) for i in range(k + 1)]
+    rows1 = [Row(0, P, P, np.arange(P + 1))]
+    h6 = rng.standard_normal((k + 1, c.d_model))
+    h1 = h6[:1].copy()
+    # repeat the sample until about 10 s of oracle work have been timed
+    tv, td, th6, th1 = [], [], [], []
+    spent, reps = 0.0, 0
+    while spent < 10.0 and reps < 400:
+        for l in verify_layers:
+            t0 = time.perf_counter()
+            dec.layer(l, cache, rows6, h6)
+            tv.append(time.perf_counter() - t0)
+        for l in draft_layers:
+            t0 = time.perf_counter()
+            dec.layer(l, cache, rows1, h1)
+            td.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        dec.head(h6)
+        th6.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        dec.head(h1)
+        th1.append(time.perf_counter() - t0)
+        spent = sum(tv) + sum(td) + sum(th6) + sum(th1)
+        reps += 1
+    t_v, t_d = sum(tv) / len(tv), sum(td) / len(td)
+    t_h6, t_h1 = sum(th6) / len(th6), sum(th1) / len(th1)
+    nv = c.n_layers - c.exit_layer
+    round_s = (k + 1) * c.exit_layer * t_d + k * t_h1 + nv * t_v + t_h6
+    out = {"value": 1.0 / round_s, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": (f"float64 numpy oracle, {spent:.1f} s timed: {reps} repetitions of {len(verify_layers)} verify "
+                      f"layers ({k + 1} rows, context {P}, "
+                      f"random committed KV), {len(draft_layers)} draft layers (1 row), head on {k + 1} and 1 rows; "
+                      f"round = {k + 1}x{c.exit_layer} draft layers + {k} draft heads + {nv} verify layers + "
+                      f"1 verify head, one committed token per round as on the GPU (acceptance ~0)"),
+           "cores_note": "BLAS threads of the matrix products; the oracle's per-row attention loops run on one core",
+           "round_s": round_s, "verify_step_s": nv * t_v + t_h6, "timed_s": spent}
+    out.update(host_info())
+    return out
+
+
+def cpu_verify_sample(c, ctx, rows, tree_rows=None, budget_s=6.0):
+    """The oracle's verify step on a bounded sample: the first verify layer
+    over the workload's rows at its contexts (random committed KV), repeated
+    until about budget_s, and the head over the rows; extrapolated to the
+    N - L verify layers."""
+    import numpy as np
+
+    from oracle import spec
+    from oracle.decoder import Decoder, KVCache
+    from synth.model_weights import SynthWeights
+
+    weights = SynthWeights(c, precision="bf16", cache=True)
+    dec = Decoder(c, weights)
+    rng = np.random.default_rng(1)
+    l = c.exit_layer
+    for t in range(1, 10):
+        weights.get(t, l)
+    weights.get(10), weights.get(11)
+    caches, row_sets, hs = [], [], []
+    for i, (P, n) in enumerate(zip(ctx, rows)):
+        cache = KVCache(c, P + n + 1)
+        K, V = cache.get(i, l)
+        K[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+        V[:, :P] = rng.standard_normal((c.n_kv_heads, P, c.head_dim))
+        caches.append(cache)
+        rs = tree_rows(i, P) if tree_rows else spec.chain_rows(i, P, n)
+        row_sets.append(rs)
+        hs.append(rng.standard_normal((n, c.d_model)))
+    t_layer, reps = [], 0
+    while sum(t_layer) < budget_s and reps < 100:
+        t0 = time.perf_counter()
+        for cache, rs, h in zip(caches, row_sets, hs):
+            dec.layer(l, cache, rs, h)
+        t_layer.append(time.perf_counter() - t0)
+        reps += 1
+    hall = np.concatenate(hs)
+    t0 = time.perf_counter()
+    dec.head(hall)
+    t_head = time.perf_counter() - t0
+    nv = c.n_layers - c.exit_layer
+    t_v = sum(t_layer) / len(t_layer)
+    step_s = nv * t_v + t_head
+    out = {"value": step_s * 1e3, "unit": "ms per verify step", "cores": blas_threads(), "kind": "oracle",
+           "sample": (f"float64 numpy oracle: layer {l} over {sum(rows)} rows of {len(ctx)} sequences "
+                      f"(contexts {min(ctx)}..{max(ctx)}, random committed KV), {reps} repetitions, "
+                      f"{sum(t_layer):.1f} s timed, plus the head over the rows; extrapolated to the {nv} verify "
+                      f"layers"),
+           "cores_note": "BLAS threads of the matrix products; the oracle's per-row attention loops run on one core",
+           "layer_s": t_v, "head_s": t_head}
+    out.update(host_info())
+    return out
+
+
+def read_probe(B):
+    """Achievable HBM read bandwidth: the library's streaming-read probe over
+    2 GiB, 10 timed launches after 2 warm-up launches."""
+    import torch
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        B.vs_read_probe(buf.data_ptr(), n, sink.data_ptr(), st)
+    ts = []
+    for _ in range(10):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        B.vs_read_probe(buf.data_ptr(), n, sink.data_ptr(), st)
+        t1.record()
+        torch.cuda.synchronize()
+        ts.append(t0.elapsed_time(t1))
+    del buf
+    best, mean = min(ts), sum(ts) / len(ts)
+    return {"gbs_best": n / (best * 1e-3) / 1e9, "gbs_mean": n / (mean * 1e-3) / 1e9, "bytes": n,
+            "kernel": "vs_read_probe (2048 workgroups x 256 threads, contiguous range each, 16-byte loads)"}
+
+
+def family_table(stats):
+    return {n: {"launches": s[0], "avg_us": s[1] / s[0] * 1e3 if s[0] else None,
+                "ms": s[1], "gbs": (s[2] / (s[1] * 1e-3) / 1e9) if s[1] else None}
+            for n, s in stats.items() if s[0]}
+
+
+def verify_roofs(c, ctx, M, ms):
+    """Algorithmic HBM bytes and MFMA flops of one verify step and the rates
+    at ms per step: weights of the verify layers and the head once, the
+    committed KV once, in-round KV, hidden rows and logits; 2 flops per
+    weight per row."""
+    nl = c.n_layers - c.exit_layer
+    kv_row = c.n_kv_heads * c.head_dim * 2 * 2
+    params = nl * layer_bytes(c) // 2 + c.vocab * c.d_model
+    bytes_ = (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * sum(ctx) * kv_row + nl * M * kv_row
+              + M * c.d_model * 4 * 2 + M * c.vocab * 4)
+    flops = 2.0 * M * params
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    return bytes_, flops, {
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "mfma": {"achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0,
+                 "note": "algorithmic flops 2 x rows x weights of the verify layers and head; the split-bf16 "
+                         "activations issue twice as many MFMA operations"}}
+
+
+def verify_steps(e, B, batch, step, rewind, steps, warmup):
+    """Times `steps` verify steps (verify + accept + commit, HIP events on the
+    stream) with the context rewound after each; then one more step with every
+    kernel family bracketed.  prepare (inside step) runs before the events."""
+    import numpy as np
+    import torch
+    for r in range(warmup):
+        step(r, None)
+        rewind()
+    torch.cuda.synchronize()
+    times = []
+    for r in range(steps):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step(warmup + r, (t0, t1))
+        rewind()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    B.vs_stats_reset(e.model)
+    step(warmup + steps, "stats")
+    torch.cuda.synchronize()
+    B.vs_stats_enable(e.model, 0)
+    fam = family_table(B.vs_stats_read(e.model))
+    rewind()
+    return float(np.mean(times)), fam
+
+
+def config_7b(e, B, w, steps, warmup):
+    """Verify step of a 7B-shape workload on the headline engine: the
+    stochastic batch of 8 (8 prompts of 2048 ids prefilled, each step drafts
+    k = 4 tokens per request by sampling at T = 1 with fresh uniforms, then
+    verify + stochastic accept + commit) or the 63-node tree (a prompt of 4096
+    ids prefilled, the tree drafted once by vs_draft_tree, then verify +
+    greedy tree accept + compaction commit)."""
+    import numpy as np
+    import torch
+
+    import synth
+    c = w.model
+    st = e.stream
+    tree = bool(w.tree)
+    n = 1 if tree else w.batch
+    seqs = []
+    for i in range(n):
+        s = e.open(w.prompt_len + 80)
+        p = synth.tokens(synth.SEED_PROMPTS, synth.stream_prompt(100 + i), c.vocab, w.prompt_len)
+        B.vs_prefill(e.model, e.kv, s, torch.tensor(p, dtype=torch.int32, device="cuda").data_ptr(), w.prompt_len,
+                     B.VS_GREEDY, 1.0, None, None, st)
+        seqs.append(s)
+    e.sync()
+    P0 = [e.state()[0][s] for s in seqs]
+    pend0 = [e.state()[1][s] for s in seqs]
+    if tree:
+        ex = w.extra
+        M = 1 + ex["nodes"]
+        toks = torch.empty(M, dtype=torch.int32, device="cuda")
+        depth = torch.empty(M, dtype=torch.int32, device="cuda")
+        mask = torch.empty(M, dtype=torch.int64, device="cuda")
+        parent = torch.empty(M, dtype=torch.int32, device="cuda")
+        hL = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
+        B.vs_draft_tree(e.model, e.kv, seqs[0], ex["topk"], ex["depth"], ex["nodes"], 1.0, toks.data_ptr(),
+                        depth.data_ptr(), mask.data_ptr(), parent.data_ptr(), hL.data_ptr(), None, st)
+        rows = [M]
+        batch = B.make_batch(seqs, rows, depth.data_ptr(), mask.data_ptr())
+    else:
+        rows = [w.k + 1] * n
+        M = sum(rows)
+        toks = torch.empty(M, dtype=torch.int32, device="cuda")
+        hL = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
+        zd = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+        batch = B.make_batch(seqs, rows)
+    z = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
+    res = torch.zeros((n, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    flagged = [0, 0]  # flagged sequences, sequences
+    accepted = [0, 0]
+
+    def step(r, ev):
+        if not tree:
+            U = np.stack([synth.uniforms(synth.SEED_UNIFORMS, synth.stream_uniform(100 + i, r + 1), B.VS_N_UNIFORMS)
+                          for i in range(n)])
+            du = torch.from_numpy(U.reshape(-1)).cuda()
+            B.vs_draft(e.model, e.kv, seqs, [w.k] * n, B.VS_SAMPLE, w.temperature, du.data_ptr(), toks.data_ptr(),
+                       hL.data_ptr(), zd.data_ptr(), st)
+        if ev == "stats":
+            B.vs_stats_enable(e.model, -1)
+        elif ev is not None:
+            ev[0].record()
+        B.vs_verify(e.model, e.kv, batch, c.exit_layer, toks.data_ptr(), hL.data_ptr(), z.data_ptr(), st)
+        if tree:
+            B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, toks.data_ptr(), z.data_ptr(), None, None, res.data_ptr(),
+                        st)
+        else:
+            B.vs_accept(e.model, batch, B.VS_SAMPLE, w.temperature, toks.data_ptr(), z.data_ptr(), zd.data_ptr(),
+                        du.data_ptr(), res.data_ptr(), st)
+        B.vs_commit(e.model, e.kv, batch, res.data_ptr(), st)
+        if ev is not None and ev != "stats":
+            ev[1].record()
+            rr = res.cpu().numpy()
+            flagged[0] += int(np.sum(rr[:, 2] & 1))
+            flagged[1] += n
+            accepted[0] += int(np.sum(rr[:, 0]))
+            accepted[1] += sum(rows) - n
+
+    def rewind():
+        for i, s in enumerate(seqs):
+            B.vs_seq_rewind(e.kv, s, P0[i], pend0[i], st)
+
+    ms, fam = verify_steps(e, B, batch, step, rewind, steps, warmup)
+    for s in seqs:
+        B.vs_seq_close(e.kv, s)
+    bytes_, flops, roofs = verify_roofs(c, P0, M, ms)
+    out = {"metric": "verify-step algorithmic HBM GB/s", "value": roofs["roofline"]["achieved"], "unit": "GB/s",
+           "steps": steps, "warmup": warmup, "ms_per_step": ms, "dtype": "bf16",
+           "data": "synthetic (random-init bf16 weights, uniform-random prompts prefilled"
+                   + (", the tree drafted on the GPU once)" if tree else ", sampled drafts every step)"),
+           "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": sum(P0), "exit_layer": c.exit_layer,
+                      "layers": c.n_layers, "mode": w.mode},
+           **roofs, "verify_step_bytes": bytes_, "verify_step_flops": flops,
+           "flagged": {"sequences": flagged[0], "of": flagged[1],
+                       "rule": "greedy: top-1 - top-2 logit gap < 4e-2 on the walk; stochastic: |p/q - u| < 1e-3"},
+           "kernel_families_bracketed": fam}
+    if not tree:
+        out["alpha"] = accepted[0] / max(1, accepted[1])
+    return out
+
+
+def config_70b(B, w, steps, warmup):
+    """Verify step of the 70B ragged batch: 32 requests with contexts
+    U[512, 8192] and draft lengths U[2, 16] drawn by seed; the committed KV
+    is drawn by the generator (N(0, 1) bf16) instead of 32 prefills through
+    80 layers, and the draft rows get random ids and layer-L inputs (the
+    verify step's cost does not depend on their values)."""
     import numpy as np
     import torch
 
     import synth
     from synth import gpu_weights
-    from synth.workloads import WORKLOADS, ragged_batch
-    from verification_verify_step_amd import binding as B
+    from synth.workloads import ragged_batch
     from verification_verify_step_amd.runtime import Engine
 
-    w = WORKLOADS[args.workload]
     c = w.model
     rng = np.random.default_rng(5)
-    tree = bool(getattr(w, "tree", False))
-    if w.name == "llama70b_ragged_b32":
-        ctx, ks, pend = ragged_batch(w)
-        rows = [int(k) + 1 for k in ks]
-    elif tree:
-        ctx, rows = [w.prompt_len], [1 + w.extra["nodes"]]
-        pend = rng.integers(0, c.vocab, 1)
-    else:
-        ctx, rows = [w.prompt_len] * w.batch, [w.k + 1] * w.batch
-        pend = rng.integers(0, c.vocab, w.batch)
-    ctx = [int(x) for x in ctx]
+    ctx, ks, pend = ragged_batch(w)
+    rows = [int(k) + 1 for k in ks]
     n, M = len(ctx), sum(rows)
     max_ctx = max(ctx) + 80
-    bps = (max_ctx + 15) // 16 + 2
     e = Engine(c, max_rows=M, max_seqs=n, max_ctx=max_ctx, n_blocks=sum((x + 80 + 15) // 16 for x in ctx) + 16,
-               max_blocks_per_seq=bps)
+               max_blocks_per_seq=(max_ctx + 15) // 16 + 2)
     st = e.stream
     t_load = time.time()
     gpu_weights.load(e, c)
@@ -339,98 +579,120 @@ def workload_verify(args):
         s = e.open(ctx[i] + 72)
         B.vs_seq_assume(e.kv, s, ctx[i], int(pend[i]), st)
         seqs.append(s)
-    torch.cuda.synchronize()
-    if tree:
-        ex = w.extra
-        toks = torch.empty(M, dtype=torch.int32, device="cuda")
-        depth = torch.empty(M, dtype=torch.int32, device="cuda")
-        mask = torch.empty(M, dtype=torch.int64, device="cuda")
-        parent = torch.empty(M, dtype=torch.int32, device="cuda")
-        hL = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
-        lz = torch.empty((ex["depth"], M, c.vocab), dtype=torch.float32, device="cuda")
-        B.vs_draft_tree(e.model, e.kv, seqs[0], ex["topk"], ex["depth"], ex["nodes"], 1.0, toks.data_ptr(),
-                        depth.data_ptr(), mask.data_ptr(), parent.data_ptr(), hL.data_ptr(), lz.data_ptr(), st)
-        batch = B.make_batch(seqs, rows, depth.data_ptr(), mask.data_ptr())
-    else:
-        hL = torch.from_numpy(rng.standard_normal((M, c.d_model)).astype(np.float32)).cuda()
-        toks = torch.from_numpy(rng.integers(0, c.vocab, M).astype(np.int32)).cuda()
-        batch = B.make_batch(seqs, rows)
+    hL = torch.from_numpy(rng.standard_normal((M, c.d_model)).astype(np.float32)).cuda()
+    toks = torch.from_numpy(rng.integers(0, c.vocab, M).astype(np.int32)).cuda()
+    batch = B.make_batch(seqs, rows)
     torch.cuda.synchronize()
     t_load = time.time() - t_load
-    sample = w.mode == "sample"
     z = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
-    zd = torch.from_numpy(rng.standard_normal((M, c.vocab)).astype(np.float32)).cuda() if sample else None
-    u = torch.from_numpy(rng.random(n * B.VS_N_UNIFORMS)).cuda() if sample else None
     res = torch.zeros((n, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
 
-    def step():
+    def step(r, ev):
+        if ev == "stats":
+            B.vs_stats_enable(e.model, -1)
+        elif ev is not None:
+            ev[0].record()
         B.vs_verify(e.model, e.kv, batch, c.exit_layer, toks.data_ptr(), hL.data_ptr(), z.data_ptr(), st)
-        B.vs_accept(e.model, batch, B.VS_SAMPLE if sample else B.VS_GREEDY, w.temperature, toks.data_ptr(),
-                    z.data_ptr(), zd.data_ptr() if sample else None, u.data_ptr() if sample else None,
-                    res.data_ptr(), st)
+        B.vs_accept(e.model, batch, B.VS_GREEDY, 1.0, toks.data_ptr(), z.data_ptr(), None, None, res.data_ptr(), st)
         B.vs_commit(e.model, e.kv, batch, res.data_ptr(), st)
+        if ev is not None and ev != "stats":
+            ev[1].record()
 
-    def rewind():  # the committed context below P is never written by a round
+    def rewind():
         for i, s in enumerate(seqs):
             B.vs_seq_rewind(e.kv, s, ctx[i], int(pend[i]), st)
 
-    for _ in range(args.warmup):
-        step()
-        rewind()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(args.steps):
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        step()
-        t1.record()
-        rewind()
+    ms, fam = verify_steps(e, B, batch, step, rewind, steps, warmup)
+    e.close()
+    del e
+    torch.cuda.empty_cache()
+    bytes_, flops, roofs = verify_roofs(c, ctx, M, ms)
+    return {"metric": "verify-step algorithmic HBM GB/s", "value": roofs["roofline"]["achieved"], "unit": "GB/s",
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "dtype": "bf16",
+            "data": "synthetic (random-init bf16 weights, generator-filled committed KV, random draft rows)",
+            "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": sum(ctx),
+                       "exit_layer": c.exit_layer, "layers": c.n_layers, "mode": w.mode},
+            **roofs, "verify_step_bytes": bytes_, "verify_step_flops": flops, "weights_load_s": t_load,
+            "kernel_families_bracketed": fam}
+
+
+def config_tiny(B, w, reps=20):
+    """Tokens/s of the tiny decoder's greedy chain (k = 4) generating its 32
+    tokens after a 64-token prompt, on the GPU (bf16 weights) and in the
+    oracle (the whole generation, float64)."""
+    import torch
+
+    import synth
+    from synth import gpu_weights
+    from verification_verify_step_amd.runtime import Engine
+
+    c = w.model
+    # the host's bound of the context grows by k + 1 per round (vs_step does
+    # not read the accepted count back), so the sequence holds that much
+    cap = w.prompt_len + (w.new_tokens + 2) * (w.k + 1) + 8
+    e = Engine(c, max_rows=64, max_seqs=2, max_ctx=cap)
+    gpu_weights.load(e, c, force_host=True)
+    st = e.stream
+    prompt = synth.tokens(synth.SEED_PROMPTS, synth.stream_prompt(0), c.vocab, w.prompt_len)
+    dprompt = torch.tensor(prompt, dtype=torch.int32, device="cuda")
+    toks = torch.empty(64, dtype=torch.int32, device="cuda")
+    res = torch.zeros((1, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+
+    def generate():
+        s = e.open(cap)
+        B.vs_prefill(e.model, e.kv, s, dprompt.data_ptr(), w.prompt_len, B.VS_GREEDY, 1.0, None, None, st)
         torch.cuda.synchronize()
-        times.append(t0.elapsed_time(t1))
-    ms = float(np.mean(times))
-    # one more step with every kernel family bracketed by events
-    B.vs_stats_reset(e.model)
-    B.vs_stats_enable(e.model, -1)
-    step()
-    torch.cuda.synchronize()
-    B.vs_stats_enable(e.model, 0)
-    fam = {k: {"launches": v[0], "ms": v[1], "gbs": (v[2] / (v[1] * 1e-3) / 1e9) if v[1] else None}
-           for k, v in B.vs_stats_read(e.model).items() if v[0]}
-    rewind()
-    nl = c.n_layers - c.exit_layer
-    kv_row = c.n_kv_heads * c.head_dim * 2 * 2
-    params = nl * layer_bytes(c) // 2 + c.vocab * c.d_model
-    bytes_ = (nl * layer_bytes(c) + 2 * c.vocab * c.d_model + nl * sum(ctx) * kv_row + nl * M * kv_row
-              + M * c.d_model * 4 * 2 + M * c.vocab * 4)
-    flops = 2.0 * M * params
-    gbs = bytes_ / (ms * 1e-3) / 1e9
-    tflops = flops / (ms * 1e-3) / 1e12
-    print(json.dumps({
-        "metric": f"verify-step algorithmic HBM GB/s ({w.name})", "value": gbs, "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (random-init bf16 weights, generator-filled committed KV"
-                + (", a tree drafted on the GPU)" if tree else ", random draft rows)"),
-        "config": {"workload": w.name, "requests": n, "rows": M, "sum_ctx": sum(ctx), "exit_layer": c.exit_layer,
-                   "layers": c.n_layers, "mode": w.mode},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-        "mfma": {"achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0,
-                 "note": "algorithmic flops 2 x rows x weights of the verify layers and head; the split-bf16 "
-                         "activations issue twice as many MFMA operations"},
-        "verify_step_bytes": bytes_, "verify_step_flops": flops, "weights_load_s": t_load,
-        "kernel_families_bracketed": fam,
-    }))
+        t0 = time.perf_counter()
+        made, rounds = 0, 0
+        while made < w.new_tokens:
+            B.vs_step(e.model, e.kv, [s], [w.k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), res.data_ptr(), st)
+            made += int(res[0, 0].item()) + 1  # the host reads a to stop at 32 tokens
+            rounds += 1
+        dt = time.perf_counter() - t0
+        B.vs_seq_close(e.kv, s)
+        return made, rounds, dt
+
+    generate()
+    runs = [generate() for _ in range(reps)]
+    made = sum(r[0] for r in runs)
+    dt = sum(r[2] for r in runs)
+    e.close()
+    # the oracle: the same generation in float64
+    from oracle import spec
+    from oracle.decoder import Decoder, KVCache
+    from synth.model_weights import SynthWeights
+    dec = Decoder(c, SynthWeights(c, precision="bf16", cache=True))
+    cache = KVCache(c, 256)
+    t0 = time.perf_counter()
+    out, _ = spec.generate_spec(dec, cache, 0, prompt, w.new_tokens, w.k)
+    t_cpu = time.perf_counter() - t0
+    cpu = {"value": len(out) / t_cpu, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": f"the whole float64 generation of {len(out)} tokens (prompt {w.prompt_len}, k {w.k}) once",
+           "cores_note": "BLAS threads of the matrix products; the oracle's per-row attention loops run on one core"}
+    cpu.update(host_info())
+    return {"metric": "verified tokens/s", "value": made / dt, "unit": "tokens/s", "dtype": "bf16",
+            "data": "synthetic (random-init bf16 weights, uniform-random prompt)",
+            "config": {"workload": w.name, "layers": c.n_layers, "d_model": c.d_model, "k": w.k,
+                       "prompt": w.prompt_len, "new_tokens": w.new_tokens},
+            "runs": reps, "rounds_per_run": runs[0][1], "tokens_per_run": runs[0][0],
+            "note": "each round reads its accepted count back to stop at the token budget; the weights are "
+                    "cache-resident (no HBM roofline)",
+            "cpu_baseline": cpu}
+
+
+def reload_upper(e, c, st, eps=None, head_scale=None):
+    """W_o and W_down of the verify layers, and the head, back from the
+    generator (scaled by eps / head_scale when given)."""
+    import synth
+    from synth import gpu_weights
+    for l in range(c.exit_layer, c.n_layers):
+        for t in (synth.T_WO, synth.T_W_DOWN):
+            e.set_tensor(t, l, gpu_weights.device_bits(c, t, l, e.device, st, eps=eps))
+    e.set_tensor(synth.T_HEAD, 0, gpu_weights.device_bits(c, synth.T_HEAD, 0, e.device, st, head_scale=head_scale))
 
 
 def main():
     args = parse()
-    if args.workload != "llama7b_chain_k5":
-        if args.gpus != 1:
-            print(json.dumps({"error": "this build measures one GPU only"}))
-            sys.exit(2)
-        workload_verify(args)
-        return
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -447,12 +709,28 @@ def main():
     from verification_verify_step_amd import binding as B
     from verification_verify_step_amd.runtime import Engine
 
+    if args.workload != "llama7b_chain_k5":  # one other workload's line on its own
+        w = WORKLOADS[args.workload]
+        if w.name == "llama70b_ragged_b32":
+            line = config_70b(B, w, args.steps, args.warmup)
+        elif w.name == "tiny_chain_k4":
+            line = config_tiny(B, w)
+        else:
+            e = Engine(w.model, max_rows=64, max_seqs=w.batch + 1, max_ctx=w.prompt_len + 160)
+            gpu_weights.load(e, w.model)
+            line = config_7b(e, B, w, args.steps, args.warmup)
+        line.update({"n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None})
+        print(json.dumps(line))
+        return
+
     w = WORKLOADS[args.workload]
     c, k = w.model, w.k
     P0 = w.prompt_len
-    rounds = args.warmup + 3 * args.steps
-    cap = P0 + 2 + (rounds + args.steps + 8) * (k + 1) + 128
-    e = Engine(c, max_rows=64, max_seqs=4, max_ctx=cap, max_blocks_per_seq=(cap + 15) // 16 + 1)
+    n_extra = min(args.steps, 40)
+    rounds = args.warmup + args.steps
+    cap = P0 + 2 + (max(rounds, args.warmup + n_extra) + 8) * (k + 1) + 128
+    ctx_max = max(cap, max(WORKLOADS[n].prompt_len for n in ("llama7b_sample_k4_b8", "llama7b_tree63")) + 160)
+    e = Engine(c, max_rows=64, max_seqs=10, max_ctx=ctx_max, max_blocks_per_seq=(ctx_max + 15) // 16 + 1)
     t_load = time.time()
     gpu_weights.load(e, c)
     t_load = time.time() - t_load
@@ -467,13 +745,15 @@ def main():
         return s
 
     seq = open_prefilled()
+    pend0 = e.state()[1][seq]
     M = k + 1
     toks = torch.empty(64, dtype=torch.int32, device="cuda")
     hidden = torch.empty((M, c.d_model), dtype=torch.float32, device="cuda")
     logits = torch.empty((M, c.vocab), dtype=torch.float32, device="cuda")
-    res = torch.zeros((rounds, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    res = torch.zeros((rounds + n_extra + 8, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
     batch = B.make_batch([seq], [M])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(rounds + n_extra + 8)]
 
     def one_round(r, s=seq, b=batch):
         B.vs_draft(e.model, e.kv, [s], [k], B.VS_GREEDY, 1.0, None, toks.data_ptr(), hidden.data_ptr(), None, st)
@@ -486,14 +766,15 @@ def main():
 
     for r in range(args.warmup):
         one_round(r)
-    e.sync()
     torch.cuda.synchronize()
 
-    def timed_region(first, mask):
-        """args.steps rounds; library event brackets on the families in mask."""
+    def timed_region(mask):
+        """args.steps rounds from the prompt's context (rewound), library event
+        brackets on the families in mask."""
+        B.vs_seq_rewind(e.kv, seq, P0, pend0, st)
         B.vs_stats_reset(e.model)
         B.vs_stats_enable(e.model, mask)
-        p0 = e.state()[0][seq]
+        first = args.warmup
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record()
@@ -502,27 +783,30 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         B.vs_stats_enable(e.model, 0)
-        r_host = res.cpu().numpy()
-        committed = int(sum(r_host[r][0] + 1 for r in range(first, first + args.steps)))
-        accepted = int(sum(r_host[r][0] for r in range(first, first + args.steps)))
+        r_host = res.cpu().numpy()[first:first + args.steps]
+        committed = int(np.sum(r_host[:, 0] + 1))
+        accepted = int(np.sum(r_host[:, 0]))
+        flagged = int(np.sum(r_host[:, 2] & 1))
         p1 = e.state()[0][seq]
-        assert p1 == p0 + committed, (p0, p1, committed)
+        assert p1 == P0 + committed, (P0, p1, committed)
         v_ms = float(np.mean([ev[r][0].elapsed_time(ev[r][1]) for r in range(first, first + args.steps)]))
-        e.sync()
-        return t0.elapsed_time(t1), committed, accepted, v_ms, p0, B.vs_stats_read(e.model)
+        return t0.elapsed_time(t1), committed, accepted, flagged, v_ms, B.vs_stats_read(e.model)
 
     # A: clean (no per-launch events) -> headline numbers
-    total_ms, committed, accepted, v_ms, P_start, _ = timed_region(args.warmup, 0)
+    total_ms, committed, accepted, flagged, v_ms, _ = timed_region(0)
     # B: every family bracketed -> per-family table, dominant family
-    _, _, _, _, _, stats = timed_region(args.warmup + args.steps, -1)
+    _, _, _, _, _, stats = timed_region(-1)
     fam = {n: s for n, s in stats.items() if n != "small" and s[0] > 0}
     dom = max(fam, key=lambda n: fam[n][1])
     # C: only the dominant family bracketed -> its average launch duration
-    _, _, _, _, _, stats_c = timed_region(args.warmup + 2 * args.steps, 1 << B.STAT_FAMILIES.index(dom))
+    _, _, _, _, _, stats_c = timed_region(1 << B.STAT_FAMILIES.index(dom))
     n_l, ms_l, by_l = stats_c[dom]
     achieved = (by_l / n_l) / (ms_l / n_l * 1e-3) / 1e9
-    P_mid = P_start + committed // 2
+    B.vs_seq_rewind(e.kv, seq, P0, pend0, st)
+    P_mid = P0 + committed // 2
     v_bytes = verify_step_bytes(c, P_mid, M)
+    probe = read_probe(B)
+    v_gbs = v_bytes / (v_ms * 1e-3) / 1e9
     out = {
         "metric": "verified tokens/s at 7B-shape batch 1; verify-step HBM GB/s vs peak",
         "value": committed / (total_ms * 1e-3),
@@ -538,21 +822,26 @@ def main():
         "data": "synthetic (random-init N(0,0.02) bf16 weights, uniform-random prompt ids, seeded)",
         "config": {"workload": w.name, "layers": c.n_layers, "d_model": c.d_model, "heads": c.n_heads,
                    "head_dim": c.head_dim, "d_ffn": c.d_ffn, "vocab": c.vocab, "exit_layer": c.exit_layer,
-                   "k": k, "batch": w.batch, "prompt": P0, "mode": w.mode},
+                   "k": k, "batch": w.batch, "prompt": P0, "mode": w.mode,
+                   "context": [P0, P0 + committed], "committed_tokens": committed},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": pmc_traffic(w.name, dom),
-                     "launches": n_l, "avg_launch_us": ms_l / n_l * 1e3, "bytes_per_launch": by_l / n_l},
+                     "launches": n_l, "avg_launch_us": ms_l / n_l * 1e3, "bytes_per_launch": by_l / n_l,
+                     "frac_of_achievable": achieved / probe["gbs_best"]},
         "verify_step_ms": v_ms,
-        "verify_step_gbs": v_bytes / (v_ms * 1e-3) / 1e9,
-        "verify_step_frac_of_peak": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "verify_step_gbs": v_gbs,
+        "verify_step_frac_of_peak": v_gbs / HBM_PEAK_GBS,
+        "verify_step_frac_of_achievable": v_gbs / probe["gbs_best"],
         "verify_step_bytes": v_bytes,
+        "achievable_read": probe,
         "alpha": accepted / (args.steps * k),
         "tokens_per_round": committed / args.steps,
-        "kernel_families_bracketed": {n: {"launches": s[0], "avg_us": s[1] / s[0] * 1e3 if s[0] else None,
-                                          "gbs": (s[2] / (s[1] * 1e-3) / 1e9) if s[1] else None}
-                                      for n, s in stats.items()},
+        "flagged": {"rounds": flagged, "of": args.steps, "rule": "a greedy choice on the accept walk whose top-1 - "
+                    "top-2 logit gap is below 4e-2 (twice the logit tolerance)"},
+        "kernel_families_bracketed": family_table(stats),
         "weights_load_s": t_load,
     }
+    B.vs_seq_close(e.kv, seq)
     if not args.no_extras:
         # plain greedy AR on the same kernels: the pending token through all layers
         sB = open_prefilled()
@@ -570,54 +859,119 @@ def main():
             ar_step()
         torch.cuda.synchronize()
         a0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(n_extra):
             ar_step()
         torch.cuda.synchronize()
-        out["ar_tokens_per_s"] = args.steps / (time.perf_counter() - a0)
+        out["ar_tokens_per_s"] = n_extra / (time.perf_counter() - a0)
         B.vs_seq_close(e.kv, sB)
         # confidence-scheduled draft length ("DSpark" page, §2.2-§2.3) from k = 5
-        out["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        out["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, n_extra, args.warmup)
         # windowed dynamic k with the context-cost cut-off (self-speculative page, §3.2, §5.3)
-        out["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
-                                          c.exit_layer / c.n_layers)
+        out["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, n_extra, args.warmup, c.exit_layer / c.n_layers)
         # prompt-copy drafting with a full-depth verify
-        out["ngram"] = ngram_rounds(e, B, prompt, open_prefilled, args.steps, args.warmup)
+        out["ngram"] = ngram_rounds(e, B, prompt, open_prefilled, n_extra, args.warmup)
         # stochastic accept of the k+1 verify rows, plain and with a top-p target
-        out["accept_us"] = accept_timing(e, B, seq, M, c.vocab, k)
-        # acceptance-calibrated synthetic model: W_o, W_down of layers >= L
-        # scaled by 0 (same bytes, target == draft, every draft accepted)
-        for l in range(c.exit_layer, c.n_layers):
-            for t in (synth.T_WO, synth.T_W_DOWN):
-                src = gpu_weights.device_bits(c, t, l, e.device, st, eps=0.0)
-                e.set_tensor(t, l, src)
-        sC = open_prefilled()
-        bC = B.make_batch([sC], [M])
-        for r in range(min(args.warmup, rounds)):
-            one_round(r, sC, bC)
-        torch.cuda.synchronize()
-        Pc = e.state()[0][sC]
-        a0 = time.perf_counter()
-        n_cal = min(args.steps, rounds - args.warmup)
-        for r in range(args.warmup, args.warmup + n_cal):
-            one_round(r, sC, bC)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - a0
-        Pc2 = e.state()[0][sC]
-        out["calibrated_alpha1"] = {"tokens_per_s": (Pc2 - Pc) / dt, "tokens_per_round": (Pc2 - Pc) / n_cal,
-                                    "note": "synthetic model with upper-layer W_o and W_down zeroed (same bytes)"}
-        B.vs_seq_close(e.kv, sC)
-        out["calibrated_alpha1"]["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
-        out["calibrated_alpha1"]["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, args.steps, args.warmup,
+        sT = open_prefilled()
+        out["accept_us"] = accept_timing(e, B, sT, M, c.vocab, k)
+        B.vs_seq_close(e.kv, sT)
+
+        def calibrated(eps, n_rounds):
+            """Fixed-k rounds on the synthetic model with W_o, W_down of the
+            verify layers scaled by eps (same bytes)."""
+            reload_upper(e, c, st, eps=eps)
+            sC = open_prefilled()
+            bC = B.make_batch([sC], [M])
+            for r in range(args.warmup):
+                one_round(r, sC, bC)
+            torch.cuda.synchronize()
+            Pc = e.state()[0][sC]
+            a0 = time.perf_counter()
+            for r in range(args.warmup, args.warmup + n_rounds):
+                one_round(r, sC, bC)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - a0
+            acc = int(res[args.warmup:args.warmup + n_rounds, 0].sum().item())
+            Pc2 = e.state()[0][sC]
+            B.vs_seq_close(e.kv, sC)
+            return {"eps": eps, "alpha": acc / (n_rounds * k), "tokens_per_s": (Pc2 - Pc) / dt,
+                    "tokens_per_round": (Pc2 - Pc) / n_rounds, "rounds": n_rounds}
+
+        # acceptance-calibrated points near the self-speculative page's alphas
+        # (§4.6: 0.62 before and 0.81 after layer-drop training)
+        n_cal = min(args.steps, 100)
+        out["calibrated"] = {
+            "note": "synthetic model: W_o and W_down of layers >= L scaled by eps (same bytes); eps chosen so that "
+                    "the measured alpha lands near the page's 0.62 and 0.81",
+            "alpha_0.81": calibrated(3.0 / 128, n_cal), "alpha_0.62": calibrated(3.0 / 64, n_cal)}
+        # eps = 0: the target equals the draft, every draft is accepted
+        cal1 = calibrated(0.0, n_extra)
+        cal1["note"] = "synthetic model with upper-layer W_o and W_down zeroed (same bytes)"
+        out["calibrated_alpha1"] = cal1
+        out["calibrated_alpha1"]["scheduled"] = scheduled_rounds(e, B, open_prefilled, k, n_extra, args.warmup)
+        out["calibrated_alpha1"]["dynamic_k"] = dynamic_rounds(e, B, open_prefilled, k, n_extra, args.warmup,
                                                                c.exit_layer / c.n_layers)
         # the same with the LM head x4: sharper distributions (the same argmax,
         # so the same tokens), so the schedule sees a confident target
         e.set_tensor(synth.T_HEAD, 0, gpu_weights.device_bits(c, synth.T_HEAD, 0, e.device, st, head_scale=4.0))
-        sched4 = scheduled_rounds(e, B, open_prefilled, k, args.steps, args.warmup)
+        sched4 = scheduled_rounds(e, B, open_prefilled, k, n_extra, args.warmup)
         sched4["note"] = "as above with the LM head scaled by 4 (same argmax everywhere)"
         out["calibrated_alpha1"]["scheduled_head_x4"] = sched4
+        reload_upper(e, c, st)  # the random model again
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, P0, args.cpu_layers)
+    if not args.no_configs:
+        cfgs = {}
+        cs = min(args.config_steps, args.steps)
+        for name in ("llama7b_sample_k4_b8", "llama7b_tree63"):
+            cw = WORKLOADS[name]
+            cfgs[name] = config_7b(e, B, cw, cs, args.warmup)
+        e.close()
+        del e
+        torch.cuda.empty_cache()
+        cfgs["llama70b_ragged_b32"] = config_70b(B, WORKLOADS["llama70b_ragged_b32"], cs, args.warmup)
+        cfgs["tiny_chain_k4"] = config_tiny(B, WORKLOADS["tiny_chain_k4"])
+        if not args.no_cpu:
+            for name in ("llama7b_sample_k4_b8", "llama7b_tree63", "llama70b_ragged_b32"):
+                cw = WORKLOADS[name]
+                cfg = cfgs[name]["config"]
+                if name == "llama7b_tree63":
+                    # the 64 rows of a chain-free tree: rows see the ancestors of
+                    # a level-order top-5 tree (depth <= 4), built on the host
+                    ctxs, rows, tree_rows = [cw.prompt_len], [cfg["rows"]], _tree_rows_fn(cfg["rows"])
+                elif name == "llama70b_ragged_b32":
+                    from synth.workloads import ragged_batch
+                    cc, kk, _ = ragged_batch(cw)
+                    ctxs, rows, tree_rows = list(cc), [x + 1 for x in kk], None
+                else:
+                    ctxs, rows, tree_rows = [cw.prompt_len] * cw.batch, [cw.k + 1] * cw.batch, None
+                cfgs[name]["cpu_baseline"] = cpu_verify_sample(cw.model, ctxs, rows, tree_rows)
+                cfgs[name]["cpu_baseline"]["gpu_speedup"] = cfgs[name]["cpu_baseline"]["value"] / cfgs[name][
+                    "ms_per_step"]
+        out["configs"] = cfgs
     print(json.dumps(out))
+
+
+def _tree_rows_fn(R):
+    """Oracle rows of an R-row level-order tree for the CPU sample: row r's
+    parent is row (r - 1) // 5 (a complete top-5 tree cut at R rows)."""
+    import numpy as np
+
+    from oracle.decoder import Row
+
+    def rows_of(sid, P):
+        parent = [-1] + [(r - 1) // 5 for r in range(1, R)]
+        depth = [0] * R
+        for r in range(1, R):
+            depth[r] = depth[parent[r]] + 1
+        out = []
+        for r in range(R):
+            anc, x = [], r
+            while x >= 0:
+                anc.append(P + x)
+                x = parent[x]
+            out.append(Row(sid, P + depth[r], P + r, np.concatenate([np.arange(P), np.array(sorted(anc))])))
+        return out
+    return rows_of
 
 
 if __name__ == "__main__":

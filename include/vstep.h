@@ -383,6 +383,14 @@ vs_status vs_stats_enable(vs_model* m, int32_t mask);
 vs_status vs_stats_read(vs_model* m, vs_kernel_stat* out, int32_t max, int32_t* n_out);
 vs_status vs_stats_reset(vs_model* m);
 
+/* Achievable HBM read bandwidth, the denominator beside the 8 TB/s peak when
+ * the weight streams of the verify step are judged: one launch reads `bytes`
+ * (a positive multiple of 16; d_src 16-byte aligned) with 16-byte loads,
+ * 2048 workgroups of 256 threads each streaming one contiguous range, and
+ * writes one checksum word per workgroup to d_sink (2048 words).  The caller
+ * times it (events on `stream`).  Errors: VS_E_INVAL. */
+vs_status vs_read_probe(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ EXPORTS = [
     "vs_kv_sync", "vs_prefill", "vs_forward_layers", "vs_head", "vs_draft", "vs_draft_tree", "vs_verify", "vs_accept", "vs_accept_top_p", "vs_accept_noalloc", "vs_commit",
     "vs_step", "vs_confidence", "vs_sched_init", "vs_sched_update", "vs_step_sched", "vs_dynk_init",
     "vs_dynk_update", "vs_ngram_propose", "vs_step_ngram", "vs_stats_enable", "vs_stats_read",
-    "vs_stats_reset",
+    "vs_stats_reset", "vs_read_probe",
 ]
 
 
@@ -129,6 +129,7 @@ def lib():
             "vs_stats_enable": (I32, [VP, I32]),
             "vs_stats_read": (I32, [VP, P(vs_kernel_stat), I32, pI]),
             "vs_stats_reset": (I32, [VP]),
+            "vs_read_probe": (I32, [VP, SZ, VP, VP]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -385,3 +386,7 @@ def vs_stats_read(model):
     n = ctypes.c_int32()
     _check("vs_stats_read", lib().vs_stats_read(model, arr, 16, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms, arr[i].bytes) for i in range(n.value)}
+
+
+def vs_read_probe(d_src, nbytes, d_sink, stream):
+    _check("vs_read_probe", lib().vs_read_probe(d_src, nbytes, d_sink, stream))

@@ -1866,6 +1866,14 @@ vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* se
   return VS_OK;
 }
 
+vs_status vs_read_probe(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (d_src == nullptr || d_sink == nullptr) return fail(VS_E_INVAL, "vs_read_probe: null argument");
+  if (bytes < 16 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(d_src) & 15) != 0)
+    return fail(VS_E_INVAL, "vs_read_probe: %zu bytes (a positive multiple of 16, 16-byte aligned)", bytes);
+  launch_read_probe(static_cast<const u32x4*>(d_src), bytes / 16, d_sink, S(stream));
+  return check_launch("vs_read_probe");
+}
+
 vs_status vs_stats_enable(vs_model* m, int32_t on) {
   if (m == nullptr) return fail(VS_E_INVAL, "vs_stats_enable: null model");
   m->stats_mask = on;

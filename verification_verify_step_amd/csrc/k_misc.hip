@@ -60,6 +60,35 @@ void launch_fill_i32(int* p, int v, size_t n, hipStream_t st) {
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, v, n);
 }
 
+// Streaming read: workgroup b reads units [b*per, (b+1)*per) of the buffer,
+// 8 16-byte loads per thread in flight per iteration; the XOR of everything
+// it read goes to sink[b] so that no load is dropped.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  constexpr int kUnroll = 8;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per, hi = lo + per < n16 ? lo + per : n16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  size_t i = lo + threadIdx.x;
+  for (; i + (kUnroll - 1) * 256 < hi; i += kUnroll * 256) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  for (; i < hi; i += 256) acc ^= __builtin_nontemporal_load(src + i);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  x = wave_sum(x);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+void launch_read_probe(const u32x4* src, size_t n16, uint32_t* sink, hipStream_t st) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kReadProbeBlocks), dim3(256), 0, st, src, n16, sink);
+}
+
 __global__ void set_blocks_kernel(BlockSetArgs a) {
   const int i = threadIdx.x;
   if (i < a.n) a.bt[a.seq * a.bps + a.first + i] = a.ids[i];

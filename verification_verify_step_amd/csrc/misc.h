@@ -179,6 +179,10 @@ void launch_tree_expand(const TreeArgs& a, hipStream_t st);
 void launch_pack(const PackArgs& a, hipStream_t st);
 void launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t st);
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
+// Streaming read of n16 16-byte units by kReadProbeBlocks workgroups, each a
+// contiguous range; one checksum word per workgroup into sink.
+constexpr int kReadProbeBlocks = 2048;
+void launch_read_probe(const u32x4* src, size_t n16, uint32_t* sink, hipStream_t st);
 void launch_set_blocks(const BlockSetArgs& a, hipStream_t st);
 void launch_set_state(int* P, int* pending, int* committed, int seq, int p, int pend, hipStream_t st);
 void launch_load_rows(const LoadArgs& a, hipStream_t st);
