@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -215,11 +216,46 @@ struct vs_kv {
   std::vector<int> free_blocks;
   std::vector<std::vector<int>> blocks;
   std::vector<int> open, cap, P_ub, prefilled;
+  // The host's bound P_ub of each sequence's KV length: the exact value at
+  // the last host-side setting (open, prefill, assume, rewind, sync) plus the
+  // rows of every commit since.  Commits are numbered per sequence and the
+  // commit kernel stores (number << 32 | new P) into a pinned host mirror,
+  // so once the host sees a commit there the bound becomes that exact P plus
+  // the rows of the later commits only.  No host wait is involved.
+  uint64_t* mirror = nullptr;  // pinned [max_seqs]
+  std::vector<unsigned> commit_no, base_no;
+  std::vector<int> P_base;
+  std::vector<std::deque<std::pair<unsigned, int>>> in_flight;  // (commit number, rows) not yet seen
 };
 
 namespace {
 
 hipStream_t S(void* st) { return reinterpret_cast<hipStream_t>(st); }
+
+// The bound becomes exact: P is known on the host (in stream order after
+// every earlier commit of the sequence).
+void kv_set_exact(vs_kv* kv, int s, int P) {
+  kv->P_ub[s] = kv->P_base[s] = P;
+  kv->base_no[s] = kv->commit_no[s] + 1;
+  kv->in_flight[s].clear();
+}
+
+// Tightens P_ub[s] from the mirror.
+void kv_refresh(vs_kv* kv, int s) {
+  if (kv->mirror == nullptr) return;
+  const uint64_t m = __atomic_load_n(kv->mirror + s, __ATOMIC_ACQUIRE);
+  const unsigned no = (unsigned)(m >> 32);
+  auto& q = kv->in_flight[s];
+  int bound;
+  if (no >= kv->base_no[s] && no <= kv->commit_no[s]) {  // a commit since the exact setting has landed
+    while (!q.empty() && q.front().first <= no) q.pop_front();
+    bound = (int)(uint32_t)m;
+  } else {
+    bound = kv->P_base[s];
+  }
+  for (const auto& c : q) bound += c.second;
+  kv->P_ub[s] = bound;
+}
 
 vs_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
@@ -616,6 +652,7 @@ vs_status batch_rowmap(vs_kv* kv, const vs_batch* b, RowMap* rm) {
   for (int i = 0; i < b->n_seq; ++i) {
     const int s = b->seq[i];
     if (s < 0 || s >= kv->max_seqs || !kv->open[s]) return fail(VS_E_STATE, "batch: sequence %d is not open", s);
+    kv_refresh(kv, s);
     for (int j = 0; j < i; ++j)
       if (b->seq[j] == s) return fail(VS_E_INVAL, "batch: sequence %d listed twice", s);
     if (b->n_rows[i] < 1 || b->n_rows[i] > kMaxRows)
@@ -894,6 +931,16 @@ vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_se
   kv->cap.assign(max_seqs, 0);
   kv->P_ub.assign(max_seqs, 0);
   kv->prefilled.assign(max_seqs, 0);
+  kv->commit_no.assign(max_seqs, 0);
+  kv->base_no.assign(max_seqs, 1);
+  kv->P_base.assign(max_seqs, 0);
+  kv->in_flight.resize(max_seqs);
+  if (hipHostMalloc(reinterpret_cast<void**>(&kv->mirror), (size_t)max_seqs * 8, hipHostMallocCoherent) != hipSuccess) {
+    (void)hipGetLastError();
+    delete kv;
+    return fail(VS_E_DEVICE, "vs_kv_create: pinned host mirror of the KV lengths");
+  }
+  memset(kv->mirror, 0, (size_t)max_seqs * 8);
   vs_status rc = check_launch("vs_kv_create");
   if (rc != VS_OK) {
     delete kv;
@@ -903,7 +950,14 @@ vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_se
   return VS_OK;
 }
 
-void vs_kv_destroy(vs_kv* kv) { delete kv; }
+void vs_kv_destroy(vs_kv* kv) {
+  if (kv == nullptr) return;
+  if (kv->mirror != nullptr) {
+    (void)hipDeviceSynchronize();  // no commit kernel may still write it
+    (void)hipHostFree(kv->mirror);
+  }
+  delete kv;
+}
 
 vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id) {
   if (kv == nullptr || seq_id == nullptr) return fail(VS_E_INVAL, "vs_seq_open: null argument");
@@ -945,7 +999,7 @@ vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id)
   if (rc != VS_OK) return rc;
   kv->open[s] = 1;
   kv->cap[s] = nb * kBlock;
-  kv->P_ub[s] = 0;
+  kv_set_exact(kv, s, 0);
   kv->prefilled[s] = 0;
   *seq_id = s;
   return VS_OK;
@@ -960,7 +1014,7 @@ vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void
   launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, S(stream));
   vs_status rc = check_launch("vs_seq_assume");
   if (rc != VS_OK) return rc;
-  kv->P_ub[seq] = P;
+  kv_set_exact(kv, seq, P);
   kv->prefilled[seq] = 1;
   return VS_OK;
 }
@@ -980,7 +1034,7 @@ vs_status vs_seq_rewind(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void
   launch_set_state(kv->P, kv->pending, kv->committed, seq, P, pending, st);
   vs_status rc = check_launch("vs_seq_rewind");
   if (rc != VS_OK) return rc;
-  kv->P_ub[seq] = P;
+  kv_set_exact(kv, seq, P);
   return VS_OK;
 }
 
@@ -1018,7 +1072,7 @@ vs_status vs_kv_sync(vs_kv* kv, void* stream) {
   if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
   if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_kv_sync: %s", hipGetErrorString(e));
   for (int s = 0; s < kv->max_seqs; ++s)
-    if (kv->open[s]) kv->P_ub[s] = P[s];
+    if (kv->open[s]) kv_set_exact(kv, s, P[s]);
   return VS_OK;
 }
 
@@ -1116,6 +1170,7 @@ vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_token
     }
   }
   kv->prefilled[seq] = 1;
+  kv_set_exact(kv, seq, kv->P_ub[seq]);  // the prompt's length, exactly
   return check_launch("vs_prefill");
 }
 
@@ -1134,6 +1189,7 @@ vs_status validate_chain(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, 
     const int s = seq[i];
     if (s < 0 || s >= kv->max_seqs || !kv->open[s]) return fail(VS_E_STATE, "sequence %d is not open", s);
     if (!kv->prefilled[s]) return fail(VS_E_STATE, "sequence %d has no prefill", s);
+    kv_refresh(kv, s);
     for (int j = 0; j < i; ++j)
       if (seq[j] == s) return fail(VS_E_INVAL, "sequence %d listed twice", s);
     if (k[i] < 0 || k[i] > VS_MAX_K) return fail(VS_E_INVAL, "k = %d not in [0, %d]", k[i], VS_MAX_K);
@@ -1301,6 +1357,7 @@ vs_status vs_draft_tree(vs_model* m, vs_kv* kv, int32_t seq, int32_t topk, int32
     return fail(VS_E_INVAL, "vs_draft_tree: null argument");
   if (seq < 0 || seq >= kv->max_seqs || !kv->open[seq]) return fail(VS_E_STATE, "vs_draft_tree: sequence %d is not open", seq);
   if (!kv->prefilled[seq]) return fail(VS_E_STATE, "vs_draft_tree: sequence %d has no prefill", seq);
+  kv_refresh(kv, seq);
   if (topk < 1 || topk > kTreeMaxTopk) return fail(VS_E_INVAL, "vs_draft_tree: topk %d not in [1, %d]", topk, kTreeMaxTopk);
   if (depth < 1 || depth > kTreeMaxDepth)
     return fail(VS_E_INVAL, "vs_draft_tree: depth %d not in [1, %d]", depth, kTreeMaxDepth);
@@ -1604,9 +1661,16 @@ vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_
   a.n_layers = m->c.n_layers;
   a.Hkv = m->c.n_kv_heads;
   a.hd = m->c.head_dim;
+  a.mirror = kv->mirror;
+  for (int i = 0; i < rm.n_seq; ++i) a.commit_no[i] = kv->commit_no[rm.seq[i]] + 1;
   if (b->d_mask != nullptr) timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_compact(a, st); });
   timed(m, F_SMALL, 0, st, [&](hipEvent_t, hipEvent_t) { launch_commit(a, st); });
-  for (int i = 0; i < rm.n_seq; ++i) kv->P_ub[rm.seq[i]] += rm.row_start[i + 1] - rm.row_start[i];
+  for (int i = 0; i < rm.n_seq; ++i) {  // the bound counts every row until the mirror shows the commit
+    const int s = rm.seq[i], rows = rm.row_start[i + 1] - rm.row_start[i];
+    kv->commit_no[s] += 1;
+    kv->in_flight[s].emplace_back(kv->commit_no[s], rows);
+    kv->P_ub[s] += rows;
+  }
   return check_launch("vs_commit");
 }
 
@@ -1822,8 +1886,6 @@ vs_status vs_step_ngram(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* h_hi
   e = hipMemcpyAsync(h_result, d_result, VS_RESULT_INTS * sizeof(int32_t), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_ngram: %s", hipGetErrorString(e));
-  // the commit counted all k+1 rows into the host's bound of P; a + 1 were kept
-  kv->P_ub[seq] -= n_rows - (h_result[0] + 1);
   *k_out = k;
   return VS_OK;
 }
@@ -1853,8 +1915,6 @@ vs_status vs_step_sched(vs_model* m, vs_kv* kv, int32_t n_seq, const int32_t* se
   if (e == hipSuccess) e = hipMemcpyAsync(conf.data(), m->conf, conf.size() * 8, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_step_sched: %s", hipGetErrorString(e));
-  // the commit counted all k+1 rows into the host's bound of P; a + 1 were kept
-  for (int i = 0; i < n_seq; ++i) kv->P_ub[seq[i]] -= rows[i] - (h_result[i * VS_RESULT_INTS] + 1);
   for (int i = 0; i < n_seq; ++i) {
     if ((rc = vs_sched_update(c, &states[i], h_result[i * VS_RESULT_INTS], conf[2 * i], conf[2 * i + 1])) != VS_OK)
       return rc;

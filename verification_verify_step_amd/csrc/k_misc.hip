@@ -627,9 +627,13 @@ __global__ void commit_kernel(CommitArgs a) {
   if (i >= a.rows.n_seq) return;
   const int* res = a.result + i * VS_RESULT_INTS;
   const int sq = a.rows.seq[i];
-  a.P[sq] += res[0] + 1;
+  const int P = a.P[sq] + res[0] + 1;
+  a.P[sq] = P;
   a.pending[sq] = res[1];
   a.committed[sq] += res[0] + 1;
+  if (a.mirror != nullptr)
+    __hip_atomic_store(a.mirror + sq, ((uint64_t)a.commit_no[i] << 32) | (uint32_t)P, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
 }
 void launch_commit(const CommitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, a);

@@ -126,6 +126,10 @@ struct CommitArgs {
   uint16_t** kpool;       // [n_layers] device array of layer K pools
   uint16_t** vpool;
   int n_layers, Hkv, hd;
+  // host-visible record of each committed sequence's new KV length:
+  // mirror[seq] = (commit number << 32) | P, one 64-bit store (optional)
+  uint64_t* mirror;
+  unsigned commit_no[kMaxSeq];
 };
 
 // Target-model confidence of each sequence's verify rows: the mean over its
