@@ -504,13 +504,12 @@ vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
     pl->has_one = true;
     a.n_qg = 1;
     a.qg_size = nr_one * G;
-    // Chunks of each sequence (8 one-step splits and the window), then the
-    // chunks per workgroup (cpw) that minimise a launch-time model: a
-    // workgroup starts in about kStart, runs its chunks one after another at
-    // about kChunk each (one step, the merge; the next chunk's loads in
-    // flight meanwhile), with about ceil(workgroups / CUs) workgroups per
-    // CU, plus the cross-workgroup combine when a unit has several
-    // workgroups.  One sequence at a short context takes one chunk per
+    // Chunks of each sequence (4 one-step splits and the window), then the
+    // chunks per workgroup (cpw, at most kAttnMaxCpw) that minimise a
+    // launch-time model: a workgroup starts in about kStart, runs its chunks
+    // one after another at about kChunk each (one step, the merge; the next
+    // chunk's loads in flight meanwhile), two workgroups per CU, plus the
+    // cross-workgroup combine when a unit has several workgroups.  One sequence at a short context takes one chunk per
     // workgroup (parallel over the chip); many sequences or long contexts
     // take several (fewer starts and combines).
     int chunks[kMaxSeq];
@@ -522,14 +521,11 @@ vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
       chunks[i] = (ns + 1 + kAttnWaves - 1) / kAttnWaves;
       cmax = std::max(cmax, chunks[i]);
     }
-    if ((size_t)cmax * a.qg_size > (size_t)kAttnCombineSlots)
-      return fail(VS_E_SHAPE, "attention: a context needs %d chunks of %d keys, beyond the combine's %d slots", cmax,
-                  kAttnWaves * kAttnStepKeys, kAttnCombineSlots / a.qg_size);
     constexpr double kStart = 5.0, kChunk = 3.0, kCombine = 5.0;  // us
-    const int ncu = std::max(1, m->n_cu);
+    const int ncu = 2 * std::max(1, m->n_cu);  // workgroup slots
     double best = 1e30;
     int best_cpw = 1;
-    for (int cpw = 1; cpw <= cmax; ++cpw) {
+    for (int cpw = 1; cpw <= std::min(cmax, kAttnMaxCpw); ++cpw) {
       if (cpw > 1 && (cmax + cpw - 1) / cpw == (cmax + cpw - 2) / (cpw - 1)) continue;  // same split of the longest
       long wgs = 0;
       bool multi = false;

@@ -12,8 +12,8 @@
 namespace vs {
 
 // Workgroup layout of sequence i (AttnArgs.wg_start, 8-aligned): its
-// groups g = kvh * nsplit[i] + s (KV head, split of the host's bound; the
-// count padded to a multiple of 8) times its blocks of query groups, laid
+// groups g = s * Hkv + kvh (split of the host's bound, KV head; the count
+// padded to a multiple of 8, splits the device's P does not need last) times its blocks of query groups, laid
 // out so that the blocks of one group sit on one XCD back to back: local
 // index ((g / 8) * nqb + qb) * 8 + g % 8 (block b runs on XCD b % 8).  The
 // device's own split count max(1, ceil(P / kps)) decides which splits run;

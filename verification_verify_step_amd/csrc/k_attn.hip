@@ -19,8 +19,10 @@
 // the other sequences of its pass or on how the work is spread:
 //  * committed split j holds keys [32 j, 32 j + 32) below P (one step); the
 //    in-round window is split ceil(P / 32);
-//  * chunk c is splits [8 c, 8 c + 8), one per wave; its waves' (max, sum,
-//    o) are merged in LDS in wave order into the chunk's partial;
+//  * chunk c is splits [4 c, 4 c + 4), one per wave (4-wave workgroups, two
+//    per CU: the loads of a workgroup go through its CU at a few tens of
+//    GB/s, so a pass spreads them over every CU); its waves' (max, sum, o)
+//    are merged in LDS in wave order into the chunk's partial;
 //  * the chunks of a unit (sequence, KV head) are combined in chunk order.
 // A workgroup runs cpw consecutive chunks of one unit (the host picks cpw
 // for the pass): the loads of a wave's next step, in the next chunk too, are
@@ -44,8 +46,6 @@ namespace {
 // stay in flight (unlike __syncthreads(), which waits for them too).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int cmax(int x, int y) { return x > y ? x : y; }
-
 }  // namespace
 
 // Sequence of workgroup b: the last i with wg_start[i] <= b.
@@ -68,10 +68,12 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   constexpr int QR = 16;        // query vectors of the MFMA tile
   constexpr int PS = kStep + 4;  // P scratch row stride (floats)
   constexpr int HDP = HD + 4;    // merge row stride (floats): rows one lane group apart in other banks
-  constexpr int PL_FLOATS = WV * QR * PS;
-  constexpr int MG_FLOATS = WV * QR * HDP + 2 * WV * QR + 2 * QR + WV * QR;
-  constexpr int CB_FLOATS = 3 * kAttnCombineSlots + kAttnQG;
-  constexpr int SM_FLOATS = cmax(cmax(PL_FLOATS, MG_FLOATS), CB_FLOATS);
+  constexpr int PL_FLOATS = WV * QR * PS;                 // per-wave P scratch
+  constexpr int MG_FLOATS = WV * QR * HDP + 2 * WV * QR;  // one merge buffer: o, then (max, sum)
+  constexpr int SM_FLOATS = PL_FLOATS + 2 * MG_FLOATS;
+  // P scratch, then two merge buffers used by alternate chunks, so that a
+  // chunk's merge needs one barrier: the next chunk writes the other buffer,
+  // and the one after that passes this chunk's barrier first.
   __shared__ float smem[SM_FLOATS];
   __shared__ int last_wg;
 
@@ -79,9 +81,11 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const int b = blockIdx.x;
   if (b >= a.wg_start[a.rows.n_seq]) return;
   const int i = attn_seq_of(a, b);
-  const int nwg_ub = (a.wg_start[i + 1] - a.wg_start[i]) / a.Hkv;
+  // Workgroups of a sequence in order of their chunks, KV heads fastest:
+  // the ones past what the device's context needs (the host lays out its
+  // upper bound) come last and exit as soon as they are dispatched.
   const int local = b - a.wg_start[i];
-  const int kvh = local / nwg_ub, wgi = local - kvh * nwg_ub;
+  const int wgi = local / a.Hkv, kvh = local - wgi * a.Hkv;
   const int sq = a.rows.seq[i];
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
@@ -117,10 +121,26 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
     }
   };
   u32x4 kb[2][KSQ], vb[NDT];
+  // Block-table entries of this wave's steps, read once into lane-indexed
+  // registers so that no K/V load waits on a table load: lane l of bt_c
+  // holds block 2 * (WV c + wave) + l % 2 of chunk c = c0 + l / 2 (its
+  // committed split; a workgroup runs at most 32 chunks); lane l of bt_w
+  // holds block wfirst / 16 + l of the window's steps.  Entries are clamped to the table; data outside a split
+  // is masked.
+  const int wfirst = wlo / kStep * kStep;
+  const int bt_c = bt[min(2 * (WV * (c0 + (lane >> 1)) + wave) + (lane & 1), a.kv.bps - 1)];
+  const int bt_w = bt[min(wfirst / kBlock + lane, a.kv.bps - 1)];
   int nb0 = 0, nb1 = 0;  // blocks of the step being loaded
-  auto blocks_of = [&](int base) {
-    nb0 = bt[min(base / kBlock, a.kv.bps - 1)];  // clamped to the table; data outside the split is masked
-    nb1 = bt[min(base / kBlock + 1, a.kv.bps - 1)];
+  auto blocks_of = [&](int c, int base) {  // step at key `base`, in chunk c
+    if (c * WV + wave < ns) {
+      const int l = 2 * (c - c0);
+      nb0 = __builtin_amdgcn_readlane(bt_c, l);
+      nb1 = __builtin_amdgcn_readlane(bt_c, l + 1);
+    } else {
+      const int l = (base - wfirst) / kBlock;
+      nb0 = __builtin_amdgcn_readlane(bt_w, l);
+      nb1 = __builtin_amdgcn_readlane(bt_w, l + 1);
+    }
   };
   auto load_k = [&]() {
 #pragma unroll
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   // entries); the queries are split while K/V are in flight.
   int first, last;
   split_steps(c0, first, last);
-  if (first < last) blocks_of(first);
+  if (first < last) blocks_of(c0, first);
   float4 qraw[KSQ][2];
   uint64_t qmask[4];  // visibility masks of the 4 rows this lane holds in S
   {
@@ -190,11 +210,6 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   uint64_t* pml = reinterpret_cast<uint64_t*>(a.part + a.ml_off);  // [units][n_split][QG] (max, sum)
   float* pw = smem + wave * QR * PS;
   constexpr int DS = HD / WV;  // dims merged by one wave
-  float* xo = smem;                                               // [WV][QR][HDP]
-  float2* xml = reinterpret_cast<float2*>(smem + WV * QR * HDP);  // [WV][QR]
-  float* rl = reinterpret_cast<float*>(xml + WV * QR);            // [QR] merged sum
-  float* rm = rl + QR;                                            // [QR] merged max
-  float* wts = rm + QR;                                           // [WV][QR]
 
   for (int c = c0; c < c1; ++c) {
     const int sp = c * WV + wave;
@@ -212,16 +227,23 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
     for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int base = first; base < last; base += kStep) {
       // the next step to load: this split's next one, else the first step
-      // of this wave's split in the next chunk of the workgroup
-      int nbase = base + kStep;
-      bool more = nbase < last;
-      if (!more && c + 1 < c1) {
-        int nf, nl;
-        split_steps(c + 1, nf, nl);
-        nbase = nf;
-        more = nf < nl;
+      // of this wave's split in the next chunk of the workgroup, else this
+      // step again (an L2 hit): the loads are issued on every path, so that
+      // the compiler's waits count them exactly and the next step stays in
+      // flight while this one computes
+      int nbase = base + kStep, nc = c;
+      if (nbase >= last) {
+        nbase = base;
+        if (c + 1 < c1) {
+          int nf, nl;
+          split_steps(c + 1, nf, nl);
+          if (nf < nl) {
+            nbase = nf;
+            nc = c + 1;
+          }
+        }
       }
-      if (more) blocks_of(nbase);
+      blocks_of(nc, nbase);
       // S = Q.K^T for the two 16-key tiles
       f32x4 sacc[2];
 #pragma unroll
@@ -234,7 +256,7 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
         }
         sacc[t] = cc;
       }
-      if (more) load_k();
+      load_k();
       // mask, online softmax update, P into the scratch (row, key) layout; a
       // step of committed keys inside the split needs no mask, and the
       // accumulators are rescaled only when some factor is not exactly 1
@@ -287,15 +309,17 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
           oacc[t] = mfma16(pl, vb[t], oacc[t]);
         }
       }
-      if (more) load_v();
+      load_v();
     }
 
     // ---- merge the chunk's WV split partials: every wave puts its (max,
-    // sum, o) for the rows below nq in LDS; the per-row weights
-    // exp2(m_j - max) and the merged (max, sum) are computed once per row;
-    // then wave w merges dims [w*DS, (w+1)*DS) of all WV partials in wave
-    // order and writes that slice of the chunk's partial (or of the result).
-    lds_sync();  // every wave is done with its P scratch (the merge area)
+    // sum, o) for the rows below nq in the chunk's merge buffer; after one
+    // barrier, wave w merges dims [w*DS, (w+1)*DS) of all WV partials in
+    // wave order and writes that slice of the chunk's partial (or of the
+    // result).  Each lane takes the weights exp2(m_j - max) of its row
+    // itself (the same operations in the same order for every lane).
+    float* xo = smem + PL_FLOATS + (c & 1) * MG_FLOATS;             // [WV][QR][HDP]
+    float2* xml = reinterpret_cast<float2*>(xo + WV * QR * HDP);     // [WV][QR]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * kq + r;
@@ -306,45 +330,38 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       }
     }
     lds_sync();
-    for (int row = threadIdx.x; row < nq; row += kThreads) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < WV; ++j) {
-        const float2 v = xml[j * QR + row];
-        if (v.y > 0.f) mx = fmaxf(mx, v.x);  // a split that saw no key has sum 0
-      }
-      float l = 0.f;
-#pragma unroll
-      for (int j = 0; j < WV; ++j) {
-        const float2 v = xml[j * QR + row];
-        const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
-        wts[j * QR + row] = w;
-        l += w * v.y;
-      }
-      rl[row] = l;
-      rm[row] = mx;
-    }
-    lds_sync();
     const size_t rec = (size_t)unit * a.n_split + c;
     for (int e = lane; e < nq * DS; e += 64) {
       const int row = e / DS, d = wave * DS + e % DS;
-      float o = 0.f;
+      float2 ml[WV];
+      float xv[WV];
 #pragma unroll
-      for (int j = 0; j < WV; ++j) o += wts[j * QR + row] * xo[(j * QR + row) * HDP + d];
-      if (single)
-        xa_store(a.xa_o, (kvh * G + row / nr) * HD + d, r0 + row % nr, a.M, o / rl[row]);
-      else
+      for (int j = 0; j < WV; ++j) {  // every LDS read first, one wait
+        ml[j] = xml[j * QR + row];
+        xv[j] = xo[(j * QR + row) * HDP + d];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < WV; ++j)
+        if (ml[j].y > 0.f) mx = fmaxf(mx, ml[j].x);  // a split that saw no key has sum 0
+      float o = 0.f, l = 0.f;
+#pragma unroll
+      for (int j = 0; j < WV; ++j) {
+        const float w = ml[j].y > 0.f ? __builtin_amdgcn_exp2f(ml[j].x - mx) : 0.f;
+        l += w * ml[j].y;
+        o += w * xv[j];
+      }
+      if (single) {
+        xa_store(a.xa_o, (kvh * G + row / nr) * HD + d, r0 + row % nr, a.M, o / l);
+      } else {
         __hip_atomic_store(po + (rec * QG + row) * HD + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          const uint64_t bits = (uint64_t)__float_as_uint(mx) | ((uint64_t)__float_as_uint(l) << 32);
+          __hip_atomic_store(pml + rec * QG + row, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
-    if (!single && threadIdx.x < nq) {
-      const int row = threadIdx.x;
-      const uint64_t bits = (uint64_t)__float_as_uint(rm[row]) | ((uint64_t)__float_as_uint(rl[row]) << 32);
-      __hip_atomic_store(pml + rec * QG + row, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (c + 1 < c1) {
-      lds_sync();  // the merge area is the next chunk's P scratch
-      split_steps(c + 1, first, last);
-    }
+    if (c + 1 < c1) split_steps(c + 1, first, last);
   }
   if (single) return;
 
@@ -367,74 +384,87 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   }
 
   // ---- the unit's last workgroup: combine its n_chunks partials in chunk
-  // order.  Each row's weights exp2(m_j - max) and total are computed once in
-  // LDS; a thread then sums one pair of dims of one query vector over the
-  // partials, with the loads of up to kCB partials in flight at once (the
-  // first batch is requested before the weights exist).
-  constexpr int HP = HD / 2;  // dim pairs
-  constexpr int kCG = 8;      // partials per guarded group
-  constexpr int kCB = 16;     // partials requested per batch
+  // order.  A thread takes one or two pairs of dims of one query vector: it
+  // requests every (max, sum) record of the vector's row and every partial
+  // of its pairs at once (kCB chunks at a time), then forms the weights
+  // exp2(m_j - max) and the sums in chunk order itself: one round trip to
+  // memory, no barrier.
+  constexpr int HP = HD / 2;   // dim pairs
+  constexpr int kCB = 16;      // chunks requested per batch
+  constexpr int kPairs = 2;    // pairs per thread per round
   const int nc = n_chunks;
-  float2* cml = reinterpret_cast<float2*>(smem);  // [nc][nq] (max, sum)
-  float* cwt = smem + 2 * kAttnCombineSlots;      // [nc][nq] weights
-  float* ctot = cwt + kAttnCombineSlots;          // [nq]
   const uint64_t* src0 = reinterpret_cast<const uint64_t*>(po) + (size_t)unit * a.n_split * QG * HP;
+  const uint64_t* ml0 = pml + (size_t)unit * a.n_split * QG;
   const int S = (int)QG * HP;  // pairs between consecutive partials
   const int npair = nq * HP;
-  uint64_t xc[kCB];
-  auto load_batch = [&](int p, int j0) {
-    const uint64_t* src = src0 + min(p, npair - 1);
+  for (int p0 = threadIdx.x; p0 < npair; p0 += kPairs * kThreads) {
+    int pr[kPairs], rr[kPairs];
 #pragma unroll
-    for (int g = 0; g < kCB / kCG; ++g)
-      if (j0 + g * kCG < nc) {
-#pragma unroll
-        for (int e = g * kCG; e < (g + 1) * kCG; ++e)
-          xc[e] = __hip_atomic_load(src + min(j0 + e, nc - 1) * S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-  };
-  if (threadIdx.x < npair) load_batch(threadIdx.x, 0);
-  for (int e = threadIdx.x; e < nc * nq; e += kThreads) {
-    const int j = e / nq, r = e - j * nq;
-    const uint64_t bits = __hip_atomic_load(pml + ((size_t)unit * a.n_split + j) * QG + r, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    cml[e] = make_float2(__uint_as_float((uint32_t)bits), __uint_as_float((uint32_t)(bits >> 32)));
-  }
-  __syncthreads();
-  for (int r = threadIdx.x; r < nq; r += kThreads) {
-    float mx = -INFINITY;
-    for (int j = 0; j < nc; ++j)
-      if (cml[j * nq + r].y > 0.f) mx = fmaxf(mx, cml[j * nq + r].x);
-    float tot = 0.f;
-    for (int j = 0; j < nc; ++j) {
-      const float2 v = cml[j * nq + r];
-      const float w = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
-      cwt[j * nq + r] = w;
-      tot += w * v.y;
+    for (int q = 0; q < kPairs; ++q) {
+      pr[q] = min(p0 + q * kThreads, npair - 1);
+      rr[q] = pr[q] / HP;
     }
-    ctot[r] = tot;
-  }
-  __syncthreads();
-  for (int p = threadIdx.x; p < npair; p += kThreads) {
-    const int r = p / HP, cp = p - r * HP;
-    float o0 = 0.f, o1 = 0.f;
-    for (int j0 = 0; j0 < nc; j0 += kCB) {
-      if (p != threadIdx.x || j0 > 0) load_batch(p, j0);
+    float mx[kPairs], tot[kPairs], o0[kPairs], o1[kPairs];
 #pragma unroll
-      for (int g = 0; g < kCB / kCG; ++g)
-        if (j0 + g * kCG < nc) {
+    for (int q = 0; q < kPairs; ++q) {
+      mx[q] = -INFINITY;
+      tot[q] = o0[q] = o1[q] = 0.f;
+    }
+    uint64_t mlv[kPairs][kCB], xv[kPairs][kCB];
+    auto load = [&](int j0, bool with_x) {
 #pragma unroll
-          for (int e = g * kCG; e < (g + 1) * kCG; ++e) {
-            const int j = j0 + e;
-            const float w = j < nc ? cwt[j * nq + r] : 0.f;
-            o0 += w * __uint_as_float((uint32_t)xc[e]);
-            o1 += w * __uint_as_float((uint32_t)(xc[e] >> 32));
-          }
+      for (int q = 0; q < kPairs; ++q)
+#pragma unroll
+        for (int e = 0; e < kCB; ++e) {
+          const int j = min(j0 + e, nc - 1);
+          mlv[q][e] = __hip_atomic_load(ml0 + (size_t)j * QG + rr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (with_x)
+            xv[q][e] = __hip_atomic_load(src0 + (size_t)j * S + pr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    };
+    auto take_max = [&](int j0) {  // a chunk that saw no key has sum 0
+#pragma unroll
+      for (int q = 0; q < kPairs; ++q)
+#pragma unroll
+        for (int e = 0; e < kCB; ++e) {
+          const float m = __uint_as_float((uint32_t)mlv[q][e]), l = __uint_as_float((uint32_t)(mlv[q][e] >> 32));
+          if (j0 + e < nc && l > 0.f) mx[q] = fmaxf(mx[q], m);
+        }
+    };
+    auto add = [&](int j0) {  // weights exp2(m_j - max), sums in chunk order
+#pragma unroll
+      for (int q = 0; q < kPairs; ++q)
+#pragma unroll
+        for (int e = 0; e < kCB; ++e) {
+          const float m = __uint_as_float((uint32_t)mlv[q][e]), l = __uint_as_float((uint32_t)(mlv[q][e] >> 32));
+          const float w = (j0 + e < nc && l > 0.f) ? __builtin_amdgcn_exp2f(m - mx[q]) : 0.f;
+          tot[q] += w * l;
+          o0[q] += w * __uint_as_float((uint32_t)xv[q][e]);
+          o1[q] += w * __uint_as_float((uint32_t)(xv[q][e] >> 32));
+        }
+    };
+    if (nc <= kCB) {  // one batch: every load in flight at once
+      load(0, true);
+      take_max(0);
+      add(0);
+    } else {  // the maxima over every chunk first, then the sums
+      for (int j0 = 0; j0 < nc; j0 += kCB) {
+        load(j0, false);
+        take_max(j0);
+      }
+      for (int j0 = 0; j0 < nc; j0 += kCB) {
+        load(j0, true);
+        add(j0);
+      }
     }
-    const float tot = ctot[r];
-    const int m = r0 + r % nr, h = kvh * G + r / nr;
-    xa_store(a.xa_o, h * HD + 2 * cp, m, a.M, o0 / tot);
-    xa_store(a.xa_o, h * HD + 2 * cp + 1, m, a.M, o1 / tot);
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      if (p0 + q * kThreads >= npair) continue;
+      const int r = rr[q], cp = pr[q] - r * HP;
+      const int m = r0 + r % nr, h = kvh * G + r / nr;
+      xa_store(a.xa_o, h * HD + 2 * cp, m, a.M, o0[q] / tot[q]);
+      xa_store(a.xa_o, h * HD + 2 * cp + 1, m, a.M, o1[q] / tot[q]);
+    }
   }
 }
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   const int g = (t8 / nqb) * kAttnXcds + l % kAttnXcds, qb = t8 % nqb;
   const int ns_ub = a.nsplit[i];
   if (g >= a.Hkv * ns_ub) return;  // padding of the group count to the XCDs
-  const int kvh = g / ns_ub, s = g % ns_ub;
+  const int s = g / a.Hkv, kvh = g - s * a.Hkv;  // splits in order, KV heads fastest: unneeded splits come last
   const int P = a.kv.P[a.rows.seq[i]];
   const int ns = min(max(1, (P + a.kps - 1) / a.kps), ns_ub);  // this sequence's splits (P <= the host's bound)
   if (s >= ns) return;  // past what its context needs

@@ -127,8 +127,8 @@ constexpr size_t kGemmSplitFloats = size_t(8) * 8192 * 64;  // K-split chunk sum
 // workgroup's combine over the chunks of its unit.
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 constexpr int kAttnQG = 16;              // query vectors per query group
-constexpr int kAttnWaves = 8;            // one-group kernel: waves (splits) per chunk
-constexpr int kAttnCombineSlots = 4096;  // one-group kernel: chunks per unit x query vectors, at most
+constexpr int kAttnWaves = 4;            // one-group kernel: waves (splits) per chunk
+constexpr int kAttnMaxCpw = 32;          // one-group kernel: chunks per workgroup at most
 constexpr int kAttnMaxUnits = 16384;     // arrival counters
 hipError_t attn_init();
 
