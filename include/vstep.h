@@ -133,11 +133,26 @@ vs_status vs_model_set_attn_split(vs_model* m, int32_t keys);
 int32_t vs_model_attn_split(const vs_model* m);
 
 /* ---- KV cache ---- */
+/* A paged KV pool of n_blocks blocks of 16 token slots over the caller's
+ * buffer d_kv (vs_kv_bytes bytes; layouts of vs_kv_layer), shared by the
+ * draft and the verify of every sequence (self-speculative decoding page,
+ * §2.3 and §3.3: one cache, one slot per position, the draft's first-L
+ * entries read back by the verify).  The pool must hold finite values when
+ * it is created (zeroed memory will do): attention loads whole 16-slot
+ * blocks and weights slots past a sequence's length by exactly zero, which
+ * keeps them out of the result only if they are finite.  The caller keeps
+ * d_kv alive until vs_kv_destroy, which waits for the device. */
 vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_seqs, int32_t max_blocks_per_seq,
                        void* stream, vs_kv** out);
 void vs_kv_destroy(vs_kv* kv);
 /* Open a sequence able to hold max_len KV slots (prompt + generated tokens
- * + in-round scratch); reserves its blocks from the pool up front. */
+ * + in-round scratch); reserves its blocks from the pool up front and keeps
+ * them until vs_seq_close (the "FlashSpec" page, §4.3 and §5.4, allocates
+ * the KV cache statically for the longest generation; a rollback only moves
+ * the sequence's length back, self-speculative decoding page §3.3, and the
+ * slots past it are rewritten by the next round).  VS_E_NOKV when the pool
+ * has too few free blocks, max_len needs more than max_blocks_per_seq
+ * blocks, or every sequence slot is in use. */
 vs_status vs_seq_open(vs_kv* kv, int32_t max_len, void* stream, int32_t* seq_id);
 /* Declare a context the caller wrote itself: the K/V of slots 0..P-1 of
  * every layer are already in the sequence's blocks (layout of vs_kv_layer),
@@ -148,10 +163,9 @@ vs_status vs_seq_assume(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void
 /* Rewind a sequence that holds a context to its first P positions: KV of
  * slots 0..P-1 is kept as it is, `pending` becomes the token at position P
  * (no KV), committed = P + 1, and later slots become garbage.  P must not
- * exceed the sequence's current KV length (the host checks it against its
- * upper bound of that length; a P between the true length and that bound
- * leaves garbage slots below P).  Errors: VS_E_STATE (not open, no context),
- * VS_E_NOKV (P beyond the bound), VS_E_INVAL (token id). */
+ * exceed the sequence's current KV length, which the call reads back from
+ * the device (it blocks on `stream`).  Errors: VS_E_STATE (not open, no
+ * context), VS_E_NOKV (P beyond the length), VS_E_INVAL (token id). */
 vs_status vs_seq_rewind(vs_kv* kv, int32_t seq, int32_t P, int32_t pending, void* stream);
 vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
 /* Device pointers of the per-sequence state arrays [max_seqs]:
@@ -167,19 +181,33 @@ vs_status vs_kv_sync(vs_kv* kv, void* stream); /* blocks: reads P back */
 /* ---- the round ---- */
 /* Prompt of n tokens (device) through all layers in passes of <= 64 rows;
  * sets P = n and pending = argmax (greedy) or a draw with d_u[32] (sample,
- * softmax at temperature temp) of the last row.  d_logits_last [V] optional. */
+ * softmax at temperature temp) of the last row.  d_logits_last [V] optional.
+ * This is the state every round starts from (self-speculative decoding page,
+ * §4.2: the first draft input is the last accepted token, its position the
+ * accepted length).  VS_E_STATE for a sequence that already holds a context,
+ * VS_E_NOKV past its capacity. */
 vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_tokens, int32_t n, int32_t mode,
                      float temp, const double* d_u, float* d_logits_last, void* stream);
 
-/* The pages' forward_layers(start, end): layers [start, end) over the rows.
- * Input: token ids (start == 0) or hidden rows [M][d] (start > 0).  Writes
- * each layer's K/V at the rows' slots.  d_hidden_out [M][d] optional. */
+/* forward_layers(start, end) of the self-speculative decoding page (§4.2,
+ * §4.3: one decoder over a shared cache, run from any start layer to any end
+ * layer at a position offset): layers [start, end) over the batch rows.
+ * Input: token ids (start == 0) or hidden rows [M][d] (start > 0), rows in
+ * batch order.  Writes each layer's K/V at the rows' slots (P + in-round
+ * index).  d_hidden_out [M][d] optional (the hidden rows after layer end-1,
+ * before any final norm).  Errors as vs_verify. */
 vs_status vs_forward_layers(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start, int32_t end,
                             const int32_t* d_tokens, const float* d_hidden_in, float* d_hidden_out, void* stream);
-/* Final RMSNorm + LM head of hidden rows [M][d] -> logits [M][V]. */
+/* Final RMSNorm + LM head of hidden rows [M][d] -> logits [M][V] (fp32).
+ * The page applies the final norm also after the exit layer (self-
+ * speculative decoding page, §3.1 and §4.2).  M in 1..max_rows of the
+ * model (VS_E_SHAPE otherwise). */
 vs_status vs_head(vs_model* m, int32_t M, const float* d_hidden, float* d_logits, void* stream);
 
-/* Chain draft of k[i] tokens for each sequence (host array, 0..16): k[i]
+/* Chain draft (self-speculative decoding page, §2.1 and §4.2: the first L
+ * layers + final norm + head, k serial steps, each writing its first-L KV
+ * into the shared cache at slot P + s; §3.3 for the reuse by the verify) of
+ * k[i] tokens for each sequence (host array, 0..16): k[i]
  * serial steps of layers 0..L-1 + final norm + head, then a finishing
  * first-L pass over the last draft token.  Greedy takes the argmax; sample
  * draws from softmax(z/temp) with uniform slot s of d_u[i][48].
@@ -212,12 +240,31 @@ vs_status vs_draft_tree(vs_model* m, vs_kv* kv, int32_t seq, int32_t topk, int32
                         int32_t* d_tokens, int32_t* d_depth, uint64_t* d_mask, int32_t* d_parent, float* d_hidden_L,
                         float* d_level_logits, void* stream);
 
-/* Verify: layers start_layer..N-1 over the batch rows (input hidden_L rows,
- * or token ids when start_layer == 0), then the head -> d_logits [M][V]. */
+/* Verify (self-speculative decoding page, §4.3: one forward over the k+1
+ * rows from the exit layer at position offset P, reusing the draft's
+ * first-L KV, §2.3; "FlashSpec" page, §2.2 and §3.2, for a tree: the rows
+ * in level order with ancestor masks and per-node positions P + depth):
+ * layers start_layer..N-1 over the batch rows (input hidden_L rows [M][d],
+ * or token ids [M] when start_layer == 0), then the final norm and head ->
+ * d_logits [M][V] fp32, rows in batch order.  Writes the rows' K/V of layers
+ * start_layer..N-1 at slots P + in-round index.  Enqueues only (no host
+ * synchronisation).  Depth and mask arrays are device data and are not
+ * checked: a mask bit must name an earlier row of the same sequence, or the
+ * row itself.  Errors: VS_E_INVAL (start layer, NULL buffers, a sequence
+ * listed twice), VS_E_SHAPE (more than 64 rows for a sequence, more than the
+ * model's max_rows or VS_MAX_PASS_ROWS in all, a pass the attention
+ * workspace cannot hold), VS_E_NOKV (rows past a sequence's capacity),
+ * VS_E_STATE (sequence not open or without context). */
 vs_status vs_verify(vs_model* m, vs_kv* kv, const vs_batch* b, int32_t start_layer, const int32_t* d_tokens,
                     const float* d_hidden_in, float* d_logits, void* stream);
 
-/* Accept.  Greedy (any mask shape): walk from row 0 of each sequence to the
+/* Accept (self-speculative decoding page, §2.4 and §4.3: min(1, p/q) left
+ * to right, residual max(0, p - q) renormalised on the first reject, p
+ * itself if that is empty, a bonus draw from the last row when all pass;
+ * "DSpark" page, §2.1, for greedy block verification; "FlashSpec" page,
+ * §2.2, for the longest accepted root-to-leaf path of a tree; the
+ * "推测解码" page, §2.2, for the three-stage flow).
+ * Greedy (any mask shape): walk from row 0 of each sequence to the
  * child whose token equals the argmax of the current row (lowest id on
  * ties); a = path length, y = argmax at the last node.  Sample (chain only):
  * for i < k test u[16+i] < min(1, p_i(d)/q_i(d)) with p = softmax(z/temp) of
@@ -258,9 +305,15 @@ vs_status vs_accept_noalloc(int32_t vocab, const vs_batch* b, int32_t mode, floa
                             const float* d_logits, const float* d_draft_logits, const double* d_u, int32_t* d_result,
                             void* stream);
 
-/* Commit: P += a + 1, pending = y, committed += a + 1.  For masks that are not
+/* Commit (self-speculative decoding page, §3.3: the write position goes back
+ * to the accepted length, and the cache position must equal the sequence
+ * length after it; §4.5: each sequence of a batch advances by its own
+ * count): P += a + 1, pending = y, committed += a + 1, read from d_result
+ * on the device (no host synchronisation).  For masks that are not
  * chains, first copies the K/V (all layers) of the accepted path rows
- * P + path[i] to slots P + 1 + i. */
+ * P + path[i] to slots P + 1 + i (the "FlashSpec" page, §2.2: the accepted
+ * path is what the next round continues from).  Same batch as the accept
+ * that wrote d_result. */
 vs_status vs_commit(vs_model* m, vs_kv* kv, const vs_batch* b, const int32_t* d_result, void* stream);
 
 /* One chain round: vs_draft + vs_verify(exit_layer) + vs_accept + vs_commit

@@ -521,11 +521,19 @@ vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
       chunks[i] = (ns + 1 + kAttnWaves - 1) / kAttnWaves;
       cmax = std::max(cmax, chunks[i]);
     }
+    // Once the units alone give every CU one (one workgroup per unit), a
+    // second workgroup per unit costs more than it hides: at 8 sequences x
+    // 2048 keys (256 units) one workgroup per unit took 71.6 us against 78.0
+    // us at two (each CU then streams two workgroups' keys, and every unit
+    // pays the combine).
+    long units_one = 0;
+    for (int i = 0; i < rm.n_seq; ++i)
+      if (!grp[i]) units_one += c.n_kv_heads;
     constexpr double kStart = 5.0, kChunk = 3.0, kCombine = 5.0;  // us
     const int ncu = 2 * std::max(1, m->n_cu);  // workgroup slots
     double best = 1e30;
-    int best_cpw = 1;
-    for (int cpw = 1; cpw <= std::min(cmax, kAttnMaxCpw); ++cpw) {
+    int best_cpw = units_one >= m->n_cu ? std::min(cmax, kAttnMaxCpw) : 1;
+    for (int cpw = 1; units_one < m->n_cu && cpw <= std::min(cmax, kAttnMaxCpw); ++cpw) {
       if (cpw > 1 && (cmax + cpw - 1) / cpw == (cmax + cpw - 2) / (cpw - 1)) continue;  // same split of the longest
       long wgs = 0;
       bool multi = false;
