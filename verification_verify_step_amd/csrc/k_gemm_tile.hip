@@ -491,6 +491,7 @@ void go_epi(const GemmArgs& a, const TileShape& sh, hipStream_t st, Ev ev) {
   switch (sh.mw) {
     case 1: go_ntw<EPI, 1, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
     case 2: go_ntw<EPI, 2, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
+    case 4: go_ntw<EPI, 4, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
     default: go_ntw<EPI, 3, false>(a, sh.n_mblk, sh.ntw, st, ev); break;
   }
 }
@@ -499,7 +500,8 @@ void go_epi(const GemmArgs& a, const TileShape& sh, hipStream_t st, Ev ev) {
 
 // Up to 4 m-tiles (64 rows, bound by the weight stream): blocks of 2
 // m-tiles, which keeps more workgroups and waves in flight (measured at 17,
-// 40 and 64 rows on the 7B QKV, gate/up and head); the narrow matrices
+// 40 and 64 rows on the 7B QKV, gate/up and head), except on the widest
+// matrices at 3 or 4 m-tiles (one block, below); the narrow matrices
 // split K over workgroups as well (gemm_tile_split).  More rows (bound by
 // MFMA issue and LDS reads): blocks of 3 m-tiles, whose waves take 4
 // n-tiles each where the grid stays full (an LDS fragment then feeds 8
@@ -524,6 +526,16 @@ TileShape gemm_tile_shape(int n_tiles, int M, int ntw) {
       }
   }
   if (sh.mw > 3 && sh.ntw == 4) sh.ntw = 2;
+  // The widest matrices (>= 1024 n-tiles: the 7B gate/up and head) at 33 to
+  // 64 rows: one row block of all rows (3 or 4 m-tiles) with 2 n-tiles per
+  // wave.  Measured on gate/up: 54.0 against 61-63 us at 40 rows, 62.3
+  // against 66-68 us at 64 rows; QKV (768 n-tiles) lost (51-59 against
+  // 42-47 us) and keeps two 32-row blocks.
+  if (!sh.split && mt >= 3 && mt <= 4 && n_tiles >= 1024 && ntw != 1 && ntw != 4) {
+    sh.mw = mt;
+    sh.n_mblk = 1;
+    sh.ntw = 2;
+  }
   return sh;
 }
 
