@@ -11,6 +11,7 @@
 
 #include "attn_group.h"
 #include "kernels.h"
+#include "gemm_dev.h"
 #include "misc.h"
 
 using namespace vs;
@@ -848,6 +849,7 @@ vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const 
     p.k_steps = K / 32;
     p.row_off = row_off;
     p.map = map;
+    p.wide32 = gemm_wide32(W.n_tiles, W.k_steps) ? 1 : 0;
     launch_pack(p, st);
   };
   switch (tensor) {

@@ -14,6 +14,7 @@ namespace vs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -40,6 +41,35 @@ __host__ __device__ __forceinline__ bool gemm_tile_fits(int n_tiles, int k_steps
   if (n_tiles < 512) return gemm_tile_split(n_tiles, k_steps, M);
   return k_steps % (gemm_k_chunks(n_tiles) * 8) == 0;
 }
+
+// The widest matrices (>= 1024 n-tiles of 16 columns, an even count, K
+// chunks that fit the row-tiled form: gate/up and the head at the 7B and 70B
+// shapes) use v_mfma_f32_32x32x16_bf16 in both forms.  On gfx950 it issues
+// about twice the flops per second of the 16x16x32 instruction (2.1-2.4
+// against 0.9-1.5 PFLOP/s in a register-only loop at one to eight waves per
+// SIMD) and gets twice the flops out of each activation fragment.  One
+// instruction takes the hi parts of 16 rows (A rows 0-15) and their lo parts
+// (A rows 16-31) against 32 columns over 16 inputs; a matrix's rows see the
+// same instruction, K order and partial-sum grouping in every form.  The
+// other matrices keep the 16x16x32 forms: with 32-column tiles the 7B QKV
+// (768 n-tiles) has 384 skinny workgroups for 256 CUs and measured 1.6 us
+// slower at 6 rows.
+__host__ __device__ __forceinline__ bool gemm_wide32(int n_tiles, int k_steps) {
+  return n_tiles >= 1024 && n_tiles % 2 == 0 && k_steps % (gemm_k_chunks(n_tiles) * 8) == 0;
+}
+// 32x32x16 lane layout (checked on the device): lane l holds A[l % 32][8 (l /
+// 32) .. +8] and B[8 (l / 32) .. +8][l % 32]; result element e of lane l is
+// D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].  Packed weights of a wide matrix:
+// fragment (32-column tile T, k-step s, half h) = 64 lanes x 16 bytes, lane l
+// holding W[32 T + l % 32][32 s + 16 h + 8 (l / 32) .. +8], at
+// ((T * k_steps + s) * 2 + h) * 64 + l.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+// Activation unit (part * 4 + quad) of half h read by lane l for A rows l % 32:
+// rows 0-15 the hi parts, 16-31 the lo parts of the m-tile's 16 rows.
+__device__ __forceinline__ int a32_unit(int lane, int h) { return ((lane & 31) >> 4) * 4 + 2 * h + (lane >> 5); }
 
 // RMSNorm scale from the four strided partial sums S_q (q = group mod 4).
 __device__ __forceinline__ float norm_scale(float s0, float s1, float s2, float s3, float inv_d, float eps) {

@@ -392,6 +392,11 @@ bool gemm_uses_tile(int n_tiles, int k_steps, int M, int cfg) {
 }
 
 int launch_gemm(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  // the wide matrices: the 32x32x16 forms (skinny up to 8 rows, else row-tiled)
+  if (gemm_wide32(a.n_tiles, a.k_steps)) {
+    if (a.M <= 8) return launch_gemm32(a, epi, st, ev0, ev1);
+    return launch_gemm_tile32(a, epi, a.cfg >= kGemmCfgTile ? a.cfg - kGemmCfgTile : 0, st, ev0, ev1);
+  }
   if (gemm_uses_tile(a.n_tiles, a.k_steps, a.M, a.cfg)) return launch_gemm_tile(a, epi, a.cfg - kGemmCfgTile, st, ev0, ev1);
   const Ev ev{ev0, ev1};
   int cfg = (a.cfg > 0 && a.cfg < kGemmCfgs) ? a.cfg : gemm_pick(a.n_tiles, a.k_steps, a.M);

@@ -439,6 +439,16 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   }
 }
 
+void launch_row_scale(const GemmArgs& a, hipStream_t st, hipEvent_t start) {
+  const dim3 sg((a.M + kScaleRows - 1) / kScaleRows);
+  if (start != nullptr)
+    hipExtLaunchKernelGGL(row_scale_kernel, sg, dim3(4 * kScaleRows), 0, st, start, nullptr, 0, a.ss, a.ss_groups, a.ld,
+                          a.m0, a.M, a.inv_d, a.eps, a.rs_buf);
+  else
+    hipLaunchKernelGGL(row_scale_kernel, sg, dim3(4 * kScaleRows), 0, st, a.ss, a.ss_groups, a.ld, a.m0, a.M, a.inv_d,
+                       a.eps, a.rs_buf);
+}
+
 namespace {
 
 struct Ev {
@@ -454,13 +464,7 @@ void go_tile(const GemmArgs& a, int n_mblk, hipStream_t st, Ev ev) {
   GemmArgs g = a;
   hipEvent_t start = ev.a;
   if (a.ss != nullptr) {
-    const dim3 sg((a.M + kScaleRows - 1) / kScaleRows);
-    if (start != nullptr)
-      hipExtLaunchKernelGGL(row_scale_kernel, sg, dim3(4 * kScaleRows), 0, st, start, nullptr, 0, a.ss, a.ss_groups,
-                            a.ld, a.m0, a.M, a.inv_d, a.eps, a.rs_buf);
-    else
-      hipLaunchKernelGGL(row_scale_kernel, sg, dim3(4 * kScaleRows), 0, st, a.ss, a.ss_groups, a.ld, a.m0, a.M, a.inv_d,
-                         a.eps, a.rs_buf);
+    launch_row_scale(a, st, start);
     start = nullptr;
     g.rs = a.rs_buf;
   }

@@ -29,9 +29,13 @@ __global__ void pack_kernel(PackArgs a) {
       p = r;
     }
     p += a.row_off;
-    const int tile = p / 16, lane = (p % 16) + 16 * j;
+    size_t frag;  // 16-byte unit of (column p, inputs 32 s + 8 j .. +8)
+    if (a.wide32)
+      frag = ((((size_t)(p / 32) * a.k_steps + s) * 2 + (j >> 1)) * 64) + (p % 32) + 32 * (j & 1);
+    else
+      frag = ((size_t)(p / 16) * a.k_steps + s) * 64 + (p % 16) + 16 * j;
     const uint4 v = *reinterpret_cast<const uint4*>(a.src + (size_t)r * a.K + 32 * s + 8 * j);
-    *reinterpret_cast<uint4*>(a.dst + (((size_t)tile * a.k_steps + s) * 64 + lane) * 8) = v;
+    *reinterpret_cast<uint4*>(a.dst + frag * 8) = v;
   }
 }
 

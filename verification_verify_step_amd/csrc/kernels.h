@@ -84,6 +84,15 @@ struct TileShape {
 };
 TileShape gemm_tile_shape(int n_tiles, int M, int ntw);
 int launch_gemm_tile(const GemmArgs& a, int epi, int ntw, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// The row-tiled form's per-row norm scales (a.ss -> a.rs_buf), launched
+// before the product; `start` (optional) is stamped at its start.
+void launch_row_scale(const GemmArgs& a, hipStream_t st, hipEvent_t start);
+// The wide matrices (gemm_wide32): 32x32x16 MFMA forms, skinny (up to 8 rows)
+// and row-tiled (tiles of 32 columns, ntw of them per wave).  Both return the
+// number of 16-column groups (= n_tiles).
+int launch_gemm32(const GemmArgs& a, int epi, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+TileShape gemm_tile32_shape(int n_tiles, int M, int ntw);
+int launch_gemm_tile32(const GemmArgs& a, int epi, int ntw, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 struct AttnArgs {
   RowMap rows;

@@ -10,6 +10,7 @@ struct PackArgs {
   const uint16_t* src;  // canonical [rows][K]
   uint16_t* dst;        // packed matrix
   int rows, K, k_steps, row_off, map, hd;
+  int wide32;           // fragments of 32 columns x 16 inputs (gemm_wide32)
 };
 
 struct BlockSetArgs {
