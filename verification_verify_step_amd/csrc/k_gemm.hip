@@ -359,7 +359,7 @@ struct Ev {
 
 template <int EPI, int MT, int NTW, int NW>
 static void go(const GemmArgs& a, hipStream_t st, Ev ev) {
-  constexpr int PD = MT >= 4 ? (NTW == 2 ? 2 : 4) : (NTW == 2 ? 4 : 8);
+  constexpr int PD = MT >= 3 ? (NTW == 2 ? 2 : 4) : (NTW == 2 ? 4 : 8);
   if (ev.a != nullptr || ev.b != nullptr)
     hipExtLaunchKernelGGL((gemm_kernel<MT, NTW, NW, PD, EPI>), dim3(a.n_tiles / NTW), dim3(NW * 64), 0, st, ev.a,
                           ev.b, 0, a);
@@ -383,6 +383,7 @@ static void launch_epi(const GemmArgs& a, int cfg, hipStream_t st, Ev ev) {
   if (a.M <= 8) launch_mt<EPI, 0>(a, cfg, st, ev);
   else if (mt == 1) launch_mt<EPI, 1>(a, cfg, st, ev);
   else if (mt == 2) launch_mt<EPI, 2>(a, cfg, st, ev);
+  else if (mt == 3) launch_mt<EPI, 3>(a, cfg, st, ev);
   else launch_mt<EPI, 4>(a, cfg, st, ev);
 }
 
