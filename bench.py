@@ -62,6 +62,11 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n}))
 
 
+# The sources of the dominant family's kernels (the skinny GEMMs and their
+# dispatch); a change to any of them voids the stored counter readings.
+GEMM_SOURCES = ("k_gemm.hip", "k_gemm32.hip", "gemm_dev.h", "kernels.h", "common.h")
+
+
 def pmc_traffic(workload, family):
     """HBM bytes per launch of `family` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy's readings), or
@@ -76,7 +81,7 @@ def pmc_traffic(workload, family):
             k, v = line.rsplit(":", 1)
             kv[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "gemm_dev.h", "kernels.h", "common.h"):
+    for f in GEMM_SOURCES:
         h.update(open(os.path.join(ROOT, "verification_verify_step_amd", "csrc", f), "rb").read())
     if kv.get("sources_sha256_16") != h.hexdigest()[:16]:
         return None

@@ -171,9 +171,10 @@ vs_status vs_seq_close(vs_kv* kv, int32_t seq_id);
 /* Device pointers of the per-sequence state arrays [max_seqs]:
  * P (KV length), pending token, committed count (read-only for callers). */
 vs_status vs_kv_state(vs_kv* kv, int32_t** d_P, int32_t** d_pending, int32_t** d_committed);
-/* Device pointers of layer `layer`'s K pool [n_blocks][Hkv][16 keys][hd],
- * V pool [n_blocks][Hkv][hd][16 keys] (bf16) and the block table
- * [max_seqs][max_blocks_per_seq] (int32). */
+/* Device pointers of layer `layer`'s K pool [n_blocks][Hkv][hd/8][16 keys][8]
+ * (each block's K tile cut into 8-dim pieces, piece-major: key j, dim d at
+ * ((d/8)*16 + j)*8 + d%8), V pool [n_blocks][Hkv][hd][16 keys] (bf16) and the
+ * block table [max_seqs][max_blocks_per_seq] (int32). */
 vs_status vs_kv_layer(vs_kv* kv, int32_t layer, void** d_k, void** d_v, int32_t** d_block_table);
 /* Host-side upper bound of P for a sequence (exact after vs_kv_sync). */
 vs_status vs_kv_sync(vs_kv* kv, void* stream); /* blocks: reads P back */

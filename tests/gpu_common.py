@@ -50,7 +50,7 @@ def kv_slots(e, seq, layer, slots):
     blocks = bt[seq].cpu().numpy()[slots // 16]
     idx_b = torch.from_numpy(blocks.astype(np.int64)).cuda()
     idx_o = torch.from_numpy((slots % 16).astype(np.int64)).cuda()
-    k = K[idx_b, :, idx_o, :].permute(1, 0, 2).double().cpu().numpy()
+    k = K[idx_b, :, :, idx_o, :].reshape(len(slots), K.shape[1], -1).permute(1, 0, 2).double().cpu().numpy()
     v = V[idx_b, :, :, idx_o].permute(1, 0, 2).double().cpu().numpy()
     return k, v
 

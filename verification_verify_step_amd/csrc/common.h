@@ -33,12 +33,27 @@ struct RowMap {
 };
 
 struct KvView {
-  uint16_t* k;            // layer pool [n_blocks][Hkv][16][hd] bf16
-  uint16_t* v;
+  uint16_t* k;            // layer pool [n_blocks][Hkv][hd/8][16][8] bf16 (kv_tile, k_tile_off)
+  uint16_t* v;            // layer pool [n_blocks][Hkv][hd][16]
   const int* P;           // [max_seqs]
   const int* bt;          // [max_seqs][bps]
   int bps;
 };
+
+// Element offset of the (block, KV head) tile of kBlock keys x hd dims in a
+// layer pool [n_blocks][Hkv][tile].
+__device__ __forceinline__ size_t kv_tile(int blk, int kvh, int Hkv, int hd) {
+  return ((size_t)blk * Hkv + kvh) * (size_t)(kBlock * hd);
+}
+
+// Offset of key slot j (0..15), dim d inside one (block, KV head) K tile:
+// the dims are cut into 8-dim pieces and the tile is piece-major,
+// [hd/8][16 keys][8 dims].  A wave's 16x16x32 MFMA operand for one k-step
+// (16 keys x 4 pieces) is then 1 KiB of consecutive bytes, so each of its
+// loads fills whole cache lines instead of half-lines of 16 key rows.
+__device__ __forceinline__ size_t k_tile_off(int j, int d) {
+  return (size_t)(d >> 3) * (kBlock * 8) + j * 8 + (d & 7);
+}
 
 // --------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t).

@@ -9,10 +9,13 @@
 // may leak).  All query rows and grouped heads of a KV head share one read
 // of each K/V block.
 //
-// KV layout per layer: K [block][kv head][16 keys][head_dim], V [block][kv
-// head][head_dim][16 keys].  With that layout both MFMA operands come straight
-// from HBM as 16-byte pieces: for S = Q.K^T a lane reads 8 dims of one key
-// row, for O += P.V a lane reads 8 consecutive keys of one dim.
+// KV layout per layer: K [block][kv head][head_dim/8][16 keys][8 dims], V
+// [block][kv head][head_dim][16 keys].  With that layout both MFMA operands
+// come straight from HBM as 16-byte pieces: for S = Q.K^T a lane reads 8 dims
+// of one key, and the 64 lanes of one k-step read 1 KiB of consecutive bytes
+// (whole cache lines: a vector L1 miss costs one 128-byte request, and the
+// number of misses a CU can keep in flight is what bounds its bandwidth);
+// for O += P.V a lane reads 8 consecutive keys of one dim.
 //
 // Split structure, fixed by absolute key index and the sequence's own KV
 // length P (read here on the device), so that a row's bits never depend on
@@ -103,7 +106,6 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
   const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
   const int mrow = lane & 15, kq = lane >> 4;
-  const size_t head_stride = (size_t)kBlock * HD;  // elements per (block, kv head)
 
   // Steps of 32 keys aligned to blocks: [base, base+32) covers slots of two
   // blocks.  This wave's split in chunk c: a committed split is one step;
@@ -145,13 +147,14 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   auto load_k = [&]() {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t* kr = a.kv.k + ((size_t)(t ? nb1 : nb0) * a.Hkv + kvh) * head_stride + mrow * HD + 8 * kq;
+      const uint16_t* kr = a.kv.k + kv_tile(t ? nb1 : nb0, kvh, a.Hkv, HD) + k_tile_off(mrow, 8 * kq);
 #pragma unroll
-      for (int s = 0; s < KSQ; ++s) kb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s));
+      for (int s = 0; s < KSQ; ++s)
+        kb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + k_tile_off(0, 32 * s)));
     }
   };
   auto load_v = [&]() {  // lane: keys 8*kq .. +8 of dim 16t + lane%16, i.e. block kq/2, keys 8*(kq%2) ..
-    const uint16_t* vr = a.kv.v + ((size_t)((kq >> 1) ? nb1 : nb0) * a.Hkv + kvh) * head_stride + 8 * (kq & 1);
+    const uint16_t* vr = a.kv.v + kv_tile((kq >> 1) ? nb1 : nb0, kvh, a.Hkv, HD) + 8 * (kq & 1);
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
       vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (size_t)(16 * t + mrow) * kBlock));

@@ -99,13 +99,12 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   // Block-table entries of the split, one per lane (two per step).
   const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
   const int btreg = bt[min(first / kBlock + lane, a.kv.bps - 1)];
-  const size_t head_stride = (size_t)kBlock * HD;  // elements per (block, kv head)
   const uint16_t* const kpool = a.kv.k;
   const uint16_t* const vpool = a.kv.v;
   __builtin_assume(threadIdx.x < kThreads);
 
   // piece x of a step: K (x < 4 HD) or V, block (x / 2 HD) % 2, 16-byte
-  // offset x % 2 HD inside that block's [16][HD] tile (V: [HD][16])
+  // offset x % 2 HD inside that block's tile (K: [HD/8][16][8], V: [HD][16])
   auto load_step = [&](int t, u32x4(&r)[PPT]) {
     const int nb0 = __builtin_amdgcn_readlane(btreg, 2 * t);
     const int nb1 = __builtin_amdgcn_readlane(btreg, 2 * t + 1);
@@ -113,7 +112,7 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
     for (int j = 0; j < PPT; ++j) {
       const int x = threadIdx.x + j * kThreads;
       const int isv = x / (4 * HD), blk = (x / (2 * HD)) & 1, off = x % (2 * HD);
-      const uint16_t* src = (isv ? vpool : kpool) + ((size_t)(blk ? nb1 : nb0) * a.Hkv + kvh) * head_stride;
+      const uint16_t* src = (isv ? vpool : kpool) + kv_tile(blk ? nb1 : nb0, kvh, a.Hkv, HD);
       r[j] = reinterpret_cast<const u32x4*>(src)[off];
     }
   };
@@ -124,7 +123,7 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
       const int x = threadIdx.x + j * kThreads;
       const int isv = x / (4 * HD), blk = (x / (2 * HD)) & 1, off = x % (2 * HD);
       uint16_t* dst = isv ? d + KPART + blk * kBlock * HD + off * 8
-                          : d + (blk * kBlock + off / (HD / 8)) * KROW + (off % (HD / 8)) * 8;
+                          : d + (blk * kBlock + off % kBlock) * KROW + (off / kBlock) * 8;
       *reinterpret_cast<u32x4*>(dst) = r[j];
     }
   };

@@ -287,11 +287,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           const bool is_k = hb < a.H + a.Hkv;
           const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
           const int dst = pre_kv[j];  // block * 16 + offset in the block
-          const size_t head = ((size_t)(dst / kBlock) * a.Hkv + kvh) * kBlock * hd;
-          if (is_k) {  // K rows: [16 keys][hd]
-            uint16_t* kp = a.kv.k + head + (size_t)(dst % kBlock) * hd;
-            kp[ci] = f2bf(o0);
-            kp[ci + half] = f2bf(o1);
+          const size_t head = kv_tile(dst / kBlock, kvh, a.Hkv, hd);
+          if (is_k) {  // K tile: piece-major (k_tile_off)
+            uint16_t* kp = a.kv.k + head;
+            kp[k_tile_off(dst % kBlock, ci)] = f2bf(o0);
+            kp[k_tile_off(dst % kBlock, ci + half)] = f2bf(o1);
           } else {     // V columns: [hd][16 keys]
             uint16_t* vp = a.kv.v + head + (dst % kBlock);
             vp[(size_t)ci * kBlock] = f2bf(o0);

@@ -208,11 +208,11 @@ __global__ __launch_bounds__(NW * 64) void gemm32_kernel(const GemmArgs a) {
           const bool is_k = hb < a.H + a.Hkv;
           const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
           const int dst = pre_kv[j];
-          const size_t head = ((size_t)(dst / kBlock) * a.Hkv + kvh) * kBlock * hd;
+          const size_t head = kv_tile(dst / kBlock, kvh, a.Hkv, hd);
           if (is_k) {
-            uint16_t* kp = a.kv.k + head + (size_t)(dst % kBlock) * hd;
-            kp[ci] = f2bf(o0);
-            kp[ci + half] = f2bf(o1);
+            uint16_t* kp = a.kv.k + head;
+            kp[k_tile_off(dst % kBlock, ci)] = f2bf(o0);
+            kp[k_tile_off(dst % kBlock, ci + half)] = f2bf(o1);
           } else {
             uint16_t* vp = a.kv.v + head + (dst % kBlock);
             vp[(size_t)ci * kBlock] = f2bf(o0);

@@ -384,9 +384,9 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
             const bool is_k = rot;
             const int kvh = is_k ? hb - a.H : hb - a.H - a.Hkv;
             const int dst = kvr[mt][r];
-            const size_t head = ((size_t)(dst / kBlock) * a.Hkv + kvh) * kBlock * hd;
+            const size_t head = kv_tile(dst / kBlock, kvh, a.Hkv, hd);
             if (is_k)
-              a.kv.k[head + (size_t)(dst % kBlock) * hd + el] = f2bf(o);
+              a.kv.k[head + k_tile_off(dst % kBlock, el)] = f2bf(o);
             else
               a.kv.v[head + (size_t)el * kBlock + dst % kBlock] = f2bf(o);
           }

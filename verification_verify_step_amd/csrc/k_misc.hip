@@ -593,7 +593,7 @@ void launch_accept(const AcceptArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Tree compaction: K/V of accepted path rows P + path[j] -> P + 1 + j in
-// every layer (K rows [16][hd] per block and head, V columns [hd][16]).
+// every layer (tiles kv_tile; K piece-major, k_tile_off; V columns [hd][16]).
 // Sources increase along the path and never lie below their destination, so
 // copying j in increasing order per element is safe.
 __global__ void compact_kernel(CommitArgs a) {
@@ -605,7 +605,6 @@ __global__ void compact_kernel(CommitArgs a) {
   const int sq = a.rows.seq[i];
   const int P = a.P[sq];
   uint16_t* pool = is_v ? a.vpool[layer] : a.kpool[layer];
-  const size_t head = (size_t)kBlock * a.hd;  // elements per (block, kv head)
   for (int e = threadIdx.x; e < a.Hkv * a.hd; e += blockDim.x) {  // one (kv head, dim) per thread
     const int kvh = e / a.hd, d = e % a.hd;
     for (int j = 0; j < n_path; ++j) {
@@ -613,12 +612,12 @@ __global__ void compact_kernel(CommitArgs a) {
       if (r < 1 || r >= nr) break;  // a path row outside this sequence's rows
       const int src = P + r, dst = P + 1 + j;
       if (src == dst) continue;
-      const size_t bs = ((size_t)a.bt[sq * a.bps + src / kBlock] * a.Hkv + kvh) * head;
-      const size_t bd = ((size_t)a.bt[sq * a.bps + dst / kBlock] * a.Hkv + kvh) * head;
+      const size_t bs = kv_tile(a.bt[sq * a.bps + src / kBlock], kvh, a.Hkv, a.hd);
+      const size_t bd = kv_tile(a.bt[sq * a.bps + dst / kBlock], kvh, a.Hkv, a.hd);
       if (is_v)
         pool[bd + (size_t)d * kBlock + dst % kBlock] = pool[bs + (size_t)d * kBlock + src % kBlock];
       else
-        pool[bd + (size_t)(dst % kBlock) * a.hd + d] = pool[bs + (size_t)(src % kBlock) * a.hd + d];
+        pool[bd + k_tile_off(dst % kBlock, d)] = pool[bs + k_tile_off(src % kBlock, d)];
     }
   }
 }

@@ -72,11 +72,12 @@ class Engine:
                 for ptr in B.vs_kv_state(self.kv)]
 
     def kv_layer(self, layer):
-        """Views of layer `layer`: K [blocks][Hkv][16][hd], V [blocks][Hkv][hd][16], block table."""
+        """Views of layer `layer`: K [blocks][Hkv][hd/8][16][8] (each block's K tile is cut
+        into 8-dim pieces, piece-major), V [blocks][Hkv][hd][16], block table."""
         k, v, bt = B.vs_kv_layer(self.kv, layer)
         c = self.cfg
         n = self.n_blocks * c.n_kv_heads * 16 * c.head_dim
-        kt = _view(self.kvbuf, k, n * 2).view(torch.bfloat16).view(self.n_blocks, c.n_kv_heads, 16, c.head_dim)
+        kt = _view(self.kvbuf, k, n * 2).view(torch.bfloat16).view(self.n_blocks, c.n_kv_heads, c.head_dim // 8, 16, 8)
         vt = _view(self.kvbuf, v, n * 2).view(torch.bfloat16).view(self.n_blocks, c.n_kv_heads, c.head_dim, 16)
         btt = _view(self.kvbuf, bt, self.max_seqs * self.bps * 4).view(torch.int32).view(self.max_seqs, self.bps)
         return kt, vt, btt
