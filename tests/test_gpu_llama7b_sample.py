@@ -99,6 +99,27 @@ def test_layer_parity_40_rows(ctx, layer):
         assert err <= 1e-3 * scale + 1e-4, (layer, i, err, scale)
 
 
+def test_layer_rows_identical_alone_and_in_the_pass(ctx):
+    """A request's rows of one verify layer carry the same bits alone (5
+    rows: 32 attention units, one chunk per workgroup and the cross-workgroup
+    combine; skinny GEMMs) as inside the 40-row pass (256 units: one
+    workgroup per unit runs all 17 chunks; 40-row GEMM forms).  Both passes
+    append the same in-round K/V, since the QKV rows do not depend on the
+    pass either."""
+    e, seqs, batch = ctx["e"], ctx["seqs"], ctx["batch"]
+    layer = CFG.exit_layer
+    X, toks = ctx["hL"], ctx["toks"]
+    Y = _forward(e, batch, layer, layer + 1, toks, X)
+    torch.cuda.synchronize()
+    for i in (0, 5):
+        rs = slice(i * (K + 1), (i + 1) * (K + 1))
+        out = torch.empty((K + 1, CFG.d_model), dtype=torch.float32, device="cuda")
+        B.vs_forward_layers(e.model, e.kv, B.make_batch([seqs[i]], [K + 1]), layer, layer + 1, toks[rs].data_ptr(),
+                            X[rs].data_ptr(), out.data_ptr(), e.stream)
+        torch.cuda.synchronize()
+        assert torch.equal(out, Y[rs]), (i, (out - Y[rs]).abs().max().item())
+
+
 def test_head_and_stochastic_accept(ctx):
     """Verify logits of sampled rows against the oracle head; accept decisions
     of all 8 requests on the GPU's own logits equal the oracle's

@@ -853,9 +853,11 @@ vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const 
     launch_pack(p, st);
   };
   switch (tensor) {
-    case VS_T_EMBED:
-      hipMemcpyAsync(m->embed, src, (size_t)V * d * 2, hipMemcpyDeviceToDevice, st);
+    case VS_T_EMBED: {
+      const hipError_t e = hipMemcpyAsync(m->embed, src, (size_t)V * d * 2, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_model_set_tensor: %s", hipGetErrorString(e));
       break;
+    }
     case VS_T_ATTN_NORM: launch_bf16_to_f32(src, m->g_attn[layer], d, st); break;
     case VS_T_FFN_NORM: launch_bf16_to_f32(src, m->g_ffn[layer], d, st); break;
     case VS_T_FINAL_NORM: launch_bf16_to_f32(src, m->g_final, d, st); break;
@@ -873,7 +875,7 @@ vs_status vs_model_set_tensor(vs_model* m, int32_t tensor, int32_t layer, const 
 
 void vs_model_destroy(vs_model* m) {
   if (!m) return;
-  for (auto e : m->ev_pool) hipEventDestroy(e);
+  for (auto e : m->ev_pool) (void)hipEventDestroy(e);  // nothing to report from a destructor
   delete m;
 }
 
@@ -1170,9 +1172,11 @@ vs_status vs_prefill(vs_model* m, vs_kv* kv, int32_t seq, const int32_t* d_token
       p.uidx[0] = 0;
       p.dst[0] = seq;
       launch_pick(p, st);
-      if (d_logits_last)
-        hipMemcpyAsync(d_logits_last, m->logits + (size_t)(nc - 1) * m->c.vocab, (size_t)m->c.vocab * 4,
-                       hipMemcpyDeviceToDevice, st);
+      if (d_logits_last) {
+        const hipError_t e = hipMemcpyAsync(d_logits_last, m->logits + (size_t)(nc - 1) * m->c.vocab,
+                                            (size_t)m->c.vocab * 4, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_prefill: %s", hipGetErrorString(e));
+      }
     }
   }
   kv->prefilled[seq] = 1;
@@ -1292,9 +1296,12 @@ void draft_impl(vs_model* m, vs_kv* kv, int n_seq, const int32_t* seq, const int
     if (L > 0) {
       run_layers(m, kv, rm, 0, L, st, d_hidden_L, rows_src.data());
     } else {
-      for (int a = 0; a < Ma; ++a)  // with L = 0 the layer-L input is the embedding itself
-        hipMemcpyAsync(d_hidden_L + (size_t)rows_src[a] * m->c.d_model, m->h + (size_t)a * m->c.d_model,
-                       (size_t)m->c.d_model * 4, hipMemcpyDeviceToDevice, st);
+      // with L = 0 the layer-L input is the embedding itself; a failed copy
+      // is reported by the caller's check_launch (hipGetLastError returns
+      // the last failing call's code)
+      for (int a = 0; a < Ma; ++a)
+        (void)hipMemcpyAsync(d_hidden_L + (size_t)rows_src[a] * m->c.d_model, m->h + (size_t)a * m->c.d_model,
+                             (size_t)m->c.d_model * 4, hipMemcpyDeviceToDevice, st);
     }
     bool need_head = false;
     for (int a = 0; a < Ma; ++a) need_head |= k[act[a]] > s;
@@ -1949,7 +1956,10 @@ vs_status vs_stats_enable(vs_model* m, int32_t on) {
 
 vs_status vs_stats_reset(vs_model* m) {
   if (m == nullptr) return fail(VS_E_INVAL, "vs_stats_reset: null model");
-  for (const Timed& t : m->timed) hipEventSynchronize(t.b);
+  for (const Timed& t : m->timed) {
+    const hipError_t e = hipEventSynchronize(t.b);
+    if (e != hipSuccess) return fail(VS_E_DEVICE, "vs_stats_reset: %s", hipGetErrorString(e));
+  }
   m->timed.clear();
   m->ev_used = 0;
   m->prev_end = nullptr;
