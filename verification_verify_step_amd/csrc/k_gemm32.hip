@@ -146,10 +146,16 @@ __global__ __launch_bounds__(NW * 64) void gemm32_kernel(const GemmArgs a) {
   }
 
   // ---- cross-wave reduction through LDS, chunks (waves) in order ----
-  __shared__ float red[NW * 64 * 16];
+  // Element e of every lane of wave w is one row of RS floats, lanes
+  // consecutive: the stores of a wave and the reads of 32 consecutive
+  // columns each touch distinct banks, and the half-row padding puts the
+  // next element's row (the next result row, read by the other half-wave)
+  // on the other 32 banks.
+  constexpr int RS = 96;
+  __shared__ float red[NW * 16 * RS];
   __shared__ float rowtmp[8 * NC];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) red[(wave * 64 + lane) * 16 + e] = acc[e];
+  for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * RS + lane] = acc[e];
   __syncthreads();
   // row m (< 8), column c: hi at A row m, lo at A row m + 16, both in lane
   // c + 32 ((m / 4) % 2), elements 4 (m / 8) + m % 4 and that + 8
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(NW * 64) void gemm32_kernel(const GemmArgs a) {
     const int l = c + 32 * ((m >> 2) & 1), e = 4 * (m >> 3) + (m & 3);
     float y = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) y += red[(w * 64 + l) * 16 + e] + red[(w * 64 + l) * 16 + e + 8];
+    for (int w = 0; w < NW; ++w) y += red[(w * 16 + e) * RS + l] + red[(w * 16 + e + 8) * RS + l];
     return y;
   };
 
