@@ -226,6 +226,7 @@ struct vs_kv {
   uint64_t* mirror = nullptr;  // pinned [max_seqs]
   std::vector<unsigned> commit_no, base_no;
   std::vector<int> P_base;
+  std::vector<int> P_known;  // the exact P the bound starts from (last landed commit, else P_base)
   std::vector<std::deque<std::pair<unsigned, int>>> in_flight;  // (commit number, rows) not yet seen
 };
 
@@ -236,7 +237,7 @@ hipStream_t S(void* st) { return reinterpret_cast<hipStream_t>(st); }
 // The bound becomes exact: P is known on the host (in stream order after
 // every earlier commit of the sequence).
 void kv_set_exact(vs_kv* kv, int s, int P) {
-  kv->P_ub[s] = kv->P_base[s] = P;
+  kv->P_ub[s] = kv->P_base[s] = kv->P_known[s] = P;
   kv->base_no[s] = kv->commit_no[s] + 1;
   kv->in_flight[s].clear();
 }
@@ -254,8 +255,17 @@ void kv_refresh(vs_kv* kv, int s) {
   } else {
     bound = kv->P_base[s];
   }
+  kv->P_known[s] = bound;
   for (const auto& c : q) bound += c.second;
   kv->P_ub[s] = bound;
+}
+
+// A lower bound of P: the exact value the upper bound starts from plus one
+// per commit still in flight (a commit advances P by a + 1 >= 1).  With no
+// commit in flight the upper bound is exact.
+int kv_lower(const vs_kv* kv, int s) {
+  const auto& q = kv->in_flight[s];
+  return q.empty() ? kv->P_ub[s] : std::min(kv->P_ub[s], kv->P_known[s] + (int)q.size());
 }
 
 vs_status check_launch(const char* what) {
@@ -554,6 +564,7 @@ vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
     for (int i = 0; i < rm.n_seq; ++i) {
       a.wg_start[i] = (int)wgs;
       a.nsplit[i] = chunks[i];
+      a.wblk[i] = (kv_lower(kv, rm.seq[i]) + rm.win) / kAttnStepKeys * kAttnStepKeys / kBlock;
       wgs += (long)c.n_kv_heads * ((chunks[i] + a.cpw - 1) / a.cpw);
     }
     a.wg_start[rm.n_seq] = (int)wgs;
@@ -942,6 +953,7 @@ vs_status vs_kv_create(vs_model* m, void* d_kv, int32_t n_blocks, int32_t max_se
   kv->commit_no.assign(max_seqs, 0);
   kv->base_no.assign(max_seqs, 1);
   kv->P_base.assign(max_seqs, 0);
+  kv->P_known.assign(max_seqs, 0);
   kv->in_flight.resize(max_seqs);
   if (hipHostMalloc(reinterpret_cast<void**>(&kv->mirror), (size_t)max_seqs * 8, hipHostMallocCoherent) != hipSuccess) {
     (void)hipGetLastError();

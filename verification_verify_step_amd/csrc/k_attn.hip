@@ -51,17 +51,6 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 
 }  // namespace
 
-// Sequence of workgroup b: the last i with wg_start[i] <= b.
-__device__ __forceinline__ int attn_seq_of(const AttnArgs& a, int b) {
-  int lo = 0, hi = a.rows.n_seq - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.wg_start[mid] <= b) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Query vector v of a unit maps to row r0 + v % nr and head kvh*G + v / nr.
 template <int HD, int WV>
 __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
@@ -81,31 +70,70 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   __shared__ int last_wg;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x;
-  if (b >= a.wg_start[a.rows.n_seq]) return;
-  const int i = attn_seq_of(a, b);
+  const int b = blockIdx.x;  // the grid is exactly the pass's wg_start[n_seq] workgroups
+  // Memory round trips before the first scores: (1) every per-sequence field
+  // of the arguments at once, lane l holding sequence l's, the workgroup's
+  // sequence being the last whose first workgroup is <= b; (2) P, the
+  // block-table entries and the query vectors together; (3) K and V.
+  const int ls = min(lane, kMaxSeq - 1);
+  const int ws_l = a.wg_start[ls], sq_l = a.rows.seq[ls], r0_l = a.rows.row_start[ls];
+  const int r1_l = a.rows.row_start[ls + 1], nsp_l = a.nsplit[ls], wb_l = a.wblk[ls];
+  const int i = __popcll(__ballot(lane < a.rows.n_seq && ws_l <= b)) - 1;
   // Workgroups of a sequence in order of their chunks, KV heads fastest:
   // the ones past what the device's context needs (the host lays out its
-  // upper bound) come last and exit as soon as they are dispatched.
-  const int local = b - a.wg_start[i];
+  // upper bound) come last and exit as soon as P is known.
+  const int local = b - __builtin_amdgcn_readlane(ws_l, i);
   const int wgi = local / a.Hkv, kvh = local - wgi * a.Hkv;
-  const int sq = a.rows.seq[i];
-  const int r0 = a.rows.row_start[i];
-  const int nr = a.rows.row_start[i + 1] - r0;
+  const int sq = __builtin_amdgcn_readlane(sq_l, i);
+  const int r0 = __builtin_amdgcn_readlane(r0_l, i);
+  const int nr = __builtin_amdgcn_readlane(r1_l, i) - r0;
+  const int wblk = __builtin_amdgcn_readlane(wb_l, i);
   const int G = a.H / a.Hkv;
   const int nq = min(QR, nr * G);
-  const int P = a.kv.P[sq];
-  const int ns = (P + kStep - 1) / kStep;          // committed splits
-  // + the in-round window; never past the host's layout (P <= its bound)
-  const int n_chunks = min((ns + 1 + WV - 1) / WV, a.nsplit[i]);
   const int c0 = wgi * a.cpw;
+  const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
+  const int mrow = lane & 15, kq = lane >> 4;
+  // Round (2): P, the block-table entries of this wave's steps (read once
+  // into lane-indexed registers so that no K/V load waits on a table load:
+  // lane l of bt_c holds block 2 * (WV c + wave) + l % 2 of chunk c = c0 +
+  // l / 2, its committed split, a workgroup running at most 32 chunks; lane
+  // l of bt_w holds block wblk + l, the window's steps when P is within 64
+  // blocks of the host's lower bound; entries are clamped to the table and
+  // data outside a split is masked), the query vectors and the masks.
+  const int P = a.kv.P[sq];
+  const int bt_c = bt[min(2 * (WV * (c0 + (lane >> 1)) + wave) + (lane & 1), a.kv.bps - 1)];
+  const int bt_w = bt[min(wblk + lane, a.kv.bps - 1)];
+  float4 qraw[KSQ][2];
+  // Visibility masks of the 4 rows this lane holds in S: the pass's masks
+  // if it has them, else a chain's (row idx sees in-round keys 0..idx).  The
+  // loads are unconditional (a pass without masks reads its query buffer
+  // instead) and the choice is made where a mask is used: a branch here
+  // would make the compiler wait for every load in flight at its join.
+  uint64_t mraw[4];
+  const uint64_t* const mbase =
+      a.rows.mask != nullptr ? a.rows.mask + r0 : reinterpret_cast<const uint64_t*>(a.q);
+  {
+    const int gq = min(mrow, nq - 1);
+    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
+#pragma unroll
+    for (int s = 0; s < KSQ; ++s) {
+      qraw[s][0] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq);
+      qraw[s][1] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mraw[r] = mbase[min(4 * kq + r, nq - 1) % nr];
+  }
+  // every request above is issued before the branch on P below
+  asm volatile("" ::: "memory");
+
+  const int ns = (P + kStep - 1) / kStep;  // committed splits
+  // + the in-round window; never past the host's layout (P <= its bound)
+  const int n_chunks = min((ns + 1 + WV - 1) / WV, __builtin_amdgcn_readlane(nsp_l, i));
   if (c0 >= n_chunks) return;  // past what this sequence's context needs
   const int c1 = min(n_chunks, c0 + a.cpw);
   const int nwg = (n_chunks + a.cpw - 1) / a.cpw;  // workgroups of the unit with chunks
   const int unit = i * a.Hkv + kvh;
   const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
-  const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
-  const int mrow = lane & 15, kq = lane >> 4;
 
   // Steps of 32 keys aligned to blocks: [base, base+32) covers slots of two
   // blocks.  This wave's split in chunk c: a committed split is one step;
@@ -123,15 +151,6 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
     }
   };
   u32x4 kb[2][KSQ], vb[NDT];
-  // Block-table entries of this wave's steps, read once into lane-indexed
-  // registers so that no K/V load waits on a table load: lane l of bt_c
-  // holds block 2 * (WV c + wave) + l % 2 of chunk c = c0 + l / 2 (its
-  // committed split; a workgroup runs at most 32 chunks); lane l of bt_w
-  // holds block wfirst / 16 + l of the window's steps.  Entries are clamped to the table; data outside a split
-  // is masked.
-  const int wfirst = wlo / kStep * kStep;
-  const int bt_c = bt[min(2 * (WV * (c0 + (lane >> 1)) + wave) + (lane & 1), a.kv.bps - 1)];
-  const int bt_w = bt[min(wfirst / kBlock + lane, a.kv.bps - 1)];
   int nb0 = 0, nb1 = 0;  // blocks of the step being loaded
   auto blocks_of = [&](int c, int base) {  // step at key `base`, in chunk c
     if (c * WV + wave < ns) {
@@ -139,9 +158,14 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       nb0 = __builtin_amdgcn_readlane(bt_c, l);
       nb1 = __builtin_amdgcn_readlane(bt_c, l + 1);
     } else {
-      const int l = (base - wfirst) / kBlock;
-      nb0 = __builtin_amdgcn_readlane(bt_w, l);
-      nb1 = __builtin_amdgcn_readlane(bt_w, l + 1);
+      const int l = base / kBlock - wblk;
+      if (l >= 0 && l < 63) {
+        nb0 = __builtin_amdgcn_readlane(bt_w, l);
+        nb1 = __builtin_amdgcn_readlane(bt_w, l + 1);
+      } else {  // P far from the host's lower bound: read the two entries
+        nb0 = bt[min(base / kBlock, a.kv.bps - 1)];
+        nb1 = bt[min(base / kBlock + 1, a.kv.bps - 1)];
+      }
     }
   };
   auto load_k = [&]() {
@@ -160,32 +184,12 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (size_t)(16 * t + mrow) * kBlock));
   };
 
-  // Request order: block-table entries of the first step, the query vectors
-  // and masks, then the first K/V step (which waits only for the table
-  // entries); the queries are split while K/V are in flight.
+  // Round (3): the first K/V step; the queries are split while it is in
+  // flight.
   int first, last;
   split_steps(c0, first, last);
-  if (first < last) blocks_of(c0, first);
-  float4 qraw[KSQ][2];
-  uint64_t qmask[4];  // visibility masks of the 4 rows this lane holds in S
-  {
-    const int gq = min(mrow, nq - 1);
-    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
-#pragma unroll
-    for (int s = 0; s < KSQ; ++s) {
-      qraw[s][0] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq);
-      qraw[s][1] = *reinterpret_cast<const float4*>(src + 32 * s + 8 * kq + 4);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * kq + r;
-      const int rl = min(row, nq - 1) % nr;
-      const int idx = a.rows.idx_off + rl;
-      const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + rl] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
-      qmask[r] = row < nq ? mk : 0ull;
-    }
-  }
   if (first < last) {
+    blocks_of(c0, first);
     load_k();
     load_v();
   }
@@ -277,7 +281,11 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
           } else {
             const int slot = base + 16 * t + mrow;
             bool vis = slot >= key_lo && slot < key_hi;
-            if (vis && window) vis = (qmask[r] >> ((slot - key_lo) & 63)) & 1ull;  // count kept in 0..63
+            if (vis && window) {
+              const int rl = min(row, nq - 1) % nr, idx = a.rows.idx_off + rl;
+              const uint64_t mk = a.rows.mask != nullptr ? mraw[r] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+              vis = row < nq && ((mk >> ((slot - key_lo) & 63)) & 1ull);  // count kept in 0..63
+            }
             v[t] = vis ? sacc[t][r] : -INFINITY;
           }
         }

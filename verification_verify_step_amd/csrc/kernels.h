@@ -119,6 +119,11 @@ struct AttnArgs {
   // (one-group) count of sequence i.
   int wg_start[kMaxSeq + 1];
   int nsplit[kMaxSeq];
+  // One-group kernel: the block-table row of the first step of sequence i's
+  // in-round window at the host's lower bound of P, so that the window's
+  // table entries are requested with P itself (a device P outside the 64
+  // entries read from there takes two scalar loads instead).
+  int wblk[kMaxSeq];
   int n_split;      // largest nsplit: the partials' records per unit
   // Partials of a unit (sequence, KV head, query group), record j (split or
   // chunk): o at part[((unit * n_split + j) * qg_size + v) * hd + dim],
