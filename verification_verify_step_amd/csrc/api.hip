@@ -559,6 +559,17 @@ vs_status attn_plan(vs_model* m, vs_kv* kv, const RowMap& rm, AttnPlan* pl) {
       }
     }
     a.cpw = best_cpw;
+    // One workgroup per unit and one per CU (the LDS records leave room for
+    // one workgroup per CU), and each unit's chunk partials (chunks x query
+    // vectors) fit the records: they stay in LDS for the combine.
+    a.lp = 0;
+    if (units_one == m->n_cu && cmax <= kAttnMaxCpw) {
+      a.lp = 1;
+      for (int i = 0; i < rm.n_seq; ++i) {
+        const int nq = std::min(kAttnQG, (rm.row_start[i + 1] - rm.row_start[i]) * G);
+        if (!grp[i] && chunks[i] * nq > kAttnLpRecords) a.lp = 0;
+      }
+    }
     a.kps = kAttnStepKeys;
     long wgs = 0;
     for (int i = 0; i < rm.n_seq; ++i) {

@@ -52,7 +52,10 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 }  // namespace
 
 // Query vector v of a unit maps to row r0 + v % nr and head kvh*G + v / nr.
-template <int HD, int WV>
+// LP: every unit of the pass is one workgroup's and its chunk partials fit
+// kAttnLpRecords records in LDS, where they stay until the combine instead
+// of making a round trip through memory.
+template <int HD, int WV, bool LP>
 __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   constexpr int kThreads = WV * 64;
   constexpr int KSQ = HD / 32;  // k-steps of S over head dims
@@ -68,6 +71,10 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   // and the one after that passes this chunk's barrier first.
   __shared__ float smem[SM_FLOATS];
   __shared__ int last_wg;
+  // LP: chunk partial (chunk j, query v) at lpo[(j * nq + v) * HD], its
+  // (max, sum) at lml[j * nq + v]
+  __shared__ float lpo[LP ? kAttnLpRecords * HD : 1];
+  __shared__ float2 lml[LP ? kAttnLpRecords : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.x;  // the grid is exactly the pass's wg_start[n_seq] workgroups
@@ -364,6 +371,9 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       }
       if (single) {
         xa_store(a.xa_o, (kvh * G + row / nr) * HD + d, r0 + row % nr, a.M, o / l);
+      } else if constexpr (LP) {  // c0 = 0: one workgroup holds every chunk of the unit
+        lpo[(c * nq + row) * HD + d] = o;
+        if (d == 0) lml[c * nq + row] = make_float2(mx, l);
       } else {
         __hip_atomic_store(po + (rec * QG + row) * HD + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
@@ -375,6 +385,34 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
     if (c + 1 < c1) split_steps(c + 1, first, last);
   }
   if (single) return;
+
+  if constexpr (LP) {
+    // The unit's combine from LDS, with the arithmetic of the combine
+    // below: the largest chunk maximum over chunks that saw a key, then
+    // the weights exp2(m_j - max) and the sums in chunk order.
+    constexpr int HP = HD / 2;
+    __syncthreads();
+    for (int p = threadIdx.x; p < nq * HP; p += kThreads) {
+      const int r = p / HP, cp = p - r * HP;
+      float mx = -INFINITY;
+      for (int j = 0; j < n_chunks; ++j) {
+        const float2 ml = lml[j * nq + r];
+        if (ml.y > 0.f) mx = fmaxf(mx, ml.x);
+      }
+      float tot = 0.f, o0 = 0.f, o1 = 0.f;
+      for (int j = 0; j < n_chunks; ++j) {
+        const float2 ml = lml[j * nq + r];
+        const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+        tot += w * ml.y;
+        o0 += w * lpo[(j * nq + r) * HD + 2 * cp];
+        o1 += w * lpo[(j * nq + r) * HD + 2 * cp + 1];
+      }
+      const int m = r0 + r % nr, h = kvh * G + r / nr;
+      xa_store(a.xa_o, h * HD + 2 * cp, m, a.M, o0 / tot);
+      xa_store(a.xa_o, h * HD + 2 * cp + 1, m, a.M, o1 / tot);
+    }
+    return;
+  }
 
   // The partial stores must have completed (written through to device
   // scope) before the workgroup is counted in or the partials are read back.
@@ -483,15 +521,20 @@ hipError_t attn_init() { return hipSuccess; }
 
 void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid(a.wg_start[a.rows.n_seq]);
-#define VS_ATT(HD)                                                                                          \
-  do {                                                                                                      \
-    if (ev0 != nullptr || ev1 != nullptr)                                                                   \
-      hipExtLaunchKernelGGL((attn_kernel<HD, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, ev0, ev1, 0, a); \
-    else                                                                                                    \
-      hipLaunchKernelGGL((attn_kernel<HD, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a);            \
+#define VS_ATT(HD, LP)                                                                                    \
+  do {                                                                                                    \
+    if (ev0 != nullptr || ev1 != nullptr)                                                                 \
+      hipExtLaunchKernelGGL((attn_kernel<HD, kAttnWaves, LP>), grid, dim3(kAttnWaves * 64), 0, st, ev0, ev1, 0, a); \
+    else                                                                                                  \
+      hipLaunchKernelGGL((attn_kernel<HD, kAttnWaves, LP>), grid, dim3(kAttnWaves * 64), 0, st, a);      \
   } while (0)
-  if (a.hd == 128) VS_ATT(128);
-  else VS_ATT(64);
+  if (a.hd == 128) {
+    if (a.lp) VS_ATT(128, true);
+    else VS_ATT(128, false);
+  } else {
+    if (a.lp) VS_ATT(64, true);
+    else VS_ATT(64, false);
+  }
 #undef VS_ATT
 }
 

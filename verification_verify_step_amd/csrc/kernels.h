@@ -113,6 +113,7 @@ struct AttnArgs {
   //    last one also taking the in-round window.
   int kps;
   int cpw;
+  int lp;           // one-group kernel: every unit one workgroup's, chunk partials kept in LDS
   // Workgroups of sequence i: [wg_start[i], wg_start[i+1]), laid out from
   // the host's upper bound of P; workgroups the device's P does not need
   // exit at once.  nsplit[i]: the bound's split (grouped) or chunk
@@ -143,6 +144,7 @@ void launch_attention(const AttnArgs& a, hipStream_t st, hipEvent_t ev0 = nullpt
 constexpr int kAttnQG = 16;              // query vectors per query group
 constexpr int kAttnWaves = 4;            // one-group kernel: waves (splits) per chunk
 constexpr int kAttnMaxCpw = 32;          // one-group kernel: chunks per workgroup at most
+constexpr int kAttnLpRecords = 96;       // one-group kernel: chunk partials one workgroup keeps in LDS
 constexpr int kAttnMaxUnits = 16384;     // arrival counters
 hipError_t attn_init();
 
