@@ -57,48 +57,71 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stg[2 * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x;
-  if (b >= a.wg_start[a.rows.n_seq]) return;
-  int i = 0;
-  {  // the last sequence with wg_start[i] <= b
-    int hi = a.rows.n_seq - 1;
-    while (i < hi) {
-      const int mid = (i + hi + 1) >> 1;
-      if (a.wg_start[mid] <= b) i = mid;
-      else hi = mid - 1;
-    }
-  }
-  const int nr_i = a.rows.row_start[i + 1] - a.rows.row_start[i];
-  const int nqb = ((nr_i * (a.H / a.Hkv) + a.qg_size - 1) / a.qg_size + WV - 1) / WV;
-  const int l = b - a.wg_start[i], t8 = l / kAttnXcds;
+  const int b = blockIdx.x;  // the grid is exactly the pass's wg_start[n_seq] workgroups
+  // Memory round trips before the first step: (1) every per-sequence field
+  // of the arguments at once, lane l holding sequence l's, the workgroup's
+  // sequence being the last whose first workgroup is <= b; (2) P, the
+  // split's block-table entries, the query vector and its mask together;
+  // (3) the ring of K/V steps.
+  const int ls = min(lane, kMaxSeq - 1);
+  const int ws_l = a.wg_start[ls], sq_l = a.rows.seq[ls], r0_l = a.rows.row_start[ls];
+  const int r1_l = a.rows.row_start[ls + 1], nsp_l = a.nsplit[ls];
+  const int i = __popcll(__ballot(lane < a.rows.n_seq && ws_l <= b)) - 1;
+  const int sq = __builtin_amdgcn_readlane(sq_l, i);
+  const int r0 = __builtin_amdgcn_readlane(r0_l, i);
+  const int nr = __builtin_amdgcn_readlane(r1_l, i) - r0;
+  const int G = a.H / a.Hkv;
+  const int nqb = ((nr * G + a.qg_size - 1) / a.qg_size + WV - 1) / WV;
+  const int l = b - __builtin_amdgcn_readlane(ws_l, i), t8 = l / kAttnXcds;
   const int g = (t8 / nqb) * kAttnXcds + l % kAttnXcds, qb = t8 % nqb;
-  const int ns_ub = a.nsplit[i];
+  const int ns_ub = __builtin_amdgcn_readlane(nsp_l, i);
   if (g >= a.Hkv * ns_ub) return;  // padding of the group count to the XCDs
   const int s = g / a.Hkv, kvh = g - s * a.Hkv;  // splits in order, KV heads fastest: unneeded splits come last
-  const int P = a.kv.P[a.rows.seq[i]];
-  const int ns = min(max(1, (P + a.kps - 1) / a.kps), ns_ub);  // this sequence's splits (P <= the host's bound)
-  if (s >= ns) return;  // past what its context needs
-  const bool last_split = s == ns - 1;
-  const int sq = a.rows.seq[i];
-  const int r0 = a.rows.row_start[i];
-  const int nr = a.rows.row_start[i + 1] - r0;
-  const int G = a.H / a.Hkv;
   const int qg = qb * WV + wave;
   const int q0 = qg * a.qg_size;
   const int nq = qg < a.n_qg ? max(0, min(a.qg_size, nr * G - q0)) : 0;  // this wave's query vectors
-  const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
-  const int clo = s * a.kps, chi = min(P, clo + a.kps);            // committed keys of this split
-  int first = clo, last = min(clo + a.kps, (P + kStep - 1) / kStep * kStep);
-  if (last_split) {
-    first = min(first, wlo / kStep * kStep);
-    last = (whi + kStep - 1) / kStep * kStep;
+  // A split's steps start at clo = s * kps: a committed split's keys do,
+  // and the last split's in-round keys start at P + win >= clo.
+  const int clo = s * a.kps;
+  const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
+
+  // (2): P, the block-table entries of the split, one per lane (two per
+  // step), this lane's query vector (query mrow of the wave's group, vector
+  // gq mapping to row r0 + gq % nr and head kvh*G + gq / nr) and its mask
+  // (the pass's if it has them, else read from the query buffer and not
+  // used: a load under a branch would make the compiler wait for every load
+  // in flight where the branch joins).
+  const int P = a.kv.P[sq];
+  const int btreg = bt[min(clo / kBlock + lane, a.kv.bps - 1)];
+  const int mrow = lane & 15, kq = lane >> 4;
+  const bool qok = mrow < nq;
+  const int gq = min(q0 + min(mrow, max(nq, 1) - 1), nr * G - 1);
+  float4 qraw[KSQ][2];
+  uint64_t mraw;
+  {
+    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
+#pragma unroll
+    for (int s2 = 0; s2 < KSQ; ++s2) {
+      qraw[s2][0] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq);
+      qraw[s2][1] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq + 4);
+    }
+    const uint64_t* const mbase =
+        a.rows.mask != nullptr ? a.rows.mask + r0 : reinterpret_cast<const uint64_t*>(a.q);
+    mraw = mbase[gq % nr];
   }
+  // every request above is issued before the branch on P below
+  asm volatile("" ::: "memory");
+
+  const int ns = min(max(1, (P + a.kps - 1) / a.kps), ns_ub);  // this sequence's splits (P <= the host's bound)
+  if (s >= ns) return;  // past what its context needs
+  const bool last_split = s == ns - 1;
+  const int wlo = P + a.rows.win, whi = wlo + a.rows.idx_off + nr;  // in-round keys
+  const int chi = min(P, clo + a.kps);                             // committed keys of this split
+  const int first = clo;
+  const int last = last_split ? (whi + kStep - 1) / kStep * kStep : min(clo + a.kps, (P + kStep - 1) / kStep * kStep);
   // both ends are step-aligned; the host keeps a split within kAttnGroupSteps
   const int n_steps = min(last > first ? (last - first) / kStep : 0, kAttnGroupSteps);
 
-  // Block-table entries of the split, one per lane (two per step).
-  const int* bt = a.kv.bt + (size_t)sq * a.kv.bps;
-  const int btreg = bt[min(first / kBlock + lane, a.kv.bps - 1)];
   const uint16_t* const kpool = a.kv.k;
   const uint16_t* const vpool = a.kv.v;
   __builtin_assume(threadIdx.x < kThreads);
@@ -137,23 +160,11 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load_step(min(d, t_end), ring[d]);
 
-  // This lane's query vector (query mrow of the wave's group) and its
-  // visibility mask; vector gq maps to row r0 + gq % nr and head
-  // kvh*G + gq / nr.
-  const int mrow = lane & 15, kq = lane >> 4;
-  const bool qok = mrow < nq;
-  const int gq = min(q0 + min(mrow, max(nq, 1) - 1), nr * G - 1);
-  float4 qraw[KSQ][2];
+  // this lane's visibility mask over the in-round keys
   uint64_t qmask;
   {
-    const float* src = a.q + ((size_t)(r0 + gq % nr) * a.H + kvh * G + gq / nr) * HD;
-#pragma unroll
-    for (int s2 = 0; s2 < KSQ; ++s2) {
-      qraw[s2][0] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq);
-      qraw[s2][1] = *reinterpret_cast<const float4*>(src + 32 * s2 + 8 * kq + 4);
-    }
     const int idx = a.rows.idx_off + gq % nr;
-    const uint64_t mk = a.rows.mask ? a.rows.mask[r0 + gq % nr] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+    const uint64_t mk = a.rows.mask != nullptr ? mraw : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
     qmask = qok ? mk : 0ull;
   }
 
