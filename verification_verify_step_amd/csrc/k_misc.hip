@@ -118,59 +118,50 @@ void launch_set_state(int* P, int* pending, int* committed, int seq, int p, int 
 // ---------------------------------------------------------------------------
 // Row loading: h[m] = embed[token] (or a given hidden row); the next
 // consumer's activation (h * g) as split-bf16 fragments; per 256-column group
-// sums of h^2 for the fused RMSNorm.
+// sums of h^2 for the fused RMSNorm.  One workgroup per (256-column group,
+// row), so that no row waits on another's loads; the column group of row m
+// adds its four wave sums in wave order.
 __global__ __launch_bounds__(256) void load_rows_kernel(LoadArgs a) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int bx = blockIdx.x, m = blockIdx.y;
+  const int n = bx * 256 + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ float wsum[4][kMaxRows];
-  for (int r0 = 0; r0 < a.M; r0 += kMaxRows) {  // rows in groups of kMaxRows
-    const int nr = min(kMaxRows, a.M - r0);
-    for (int mm = 0; mm < nr; ++mm) {
-      const int m = r0 + mm;
-      float v = 0.f;
-      if (n < a.d) {
-        const int src = a.src_identity ? m : a.src_row[mm];
-        if (a.tokens != nullptr) {
-          const int t = min(max(a.tokens[src], 0), a.V - 1);  // never read outside the table
-          v = bf2f(a.embed[(size_t)t * a.d + n]);
-        } else {
-          v = a.hidden[(size_t)src * a.d + n];
-        }
-        a.h[(size_t)m * a.d + n] = v;
-        xa_store(a.xa, n, m, a.M, v * a.g[n]);
-      }
-      const float s = wave_sum(v * v);
-      if (lane == 0) wsum[wave][mm] = s;
+  __shared__ float wsum[4];
+  float v = 0.f;
+  if (n < a.d) {
+    const int src = a.src_identity ? m : a.src_row[m % kMaxRows];
+    if (a.tokens != nullptr) {
+      const int t = min(max(a.tokens[src], 0), a.V - 1);  // never read outside the table
+      v = bf2f(a.embed[(size_t)t * a.d + n]);
+    } else {
+      v = a.hidden[(size_t)src * a.d + n];
     }
-    __syncthreads();
-    if (threadIdx.x < nr) {
-      const int mm = threadIdx.x;
-      a.ss[(size_t)blockIdx.x * a.M + r0 + mm] = ((wsum[0][mm] + wsum[1][mm]) + wsum[2][mm]) + wsum[3][mm];
-    }
-    __syncthreads();
+    a.h[(size_t)m * a.d + n] = v;
+    xa_store(a.xa, n, m, a.M, v * a.g[n]);
   }
-  if (a.rope != nullptr && blockIdx.x == 0) {
+  const float s = wave_sum(v * v);
+  if (lane == 0) wsum[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) a.ss[(size_t)bx * a.M + m] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  if (a.rope != nullptr && bx == 0) {
+    const int si = row_seq_index(a.rows, m);
+    const int sq = a.rows.seq[si];
+    const int idx = a.rows.idx_off + m - a.rows.row_start[si];
+    const int pos = a.P[sq] + (a.rows.depth ? a.rows.depth[m] : idx);
     // angles in fp64: position up to ~1e4 times frequencies down to 1e-4
-    for (int e = threadIdx.x; e < a.M * a.half; e += 256) {
-      const int m = e / a.half, i = e % a.half;
-      const int si = row_seq_index(a.rows, m);
-      const int idx = a.rows.idx_off + m - a.rows.row_start[si];
-      const int pos = a.P[a.rows.seq[si]] + (a.rows.depth ? a.rows.depth[m] : idx);
+    for (int i = threadIdx.x; i < a.half; i += 256) {
       const double ang = (double)pos * pow((double)a.theta, -(double)i / (double)a.half);
       double sn, cs;
       sincos(ang, &sn, &cs);
-      a.rope[e] = make_float2((float)cs, (float)sn);
+      a.rope[(size_t)m * a.half + i] = make_float2((float)cs, (float)sn);
     }
-    for (int m = threadIdx.x; m < a.M; m += 256) {
-      const int si = row_seq_index(a.rows, m);
-      const int sq = a.rows.seq[si];
-      const int slot = a.P[sq] + a.rows.win + a.rows.idx_off + m - a.rows.row_start[si];
+    if (threadIdx.x == 0) {
+      const int slot = a.P[sq] + a.rows.win + idx;
       a.kvrow[m] = a.bt[(size_t)sq * a.bps + slot / kBlock] * kBlock + slot % kBlock;
     }
   }
 }
 void launch_load_rows(const LoadArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(load_rows_kernel, dim3((a.d + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(load_rows_kernel, dim3((a.d + 255) / 256, a.M), dim3(256), 0, st, a);
 }
 
 __global__ void copy_rows_kernel(const float* src, float* dst, size_t n) {
