@@ -1504,15 +1504,16 @@ vs_status accept_core(vs_model* m, const AcceptBufs& bf, int V, int max_rows, co
   sa.amax = bf.amax;
   sa.second = bf.second;
   sa.sumexp = mode == VS_SAMPLE ? bf.sum : nullptr;
-  run((double)M * V * 4, [&]() { launch_row_stats(sa, M, st); });
-  if (mode == VS_SAMPLE) {
+  if (mode == VS_SAMPLE) {  // the target's and the draft's statistics in one launch
     StatsArgs da = sa;
     da.logits = d_draft_logits;
     da.mx = bf.dmx;
     da.amax = bf.damax;
     da.second = nullptr;
     da.sumexp = bf.dsum;
-    run((double)M * V * 4, [&]() { launch_row_stats(da, M, st); });
+    run((double)M * V * 8, [&]() { launch_row_stats2(sa, da, M, st); });
+  } else {
+    run((double)M * V * 4, [&]() { launch_row_stats(sa, M, st); });
   }
   const bool tp = top_p < 1.0;
   if (tp) {

@@ -238,9 +238,13 @@ __device__ double block_sum_fixed(double v, double* sh) {
 // largest value, and S = sum exp((z - max)/T) in fp64 when requested.  Thread
 // t takes ids t, t + 1024, ..., so each load instruction of a wave reads 256
 // contiguous bytes.
-__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a) {
+// Rows [0, M) of a, then rows [0, M) of b when b.logits is set (the
+// target's and the draft's statistics of a stochastic accept in one launch).
+__global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a0, StatsArgs b0, int M) {
   __shared__ double sh[kStatsThreads / 64];
-  const int m = blockIdx.x;
+  const bool second_set = (int)blockIdx.x >= M;
+  const StatsArgs& a = second_set ? b0 : a0;
+  const int m = second_set ? (int)blockIdx.x - M : (int)blockIdx.x;
   const float* z = a.logits + (size_t)m * a.V;
   float v[kStatsPer];
 #pragma unroll
@@ -271,7 +275,11 @@ __global__ __launch_bounds__(kStatsThreads) void row_stats_kernel(StatsArgs a) {
   }
 }
 void launch_row_stats(const StatsArgs& a, int M, hipStream_t st) {
-  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a);
+  const StatsArgs none{};
+  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatsThreads), 0, st, a, none, M);
+}
+void launch_row_stats2(const StatsArgs& a, const StatsArgs& b, int M, hipStream_t st) {
+  if (M > 0) hipLaunchKernelGGL(row_stats_kernel, dim3(2 * M), dim3(kStatsThreads), 0, st, a, b, M);
 }
 
 // Order-preserving 32-bit image of a float: a > b as floats iff key(a) >
@@ -507,17 +515,23 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
     return kk > a.tp_key[r] || (kk == a.tp_key[r] && j <= a.tp_id[r]);
   };
   __shared__ int s_a, s_flags, s_reject;
-  if (threadIdx.x == 0) {
+  __shared__ double s_ratio[kMaxRows], s_u[kMaxRows];
+  if ((int)threadIdx.x < k) {  // every row's p / q and uniform at once (their loads in flight together)
+    const int j = threadIdx.x, r = r0 + j;
+    s_u[j] = u[16 + j];
+    const int d = a.tokens[r + 1];
+    const float zd_t = a.logits[(size_t)r * a.V + d];
+    const double p = kept(r, d, zd_t) ? exp(((double)zd_t - (double)a.mx[r]) * inv_t) / (tp ? a.tp_mass[r] : a.sumexp[r])
+                                      : 0.0;
+    const double q = exp(((double)a.dlogits[(size_t)r * a.V + d] - (double)a.dmx[r]) * inv_t) / a.dsumexp[r];
+    s_ratio[j] = q > 0.0 ? p / q : 0.0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // the walk: accept row j's token while u_j < min(1, p / q)
     int acc = 0, flags = 0, reject = -1;
     for (int j = 0; j < k; ++j) {
-      const int r = r0 + j;
-      const int d = a.tokens[r + 1];
-      const float zd_t = a.logits[(size_t)r * a.V + d];
-      const double p = kept(r, d, zd_t) ? exp(((double)zd_t - (double)a.mx[r]) * inv_t) / (tp ? a.tp_mass[r] : a.sumexp[r])
-                                        : 0.0;
-      const double q = exp(((double)a.dlogits[(size_t)r * a.V + d] - (double)a.dmx[r]) * inv_t) / a.dsumexp[r];
-      const double ratio = q > 0.0 ? p / q : 0.0;
-      const double uj = u[16 + j];
+      const double ratio = s_ratio[j];
+      const double uj = s_u[j];
       if (fabs(ratio - uj) < 1e-3) flags |= 1;
       if (uj < fmin(1.0, ratio)) {
         ++acc;

@@ -193,6 +193,8 @@ void launch_set_state(int* P, int* pending, int* committed, int seq, int p, int 
 void launch_load_rows(const LoadArgs& a, hipStream_t st);
 void launch_copy_rows(const float* src, float* dst, int M, int d, hipStream_t st);
 void launch_row_stats(const StatsArgs& a, int M, hipStream_t st);
+// the rows of a, then the same rows of b, in one launch
+void launch_row_stats2(const StatsArgs& a, const StatsArgs& b, int M, hipStream_t st);
 void launch_pick(const PickArgs& a, hipStream_t st);
 void launch_accept(const AcceptArgs& a, hipStream_t st);
 void launch_compact(const CommitArgs& a, hipStream_t st);
