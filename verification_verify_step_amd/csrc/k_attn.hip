@@ -38,7 +38,9 @@
 // device-coherent loads, sums them in chunk order, writes the result as
 // split-bf16 activation fragments for the O projection and resets the
 // counter.  No agent-scope fence is used: a fence would write back or
-// invalidate the whole L2.
+// invalidate the whole L2.  When every unit of the pass is one workgroup's
+// and the chunk partials fit (LP), they stay in LDS and the workgroup
+// combines them there with the same arithmetic.
 #include "attn_dev.h"
 
 namespace vs {
