@@ -297,63 +297,78 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
 }
 
 // Merge of the splits, for sequences with more than one.  A workgroup of 4
-// waves takes 4 query vectors of one (sequence, KV head, query group): wave
-// w reads the (max, sum) of vector w of every split in one load per lane
-// (split j in lane j) and puts the weights exp2(m_j - max) and their total
-// in LDS; then each thread sums one pair of dims over the splits in split
-// order, with the loads of 16 splits in flight at a time.
+// waves takes 4 query vectors of one (sequence, KV head, query group); wave
+// w merges vector w.  Its requests go out at once, beside P: the (max, sum)
+// record of split `lane` and the lane's pair of dims of the first 16 splits,
+// for every split of the host's bound (>= the device's count; the records
+// past the device's are read but never used).  Lane j's weight
+// exp2(m_j - max) reaches the other lanes by shuffles, and each lane sums
+// its pair over the splits in split order.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   static_assert(kAttnGroupMaxSplits <= 64, "one split per lane");
-  __shared__ float wts[4][kAttnGroupMaxSplits];
-  __shared__ float tot[4];
+  constexpr int HP = HD / 2;  // dim pairs
+  static_assert(HP <= 64, "one pair per lane");
+  constexpr int kB = 16;      // splits whose pairs are requested with the records
   const int quarters = (a.qg_size + 3) / 4;
   const int unit = blockIdx.x / quarters, v0 = (blockIdx.x % quarters) * 4;
   const int qg = unit % a.n_qg, ik = unit / a.n_qg, kvh = ik % a.Hkv, i = ik / a.Hkv;
-  const int ns = min(max(1, (a.kv.P[a.rows.seq[i]] + a.kps - 1) / a.kps), a.nsplit[i]);
-  if (ns <= 1) return;  // written by the main kernel
+  const int nsb = a.nsplit[i];
+  if (nsb <= 1) return;  // one split: written by the main kernel
   const int r0 = a.rows.row_start[i];
   const int nr = a.rows.row_start[i + 1] - r0;
   const int G = a.H / a.Hkv;
   const int q0 = qg * a.qg_size;
   const int nq = max(0, min(a.qg_size, nr * G - q0));
-  if (v0 >= nq) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int v = v0 + wave;
+  if (v >= nq) return;  // this wave's vector is past the group's
   const size_t QG = a.qg_size, rec0 = (size_t)unit * a.n_split;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  {
-    const int v = v0 + wave;
-    const float2 ml = (v < nq && lane < ns) ? reinterpret_cast<const float2*>(a.part + a.ml_off)[(rec0 + lane) * QG + v]
-                                            : make_float2(-INFINITY, 0.f);
-    const float mx = wave_max(ml.y > 0.f ? ml.x : -INFINITY);  // a split that saw no key has sum 0
-    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
-    const float t = wave_sum(w * ml.y);
-    if (lane < kAttnGroupMaxSplits) wts[wave][lane] = w;
-    if (lane == 0) tot[wave] = t;
-  }
-  __syncthreads();
-  constexpr int HP = HD / 2;  // dim pairs
-  static_assert(HP <= 64, "one pair per lane");
-  const int v = v0 + wave, c = lane;
-  if (v >= nq || c >= HP) return;
-  const float* src = a.part + (rec0 * QG + v) * HD + 2 * c;
+  const int P = a.kv.P[a.rows.seq[i]];
+  const float2 mlr = lane < nsb ? reinterpret_cast<const float2*>(a.part + a.ml_off)[(rec0 + lane) * QG + v]
+                                : make_float2(-INFINITY, 0.f);
+  const int c = min(lane, HP - 1);
+  const float* base = a.part + __builtin_amdgcn_readfirstlane((int)((rec0 * QG + v) * HD));
+  const float* src = base + 2 * c;
   const size_t stride = QG * HD;  // floats between consecutive splits
+  // The first kB splits' pairs through a buffer resource whose extent ends at
+  // split nsb: a load past it returns zeros without touching memory, so the
+  // requests go out together, unbranched, and fetch only the bound's splits.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, __builtin_amdgcn_readfirstlane((int)(nsb * stride * sizeof(float))), 0x00020000);
+  float2 x[kB];
+#pragma unroll
+  for (int e = 0; e < kB; ++e) {
+    const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * c, (int)(e * stride * sizeof(float)), 0);
+    x[e] = make_float2(__uint_as_float(w2[0]), __uint_as_float(w2[1]));
+  }
+  asm volatile("" ::: "memory");  // keep the requests above the P-dependent exit
+  const int ns = min(max(1, (P + a.kps - 1) / a.kps), nsb);
+  if (ns <= 1) return;  // one split on the device: written by the main kernel
+  const float2 ml = lane < ns ? mlr : make_float2(-INFINITY, 0.f);
+  const float mx = wave_max(ml.y > 0.f ? ml.x : -INFINITY);  // a split that saw no key has sum 0
+  const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+  const float t = wave_sum(w * ml.y);
   float o0 = 0.f, o1 = 0.f;
-  for (int j0 = 0; j0 < ns; j0 += 16) {
-    float2 x[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      x[e] = *reinterpret_cast<const float2*>(src + (size_t)min(j0 + e, ns - 1) * stride);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float w = j0 + e < ns ? wts[wave][j0 + e] : 0.f;
-      o0 += w * x[e].x;
-      o1 += w * x[e].y;
+  for (int e = 0; e < kB; ++e) {
+    const float we = __shfl(w, e, 64);
+    if (e < ns) {
+      o0 += we * x[e].x;
+      o1 += we * x[e].y;
     }
   }
+  for (int j = kB; j < ns; ++j) {  // past the first kB splits (the tree's 17)
+    const float2 xj = *reinterpret_cast<const float2*>(src + (size_t)j * stride);
+    const float wj = __shfl(w, j, 64);
+    o0 += wj * xj.x;
+    o1 += wj * xj.y;
+  }
+  if (lane >= HP) return;
   const int gq = q0 + v;
   const int m = r0 + gq % nr, h = kvh * G + gq / nr;
-  xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / tot[wave]);
-  xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / tot[wave]);
+  xa_store(a.xa_o, h * HD + 2 * c, m, a.M, o0 / t);
+  xa_store(a.xa_o, h * HD + 2 * c + 1, m, a.M, o1 / t);
 }
 
 void launch_attention_group(const AttnArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
