@@ -443,17 +443,29 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   constexpr int HP = HD / 2;   // dim pairs
   constexpr int kCB = 16;      // chunks requested per batch
   constexpr int kPairs = 2;    // pairs per thread per round
+  // The loads go through buffer resources whose extents end at the unit's
+  // last chunk: a load past it (the batch's chunks beyond nc, a thread's
+  // pair beyond the vectors') returns zeros without a memory request, so
+  // the CU fetches only the partials that exist.  They keep the
+  // device-coherent cache policy (sc1) of agent-scope atomic loads.
+  constexpr int kSc1 = 16;
   const int nc = n_chunks;
-  const uint64_t* src0 = reinterpret_cast<const uint64_t*>(po) + (size_t)unit * a.n_split * QG * HP;
-  const uint64_t* ml0 = pml + (size_t)unit * a.n_split * QG;
   const int S = (int)QG * HP;  // pairs between consecutive partials
   const int npair = nq * HP;
+  const int xbytes = nc * S * 8, mlbytes = nc * (int)QG * 8;
+  const size_t ubase = (size_t)__builtin_amdgcn_readfirstlane(unit) * a.n_split * QG;
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const uint64_t*>(po) + ubase * HP), 0, xbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(pml + ubase), 0, mlbytes, 0x00020000);
   for (int p0 = threadIdx.x; p0 < npair; p0 += kPairs * kThreads) {
-    int pr[kPairs], rr[kPairs];
+    int pr[kPairs], rr[kPairs], xo[kPairs], mo[kPairs];
 #pragma unroll
     for (int q = 0; q < kPairs; ++q) {
+      const bool ok = p0 + q * kThreads < npair;
       pr[q] = min(p0 + q * kThreads, npair - 1);
       rr[q] = pr[q] / HP;
+      xo[q] = ok ? pr[q] * 8 : xbytes;  // byte offsets in chunk 0, or out of range
+      mo[q] = ok ? rr[q] * 8 : mlbytes;
     }
     float mx[kPairs], tot[kPairs], o0[kPairs], o1[kPairs];
 #pragma unroll
@@ -467,10 +479,13 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
       for (int q = 0; q < kPairs; ++q)
 #pragma unroll
         for (int e = 0; e < kCB; ++e) {
-          const int j = min(j0 + e, nc - 1);
-          mlv[q][e] = __hip_atomic_load(ml0 + (size_t)j * QG + rr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (with_x)
-            xv[q][e] = __hip_atomic_load(src0 + (size_t)j * S + pr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int j = j0 + e;
+          const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, j * (int)QG * 8 + mo[q], 0, kSc1);
+          mlv[q][e] = (uint64_t)m2[0] | ((uint64_t)m2[1] << 32);
+          if (with_x) {
+            const auto x2 = __builtin_amdgcn_raw_buffer_load_b64(rx, j * S * 8 + xo[q], 0, kSc1);
+            xv[q][e] = (uint64_t)x2[0] | ((uint64_t)x2[1] << 32);
+          }
         }
     };
     auto take_max = [&](int j0) {  // a chunk that saw no key has sum 0
