@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   float2 x[kB];
 #pragma unroll
   for (int e = 0; e < kB; ++e) {
-    const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * c, (int)(e * stride * sizeof(float)), 0);
+    const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * c + e * (int)(stride * sizeof(float)), 0, 0);
     x[e] = make_float2(__uint_as_float(w2[0]), __uint_as_float(w2[1]));
   }
   asm volatile("" ::: "memory");  // keep the requests above the P-dependent exit
