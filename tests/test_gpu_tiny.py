@@ -296,3 +296,59 @@ def test_stochastic_accept_parity(eng):
         assert (got[i][0], got[i][1]) == (a, y), (i, got[i], a, y)
     for s in seqs:
         B.vs_seq_close(eng.kv, s)
+
+
+def test_non_finite_logits_and_foreign_ids_stay_in_range(eng):
+    """Regression: ids taken from logits are used as indices by later kernels
+    (the accept's p / q lookups, the draft's embedding rows).  Logit rows that
+    are NaN or +-inf (an overflowed pass) and draft ids outside [0, V) must
+    leave every returned and stored id inside [0, V) and every accepted
+    length inside [0, k], in the greedy, sampled and top-p accepts; a commit
+    whose result claims more rows than the sequence has advances it by at
+    most its rows.  The pages define nothing for such inputs, so only the
+    ranges are checked (parity unpinned)."""
+    n_seq, k, V = 4, 4, CFG.vocab
+    M = n_seq * (k + 1)
+    rng = np.random.default_rng(11)
+    zt = rng.standard_normal((M, V)).astype(np.float32)
+    zd = rng.standard_normal((M, V)).astype(np.float32)
+    zt[0:k + 1], zd[0:k + 1] = np.nan, np.nan                    # sequence 0: NaN rows
+    zt[k + 1:2 * (k + 1)], zd[k + 1:2 * (k + 1)] = np.inf, np.inf  # sequence 1: +inf rows
+    zt[2 * (k + 1):3 * (k + 1)] = -np.inf                         # sequence 2: target -inf
+    toks = np.zeros(M, dtype=np.int32)
+    foreign = [-1, V, V + 7, np.iinfo(np.int32).max, np.iinfo(np.int32).min]
+    for r in range(M):
+        toks[r] = foreign[r % len(foreign)]
+    U = np.stack([G.uniforms(50 + i, 0) for i in range(n_seq)])
+    seqs = [eng.open(100) for _ in range(n_seq)]
+    batch = B.make_batch(seqs, [k + 1] * n_seq)
+    dzt, dzd, dtok, du = (torch.from_numpy(zt).cuda(), torch.from_numpy(zd).cuda(), G.i32(toks),
+                          G.f64(U.reshape(-1)))
+    res = torch.zeros((n_seq, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    for call in ("greedy", "sample", "top_p"):
+        res.fill_(-7)
+        if call == "greedy":
+            B.vs_accept(eng.model, batch, B.VS_GREEDY, 1.0, dtok.data_ptr(), dzt.data_ptr(), None, None,
+                        res.data_ptr(), eng.stream)
+        elif call == "sample":
+            B.vs_accept(eng.model, batch, B.VS_SAMPLE, 1.0, dtok.data_ptr(), dzt.data_ptr(), dzd.data_ptr(),
+                        du.data_ptr(), res.data_ptr(), eng.stream)
+        else:
+            B.vs_accept_top_p(eng.model, batch, 1.0, 0.9, dtok.data_ptr(), dzt.data_ptr(), dzd.data_ptr(),
+                              du.data_ptr(), res.data_ptr(), eng.stream)
+        torch.cuda.synchronize()
+        for i, (a, y, _, _) in enumerate(G.result_rows(res, n_seq)):
+            assert 0 <= a <= k and 0 <= y < V, (call, i, a, y)
+    # a result that claims more accepted rows than the sequence has, and a
+    # foreign bonus id: the commit advances by at most k + 1
+    P0 = [eng.state()[0][s] for s in seqs]
+    bad = torch.zeros((n_seq, B.VS_RESULT_INTS), dtype=torch.int32, device="cuda")
+    bad[:, 0] = torch.tensor([1000, -3, k, 0], dtype=torch.int32)
+    bad[:, 1] = torch.tensor([V + 1, -1, 3, 5], dtype=torch.int32)
+    B.vs_commit(eng.model, eng.kv, batch, bad.data_ptr(), eng.stream)
+    torch.cuda.synchronize()
+    P, pending, committed = eng.state()
+    for i, (s, adv) in enumerate(zip(seqs, [k + 1, 1, k + 1, 1])):
+        assert P[s] == P0[i] + adv, (i, P[s], P0[i])
+    for s in seqs:
+        B.vs_seq_close(eng.kv, s)

@@ -458,7 +458,10 @@ __global__ __launch_bounds__(kStatsThreads) void pick_kernel(PickArgs a) {
     double tot;
     tok = block_sample_reg(w, a.u[(size_t)a.uidx[i] * VS_N_UNIFORMS + a.slot], &tot);
   }
-  if (threadIdx.x == 0) a.tokens[a.dst[i]] = tok;
+  // Every written id lies in [0, V): with finite logits the draw and the
+  // argmax always are; non-finite logits (an overflowed pass) would give -1
+  // or INT_MAX, which later kernels use as indices.
+  if (threadIdx.x == 0) a.tokens[a.dst[i]] = min(max(tok, 0), a.V - 1);
 }
 void launch_pick(const PickArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(pick_kernel, dim3(a.n), dim3(kStatsThreads), 0, st, a);
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
         cur = nxt;
       }
       res[0] = n_path;
-      res[1] = a.amax[r0 + cur];
+      res[1] = min(max(a.amax[r0 + cur], 0), a.V - 1);  // in range also for non-finite logits
       res[2] = flags;
       res[3] = n_path;
       for (int j = 0; j < VS_RESULT_INTS - 4; ++j) res[4 + j] = j < n_path ? path[j] : -1;
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
   if ((int)threadIdx.x < k) {  // every row's p / q and uniform at once (their loads in flight together)
     const int j = threadIdx.x, r = r0 + j;
     s_u[j] = u[16 + j];
-    const int d = a.tokens[r + 1];
+    const int d = min(max(a.tokens[r + 1], 0), a.V - 1);  // an index: kept in the row whatever the caller passed
     const float zd_t = a.logits[(size_t)r * a.V + d];
     const double p = kept(r, d, zd_t) ? exp(((double)zd_t - (double)a.mx[r]) * inv_t) / (tp ? a.tp_mass[r] : a.sumexp[r])
                                       : 0.0;
@@ -586,7 +589,7 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
   }
   if (threadIdx.x == 0) {
     res[0] = s_a;
-    res[1] = y;
+    res[1] = min(max(y, 0), a.V - 1);  // -1 only if every weight vanished (non-finite logits)
     res[2] = s_flags;
     res[3] = s_a;
     for (int j = 0; j < VS_RESULT_INTS - 4; ++j) res[4 + j] = j < s_a ? j + 1 : -1;
@@ -635,10 +638,13 @@ __global__ void commit_kernel(CommitArgs a) {
   if (i >= a.rows.n_seq) return;
   const int* res = a.result + i * VS_RESULT_INTS;
   const int sq = a.rows.seq[i];
-  const int P = a.P[sq] + res[0] + 1;
+  // at most the sequence's rows minus one are accepted: the host's bound on
+  // the KV length (and so every later table lookup) relies on it
+  const int acc = min(max(res[0], 0), a.rows.row_start[i + 1] - a.rows.row_start[i] - 1);
+  const int P = a.P[sq] + acc + 1;
   a.P[sq] = P;
   a.pending[sq] = res[1];
-  a.committed[sq] += res[0] + 1;
+  a.committed[sq] += acc + 1;
   if (a.mirror != nullptr)
     __hip_atomic_store(a.mirror + sq, ((uint64_t)a.commit_no[i] << 32) | (uint32_t)P, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_SYSTEM);

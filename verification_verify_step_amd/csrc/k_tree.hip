@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kExpThreads) void tree_expand_kernel(TreeArgs a) {
         }
       }
       block_argmax(bv, bi, sh_v, sh_i);
-      ids[c] = bi;
+      ids[c] = min(bi, a.V - 1);  // no candidate (non-finite logits) leaves bi at INT_MAX: keep it an index
       if (c == 0) zmax = bv;
     }
   }
