@@ -55,6 +55,13 @@ __device__ __forceinline__ size_t k_tile_off(int j, int d) {
   return (size_t)(d >> 3) * (kBlock * 8) + j * 8 + (d & 7);
 }
 
+// Fourth word of a raw buffer resource (__builtin_amdgcn_make_buffer_rsrc) on
+// this GPU family: 32-bit data format, no swizzle, no index stride.  With
+// stride 0 a load whose offset reaches the resource's byte extent returns
+// zeros without a memory request; the kernels use that to bound their loads
+// by a count known only at run time without branches.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // --------------------------------------------------------------------------
 // bf16 helpers (bit patterns in uint16_t).
 __device__ __forceinline__ uint16_t f2bf(float f) {

@@ -455,8 +455,8 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   const int xbytes = nc * S * 8, mlbytes = nc * (int)QG * 8;
   const size_t ubase = (size_t)__builtin_amdgcn_readfirstlane(unit) * a.n_split * QG;
   const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const uint64_t*>(po) + ubase * HP), 0, xbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(pml + ubase), 0, mlbytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const uint64_t*>(po) + ubase * HP), 0, xbytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc((void*)(pml + ubase), 0, mlbytes, kRawBufferWord3);
   for (int p0 = threadIdx.x; p0 < npair; p0 += kPairs * kThreads) {
     int pr[kPairs], rr[kPairs], xo[kPairs], mo[kPairs];
 #pragma unroll

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void attn_group_combine(const AttnArgs a) {
   // split nsb: a load past it returns zeros without touching memory, so the
   // requests go out together, unbranched, and fetch only the bound's splits.
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, __builtin_amdgcn_readfirstlane((int)(nsb * stride * sizeof(float))), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, __builtin_amdgcn_readfirstlane((int)(nsb * stride * sizeof(float))), kRawBufferWord3);
   float2 x[kB];
 #pragma unroll
   for (int e = 0; e < kB; ++e) {
