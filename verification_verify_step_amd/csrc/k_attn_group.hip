@@ -8,12 +8,12 @@
 // each wave its own key range of one query group, so when a KV head has many
 // query vectors (GQA heads, or the 64 rows of a token tree) every group reads
 // the same K/V again.  Here a workgroup owns one key range (split) of one KV
-// head and up to WV query groups, one per wave (WV = 4: two workgroups per
-// CU, so that one's pipeline start overlaps the other's steps):
+// head and up to WV query groups, one per wave (WV = 4: three workgroups
+// per CU, so that one's pipeline start and waits overlap the others' steps):
 //
 //  * the workgroup's threads load each 32-key step (two 16-key blocks of K
-//    and of V, 16 KB at head_dim 128) in 16-byte pieces, kDepth steps ahead
-//    in registers, and put a step into one of two LDS stages (K rows padded
+//    and of V, 16 KB at head_dim 128) in 16-byte pieces, kDepth = 2 steps
+//    ahead in registers (a ring short enough for three waves per SIMD), and put a step into one of two LDS stages (K rows padded
 //    by 16 bytes so the fragment reads of one MFMA do not collide in a bank);
 //  * every wave then computes its group's step transposed, S^T = K.Q^T on
 //    the bf16 16x16x32 MFMA (query split hi/lo), so that a lane holds eight
@@ -43,7 +43,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 }  // namespace
 
 template <int HD, int WV>
-__global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
+// At least three waves per SIMD: the register budget (168 per lane) that
+// lets three workgroups share a CU, which measured faster than a deeper ring
+// at two (the 70B batch 255 against 310 us per launch pair, the 64-row tree
+// 35.5 against 39.5).
+__global__ __launch_bounds__(WV * 64, 3) void attn_group_kernel(const AttnArgs a) {
   constexpr int kThreads = WV * 64;
   constexpr int KSQ = HD / 32;        // k-steps of S over head dims
   constexpr int NDT = HD / 16;        // 16-dim output tiles
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(WV * 64) void attn_group_kernel(const AttnArgs a) {
   constexpr int PIECES = 8 * HD;                  // 16-byte pieces of one step's K and V
   constexpr int PPT = PIECES / kThreads;
   static_assert(PPT >= 1 && PPT * kThreads == PIECES, "pieces per thread");
-  constexpr int kDepth = 4;  // steps loaded ahead of the one in LDS (even; 8 measured no faster)
+  constexpr int kDepth = 2;  // steps loaded ahead of the one in LDS (even: the loop alternates the two stages)
   __shared__ __attribute__((aligned(16))) uint16_t stg[2 * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
