@@ -359,16 +359,31 @@ void launch_top_p(const TopPArgs& a, int M, hipStream_t st) {
 
 // Inverse-CDF draw from weights w_j >= 0 (fp64), ids ascending: the smallest
 // j with u*S < C_j, else the largest j with w_j > 0.  For 1024-thread
-// workgroups with the weights already in registers, in the coalesced layout
-// of sample_id(): wave w holds ids [2048 w, 2048 (w + 1)), lane l the ids
-// 2048 w + 64 q + l.  C_j = (sum of earlier waves) + (sum of the wave's
-// earlier 64-id rows) + (scan of the row up to lane l), each in a fixed
-// order.  Only ids with w_j > 0 are candidates: sums of the same weights
-// grouped differently may differ in the last bit, so C_j can step up by a
-// rounding error over a run of zero weights.  Returns -1 when every weight is
-// zero; *total receives S.
+// workgroups with the weights already in registers, in the layout of
+// sample_id(): wave w holds ids [2048 w, 2048 (w + 1)), lane l the 32
+// consecutive ids 2048 w + 32 l + q.  C_j = (sum of earlier waves) + (sum of
+// the wave's earlier lanes) + (the lane's own ids up to j), each in a fixed
+// order: a lane adds its ids in order, one scan across the wave adds the lane
+// sums, the wave sums are added in wave order.  Only ids with w_j > 0 are
+// candidates: sums of the same weights grouped differently may differ in the
+// last bit, so C_j can step up by a rounding error over a run of zero
+// weights.  Returns -1 when every weight is zero; *total receives S.
 __device__ __forceinline__ int sample_id(int q) {
-  return (int)(threadIdx.x >> 6) * (64 * kStatsPer) + q * 64 + (int)(threadIdx.x & 63);
+  return (int)(threadIdx.x >> 6) * (64 * kStatsPer) + (int)(threadIdx.x & 63) * kStatsPer + q;
+}
+// This thread's kStatsPer logits of row z in the sample_id() layout, with
+// 16-byte loads; ids at or past V (a multiple of 4) read as `fill`.
+__device__ __forceinline__ void load_ids(const float* z, int V, float (&v)[kStatsPer], float fill) {
+  const int j0 = sample_id(0);
+#pragma unroll
+  for (int c = 0; c < kStatsPer / 4; ++c) {
+    float4 x = make_float4(fill, fill, fill, fill);
+    if (j0 + 4 * c < V) x = *reinterpret_cast<const float4*>(z + j0 + 4 * c);
+    v[4 * c] = x.x;
+    v[4 * c + 1] = x.y;
+    v[4 * c + 2] = x.z;
+    v[4 * c + 3] = x.w;
+  }
 }
 __device__ int block_sample_reg(double (&w)[kStatsPer], double u, double* total) {
   __shared__ double wsum[kStatsThreads / 64];
@@ -382,20 +397,24 @@ __device__ int block_sample_reg(double (&w)[kStatsPer], double u, double* total)
       last = sample_id(q);
       pos |= 1u << q;
     }
-  // w[q] <- carry of the earlier rows + inclusive scan of row q up to this lane
-  double carry = 0.0;
+  // w[q] <- the lane's ids 0..q added in order; then the lane sums scanned
+  // across the wave (inclusive), and the lane's exclusive prefix
+  double run = 0.0;
 #pragma unroll
   for (int q = 0; q < kStatsPer; ++q) {
-    double incl = w[q];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    w[q] = carry + incl;
-    carry += __shfl(incl, 63, 64);
+    run += w[q];
+    w[q] = run;
   }
-  if (lane == 0) wsum[wave] = carry;
+  double incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  double excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.0;
+  const double wave_tot = __shfl(incl, 63, 64);
+  if (lane == 0) wsum[wave] = wave_tot;
   if (t == 0) {
     s_pick = INT_MAX;
     s_last = -1;
@@ -409,9 +428,10 @@ __device__ int block_sample_reg(double (&w)[kStatsPer], double u, double* total)
     tot += wsum[i];
   }
   const double target = u * tot;
+  const double lb = base + excl;
 #pragma unroll
   for (int q = 0; q < kStatsPer; ++q) {
-    if (((pos >> q) & 1u) && target < base + w[q]) {
+    if (((pos >> q) & 1u) && target < lb + w[q]) {
       atomicMin(&s_pick, sample_id(q));
       break;
     }
@@ -439,15 +459,15 @@ __global__ __launch_bounds__(kStatsThreads) void pick_kernel(PickArgs a) {
     t = block_top2_fast<kStatsThreads>(t);
     tok = t.i1;
   } else {
-    // draw from softmax(z / T): the row in registers (coalesced), its max,
-    // the weights exp((z - max) / T) once, then the inverse-CDF draw
+    // draw from softmax(z / T): the row in registers, its max, the weights
+    // exp((z - max) / T) once, then the inverse-CDF draw
     const float* z = a.logits + (size_t)a.lrow[i] * a.V;
     float v[kStatsPer];
+    load_ids(z, a.V, v, -INFINITY);
     Top2 t{-INFINITY, INT_MAX, -INFINITY};
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {
       const int j = sample_id(q);
-      v[q] = j < a.V ? z[j] : -INFINITY;
       if (j < a.V) t = top2_merge(t, Top2{v[q], j, -INFINITY});
     }
     t = block_top2_fast<kStatsThreads>(t);
@@ -554,12 +574,13 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
   double w[kStatsPer];
   double tot;
   auto target_weights = [&](int r) {  // exp((z - max)/T) on the (top-p) support
-    const float* zt = a.logits + (size_t)r * a.V;
+    float zt[kStatsPer];
+    load_ids(a.logits + (size_t)r * a.V, a.V, zt, 0.f);
     const double mt = a.mx[r];
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {
       const int j = sample_id(q);
-      w[q] = (j < a.V && kept(r, j, zt[j])) ? exp(((double)zt[j] - mt) * inv_t) : 0.0;
+      w[q] = (j < a.V && kept(r, j, zt[q])) ? exp(((double)zt[q] - mt) * inv_t) : 0.0;
     }
   };
   if (reject < 0) {
@@ -567,15 +588,16 @@ __global__ __launch_bounds__(kStatsThreads) void accept_kernel(AcceptArgs a) {
     y = block_sample_reg(w, u[32], &tot);
   } else {
     const int r = r0 + reject;
-    const float* zt = a.logits + (size_t)r * a.V;
-    const float* zd = a.dlogits + (size_t)r * a.V;
+    float zt[kStatsPer], zd[kStatsPer];
+    load_ids(a.logits + (size_t)r * a.V, a.V, zt, 0.f);
+    load_ids(a.dlogits + (size_t)r * a.V, a.V, zd, 0.f);
     const double mt = a.mx[r], md = a.dmx[r], st = tp ? a.tp_mass[r] : a.sumexp[r], sd = a.dsumexp[r];
 #pragma unroll
     for (int q = 0; q < kStatsPer; ++q) {  // residual max(0, p - q)
       const int j = sample_id(q);
       if (j < a.V) {
-        const double p = kept(r, j, zt[j]) ? exp(((double)zt[j] - mt) * inv_t) / st : 0.0;
-        const double qd = exp(((double)zd[j] - md) * inv_t) / sd;
+        const double p = kept(r, j, zt[q]) ? exp(((double)zt[q] - mt) * inv_t) / st : 0.0;
+        const double qd = exp(((double)zd[q] - md) * inv_t) / sd;
         w[q] = p > qd ? p - qd : 0.0;
       } else {
         w[q] = 0.0;
