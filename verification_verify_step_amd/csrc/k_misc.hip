@@ -372,7 +372,8 @@ __device__ __forceinline__ int sample_id(int q) {
   return (int)(threadIdx.x >> 6) * (64 * kStatsPer) + (int)(threadIdx.x & 63) * kStatsPer + q;
 }
 // This thread's kStatsPer logits of row z in the sample_id() layout, with
-// 16-byte loads; ids at or past V (a multiple of 4) read as `fill`.
+// 16-byte loads; ids at or past V read as `fill`.  V is a multiple of 16 (the
+// entry points check it), so a load lies wholly inside or wholly past the row.
 __device__ __forceinline__ void load_ids(const float* z, int V, float (&v)[kStatsPer], float fill) {
   const int j0 = sample_id(0);
 #pragma unroll
