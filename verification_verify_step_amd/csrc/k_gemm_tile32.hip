@@ -68,7 +68,14 @@ __global__ __launch_bounds__(kT32Threads) void gemm_tile32_kernel(const GemmArgs
   const int n32 = a.n_tiles / 2;                 // 32-column tiles
   const int tile0 = (grp * 4 + wave) * NWT;
 
-  __shared__ u32x4 As[4][UPT * NT];  // [k-step & 3][part*4 + quad][row], then unused padding
+  // Staged activations: [k-step % NB][part*4 + quad][row], then unused
+  // padding.  With an 8-deep ring the k-steps run in supersteps of 4 (SS):
+  // one barrier per superstep, the next superstep's activations written
+  // during the current one, so NB = 8 buffers; otherwise one barrier per
+  // k-step and NB = 4.
+  constexpr bool SS = PD == 8;
+  constexpr int NB = SS ? 8 : 4;
+  __shared__ u32x4 As[NB][UPT * NT];
   __shared__ float rs[BM];
 
   const u32x4* wbase[NWT];
@@ -150,21 +157,44 @@ __global__ __launch_bounds__(kT32Threads) void gemm_tile32_kernel(const GemmArgs
   // RMSNorm scales of the block's rows (row_scale_kernel ran just before)
   for (int r = tid; r < BM; r += NT) rs[r] = a.rs != nullptr ? a.rs[m0 + mrow0 + min(r, Mb - 1)] : 1.0f;
 
-  // Main loop over k-steps j: step j's A operands were read from LDS buffer
-  // j & 3 during step j - 1; it reads step j + 1's, runs its MFMAs, stores
-  // A(j + 2) into buffer (j + 2) & 3, refills ring slot j % PD with k-step
-  // j + PD and meets the workgroup at a barrier.  Steps run in unrolled
-  // groups of 8; chunks close between groups.
-  put(0, 0);
-  put(1, 1);
-  __syncthreads();
-  fetch(0, 0);
-  auto step = [&](int p, int j0) {
-    fetch((p + 1) & 1, (p + 1) & 3);
-    compute(p & 1, p % PD);
-    put((p + 2) % PD, (p + 2) & 3);
-    load(p % PD, j0 + p + PD);
+  // Main loop over k-steps j, in unrolled groups of 8 (chunks close between
+  // groups).  Without supersteps: step j's A operands were read from LDS
+  // buffer j & 3 during step j - 1; it reads step j + 1's, runs its MFMAs,
+  // stores A(j + 2) into buffer (j + 2) & 3, refills ring slot j % PD with
+  // k-step j + PD and meets the workgroup at a barrier.  With supersteps of
+  // 4: A(j) sits in buffer j & 7, written during the previous superstep
+  // (from ring slot j % 8, loaded 4 steps before that); step j reads A(j)
+  // first if it opens a superstep, A(j + 1) if the superstep goes on, runs
+  // its MFMAs, stores A(j + 4) into buffer (j + 4) & 7 (last read during the
+  // previous superstep), refills its ring slot with k-step j + 8, and the
+  // superstep's last step meets the workgroup at the barrier.  The MFMAs and
+  // their order are the same either way.
+  if constexpr (SS) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) put(p, p);
     __syncthreads();
+  } else {
+    put(0, 0);
+    put(1, 1);
+    __syncthreads();
+    fetch(0, 0);
+  }
+  auto step = [&](int p, int j0) {
+    if constexpr (SS) {
+      const int i = p & 3;  // place in the superstep (j0 is a multiple of 8)
+      if (i == 0) fetch(p & 1, p & 7);
+      if (i < 3) fetch((p + 1) & 1, (p + 1) & 7);
+      compute(p & 1, p);
+      put((p + 4) & 7, (p + 4) & 7);
+      load(p, j0 + p + PD);
+      if (i == 3) __syncthreads();
+    } else {
+      fetch((p + 1) & 1, (p + 1) & 3);
+      compute(p & 1, p % PD);
+      put((p + 2) % PD, (p + 2) & 3);
+      load(p % PD, j0 + p + PD);
+      __syncthreads();
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int j0 = 0; j0 + 8 <= ks; j0 += 8) {
