@@ -361,8 +361,10 @@ template <int EPI, int MT, int NTW, int NW>
 static void go(const GemmArgs& a, hipStream_t st, Ev ev) {
   // Ring depth per shape, measured: at up to 8 rows (MT 0) one 16-column
   // tile per workgroup streams best 6 k-steps ahead with 4 waves (QKV: 19.2
-  // -> 18.9 us at the 7B shape) and 8 ahead with 8 waves (O, down).
-  constexpr int PD = MT >= 3 ? (NTW == 2 ? 2 : 4) : (NTW == 2 ? 4 : (MT == 0 && NW == 4 ? 6 : 8));
+  // -> 18.9 us at the 7B shape) and 8 ahead with 8 waves (O, down); at 33-64
+  // rows (MT 3-4: O at 40 and 64 rows) 2 ahead (19.8 -> 19.2 us at 64 rows;
+  // 6 and 8 spill).
+  constexpr int PD = MT >= 3 ? 2 : (NTW == 2 ? 4 : (MT == 0 && NW == 4 ? 6 : 8));
   if (ev.a != nullptr || ev.b != nullptr)
     hipExtLaunchKernelGGL((gemm_kernel<MT, NTW, NW, PD, EPI>), dim3(a.n_tiles / NTW), dim3(NW * 64), 0, st, ev.a,
                           ev.b, 0, a);
