@@ -7,7 +7,10 @@
 //    32 columns; each k-step's activation fragments of the block (hi and lo
 //    parts, 8*BM 16-byte units) are staged once in LDS and read by all four
 //    waves, each wave streams its own tiles' weight fragments (2 per tile and
-//    k-step) into a register ring PD k-steps deep;
+//    k-step) into a register ring PD = 8 k-steps deep;
+//  * the k-steps run in supersteps of 4 with one workgroup barrier each: the
+//    next superstep's activations are written during the current one into
+//    the other half of eight LDS buffers;
 //  * per k-step a wave issues 2*MW*NWT MFMAs: for each m-tile and tile, the
 //    two 16-input halves in order, A rows 0-15 carrying the rows' hi parts and
 //    16-31 their lo parts, so hi and lo accumulate apart in one accumulator;
@@ -54,7 +57,7 @@ __device__ __forceinline__ void amax_step32(float& v, int& i) {
 template <int MW, int NWT, int PD, int EPI>
 __global__ __launch_bounds__(kT32Threads) void gemm_tile32_kernel(const GemmArgs a, const int n_chunks,
                                                                   const int n_mblk, const int n_grp) {
-  static_assert(PD == 4 || PD == 8, "ring slots and LDS buffers rotate together");
+  static_assert(PD == 8, "ring slots and LDS buffers rotate together: 8 buffers, supersteps of 4");
   constexpr int NT = kT32Threads, BM = 16 * MW, UA = 8 * BM, UPT = (UA + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // workgroup -> (row block, n-range): XCD = index mod 8, the row blocks of
@@ -68,14 +71,7 @@ __global__ __launch_bounds__(kT32Threads) void gemm_tile32_kernel(const GemmArgs
   const int n32 = a.n_tiles / 2;                 // 32-column tiles
   const int tile0 = (grp * 4 + wave) * NWT;
 
-  // Staged activations: [k-step % NB][part*4 + quad][row], then unused
-  // padding.  With an 8-deep ring the k-steps run in supersteps of 4 (SS):
-  // one barrier per superstep, the next superstep's activations written
-  // during the current one, so NB = 8 buffers; otherwise one barrier per
-  // k-step and NB = 4.
-  constexpr bool SS = PD == 8;
-  constexpr int NB = SS ? 8 : 4;
-  __shared__ u32x4 As[NB][UPT * NT];
+  __shared__ u32x4 As[8][UPT * NT];  // [k-step & 7][part*4 + quad][row], then unused padding
   __shared__ float rs[BM];
 
   const u32x4* wbase[NWT];
@@ -158,43 +154,24 @@ __global__ __launch_bounds__(kT32Threads) void gemm_tile32_kernel(const GemmArgs
   for (int r = tid; r < BM; r += NT) rs[r] = a.rs != nullptr ? a.rs[m0 + mrow0 + min(r, Mb - 1)] : 1.0f;
 
   // Main loop over k-steps j, in unrolled groups of 8 (chunks close between
-  // groups).  Without supersteps: step j's A operands were read from LDS
-  // buffer j & 3 during step j - 1; it reads step j + 1's, runs its MFMAs,
-  // stores A(j + 2) into buffer (j + 2) & 3, refills ring slot j % PD with
-  // k-step j + PD and meets the workgroup at a barrier.  With supersteps of
-  // 4: A(j) sits in buffer j & 7, written during the previous superstep
-  // (from ring slot j % 8, loaded 4 steps before that); step j reads A(j)
-  // first if it opens a superstep, A(j + 1) if the superstep goes on, runs
-  // its MFMAs, stores A(j + 4) into buffer (j + 4) & 7 (last read during the
-  // previous superstep), refills its ring slot with k-step j + 8, and the
-  // superstep's last step meets the workgroup at the barrier.  The MFMAs and
-  // their order are the same either way.
-  if constexpr (SS) {
+  // groups), as supersteps of 4.  A(j) sits in LDS buffer j & 7, written
+  // during the previous superstep (from ring slot j % 8, loaded 4 steps
+  // before that).  Step j reads A(j) first if it opens a superstep and A(j +
+  // 1) if the superstep goes on, runs its MFMAs, stores A(j + 4) into buffer
+  // (j + 4) & 7 (last read during the previous superstep) and refills its
+  // ring slot with k-step j + 8; the superstep's last step meets the
+  // workgroup at the barrier.
 #pragma unroll
-    for (int p = 0; p < 4; ++p) put(p, p);
-    __syncthreads();
-  } else {
-    put(0, 0);
-    put(1, 1);
-    __syncthreads();
-    fetch(0, 0);
-  }
+  for (int p = 0; p < 4; ++p) put(p, p);
+  __syncthreads();
   auto step = [&](int p, int j0) {
-    if constexpr (SS) {
-      const int i = p & 3;  // place in the superstep (j0 is a multiple of 8)
-      if (i == 0) fetch(p & 1, p & 7);
-      if (i < 3) fetch((p + 1) & 1, (p + 1) & 7);
-      compute(p & 1, p);
-      put((p + 4) & 7, (p + 4) & 7);
-      load(p, j0 + p + PD);
-      if (i == 3) __syncthreads();
-    } else {
-      fetch((p + 1) & 1, (p + 1) & 3);
-      compute(p & 1, p % PD);
-      put((p + 2) % PD, (p + 2) & 3);
-      load(p % PD, j0 + p + PD);
-      __syncthreads();
-    }
+    const int i = p & 3;  // place in the superstep (j0 is a multiple of 8)
+    if (i == 0) fetch(p & 1, p & 7);
+    if (i < 3) fetch((p + 1) & 1, (p + 1) & 7);
+    compute(p & 1, p);
+    put((p + 4) & 7, (p + 4) & 7);
+    load(p, j0 + p + PD);
+    if (i == 3) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int j0 = 0; j0 + 8 <= ks; j0 += 8) {
@@ -380,7 +357,7 @@ struct Ev32 {
 
 template <int EPI, int MW, int NWT>
 void go_tile32(const GemmArgs& a, int n_mblk, hipStream_t st, Ev32 ev) {
-  constexpr int PD = MW * NWT >= 6 ? 4 : 8;  // fewer registers for the rings where the k-step is long
+  constexpr int PD = 8;  // with supersteps; 4 at the 70B batch's shapes was slower (gate/up 722 against 670 us)
   const int n32 = a.n_tiles / 2;
   const int n_grp = (n32 + 4 * NWT - 1) / (4 * NWT);
   const int nc = gemm_k_chunks(a.n_tiles);
