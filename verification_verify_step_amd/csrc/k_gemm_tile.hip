@@ -96,7 +96,7 @@ __global__ __launch_bounds__(4 * kScaleRows) void row_scale_kernel(const float* 
     rs[m0 + m] = norm_scale(part[0][r], part[1][r], part[2][r], part[3][r], inv_d, eps);
 }
 
-template <int MW, int NWT, int PD, int EPI, bool SK>
+template <int MW, int NWT, int PD, int EPI, bool SK, bool SS>
 __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs a, const int n_chunks,
                                                                  const int n_mblk, const int n_grp) {
   static_assert(PD % 2 == 0, "the LDS buffer of a k-step is its parity");
@@ -117,7 +117,12 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   const int tile0 = (grp * 4 + wave) * NWT;
   const int mrow = lane & 15, kq = lane >> 4;
 
-  __shared__ u32x4 As[4][UPT * NT];  // [k-step & 3][part*4 + quad][row], then unused padding
+  // Staged activations: [k-step % NB][part*4 + quad][row], then unused
+  // padding.  With supersteps (SS) the k-steps run 4 per barrier, the next
+  // superstep's activations written during the current one: NB = 8.
+  static_assert(!SS || (PD == 8 && !SK), "supersteps need the 8-deep ring and whole-K workgroups");
+  constexpr int NB = SS ? 8 : 4;
+  __shared__ u32x4 As[NB][UPT * NT];
   __shared__ float rs[BM];
 
   const u32x4* wbase[NWT];
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   for (int r = tid; r < BM; r += NT) rs[r] = a.rs != nullptr ? a.rs[m0 + mrow0 + min(r, Mb - 1)] : 1.0f;
 
   // Main loop over the workgroup's k-steps j = 0 .. ns - 1 (k-step c0 + j).
-  // Step j: its A operands were fetched from LDS buffer j & 3 during step
+  // Without supersteps, step j: its A operands were fetched from LDS buffer j & 3 during step
   // j - 1; it fetches step j + 1's, runs its MFMAs, stores A(j + 2) into
   // buffer (j + 2) & 3, refills ring slot j % PD with step j + PD and meets
   // the workgroup at a barrier (so A(j + 2) is visible when step j + 1
@@ -204,17 +209,40 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   // free).  Steps run in unrolled groups of 8; a whole-K workgroup's chunks
   // are multiples of 8 steps (gemm_tile_fits) and close between groups, a
   // K-split workgroup runs one chunk and a guarded tail.
+  // With supersteps of 4: A(j) sits in buffer j & 7, written during the
+  // previous superstep (from ring slot j % 8, loaded 4 steps before that);
+  // step j reads A(j) first if it opens a superstep, A(j + 1) if the
+  // superstep goes on, runs its MFMAs, stores A(j + 4) into buffer (j + 4) &
+  // 7 (last read during the previous superstep), refills its ring slot with
+  // k-step j + 8, and the superstep's last step meets the workgroup at the
+  // barrier.  The MFMAs and their order are the same either way.
   static_assert(PD == 4 || PD == 8, "ring slots and LDS buffers rotate together");
-  put(0, 0);
-  put(1, 1);
-  __syncthreads();
-  fetch(0, 0);
-  auto step = [&](int p, int j0) {
-    fetch((p + 1) & 1, (p + 1) & 3);
-    compute(p & 1, p % PD);
-    put((p + 2) % PD, (p + 2) & 3);
-    load(p % PD, j0 + p + PD);
+  if constexpr (SS) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) put(p, p);
     __syncthreads();
+  } else {
+    put(0, 0);
+    put(1, 1);
+    __syncthreads();
+    fetch(0, 0);
+  }
+  auto step = [&](int p, int j0) {
+    if constexpr (SS) {
+      const int i = p & 3;  // place in the superstep (j0 is a multiple of 8)
+      if (i == 0) fetch(p & 1, p & 7);
+      if (i < 3) fetch((p + 1) & 1, (p + 1) & 7);
+      compute(p & 1, p);
+      put((p + 4) & 7, (p + 4) & 7);
+      load(p, j0 + p + PD);
+      if (i == 3) __syncthreads();
+    } else {
+      fetch((p + 1) & 1, (p + 1) & 3);
+      compute(p & 1, p % PD);
+      put((p + 2) % PD, (p + 2) & 3);
+      load(p % PD, j0 + p + PD);
+      __syncthreads();
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   int j0 = 0;
@@ -457,10 +485,13 @@ struct Ev {
 
 template <int EPI, int MW, int NWT, bool SK>
 void go_tile(const GemmArgs& a, int n_mblk, hipStream_t st, Ev ev) {
-  // fewer registers for the rings where the k-step is long; and a 4-deep
-  // ring for the K-split form, whose workgroups run one chunk (the 7B down
-  // projection at 40 and 64 rows: 35.6 -> 34.8 and 38.8 -> 38.2 us)
-  constexpr int PD = (SK || MW * NWT >= 12) ? 4 : 8;
+  // A 4-deep ring for the K-split form, whose workgroups run one chunk (the
+  // 7B down projection at 40 and 64 rows: 35.6 -> 34.8 and 38.8 -> 38.2 us);
+  // otherwise 8, with supersteps where the k-step is long (12 or more
+  // MFMA tiles per wave: the 70B batch, QKV 223 -> 216 us, down 353 -> 350
+  // us; at 40-64 rows they gained nothing)
+  constexpr int PD = SK ? 4 : 8;
+  constexpr bool SS = !SK && MW * NWT >= 12;
   const int n_grp = (a.n_tiles + 4 * NWT - 1) / (4 * NWT);
   const int nc = gemm_k_chunks(a.n_tiles);
   const dim3 grid(8 * (SK ? nc : 1) * n_mblk * ((n_grp + 7) / 8));
@@ -472,10 +503,10 @@ void go_tile(const GemmArgs& a, int n_mblk, hipStream_t st, Ev ev) {
     g.rs = a.rs_buf;
   }
   if (start != nullptr || ev.b != nullptr)
-    hipExtLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK>), grid, dim3(kTileThreads), 0, st, start, ev.b, 0, g,
+    hipExtLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK, SS>), grid, dim3(kTileThreads), 0, st, start, ev.b, 0, g,
                           nc, n_mblk, n_grp);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK>), grid, dim3(kTileThreads), 0, st, g, nc, n_mblk, n_grp);
+    hipLaunchKernelGGL((gemm_tile_kernel<MW, NWT, PD, EPI, SK, SS>), grid, dim3(kTileThreads), 0, st, g, nc, n_mblk, n_grp);
 }
 
 // Four n-tiles per wave only with up to three m-tiles: beyond that the
