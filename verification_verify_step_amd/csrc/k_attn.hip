@@ -57,8 +57,10 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 // LP: every unit of the pass is one workgroup's and its chunk partials fit
 // kAttnLpRecords records in LDS, where they stay until the combine instead
 // of making a round trip through memory.
+// Two workgroups per CU where the LDS allows it (at most 256 registers per
+// lane); the LP instance holds 128 KB of LDS and runs one.
 template <int HD, int WV, bool LP>
-__global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(WV * 64, LP ? 1 : 2) void attn_kernel(const AttnArgs a) {
   constexpr int kThreads = WV * 64;
   constexpr int KSQ = HD / 32;  // k-steps of S over head dims
   constexpr int NDT = HD / 16;  // 16-dim output tiles
@@ -78,7 +80,10 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   __shared__ float lpo[LP ? kAttnLpRecords * HD : 1];
   __shared__ float2 lml[LP ? kAttnLpRecords : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The wave index is made wave-uniform, so that every per-split decision is
+  // a scalar branch and no K/V wait is merged with a branch's loads: the
+  // compiler then waits for each K/V load alone instead of draining them all.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;  // the grid is exactly the pass's wg_start[n_seq] workgroups
   // Memory round trips before the first scores: (1) every per-sequence field
   // of the arguments at once, lane l holding sequence l's, the workgroup's
@@ -172,25 +177,30 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
         nb0 = __builtin_amdgcn_readlane(bt_w, l);
         nb1 = __builtin_amdgcn_readlane(bt_w, l + 1);
       } else {  // P far from the host's lower bound: read the two entries
-        nb0 = bt[min(base / kBlock, a.kv.bps - 1)];
-        nb1 = bt[min(base / kBlock + 1, a.kv.bps - 1)];
+        // (scalar loads: the constant address space keeps them off the
+        // vector memory counter that the K/V ring's waits count)
+        const auto* cbt = (const __attribute__((address_space(4))) int*)(bt);
+        nb0 = cbt[min(base / kBlock, a.kv.bps - 1)];
+        nb1 = cbt[min(base / kBlock + 1, a.kv.bps - 1)];
       }
     }
   };
-  auto load_k = [&]() {
+  using KBuf = u32x4[2][KSQ];
+  using VBuf = u32x4[NDT];
+  auto load_k = [&](KBuf& kbuf) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint16_t* kr = a.kv.k + kv_tile(t ? nb1 : nb0, kvh, a.Hkv, HD) + k_tile_off(mrow, 8 * kq);
 #pragma unroll
       for (int s = 0; s < KSQ; ++s)
-        kb[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + k_tile_off(0, 32 * s)));
+        kbuf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + k_tile_off(0, 32 * s)));
     }
   };
-  auto load_v = [&]() {  // lane: keys 8*kq .. +8 of dim 16t + lane%16, i.e. block kq/2, keys 8*(kq%2) ..
+  auto load_v = [&](VBuf& vbuf) {  // lane: keys 8*kq .. +8 of dim 16t + lane%16, i.e. block kq/2, keys 8*(kq%2) ..
     const uint16_t* vr = a.kv.v + kv_tile((kq >> 1) ? nb1 : nb0, kvh, a.Hkv, HD) + 8 * (kq & 1);
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
-      vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (size_t)(16 * t + mrow) * kBlock));
+      vbuf[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + (size_t)(16 * t + mrow) * kBlock));
   };
 
   // Round (3): the first K/V step; the queries are split while it is in
@@ -199,8 +209,8 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   split_steps(c0, first, last);
   if (first < last) {
     blocks_of(c0, first);
-    load_k();
-    load_v();
+    load_k(kb);
+    load_v(vb);
   }
   // query fragments (A operand of S), pre-scaled and split hi/lo.  Scores
   // are kept in base-2 units (the scale carries log2 e), so every softmax
@@ -227,111 +237,87 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
   float* pw = smem + wave * QR * PS;
   constexpr int DS = HD / WV;  // dims merged by one wave
 
-  for (int c = c0; c < c1; ++c) {
+  // One step of 32 keys at `base` of this wave's split in chunk c, its K and
+  // V in (kbuf, vbuf): S, then kload() (a later step's K into kbuf), the
+  // masked online-softmax update, O += P.V, then vload().
+  auto run_step = [&](KBuf& kbuf, VBuf& vbuf, const int c, const int base, float(&mrun)[4], float(&lrun)[4],
+                      f32x4(&oacc)[NDT], auto&& kload, auto&& vload) {
     const int sp = c * WV + wave;
     const bool window = sp == ns;
     const int key_lo = window ? wlo : sp * kStep;
     const int key_hi = window ? whi : min(P, sp * kStep + kStep);
-    float mrun[4], lrun[4];
-    f32x4 oacc[NDT];
+    // S = Q.K^T for the two 16-key tiles
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSQ; ++s) {
+        cc = mfma16(qh[s], kbuf[t][s], cc);
+        cc = mfma16(ql[s], kbuf[t][s], cc);
+      }
+      sacc[t] = cc;
+    }
+    kload();
+    // mask, online softmax update, P into the scratch (row, key) layout; a
+    // step of committed keys inside the split needs no mask, and the
+    // accumulators are rescaled only when some factor is not exactly 1
+    const bool full = !window && base >= key_lo && base + kStep <= key_hi;
+    float corr[4];
+    bool same = true;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      mrun[r] = -INFINITY;
-      lrun[r] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int base = first; base < last; base += kStep) {
-      // the next step to load: this split's next one, else the first step
-      // of this wave's split in the next chunk of the workgroup, else this
-      // step again (an L2 hit): the loads are issued on every path, so that
-      // the compiler's waits count them exactly and the next step stays in
-      // flight while this one computes
-      int nbase = base + kStep, nc = c;
-      if (nbase >= last) {
-        nbase = base;
-        if (c + 1 < c1) {
-          int nf, nl;
-          split_steps(c + 1, nf, nl);
-          if (nf < nl) {
-            nbase = nf;
-            nc = c + 1;
-          }
-        }
-      }
-      blocks_of(nc, nbase);
-      // S = Q.K^T for the two 16-key tiles
-      f32x4 sacc[2];
+      const int row = 4 * kq + r;
+      float v[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSQ; ++s) {
-          cc = mfma16(qh[s], kb[t][s], cc);
-          cc = mfma16(ql[s], kb[t][s], cc);
-        }
-        sacc[t] = cc;
-      }
-      load_k();
-      // mask, online softmax update, P into the scratch (row, key) layout; a
-      // step of committed keys inside the split needs no mask, and the
-      // accumulators are rescaled only when some factor is not exactly 1
-      const bool full = !window && base >= key_lo && base + kStep <= key_hi;
-      float corr[4];
-      bool same = true;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * kq + r;
-        float v[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          if (full) {
-            v[t] = sacc[t][r];
-          } else {
-            const int slot = base + 16 * t + mrow;
-            bool vis = slot >= key_lo && slot < key_hi;
-            if (vis && window) {
-              const int rl = min(row, nq - 1) % nr, idx = a.rows.idx_off + rl;
-              const uint64_t mk = a.rows.mask != nullptr ? mraw[r] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
-              vis = row < nq && ((mk >> ((slot - key_lo) & 63)) & 1ull);  // count kept in 0..63
-            }
-            v[t] = vis ? sacc[t][r] : -INFINITY;
+        if (full) {
+          v[t] = sacc[t][r];
+        } else {
+          const int slot = base + 16 * t + mrow;
+          bool vis = slot >= key_lo && slot < key_hi;
+          if (vis && window) {
+            const int rl = min(row, nq - 1) % nr, idx = a.rows.idx_off + rl;
+            const uint64_t mk = a.rows.mask != nullptr ? mraw[r] : (idx >= 63 ? ~0ull : ((2ull << idx) - 1ull));
+            vis = row < nq && ((mk >> ((slot - key_lo) & 63)) & 1ull);  // count kept in 0..63
           }
-        }
-        const float mx = row16_max(fmaxf(v[0], v[1]));
-        const float mnew = fmaxf(mrun[r], mx);
-        corr[r] = (mrun[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mnew);
-        same &= corr[r] == 1.f;
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float p = v[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[t] - mnew);
-          pw[row * PS + 16 * t + mrow] = p;
-          ps += p;
-        }
-        ps = row16_sum(ps);
-        lrun[r] = lrun[r] * corr[r] + ps;
-        mrun[r] = mnew;
-      }
-      if (!__all(same)) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) oacc[t][r] *= corr[r];
-      }
-      // O += P.V (P rows in A-operand order: row = lane%16, keys 8*(lane/16) .. +8)
-      {
-        u32x4 ph, pl;
-        split8(pw + mrow * PS + 8 * kq, ph, pl);
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-          oacc[t] = mfma16(ph, vb[t], oacc[t]);
-          oacc[t] = mfma16(pl, vb[t], oacc[t]);
+          v[t] = vis ? sacc[t][r] : -INFINITY;
         }
       }
-      load_v();
+      const float mx = row16_max(fmaxf(v[0], v[1]));
+      const float mnew = fmaxf(mrun[r], mx);
+      corr[r] = (mrun[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[r] - mnew);
+      same &= corr[r] == 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float p = v[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[t] - mnew);
+        pw[row * PS + 16 * t + mrow] = p;
+        ps += p;
+      }
+      ps = row16_sum(ps);
+      lrun[r] = lrun[r] * corr[r] + ps;
+      mrun[r] = mnew;
     }
-
+    if (!__all(same)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) oacc[t][r] *= corr[r];
+    }
+    // O += P.V (P rows in A-operand order: row = lane%16, keys 8*(lane/16) .. +8)
+    {
+      u32x4 ph, pl;
+      split8(pw + mrow * PS + 8 * kq, ph, pl);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        oacc[t] = mfma16(ph, vbuf[t], oacc[t]);
+        oacc[t] = mfma16(pl, vbuf[t], oacc[t]);
+      }
+    }
+    vload();
+  };
+  auto merge_chunk = [&](const int c, const float(&mrun)[4], const float(&lrun)[4], const f32x4(&oacc)[NDT]) {
     // ---- merge the chunk's WV split partials: every wave puts its (max,
     // sum, o) for the rows below nq in the chunk's merge buffer; after one
     // barrier, wave w merges dims [w*DS, (w+1)*DS) of all WV partials in
@@ -384,6 +370,43 @@ __global__ __launch_bounds__(WV * 64) void attn_kernel(const AttnArgs a) {
         }
       }
     }
+  };
+  auto init_acc = [&](float(&mrun)[4], float(&lrun)[4], f32x4(&oacc)[NDT]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mrun[r] = -INFINITY;
+      lrun[r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  for (int c = c0; c < c1; ++c) {
+    float mrun[4], lrun[4];
+    f32x4 oacc[NDT];
+    init_acc(mrun, lrun, oacc);
+    for (int base = first; base < last; base += kStep) {
+      // the next step to load: this split's next one, else the first step
+      // of this wave's split in the next chunk of the workgroup, else this
+      // step again (an L2 hit): the loads are issued on every path, so that
+      // the compiler's waits count them exactly and the next step stays in
+      // flight while this one computes
+      int nbase = base + kStep, nc = c;
+      if (nbase >= last) {
+        nbase = base;
+        if (c + 1 < c1) {
+          int nf, nl;
+          split_steps(c + 1, nf, nl);
+          if (nf < nl) {
+            nbase = nf;
+            nc = c + 1;
+          }
+        }
+      }
+      blocks_of(nc, nbase);
+      run_step(kb, vb, c, base, mrun, lrun, oacc, [&] { load_k(kb); }, [&] { load_v(vb); });
+    }
+    merge_chunk(c, mrun, lrun, oacc);
     if (c + 1 < c1) split_steps(c + 1, first, last);
   }
   if (single) return;
